@@ -1,0 +1,195 @@
+/*
+ * libkda: the KDA gated delta-rule recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * Each attention head of each sequence carries a fixed fp32 state S of d_k x d_v (rows are
+ * key channels, columns value channels) that every token updates serially
+ * ("Noyaux KDA et FlashKDA", section "Le conflit fondamental"). Per token t:
+ *
+ *     a_t  = exp(max(g_t, g_min))              per key channel; the floor is section
+ *                                              "Le rôle de la décroissance bornée"
+ *     S'   = diag(a_t) S                       decay first,
+ *     S    = S' + beta_t k_t (v_t - S'^T k_t)^T  then the beta-weighted delta correction,
+ *     o_t  = scale * S^T q_t                   then the read-out (sees token t).
+ *
+ * The update order is a reading: the pages never print the equation.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named without a _host suffix are DEVICE pointers (hipMalloc'ed or torch
+ *    tensors); every call is asynchronous on `stream` (a hipStream_t, NULL = the default
+ *    stream) and returns once the kernels are queued.
+ *  - The library never allocates, frees or synchronises. Callers own every buffer.
+ *  - Tensors are dense, row-major, with the shapes given below; all pointers must be 16-byte
+ *    aligned.
+ *  - States are stored head-contiguous, [.., H, d_k, d_v], so each head is one contiguous
+ *    byte range ("Inférence : cache KV, décodage, quantification", section on prefill/decode
+ *    disaggregation).
+ *  - Every argument is validated on the host BEFORE anything is launched; on error nothing
+ *    is launched, no output is touched and a negative kda_status is returned. Validation
+ *    makes no HIP call. Device-side values (cu_seqlens on the device, n_acc) are trusted to
+ *    match their host description; n_acc is clamped into range on the device.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 1
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL_ARG = -1,            /* a required pointer is NULL */
+  KDA_ERR_BAD_SHAPE = -2,           /* a size is out of range or inconsistent */
+  KDA_ERR_BAD_DTYPE = -3,           /* io_dtype is not a kda_dtype */
+  KDA_ERR_MISALIGNED = -4,          /* a pointer is not 16-byte aligned */
+  KDA_ERR_BAD_SEQLENS = -5,         /* cu_seqlens_host not 0-based, non-decreasing, ending at T */
+  KDA_ERR_WORKSPACE_TOO_SMALL = -6, /* workspace_bytes below kda_segment_cp_workspace_size */
+  KDA_ERR_UNSUPPORTED = -7,         /* valid but not implemented (d_k, d_v, dtype combination) */
+  KDA_ERR_LAUNCH_FAILED = -8,       /* the HIP runtime rejected a launch */
+  KDA_ERR_ALIASING = -9,            /* an output overlaps an input it must not overlap */
+  KDA_ERR_BAD_VALUE = -10           /* a scalar is out of range (g_min, eps, scale not finite) */
+} kda_status;
+
+typedef enum kda_dtype {
+  KDA_F32 = 0,  /* IEEE binary32 */
+  KDA_BF16 = 1  /* bfloat16 */
+} kda_dtype;
+
+/*
+ * kda_chunk_fwd: chunked prefill of the recurrence over one or several packed sequences
+ * ("Noyaux KDA et FlashKDA", section "FlashKDA : le noyau par blocs": parallel inside a
+ * 64-token chunk, serial across chunks; AMD blog "Dentro de los esfuerzos de optimización de
+ * Kimi K3", "Nota técnica: Precisión del KDA y memoria on-chip": per-chunk inverse of the
+ * unit lower-triangular dependency matrix in fp32, rounded to bf16 only once complete).
+ *
+ *   q, k     [T_total, H, d_k]  io_dtype
+ *   v        [T_total, H, d_v]  io_dtype
+ *   g        [T_total, H, d_k]  fp32 log-decay per key channel (floored at g_min inside)
+ *   beta     [T_total, H]       fp32
+ *   h0       [N, H, d_k, d_v]   fp32 entering state per sequence, or NULL for zeros
+ *   o        [T_total, H, d_v]  out_dtype output: KDA_F32, or io_dtype (written once; a bf16
+ *                               output is the round-to-nearest-even of the fp32 result)
+ *   ht       [N, H, d_k, d_v]   fp32 final state per sequence, or NULL to skip it
+ *
+ * Sequences: with cu_seqlens == cu_seqlens_host == NULL there are N = batch sequences of
+ * seq_len tokens each, T_total = batch * seq_len (a [batch, seq_len, H, d] tensor).
+ * Otherwise batch must be 1, both cu_seqlens (device) and cu_seqlens_host (host copy of the
+ * same N + 1 int32 offsets) are given, N = n_seqs and T_total = seq_len = cu_seqlens_host[N].
+ * Chunks restart at every sequence start; a sequence of length 0 copies h0 to ht.
+ *
+ * Supported: io_dtype KDA_BF16 with d_k = d_v in {64, 128}; KDA_F32 with d_k = d_v = 64.
+ * g_min must lie in [-5.4, 0] (the in-chunk exponent range stays finite in fp32);
+ * g values above 0 are accepted but are not decays. o must not overlap any input; ht may
+ * alias h0 (in-place state update).
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                  int num_heads, int d_k, int d_v, int io_dtype, int out_dtype, float scale,
+                  float g_min, void* o, float* ht, void* stream);
+
+/*
+ * Bytes of device workspace kda_segment_cp_fwd needs for the given sizes (n_segments = 0
+ * asks for the automatic choice). Returns KDA_OK and writes *bytes, or a negative status.
+ */
+int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v,
+                                  int n_segments, size_t* bytes);
+
+/*
+ * kda_segment_cp_fwd: segment-parallel prefill for few heads over long sequences
+ * ("Noyaux KDA et FlashKDA", section "Le parallélisme de contexte intra-appareil"; AMD blog
+ * section 5: group summaries, ordered scan, parallel replay).
+ *
+ * Same tensors, conventions and supported sizes as kda_chunk_fwd. Every sequence is cut into
+ * up to n_segments contiguous, chunk-aligned segments (n_segments = 0: automatic, otherwise
+ * 1..256). Three launches on `stream`: (1) each segment's affine summary (P, Q) with
+ * S_out = P S_in + Q, computed without its entering state; (2) an ordered scan that composes
+ * the summaries into every segment's exact entering state and the final state; (3) all
+ * segments replay their tokens in parallel from those states. The result equals
+ * kda_chunk_fwd up to rounding. `workspace` is device memory of at least
+ * kda_segment_cp_workspace_size(...) bytes, owned by the caller; its contents on entry are
+ * ignored.
+ */
+int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* h0, const int32_t* cu_seqlens,
+                       const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                       int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
+                       float scale, float g_min, void* o, float* ht, int n_segments,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One window of cached projected inputs for decode: raw (pre-convolution, pre-activation)
+ * per-token projections, all bf16, each [R, slots, H, .]. z is the output-gate input and is
+ * only read for the current window (it may be NULL in the previous one).
+ */
+typedef struct kda_token_window {
+  const void* q;     /* [R, slots, H, d_k] */
+  const void* k;     /* [R, slots, H, d_k] */
+  const void* v;     /* [R, slots, H, d_v] */
+  const void* g;     /* [R, slots, H, d_k] raw decay gate; g = max(-softplus(raw), g_min) */
+  const void* beta;  /* [R, slots, H]      raw; beta = sigmoid(raw) */
+  const void* z;     /* [R, slots, H, d_v] raw output gate; sigmoid(z) scales the output */
+  int slots;
+} kda_token_window;
+
+/*
+ * kda_decode_replay: fused speculative-verify decode ("Noyaux d'inférence", section
+ * "1. Le décodage KDA": cache only projected inputs, replay accepted drafts on chip instead
+ * of snapshotting S, one loop over replayed, bonus and draft tokens fused with short
+ * convolution, input normalisation, gating and output normalisation; AMD blog section 3:
+ * one launch that writes straight to the destination buffer; section 5: tiles own disjoint
+ * value columns and walk the same tokens in order).
+ *
+ * Per request r and head h, starting from the committed state state[r, h] (the state after
+ * the previous call's bonus token) and conv_tail[r, h]:
+ *   1. replay slots 1 .. n_acc[r] of `prev` (the accepted drafts of the previous window;
+ *      slot 0 was the previous bonus, already committed): no output;
+ *   2. state_acc[r, h] <- S (skipped when state_acc is NULL);
+ *   3. slot 0 of `cur` (the bonus token), output o[r, 0, h]; state[r, h] <- S and
+ *      conv_tail[r, h] <- tail (the new committed values);
+ *   4. slots 1 .. n_new - 1 of `cur` (the next draft window), outputs o[r, j, h]; their
+ *      states are never written.
+ * Each token: depthwise causal convolution of width conv_width over the raw q, k, v
+ * channels with the tail of the last conv_width - 1 raw inputs; SiLU if act == 1;
+ * q and k scaled by 1 / sqrt(sum x^2 + eps_l2); beta = sigmoid; g = max(-softplus, g_min);
+ * the recurrence step above; o = scale * S^T q, then o * rsqrt(mean(o^2) + eps_rms) *
+ * norm_w * sigmoid(z). The token step is one code path with a fixed operation order, so a
+ * replayed state is bit-identical to the state the same tokens reach one launch at a time.
+ *
+ *   n_acc      [R] int32 device, clamped to [0, prev->slots - 1]
+ *   conv_w     [H, 2 d_k + d_v, conv_width] fp32, channel order q, k, v; tap conv_width - 1
+ *              multiplies the current token
+ *   norm_w     [d_v] fp32, shared by all heads
+ *   state      [R, H, d_k, d_v] fp32, read then overwritten in place with S after the bonus
+ *   state_acc  [R, H, d_k, d_v] fp32 or NULL; must not overlap state
+ *   conv_tail  [R, H, 2 d_k + d_v, conv_width - 1] fp32, oldest first, updated in place
+ *   o          [R, n_new, H, d_v] bf16
+ *
+ * Supported: d_k = d_v = 128 or 64, conv_width in 1..4, 1 <= n_new <= cur->slots,
+ * prev->slots in 1..16, act in {0, 1}, eps_l2 > 0, eps_rms >= 0.
+ */
+int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_width,
+                      int n_new, const int32_t* n_acc, const kda_token_window* prev,
+                      const kda_token_window* cur, const float* conv_w, const float* norm_w,
+                      float scale, float g_min, float eps_l2, float eps_rms, int act,
+                      float* state, float* state_acc, float* conv_tail, void* o,
+                      void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(int status);
+
+/* KDA_VERSION of the built library. */
+int kda_version(void);
+
+/* The hipError_t of the last failed launch in this thread (0 if none). */
+int kda_last_launch_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

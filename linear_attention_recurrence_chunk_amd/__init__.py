@@ -1,0 +1,259 @@
+"""Python binding of libkda (the KDA gated delta-rule recurrence on MI355X).
+
+Argument marshalling only: torch tensors are turned into device pointers and the current
+HIP stream, and every step runs in the library's HIP kernels. There is no fallback: if
+libkda.so is missing or fails to load, every call raises.
+
+Entry points mirror include/kda.h: ``chunk_fwd``, ``segment_cp_fwd``,
+``segment_cp_workspace_size``, ``decode_replay``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["KDAError", "library", "library_path", "chunk_fwd", "segment_cp_fwd",
+           "segment_cp_workspace_size", "decode_replay", "status_string", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+KDA_F32 = 0
+KDA_BF16 = 1
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: libkda status {status} ({status_string(status)})")
+
+
+class TokenWindow(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("slots", ctypes.c_int)]
+
+
+def library_path():
+    return os.path.join(_HERE, "libkda.so")
+
+
+def library():
+    """Load libkda.so (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkda.so not found at {path}: build it with "
+                           "`python -m linear_attention_recurrence_chunk_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, P]
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_segment_cp_workspace_size.restype = I
+    lib.kda_segment_cp_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P,
+                                       P, I, P, ctypes.c_size_t, P]
+    lib.kda_segment_cp_fwd.restype = I
+    lib.kda_decode_replay.argtypes = [I, I, I, I, I, I, P, ctypes.POINTER(TokenWindow),
+                                      ctypes.POINTER(TokenWindow), P, P, F, F, F, F, I, P, P, P,
+                                      P, P]
+    lib.kda_decode_replay.restype = I
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.restype = I
+    lib.kda_last_launch_error.restype = I
+    _LIB = lib
+    return lib
+
+
+def status_string(status):
+    try:
+        return library().kda_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "unknown"
+
+
+def version():
+    return int(library().kda_version())
+
+
+# ------------------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise ValueError(f"unsupported io dtype {t.dtype}")
+
+
+def _out_dtype(q, out_dtype):
+    torch = _torch()
+    if out_dtype is None:
+        return q.dtype
+    if out_dtype in (torch.float32, "f32", "float32"):
+        return torch.float32
+    if out_dtype in (torch.bfloat16, "bf16", "bfloat16"):
+        return torch.bfloat16
+    raise ValueError(f"unsupported out_dtype {out_dtype}")
+
+
+def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype):
+    torch = _torch()
+    if q.dim() == 4:                 # [B, T, H, d]
+        batch, seq_len, H, dk = q.shape
+    elif q.dim() == 3:               # [T, H, d]
+        batch, (seq_len, H, dk) = 1, q.shape
+    else:
+        raise ValueError("q must be [B, T, H, d_k] or [T, H, d_k]")
+    dv = v.shape[-1]
+    dev = q.device
+    io = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, io, dev)
+    _check(g, "g", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(h0, "h0", torch.float32, dev)
+    cu_dev = cu_host = None
+    if cu_seqlens is not None:
+        if batch != 1:
+            raise ValueError("cu_seqlens needs batch 1")
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
+        n_seqs = cu_host.numel() - 1
+    else:
+        n_seqs = batch
+    odt = _out_dtype(q, out_dtype) if o is None else o.dtype
+    if o is None:
+        o = torch.empty(*q.shape[:-1], dv, dtype=odt, device=dev)
+    _check(o, "o", odt, dev)
+    if ht is None and output_final_state:
+        ht = torch.empty(n_seqs, H, dk, dv, dtype=torch.float32, device=dev)
+    _check(ht, "ht", torch.float32, dev)
+    return dict(batch=batch, seq_len=seq_len, H=H, dk=dk, dv=dv, io=_io_dtype(q), out=_io_dtype(o),
+                cu_dev=cu_dev, cu_host=cu_host, n_seqs=n_seqs, o=o, ht=ht)
+
+
+def _cu_host_ptr(cu_host):
+    return None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+
+
+# ------------------------------------------------------------------------------ entry points
+def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0, o=None,
+              ht=None, output_final_state=True, out_dtype=None, stream=None):
+    """kda_chunk_fwd. q, k: [B, T, H, d_k] or packed [T, H, d_k]; v: [.., d_v];
+    g: same shape as k (fp32); beta: [.., H] (fp32); h0: [N, H, d_k, d_v] fp32 or None;
+    cu_seqlens: [N + 1] int32 (any device) for packed varlen input; out_dtype: None (same as
+    q) or torch.float32. Returns (o, ht)."""
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
+    st = library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
+        _cu_host_ptr(a["cu_host"]), a["batch"], a["seq_len"] if a["cu_dev"] is None
+        else int(a["cu_host"][-1]), a["n_seqs"], a["H"], a["dk"], a["dv"], a["io"], a["out"],
+        float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd")
+    return a["o"], a["ht"]
+
+
+def segment_cp_workspace_size(n_seqs, H, dk, dv, n_segments=0):
+    out = ctypes.c_size_t(0)
+    st = library().kda_segment_cp_workspace_size(int(n_seqs), int(H), int(dk), int(dv),
+                                                  int(n_segments), ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_segment_cp_workspace_size")
+    return int(out.value)
+
+
+def segment_cp_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
+                   n_segments=0, workspace=None, o=None, ht=None, output_final_state=True,
+                   out_dtype=None, stream=None):
+    """kda_segment_cp_fwd (same tensors as chunk_fwd). ``workspace`` is a uint8 device
+    tensor of at least segment_cp_workspace_size(...) bytes; allocated here if None."""
+    torch = _torch()
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
+    need = segment_cp_workspace_size(a["n_seqs"], a["H"], a["dk"], a["dv"], n_segments)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = library().kda_segment_cp_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
+        _cu_host_ptr(a["cu_host"]), a["batch"], a["seq_len"] if a["cu_dev"] is None
+        else int(a["cu_host"][-1]), a["n_seqs"], a["H"], a["dk"], a["dv"], a["io"], a["out"],
+        float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]), int(n_segments),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_segment_cp_fwd")
+    return a["o"], a["ht"]
+
+
+def _window(win, slots):
+    return TokenWindow(_ptr(win["q"]), _ptr(win["k"]), _ptr(win["v"]), _ptr(win["g"]),
+                       _ptr(win["beta"]), _ptr(win.get("z")), int(slots))
+
+
+def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None, scale=1.0,
+                  g_min=-5.0, eps_l2=1e-6, eps_rms=1e-6, act=1, state_acc=None, o=None,
+                  write_state_acc=True, stream=None):
+    """kda_decode_replay. ``state`` [R, H, d_k, d_v] and ``conv_tail`` are updated in place;
+    prev / new are dicts of bf16 tensors q, k, v, g, beta (and z for new), each
+    [R, slots, H, ...]. Returns (o [R, n_new, H, d_v] bf16, state_acc or None)."""
+    torch = _torch()
+    R, H, dk, dv = state.shape
+    dev = state.device
+    conv_width = conv_w.shape[-1]
+    if n_new is None:
+        n_new = new["q"].shape[1]
+    _check(state, "state", torch.float32, dev)
+    _check(conv_tail, "conv_tail", torch.float32, dev)
+    _check(conv_w, "conv_w", torch.float32, dev)
+    _check(norm_w, "norm_w", torch.float32, dev)
+    _check(n_acc, "n_acc", torch.int32, dev)
+    for win, nm in ((prev, "prev"), (new, "new")):
+        for key in ("q", "k", "v", "g", "beta", "z"):
+            if win.get(key) is not None:
+                _check(win[key], f"{nm}.{key}", torch.bfloat16, dev)
+    if state_acc is None and write_state_acc:
+        state_acc = torch.empty_like(state)
+    _check(state_acc, "state_acc", torch.float32, dev)
+    if o is None:
+        o = torch.empty(R, n_new, H, dv, dtype=torch.bfloat16, device=dev)
+    _check(o, "o", torch.bfloat16, dev)
+    pw = _window(prev, prev["q"].shape[1])
+    nw = _window(new, new["q"].shape[1])
+    st = library().kda_decode_replay(
+        R, H, dk, dv, conv_width, int(n_new), _ptr(n_acc), ctypes.byref(pw), ctypes.byref(nw),
+        _ptr(conv_w), _ptr(norm_w), float(scale), float(g_min), float(eps_l2), float(eps_rms),
+        int(act), _ptr(state), _ptr(state_acc), _ptr(conv_tail), _ptr(o), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_decode_replay")
+    return o, state_acc

@@ -1,0 +1,563 @@
+// Chunked KDA prefill on gfx950.
+//
+// Method ("Noyaux KDA et FlashKDA", sections "FlashKDA : le noyau par blocs" and "Le rôle de
+// la décroissance bornée"; AMD blog "Dentro de los esfuerzos de optimización de Kimi K3",
+// "Nota técnica: Precisión del KDA y memoria on-chip"). For a chunk of C = 64 tokens entering
+// with state S (d_k x d_v), with Gamma the in-chunk cumulative floored log-decay per key
+// channel:
+//   A[r,s] = beta_r sum_i k[r,i] k[s,i] e^{Gamma[r,i]-Gamma[s,i]}   (s < r)
+//   T      = (I + A)^{-1}                      fp32, unit lower triangular
+//   U      = T diag(beta) (V - (K * e^Gamma) S)
+//   M[r,s] = sum_i q[r,i] k[s,i] e^{Gamma[r,i]-Gamma[s,i]}        (s <= r)
+//   O      = scale ((Q * e^Gamma) S + M U)
+//   S     <- diag(e^{Gamma_L}) S + (K * e^{Gamma_L - Gamma})^T U
+// (U is the chunk's block of beta-weighted delta errors; applying T to V - K_Gamma S keeps
+// the prediction error in fp32 before the triangular solve.)
+//
+// Exponent safety: e^{Gamma_r - Gamma_s} is never formed as e^{Gamma_r} e^{-Gamma_s} over the
+// whole chunk (that overflows fp32). The chunk is cut into four 16-token sub-blocks. Row
+// operands are referenced to the start of their sub-block (rho = e^{lambda} <= 1), column
+// operands to its end (kappa <= 1); the gap between two sub-blocks is a per-channel product
+// of whole-sub-block decays (<= 1). Inside a diagonal sub-block the column operand is k / rho,
+// at most e^{16 |g_min|}: the floor keeps it finite, which is what lets every causal tile,
+// diagonal ones included, run as a dense matrix product.
+//
+// Precision. The inverse is fp32 end to end (fp32 inputs, fp32 16x16x4 MFMA accumulation)
+// and rounded only once complete. The model's outputs are heavy-tailed (a read-out is a sum
+// of products of near-Gaussian factors, max |o| ~ 10-30 x RMS), so a single bf16 rounding of
+// a dominant factor would cost up to ~2.5% of the output RMS. Every factor on the dominant
+// paths (T diag(beta), the diagonal blocks of M and their operands, M, U, V - K_Gamma S,
+// Q e^Gamma, S in the read-out, K e^{Gamma_L - Gamma}) is therefore carried as a hi + lo pair
+// of bf16 values and multiplied with three bf16 MFMAs (hi*hi + lo*hi + hi*lo): ~16 mantissa
+// bits on matrix cores at 3/16 of the cost of fp32 MFMA.
+//
+// Work decomposition: one workgroup (4 waves) per (sequence, head, 64-wide value tile).
+// Value columns of S never mix, so each wave owns 16 columns of S in its MFMA accumulators
+// for the whole sequence (the state never leaves registers between chunks). The four waves
+// share the per-chunk prologue through LDS.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <class Pol, int DK>
+struct ChunkLayout {
+  using E = typename Pol::E;
+  static constexpr int kPadE = sizeof(E) == 2 ? 8 : 4;
+  static constexpr int LDP = DK + kPadE;   // row-major [64 tokens][DK] tiles
+  static constexpr int LDT = 64 + kPadE;   // [rows][64 tokens] tiles
+  static constexpr int LDA = 64 + 4;       // fp32 A / T working matrix
+  static constexpr int kLo = Pol::kSplit ? 1 : 0;
+  static constexpr size_t tP = size_t(64) * LDP * sizeof(E);
+  static constexpr size_t tT = size_t(DK) * LDT * sizeof(E);
+  static constexpr size_t t64 = size_t(64) * LDT * sizeof(E);
+  // ---- region X, prologue view: q rho (hi, lo), k / rho (hi, lo), k rho, k kappa
+  static constexpr size_t oQr = 0;
+  static constexpr size_t oQrLo = oQr + tP;
+  static constexpr size_t oKd = oQrLo + kLo * tP;
+  static constexpr size_t oKdLo = oKd + tP;
+  static constexpr size_t oKr = oKdLo + kLo * tP;
+  static constexpr size_t oKc = oKr + tP;
+  static constexpr size_t kXA = oKc + tP;
+  // ---- region X, recurrence view: Q e^Gamma (hi, lo), (K e^{GL-Gamma})^T (hi, lo),
+  //      K e^Gamma, T diag(beta) (hi, lo)
+  static constexpr size_t oQg = 0;
+  static constexpr size_t oQgLo = oQg + tP;
+  static constexpr size_t oKhT = oQgLo + kLo * tP;
+  static constexpr size_t oKhTLo = oKhT + tT;
+  static constexpr size_t oKg = oKhTLo + kLo * tT;
+  static constexpr size_t oT = oKg + tP;
+  static constexpr size_t oTLo = oT + t64;
+  static constexpr size_t kXD = oTLo + kLo * t64;
+  static constexpr size_t kX = kXA > kXD ? kXA : kXD;
+  // ---- region Y: fp32 A / T, later V^T of the value tile
+  static constexpr size_t oA = kX;
+  static constexpr size_t oVT = kX;
+  static constexpr size_t kY = size_t(64) * LDA * 4 > t64 ? size_t(64) * LDA * 4 : t64;
+  // ---- region Z: M (hi, lo)
+  static constexpr size_t oM = oA + kY;
+  static constexpr size_t oMLo = oM + t64;
+  // ---- small
+  static constexpr size_t oBeta = oMLo + kLo * t64;
+  static constexpr size_t oBP = oBeta + 64 * 4;        // [4][DK] sub-block decay products
+  static constexpr size_t oDecay = oBP + 4 * DK * 4;   // [DK] whole-chunk decay
+  static constexpr size_t oPair = oDecay + DK * 4;     // [3][DK] gaps between sub-blocks
+  static constexpr size_t kBytes = oPair + 3 * DK * 4;
+  static_assert(kBytes <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
+};
+
+template <class Pol>
+__device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E* lo, int idx,
+                                            float x) {
+  using E = typename Pol::E;
+  const E h = from_f32<E>(x);
+  hi[idx] = h;
+  if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(x - to_f32(h));
+}
+
+// single-task descriptors of the prologue products: 10 blocks of A, 6 off-diagonal of M
+__constant__ int kTaskI[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 1, 2, 2, 3, 3, 3};
+__constant__ int kTaskJ[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 0, 0, 1, 0, 1, 2};
+
+template <class Pol, typename Tio, typename Tout, int DK>
+__global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
+  using L = ChunkLayout<Pol, DK>;
+  using E = typename Pol::E;
+  using Frag = typename Pol::Frag;
+  constexpr int CPT = DK / 64;             // key channels per thread in the prologue
+  constexpr int NS = Pol::slices(DK);      // k-slices over key channels
+  constexpr int NT = Pol::slices(64);      // k-slices over the chunk's tokens
+  constexpr int NTD = DK / 16;             // 16-row tiles of S per wave
+  constexpr int VT = 64;
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  E* sQr = reinterpret_cast<E*>(smem + L::oQr);
+  E* sQrLo = reinterpret_cast<E*>(smem + L::oQrLo);
+  E* sKd = reinterpret_cast<E*>(smem + L::oKd);
+  E* sKdLo = reinterpret_cast<E*>(smem + L::oKdLo);
+  E* sKr = reinterpret_cast<E*>(smem + L::oKr);
+  E* sKc = reinterpret_cast<E*>(smem + L::oKc);
+  E* sQg = reinterpret_cast<E*>(smem + L::oQg);
+  E* sQgLo = reinterpret_cast<E*>(smem + L::oQgLo);
+  E* sKhT = reinterpret_cast<E*>(smem + L::oKhT);
+  E* sKhTLo = reinterpret_cast<E*>(smem + L::oKhTLo);
+  E* sKg = reinterpret_cast<E*>(smem + L::oKg);
+  E* sT = reinterpret_cast<E*>(smem + L::oT);
+  E* sTLo = reinterpret_cast<E*>(smem + L::oTLo);
+  float* sA = reinterpret_cast<float*>(smem + L::oA);
+  E* sVT = reinterpret_cast<E*>(smem + L::oVT);
+  E* sM = reinterpret_cast<E*>(smem + L::oM);
+  E* sMLo = reinterpret_cast<E*>(smem + L::oMLo);
+  float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
+  float* sBP = reinterpret_cast<float*>(smem + L::oBP);
+  float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
+  float* sPair = reinterpret_cast<float*>(smem + L::oPair);
+
+  // ---- which (sequence, head, value tile): value tiles of one unit share an XCD
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int rest = b >> 3;
+  const int vt = rest % p.n_vt;
+  const int unit = (rest / p.n_vt) * 8 + xcd;
+  if (unit >= p.n_units) return;
+  const int n = unit / p.H;
+  const int h = unit % p.H;
+  const int H = p.H;
+  const int DV = p.dv;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int q4 = lane >> 4;   // k-group of the lane inside an MFMA fragment
+  const int ln = lane & 15;   // row / column of the lane inside a 16x16 tile
+
+  int bos, eos;
+  if (p.cu_seqlens) {
+    bos = p.cu_seqlens[n];
+    eos = p.cu_seqlens[n + 1];
+  } else {
+    bos = n * p.seq_len;
+    eos = bos + p.seq_len;
+  }
+
+  const Tio* __restrict__ gq = reinterpret_cast<const Tio*>(p.q);
+  const Tio* __restrict__ gk = reinterpret_cast<const Tio*>(p.k);
+  const Tio* __restrict__ gv = reinterpret_cast<const Tio*>(p.v);
+  Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
+  const int col0 = vt * VT + 16 * w;   // first value column owned by this wave
+
+  // ---- entering state in accumulator layout: tile t, register e = row 16t + 4 q4 + e
+  f32x4 S[NTD];
+#pragma unroll
+  for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * t + 4 * q4 + e;
+      S[t][e] = p.h0 ? p.h0[((size_t(n) * H + h) * DK + c) * DV + col0 + ln] : 0.f;
+    }
+  }
+
+  // strictly upper sub-blocks of M stay zero for the whole sequence
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, s = idx & 63;
+    if ((s >> 4) > (r >> 4)) {
+      sM[r * L::LDT + s] = from_f32<E>(0.f);
+      if constexpr (Pol::kSplit) sMLo[r * L::LDT + s] = from_f32<E>(0.f);
+    }
+  }
+
+  for (int cstart = bos; cstart < eos; cstart += kChunk) {
+    const int Lc = min(kChunk, eos - cstart);
+
+    // ================= prologue 0: loads (all issued up front) ==========================
+    // thread (sub-block w, channels CPT*lane ..): 16 tokens of its sub-block
+    float gg[16][CPT], kk[16][CPT], qq[16][CPT], vv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int r = 16 * w + t;
+      const int tok = cstart + (r < Lc ? r : 0);
+      const size_t base = (size_t(tok) * H + h) * DK + CPT * lane;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        gg[t][cc] = p.g[base + cc];
+        kk[t][cc] = to_f32(gk[base + cc]);
+        qq[t][cc] = to_f32(gq[base + cc]);
+      }
+      vv[t] = to_f32(gv[(size_t(tok) * H + h) * DV + vt * VT + lane]);
+    }
+    float beta_r = 0.f;
+    if (lane < 16) {
+      const int r = 16 * w + lane;
+      beta_r = p.beta[size_t(cstart + (r < Lc ? r : 0)) * H + h];
+      if (r >= Lc) beta_r = 0.f;
+    }
+
+    // ================= prologue 1: decay factors and operand tiles ======================
+    // rho = e^{lambda} (decay from the sub-block start to token r, inclusive) <= 1;
+    // kappa = P / rho (decay after token r to the sub-block end) <= 1; 1/rho <= e^{16|g_min|}
+    float bp[CPT], rho[16][CPT];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) bp[cc] = 1.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const bool valid = 16 * w + t < Lc;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const float gt = valid ? fmaxf(gg[t][cc], p.g_min) : 0.f;
+        if (!valid) {
+          kk[t][cc] = 0.f;
+          qq[t][cc] = 0.f;
+        }
+        bp[cc] *= __expf(gt);
+        rho[t][cc] = bp[cc];
+      }
+      if (!valid) vv[t] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int r = 16 * w + t;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const int c = CPT * lane + cc;
+        const float rinv = 1.f / rho[t][cc];
+        const float kap = bp[cc] * rinv;
+        const float k0 = kk[t][cc];
+        const float qr = qq[t][cc] * rho[t][cc];
+        const int idx = r * L::LDP + c;
+        store_split<Pol>(sQr, sQrLo, idx, qr);
+        store_split<Pol>(sKd, sKdLo, idx, k0 * rinv);
+        sKr[idx] = from_f32<E>(k0 * rho[t][cc]);
+        sKc[idx] = from_f32<E>(k0 * kap);
+        qq[t][cc] = qr;                  // q rho
+        gg[t][cc] = k0 * kap;            // k kappa
+        kk[t][cc] = k0 * rho[t][cc];     // k rho
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) sBP[w * DK + CPT * lane + cc] = bp[cc];
+    if (lane < 16) sBeta[16 * w + lane] = beta_r;
+    __syncthreads();
+
+    // ---- chunk-level factors from the four sub-block products of each channel
+    float fs[CPT], fe[CPT];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int c = CPT * lane + cc;
+      const float Pb[4] = {sBP[c], sBP[DK + c], sBP[2 * DK + c], sBP[3 * DK + c]};
+      fs[cc] = 1.f;
+      fe[cc] = 1.f;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        if (bb < w) fs[cc] *= Pb[bb];
+        if (bb > w) fe[cc] *= Pb[bb];
+      }
+      if (w == 0) {
+        sDecay[c] = Pb[0] * Pb[1] * Pb[2] * Pb[3];
+        sPair[c] = Pb[1];               // gap for sub-block pair (2, 0)
+        sPair[DK + c] = Pb[2];          // (3, 1)
+        sPair[2 * DK + c] = Pb[1] * Pb[2];  // (3, 0)
+      }
+    }
+    __syncthreads();
+
+    // ================= prologue 2: A (fp32) and M (hi, lo) sub-blocks ====================
+    {
+      // diagonal block w of M from split operands (the largest entries of M)
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int pp = 0; pp < NS; ++pp) {
+        const int rowq = 16 * w + ln;
+        const Frag bh = Pol::load(sQr, L::LDP, rowq, pp, q4);
+        const Frag ah = Pol::load(sKd, L::LDP, rowq, pp, q4);
+        acc = Pol::mma(ah, bh, acc);
+        if constexpr (Pol::kSplit) {
+          acc = Pol::mma(Pol::load(sKdLo, L::LDP, rowq, pp, q4), bh, acc);
+          acc = Pol::mma(ah, Pol::load(sQrLo, L::LDP, rowq, pp, q4), acc);
+        }
+      }
+      // register e: row r = 16 w + ln, column s = 16 w + 4 q4 + e
+      const int r = 16 * w + ln;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * w + 4 * q4 + e;
+        store_split<Pol>(sM, sMLo, r * L::LDT + s, s > r ? 0.f : acc[e]);
+      }
+    }
+#pragma unroll 1
+    for (int task = 4 * w; task < 4 * w + 4; ++task) {
+      const bool isM = task >= 10;
+      const int bi = kTaskI[task], bj = kTaskJ[task];
+      const E* rowt = isM ? sQr : sKr;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int pp = 0; pp < NS; ++pp) {
+        const Frag bfr = Pol::load(rowt, L::LDP, 16 * bi + ln, pp, q4);
+        Frag afr;
+        if (bi == bj) {
+          afr = Pol::load(sKd, L::LDP, 16 * bj + ln, pp, q4);
+        } else if (bi - bj == 1) {
+          afr = Pol::load(sKc, L::LDP, 16 * bj + ln, pp, q4);
+        } else {
+          const int pi = (bi == 2) ? 0 : (bj == 1 ? 1 : 2);
+          afr = Pol::load_scaled(sKc, L::LDP, 16 * bj + ln, pp, q4, sPair + pi * DK);
+        }
+        acc = Pol::mma(afr, bfr, acc);
+      }
+      // register e: row r = 16 bi + ln, column s = 16 bj + 4 q4 + e
+      const int r = 16 * bi + ln;
+      if (!isM) {
+        const float br = sBeta[r];
+        f32x4 outv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * bj + 4 * q4 + e;
+          outv[e] = (bi == bj && s >= r) ? 0.f : br * acc[e];
+        }
+        *reinterpret_cast<f32x4*>(sA + r * L::LDA + 16 * bj + 4 * q4) = outv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          store_split<Pol>(sM, sMLo, r * L::LDT + 16 * bj + 4 * q4 + e, acc[e]);
+      }
+    }
+    __syncthreads();
+
+    // ================= prologue 3: recurrence operand tiles; fp32 inverse =================
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int r = 16 * w + t;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        const int c = CPT * lane + cc;
+        store_split<Pol>(sQg, sQgLo, r * L::LDP + c, qq[t][cc] * fs[cc]);   // q e^Gamma
+        store_split<Pol>(sKhT, sKhTLo, c * L::LDT + r, gg[t][cc] * fe[cc]); // k e^{GL-Gamma}
+        sKg[r * L::LDP + c] = from_f32<E>(kk[t][cc] * fs[cc]);              // k e^Gamma
+      }
+    }
+    if (w == 0) {
+      // diagonal sub-blocks: lane = (block bi, column j), forward substitution in fp32
+      const int bi = lane >> 4, j = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < r; ++s) acc += sA[(16 * bi + r) * L::LDA + 16 * bi + s] * x[s];
+        if (r > j) x[r] = -acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sA[(16 * bi + r) * L::LDA + 16 * bi + j] = x[r];
+    }
+    __syncthreads();
+    // off-diagonal sub-blocks T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA (16x16x4).
+    // T_ij (i > j) is stored in the free upper position (j, i) so that A_ij stays readable.
+    auto tblk = [&](int bi, int bj) -> float* {
+      return bi == bj ? sA + 16 * bi * L::LDA + 16 * bi : sA + 16 * bj * L::LDA + 16 * bi;
+    };
+    auto offdiag = [&](int bi, int bj) {
+      f32x4 X = zero4();
+      for (int m = bj; m < bi; ++m) {
+        const float* Tm = tblk(m, bj);
+#pragma unroll
+        for (int kk2 = 0; kk2 < 4; ++kk2) {
+          const float a = sA[(16 * bi + ln) * L::LDA + 16 * m + 4 * kk2 + q4];
+          const float bb = Tm[(4 * kk2 + q4) * L::LDA + ln];
+          X = mma_f32(a, bb, X);
+        }
+      }
+      const float* Ti = tblk(bi, bi);
+      f32x4 Y = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Y = mma_f32(Ti[ln * L::LDA + 4 * q4 + e], X[e], Y);
+      float* To = tblk(bi, bj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
+    };
+    if (w < 3) offdiag(w + 1, w);
+    __syncthreads();
+    if (w < 2) offdiag(w + 2, w);
+    __syncthreads();
+    if (w == 0) offdiag(3, 0);
+    __syncthreads();
+
+    // T' = T diag(beta), rounded once complete (hi, lo)
+    {
+      const int r = tid >> 2;
+      const int s0 = 16 * (tid & 3);
+      const int bi = r >> 4, bj = s0 >> 4;
+      const float* Tb = tblk(bi, bj);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int s = s0 + u;
+        const float val = s <= r ? Tb[(r & 15) * L::LDA + u] * sBeta[s] : 0.f;
+        store_split<Pol>(sT, sTLo, r * L::LDT + s, val);
+      }
+    }
+    __syncthreads();
+    // value tile, transposed, into region Y (A / T are dead now)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) sVT[lane * L::LDT + 16 * w + t] = from_f32<E>(vv[t]);
+    __syncthreads();
+
+    // ================= serial step: this wave's 16 value columns ============================
+    Frag Sh[NS], Sl[NS];
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
+    // X = V - (K e^Gamma) S, in fp32
+    f32x4 X[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[rb][e] = -to_f32(sVT[(16 * w + ln) * L::LDT + 16 * rb + 4 * q4 + e]);
+    }
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        X[rb] = Pol::mma(Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4), Sh[pp], X[rb]);
+    }
+    // (X holds K_Gamma S - V; U = T' (V - K_Gamma S) = -T' X)
+    Frag Xh[NT], Xl[NT];
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
+    f32x4 U[4], O[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      U[rb] = zero4();
+      O[rb] = zero4();
+    }
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          const Frag th = Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4);
+          U[rb] = Pol::mma(th, Xh[pp], U[rb]);
+          if constexpr (Pol::kSplit) {
+            U[rb] = Pol::mma(Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4), Xh[pp], U[rb]);
+            U[rb] = Pol::mma(th, Xl[pp], U[rb]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
+    // O = (Q e^Gamma) S + M U
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const Frag qh = Pol::load(sQg, L::LDP, 16 * rb + ln, pp, q4);
+        O[rb] = Pol::mma(qh, Sh[pp], O[rb]);
+        if constexpr (Pol::kSplit) {
+          O[rb] = Pol::mma(Pol::load(sQgLo, L::LDP, 16 * rb + ln, pp, q4), Sh[pp], O[rb]);
+          O[rb] = Pol::mma(qh, Sl[pp], O[rb]);
+        }
+      }
+    }
+    Frag Uh[NT], Ul[NT];
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(U, pp, Uh[pp], Ul[pp]);
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          const Frag mh = Pol::load(sM, L::LDT, 16 * rb + ln, pp, q4);
+          O[rb] = Pol::mma(mh, Uh[pp], O[rb]);
+          if constexpr (Pol::kSplit) {
+            O[rb] = Pol::mma(Pol::load(sMLo, L::LDT, 16 * rb + ln, pp, q4), Uh[pp], O[rb]);
+            O[rb] = Pol::mma(mh, Ul[pp], O[rb]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * q4 + e;
+        if (r < Lc)
+          go[(size_t(cstart + r) * H + h) * DV + col0 + ln] = from_f32<Tout>(p.scale * O[rb][e]);
+      }
+    }
+    // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[t][e] *= sDecay[16 * t + 4 * q4 + e];
+    }
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+#pragma unroll
+      for (int t = 0; t < NTD; ++t) {
+        const Frag kh = Pol::load(sKhT, L::LDT, 16 * t + ln, pp, q4);
+        S[t] = Pol::mma(kh, Uh[pp], S[t]);
+        if constexpr (Pol::kSplit) {
+          S[t] = Pol::mma(Pol::load(sKhTLo, L::LDT, 16 * t + ln, pp, q4), Uh[pp], S[t]);
+          S[t] = Pol::mma(kh, Ul[pp], S[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (p.ht) {
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * t + 4 * q4 + e;
+        p.ht[((size_t(n) * H + h) * DK + c) * DV + col0 + ln] = S[t][e];
+      }
+    }
+  }
+}
+
+template <class Pol, typename Tio, typename Tout, int DK>
+static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
+  const int groups = (p.n_units + 7) / 8;
+  const dim3 grid(groups * 8 * p.n_vt);
+  hipLaunchKernelGGL((chunk_fwd_kernel<Pol, Tio, Tout, DK>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, int dk,
+                            hipStream_t stream) {
+  if (io_dtype == 1) {
+    if (out_dtype == 1) {
+      if (dk == 128) return launch_one<PolBF16, __bf16, __bf16, 128>(p, stream);
+      if (dk == 64) return launch_one<PolBF16, __bf16, __bf16, 64>(p, stream);
+    } else {
+      if (dk == 128) return launch_one<PolBF16, __bf16, float, 128>(p, stream);
+      if (dk == 64) return launch_one<PolBF16, __bf16, float, 64>(p, stream);
+    }
+  } else {
+    if (dk == 64) return launch_one<PolF32, float, float, 64>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

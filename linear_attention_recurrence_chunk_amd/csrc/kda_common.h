@@ -1,0 +1,130 @@
+// Device helpers shared by the libkda kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kSub = 16;     // tokens per sub-block (one MFMA tile edge)
+constexpr int kNumSub = kChunk / kSub;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---------------------------------------------------------------------------------------------
+// MFMA policies. A 16x16 fp32 accumulator tile holds element (row m, col n) in lane
+// n + 16 * (m / 4), register m % 4. An operand fragment of lane l belongs to row/column
+// l % 16 and k-group l / 16. Every fragment here uses the same k-order inside a slice, chosen
+// so that the accumulator registers of the tiles covering a slice ARE the B fragment of that
+// slice: a result can feed the next product with no data movement. LDS fragments are read in
+// the same order, so A and B always agree.
+// ---------------------------------------------------------------------------------------------
+
+// bf16 operands, v_mfma_f32_16x16x32_bf16. Slice p covers k in [32p, 32p + 32); element e of
+// k-group q is k = 32p + 16 * (e / 4) + 4q + e % 4.
+struct PolBF16 {
+  using E = __bf16;
+  using Frag = bf16x8;
+  static constexpr int kSlice = 32;
+  static constexpr bool kSplit = true;  // products that need it use hi + lo operand pairs
+  __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static constexpr int slices(int k) { return k / 32; }
+  // slices covering the first nb 16-wide blocks of k
+  static constexpr int slices_blocks(int nb) { return (nb + 1) / 2; }
+  __device__ static __forceinline__ Frag load(const E* tile, int ld, int row, int p, int q) {
+    const E* base = tile + row * ld + 32 * p + 4 * q;
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(base);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // fragment scaled per k by fac[k] (fp32), rounded once to bf16
+  __device__ static __forceinline__ Frag load_scaled(const E* tile, int ld, int row, int p,
+                                                     int q, const float* fac) {
+    const E* base = tile + row * ld + 32 * p + 4 * q;
+    const float* fb = fac + 32 * p + 4 * q;
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(base);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16);
+    f32x4 flo = *reinterpret_cast<const f32x4*>(fb);
+    f32x4 fhi = *reinterpret_cast<const f32x4*>(fb + 16);
+    Frag r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (__bf16)((float)lo[e] * flo[e]);
+      r[e + 4] = (__bf16)((float)hi[e] * fhi[e]);
+    }
+    return r;
+  }
+  // B fragment of slice p from accumulator tiles acc[2p] and acc[2p + 1]
+  __device__ static __forceinline__ Frag from_acc(const f32x4* acc, int p) {
+    Frag r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (__bf16)acc[2 * p][e];
+      r[e + 4] = (__bf16)acc[2 * p + 1][e];
+    }
+    return r;
+  }
+  // same, as a hi + lo pair: hi = bf16(x), lo = bf16(x - hi)
+  __device__ static __forceinline__ void from_acc_split(const f32x4* acc, int p, Frag& hi,
+                                                        Frag& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = acc[2 * p + (e >> 2)][e & 3];
+      const __bf16 xh = (__bf16)x;
+      hi[e] = xh;
+      lo[e] = (__bf16)(x - (float)xh);
+    }
+  }
+};
+
+// fp32 operands, v_mfma_f32_16x16x4_f32. Slice p covers rows {16 (p/4) + 4q + p%4 : q}.
+struct PolF32 {
+  using E = float;
+  using Frag = float;
+  static constexpr int kSlice = 4;
+  static constexpr bool kSplit = false;  // fp32 operands need no second part
+  __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static constexpr int slices(int k) { return k / 4; }
+  static constexpr int slices_blocks(int nb) { return 4 * nb; }
+  __device__ static __forceinline__ Frag load(const E* tile, int ld, int row, int p, int q) {
+    return tile[row * ld + 16 * (p >> 2) + 4 * q + (p & 3)];
+  }
+  __device__ static __forceinline__ Frag load_scaled(const E* tile, int ld, int row, int p,
+                                                     int q, const float* fac) {
+    const int kk = 16 * (p >> 2) + 4 * q + (p & 3);
+    return tile[row * ld + kk] * fac[kk];
+  }
+  __device__ static __forceinline__ Frag from_acc(const f32x4* acc, int p) {
+    return acc[p >> 2][p & 3];
+  }
+  __device__ static __forceinline__ void from_acc_split(const f32x4* acc, int p, Frag& hi,
+                                                        Frag& lo) {
+    hi = acc[p >> 2][p & 3];
+    lo = 0.f;
+  }
+};
+
+// fp32 MFMA on a natural k-order (used by the triangular inverse): slice s holds k = 4s + q.
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

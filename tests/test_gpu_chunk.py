@@ -1,0 +1,109 @@
+"""Parity of kda_chunk_fwd (HIP, through the C ABI) with the fp64 CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_chunk_amd as kda
+from linear_attention_recurrence_chunk_amd import workloads as wl
+from oracle import c_recurrence_fwd
+from oracle import kda_oracle as ko
+from kda_testutil import TOL_BF16, TOL_F32, np64, rel_max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, scale=1.0, varlen=False, out_dtype=torch.float32):
+    d = to_dev(inp)
+    cu = d["cu_seqlens"] if varlen else None
+    o, ht = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=cu,
+                          scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def _oracle(inp, scale=1.0, varlen=True):
+    cu = inp["cu_seqlens"].numpy() if varlen else None
+    return c_recurrence_fwd(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), np64(inp["g"]),
+                            np64(inp["beta"]), h0=np64(inp["h0"]), cu_seqlens=cu, scale=scale)
+
+
+def test_tiny_f32_config():
+    """B=1, T=256, H=2, d=64, fp32, seed 0, h0 = 0: per-token oracle, 1e-4 x RMS."""
+    cfg = wl.CONFIGS["tiny_f32"]
+    print(f"case tiny_f32 seed={cfg['seed']}", flush=True)
+    inp = wl.prefill_inputs(T=cfg["T"], H=cfg["H"], dk=cfg["dk"], dv=cfg["dv"], dtype="f32",
+                            seed=cfg["seed"], h0_std=0.0)
+    o, ht = _run(inp)
+    o_ref, ht_ref = ko.recurrence_fwd(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]),
+                                      np64(inp["g"]), np64(inp["beta"]))
+    e_o = rel_max_err(np64(o), o_ref)
+    e_s = rel_max_err(np64(ht), ht_ref)
+    print(f"tiny_f32 err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
+
+
+@pytest.mark.parametrize("T,H,dk,dtype", [(200, 3, 128, "bf16"), (64, 2, 64, "bf16"),
+                                          (131, 2, 64, "f32"), (1, 2, 128, "bf16")])
+def test_ragged_tail_with_h0(T, H, dk, dtype):
+    print(f"case ragged T={T} H={H} dk={dk} {dtype}", flush=True)
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dk, dtype=dtype, seed=T + dk, h0_std=0.02)
+    o, ht = _run(inp, scale=0.7)
+    o_ref, ht_ref = _oracle(inp, scale=0.7, varlen=False)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht)[0:1], ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= tol and e_s <= tol
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_varlen_bf16(dk):
+    lengths = [1, 64, 65, 130, 0, 17, 256]
+    print(f"case varlen dk={dk} lengths={lengths}", flush=True)
+    inp = wl.prefill_inputs(H=2, dk=dk, dv=dk, dtype="bf16", seed=11, h0_std=0.02,
+                            lengths=lengths)
+    o, ht = _run(inp, varlen=True)
+    o_ref, ht_ref = _oracle(inp, varlen=True)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    # a length-0 sequence hands its entering state through unchanged
+    assert torch.equal(ht[4].cpu(), inp["h0"][4])
+
+
+@pytest.mark.parametrize("mode", ["floor_stress", "g_min_everywhere", "overwrite"])
+def test_decay_extremes(mode):
+    """Floor-exercising inputs: raw g x 10 (floor bites), g = -5 everywhere (largest in-block
+    exponent), and g = 0, beta = 1 over a long run (no decay, full overwrite)."""
+    print(f"case extremes {mode}", flush=True)
+    kw = dict(T=300, H=2, dk=128, dv=128, dtype="bf16", seed=5, h0_std=0.02)
+    if mode == "floor_stress":
+        inp = wl.prefill_inputs(floor_stress=True, **kw)
+    elif mode == "g_min_everywhere":
+        inp = wl.prefill_inputs(g_fill=-5.0, **kw)
+    else:
+        inp = wl.prefill_inputs(g_fill=0.0, beta_fill=1.0, **kw)
+    o, ht = _run(inp)
+    o_ref, ht_ref = _oracle(inp, varlen=False)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert np.isfinite(np64(o)).all()
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_deterministic():
+    inp = wl.prefill_inputs(T=500, H=4, dk=128, dv=128, dtype="bf16", seed=3, h0_std=0.02)
+    o1, h1 = _run(inp)
+    o2, h2 = _run(inp)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_bf16_output_is_rounded_fp32_output(dk):
+    """A bf16 output is exactly the round-to-nearest-even of the fp32 output of the same
+    arithmetic: the only extra error of the bf16 path is the format of o itself."""
+    inp = wl.prefill_inputs(T=333, H=3, dk=dk, dv=dk, dtype="bf16", seed=21, h0_std=0.02)
+    o32, h32 = _run(inp, out_dtype=torch.float32)
+    o16, h16 = _run(inp, out_dtype=torch.bfloat16)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert torch.equal(h32, h16)
