@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA prefill hot path (kda_chunk_fwd) on one MI355X.
+
+One step = one kda_chunk_fwd over the 8192-token, 96-head, d = 128 prefill (bf16 q, k, v;
+fp32 g, beta and state; entering state h0 ~ N(0, 0.02^2); bf16 output plus fp32 final
+state), inputs resident in HBM before the timed region. Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The line carries the roofline of the kernel (algorithmic bytes per launch over the average
+launch time measured with HIP events on the launch stream), the MFMA rate, the fp64 CPU
+oracle timed on the host cores, and, when they were taken on the current kernel source, the
+HBM bytes read and written per launch from rocprofv3 counters (profiles/).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+CHUNK = 64
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc", "kda_chunk.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_8k_counters.txt")
+
+
+def algorithmic_bytes(T, H, dk, dv, io_bytes, out_bytes, n_seqs=1):
+    """Bytes the method must move: q, k, v in, g (fp32) and beta (fp32) in, o out, the fp32
+    entering state in and final state out."""
+    per_tok_head = io_bytes * (2 * dk + dv) + 4 * dk + 4 + out_bytes * dv
+    return T * H * per_tok_head + 2 * n_seqs * H * dk * dv * 4
+
+
+def algorithmic_flops(T, H, dk, dv):
+    """Per token and head: 6 dk dv for the inter-chunk products (W S / K_Gamma S, Q_Gamma S,
+    K^T U) plus C (3 dk + 2 dv) for the causal intra-chunk products (A, M, W, U, M U),
+    counted triangular-aware."""
+    return T * H * (6 * dk * dv + CHUNK * (3 * dk + 2 * dv))
+
+
+def source_digest():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, scale):
+    """The fp64 C oracle, untuned, on the host cores over the same workload."""
+    import numpy as np
+    from oracle import c_recurrence_fwd, max_threads
+    f32 = lambda t: None if t is None else t.detach().float().cpu().numpy()
+    host = {k: f32(inp[k]) for k in ("q", "k", "v", "g", "beta", "h0")}
+    threads = max_threads()
+    t0 = time.perf_counter()
+    c_recurrence_fwd(host["q"], host["k"], host["v"], host["g"], host["beta"], h0=host["h0"],
+                     scale=scale, col_block=16)
+    dt = time.perf_counter() - t0
+    T, H = host["q"].shape[0], host["q"].shape[1]
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    del np
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({T} tokens x {H} heads, fp64 per-token recurrence, "
+                      f"{dt:.2f} s on {threads} threads, {cpu_model})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes --steps times (the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU: the KDA recurrence path runs "
+                          "on a single MI355X and has no multi-GPU mode (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_chunk_amd as kda
+    from linear_attention_recurrence_chunk_amd import workloads as wl
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": args.steps}))
+        return
+
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    scale = 1.0
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device=dev)
+    q, k, v, g, beta, h0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "h0"))
+    o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    ht = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_fwd(q, k, v, g, beta, h0=h0, o=o, ht=ht, scale=scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch durations with events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2)
+    nflops = algorithmic_flops(T, H, dk, dv)
+    achieved_gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    traffic = counter_traffic()
+    line = {
+        "metric": "KDA prefill tokens/s (kda_chunk_fwd)",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: q, k unit-normalised N(0,1), v N(0,1), "
+                "beta = sigmoid(N(0,1)), g = max(-softplus(N(0,1)), -5), h0 N(0, 0.02^2))",
+        "config": {"workload": "prefill_8k: B=1, T=8192, H=96, d_k=d_v=128, chunk 64, bf16 "
+                               "q/k/v and output, fp32 g/beta/state, with h0 and final state",
+                   "global_batch": 1, "seq_len": T, "heads": H, "head_dim": dk,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "mfma": {"achieved_tflops": nflops / (avg_ms * 1e-3) / 1e12,
+                 "peak_tflops_bf16": BF16_PEAK_TFLOPS,
+                 "frac": nflops / (avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "flops_per_launch": nflops, "note": "algorithmic FLOPs (triangular-aware)"},
+        "kernel": {"name": "chunk_fwd_kernel", "avg_launch_ms": avg_ms,
+                   "min_launch_ms": min(launch_ms), "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, scale)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
