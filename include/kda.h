@@ -167,7 +167,9 @@ typedef struct kda_token_window {
  *   state      [R, H, d_k, d_v] fp32, read then overwritten in place with S after the bonus
  *   state_acc  [R, H, d_k, d_v] fp32 or NULL; must not overlap state
  *   conv_tail  [R, H, 2 d_k + d_v, conv_width - 1] fp32, oldest first, updated in place
- *   o          [R, n_new, H, d_v] bf16
+ *              (may be NULL when conv_width == 1)
+ *   o          [R, n_new, H, d_v] out_dtype: KDA_BF16, or KDA_F32 (a bf16 output is the
+ *              round-to-nearest-even of the fp32 result)
  *
  * Supported: d_k = d_v = 128 or 64, conv_width in 1..4, 1 <= n_new <= cur->slots,
  * prev->slots in 1..16, act in {0, 1}, eps_l2 > 0, eps_rms >= 0.
@@ -177,7 +179,7 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
                       const kda_token_window* cur, const float* conv_w, const float* norm_w,
                       float scale, float g_min, float eps_l2, float eps_rms, int act,
                       float* state, float* state_acc, float* conv_tail, void* o,
-                      void* stream);
+                      int out_dtype, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int status);

@@ -59,7 +59,7 @@ def library():
     lib.kda_segment_cp_fwd.restype = I
     lib.kda_decode_replay.argtypes = [I, I, I, I, I, I, P, ctypes.POINTER(TokenWindow),
                                       ctypes.POINTER(TokenWindow), P, P, F, F, F, F, I, P, P, P,
-                                      P, P]
+                                      P, I, P]
     lib.kda_decode_replay.restype = I
     lib.kda_status_string.argtypes = [I]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -223,10 +223,11 @@ def _window(win, slots):
 
 def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None, scale=1.0,
                   g_min=-5.0, eps_l2=1e-6, eps_rms=1e-6, act=1, state_acc=None, o=None,
-                  write_state_acc=True, stream=None):
+                  write_state_acc=True, out_dtype=None, stream=None):
     """kda_decode_replay. ``state`` [R, H, d_k, d_v] and ``conv_tail`` are updated in place;
     prev / new are dicts of bf16 tensors q, k, v, g, beta (and z for new), each
-    [R, slots, H, ...]. Returns (o [R, n_new, H, d_v] bf16, state_acc or None)."""
+    [R, slots, H, ...]. out_dtype: None (bf16) or torch.float32.
+    Returns (o [R, n_new, H, d_v], state_acc or None)."""
     torch = _torch()
     R, H, dk, dv = state.shape
     dev = state.device
@@ -246,14 +247,18 @@ def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None
         state_acc = torch.empty_like(state)
     _check(state_acc, "state_acc", torch.float32, dev)
     if o is None:
-        o = torch.empty(R, n_new, H, dv, dtype=torch.bfloat16, device=dev)
-    _check(o, "o", torch.bfloat16, dev)
+        odt = torch.float32 if out_dtype in (torch.float32, "f32", "float32") else torch.bfloat16
+        o = torch.empty(R, n_new, H, dv, dtype=odt, device=dev)
+    if o.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("o must be bf16 or fp32")
+    _check(o, "o", None, dev)
     pw = _window(prev, prev["q"].shape[1])
     nw = _window(new, new["q"].shape[1])
     st = library().kda_decode_replay(
         R, H, dk, dv, conv_width, int(n_new), _ptr(n_acc), ctypes.byref(pw), ctypes.byref(nw),
         _ptr(conv_w), _ptr(norm_w), float(scale), float(g_min), float(eps_l2), float(eps_rms),
-        int(act), _ptr(state), _ptr(state_acc), _ptr(conv_tail), _ptr(o), _stream(stream))
+        int(act), _ptr(state), _ptr(state_acc),
+        _ptr(conv_tail) if conv_tail.numel() else None, _ptr(o), _io_dtype(o), _stream(stream))
     if st != 0:
         raise KDAError(st, "kda_decode_replay")
     return o, state_acc

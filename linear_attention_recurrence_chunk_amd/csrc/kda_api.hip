@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "../../include/kda.h"
+#include "kda_decode.h"
 #include "kda_internal.h"
 
 namespace {
@@ -27,6 +28,14 @@ bool overlaps(Range a, Range b) {
 }
 
 size_t dsize(int io_dtype) { return io_dtype == KDA_BF16 ? 2 : 4; }
+
+constexpr int kMaxSegments = 256;
+constexpr int kAutoSegments = 64;
+
+// [P | Q] summaries plus entering states, fp32, for every (sequence, segment, head)
+size_t segment_workspace_bytes(int N, int H, int dk, int dv, int ns) {
+  return size_t(N) * ns * H * dk * (size_t(dk) + 2 * size_t(dv)) * 4;
+}
 
 // Shared validation of the prefill entry points. Fills the sequence count and token total.
 int validate_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -150,6 +159,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   p.H = num_heads;
   p.dv = d_v;
   p.n_vt = d_v / 64;
+  p.n_seg = 1;
+  p.mode = kda::kModeForward;
   p.n_units = N * num_heads;
   p.scale = scale;
   p.g_min = g_min;
@@ -160,8 +171,11 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
 int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v, int n_segments,
                                   size_t* bytes) {
   if (!bytes) return KDA_ERR_NULL_ARG;
-  (void)n_seqs; (void)num_heads; (void)d_k; (void)d_v; (void)n_segments;
-  return KDA_ERR_UNSUPPORTED;
+  if (n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_BAD_SHAPE;
+  if (n_segments < 0 || n_segments > kMaxSegments) return KDA_ERR_BAD_SHAPE;
+  const int ns = n_segments == 0 ? kAutoSegments : n_segments;
+  *bytes = segment_workspace_bytes(n_seqs, num_heads, d_k, d_v, ns);
+  return KDA_OK;
 }
 
 int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -169,16 +183,94 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
                        const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                        int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
                        float scale, float g_min, void* o, float* ht, int n_segments,
-                       void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   int N = 0;
   int64_t T = 0;
   const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
                                   seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
                                   g_min, o, ht, &N, &T);
   if (st != KDA_OK) return st;
-  (void)n_segments; (void)workspace; (void)workspace_bytes; (void)stream;
-  return KDA_ERR_UNSUPPORTED;
+  if (n_segments < 0 || n_segments > kMaxSegments) return KDA_ERR_BAD_SHAPE;
+  int ns = n_segments == 0 ? kAutoSegments : n_segments;
+  const size_t need = segment_workspace_bytes(N, num_heads, d_k, d_v, ns);
+  if (!workspace) return KDA_ERR_NULL_ARG;
+  if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  {
+    const size_t es = dsize(io_dtype);
+    const Range rws = range_of(workspace, need);
+    const Range all[] = {
+        range_of(q, size_t(T) * num_heads * d_k * es), range_of(k, size_t(T) * num_heads * d_k * es),
+        range_of(v, size_t(T) * num_heads * d_v * es), range_of(g, size_t(T) * num_heads * d_k * 4),
+        range_of(beta, size_t(T) * num_heads * 4),
+        range_of(h0, h0 ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
+        range_of(o, size_t(T) * num_heads * d_v * dsize(out_dtype)),
+        range_of(ht, ht ? size_t(N) * num_heads * d_k * d_v * 4 : 0)};
+    for (Range x : all)
+      if (overlaps(rws, x)) return KDA_ERR_ALIASING;
+  }
+  if (N == 0) return KDA_OK;
+  if (n_segments == 0) {
+    // automatic: no more segments than the longest sequence has chunks
+    int64_t max_len = 0;
+    if (cu_seqlens_host) {
+      for (int i = 0; i < N; ++i) {
+        const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+        max_len = len > max_len ? len : max_len;
+      }
+    } else {
+      max_len = seq_len;
+    }
+    const int64_t max_chunks = (max_len + 63) / 64;
+    if (max_chunks < ns) ns = max_chunks < 1 ? 1 : int(max_chunks);
+  }
+  float* ws_pq = static_cast<float*>(workspace);
+  float* ws_sin = ws_pq + size_t(N) * ns * num_heads * d_k * (d_k + d_v);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  kda::ChunkParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.h0 = h0;
+  p.cu_seqlens = cu_seqlens;
+  p.o = o;
+  p.ht = nullptr;
+  p.seq_len = cu_seqlens ? 0 : seq_len;
+  p.n_seqs = N;
+  p.H = num_heads;
+  p.dv = d_v;
+  p.n_seg = ns;
+  p.n_units = N * ns * num_heads;
+  p.ws_pq = ws_pq;
+  p.ws_sin = ws_sin;
+  p.scale = scale;
+  p.g_min = g_min;
+  // (1) segment summaries [P | Q] over the widened state, without entering states
+  p.mode = kda::kModeTransition;
+  p.n_vt = (d_k + d_v) / 64;
+  int rc = launch_status(kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
+  if (rc != KDA_OK) return rc;
+  // (2) ordered scan: every segment's entering state and the final state
+  kda::ScanParams sp{};
+  sp.pq = ws_pq;
+  sp.h0 = h0;
+  sp.sin = ws_sin;
+  sp.ht = ht;
+  sp.cu_seqlens = cu_seqlens;
+  sp.seq_len = cu_seqlens ? 0 : seq_len;
+  sp.N = N;
+  sp.n_seg = ns;
+  sp.H = num_heads;
+  sp.dv = d_v;
+  rc = launch_status(kda::launch_segment_scan(sp, d_k, s));
+  if (rc != KDA_OK) return rc;
+  // (3) all segments replay their tokens in parallel
+  p.mode = kda::kModeReplay;
+  p.n_vt = d_v / 64;
+  return launch_status(kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
 }
 
 int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_width,
@@ -186,12 +278,84 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
                       const kda_token_window* cur, const float* conv_w, const float* norm_w,
                       float scale, float g_min, float eps_l2, float eps_rms, int act,
                       float* state, float* state_acc, float* conv_tail, void* o,
-                      void* stream) {
-  (void)n_requests; (void)num_heads; (void)d_k; (void)d_v; (void)conv_width; (void)n_new;
-  (void)n_acc; (void)prev; (void)cur; (void)conv_w; (void)norm_w; (void)scale; (void)g_min;
-  (void)eps_l2; (void)eps_rms; (void)act; (void)state; (void)state_acc; (void)conv_tail;
-  (void)o; (void)stream;
-  return KDA_ERR_UNSUPPORTED;
+                      int out_dtype, void* stream) {
+  if (!prev || !cur) return KDA_ERR_NULL_ARG;
+  if (!n_acc || !conv_w || !norm_w || !state || !o) return KDA_ERR_NULL_ARG;
+  if (!conv_tail && conv_width != 1) return KDA_ERR_NULL_ARG;
+  if (out_dtype != KDA_BF16 && out_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+  if (!prev->q || !prev->k || !prev->v || !prev->g || !prev->beta) return KDA_ERR_NULL_ARG;
+  if (!cur->q || !cur->k || !cur->v || !cur->g || !cur->beta || !cur->z) return KDA_ERR_NULL_ARG;
+  if (n_requests < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_BAD_SHAPE;
+  if (conv_width < 1 || conv_width > 4) return KDA_ERR_BAD_SHAPE;
+  if (prev->slots < 1 || prev->slots > 16 || cur->slots < 1 || cur->slots > 16)
+    return KDA_ERR_BAD_SHAPE;
+  if (n_new < 1 || n_new > cur->slots) return KDA_ERR_BAD_SHAPE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  if (act != 0 && act != 1) return KDA_ERR_BAD_VALUE;
+  if (!isfinite(scale) || !isfinite(g_min) || g_min > 0.f || !(eps_l2 > 0.f) ||
+      !(eps_rms >= 0.f) || !isfinite(eps_l2) || !isfinite(eps_rms))
+    return KDA_ERR_BAD_VALUE;
+  const void* ptrs[] = {n_acc,    prev->q, prev->k, prev->v, prev->g, prev->beta, cur->q,
+                        cur->k,   cur->v,  cur->g,  cur->beta, cur->z, conv_w,   norm_w,
+                        state,    state_acc, conv_tail, o};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const size_t R = size_t(n_requests), H = size_t(num_heads), D = size_t(d_k);
+  const size_t C3 = 3 * D;
+  const Range rstate = range_of(state, R * H * D * D * 4);
+  const Range racc = range_of(state_acc, state_acc ? R * H * D * D * 4 : 0);
+  const Range rtail = range_of(conv_tail, R * H * C3 * size_t(conv_width - 1) * 4);
+  const Range ro = range_of(o, R * size_t(n_new) * H * D * dsize(out_dtype));
+  const Range ins[] = {
+      range_of(n_acc, R * 4),
+      range_of(prev->q, R * prev->slots * H * D * 2), range_of(prev->k, R * prev->slots * H * D * 2),
+      range_of(prev->v, R * prev->slots * H * D * 2), range_of(prev->g, R * prev->slots * H * D * 2),
+      range_of(prev->beta, R * prev->slots * H * 2),
+      range_of(cur->q, R * cur->slots * H * D * 2), range_of(cur->k, R * cur->slots * H * D * 2),
+      range_of(cur->v, R * cur->slots * H * D * 2), range_of(cur->g, R * cur->slots * H * D * 2),
+      range_of(cur->beta, R * cur->slots * H * 2), range_of(cur->z, R * cur->slots * H * D * 2),
+      range_of(conv_w, H * C3 * size_t(conv_width) * 4), range_of(norm_w, D * 4)};
+  for (Range out : {rstate, racc, rtail, ro})
+    for (Range in : ins)
+      if (overlaps(out, in)) return KDA_ERR_ALIASING;
+  if (overlaps(rstate, racc) || overlaps(rstate, ro) || overlaps(rstate, rtail) ||
+      overlaps(racc, ro) || overlaps(racc, rtail) || overlaps(ro, rtail))
+    return KDA_ERR_ALIASING;
+  if (n_requests == 0) return KDA_OK;
+
+  kda::DecodeParams p{};
+  p.R = n_requests;
+  p.H = num_heads;
+  p.D = d_k;
+  p.conv_width = conv_width;
+  p.n_new = n_new;
+  p.prev_slots = prev->slots;
+  p.cur_slots = cur->slots;
+  p.act = act;
+  p.n_acc = n_acc;
+  p.prev_q = static_cast<const __bf16*>(prev->q);
+  p.prev_k = static_cast<const __bf16*>(prev->k);
+  p.prev_v = static_cast<const __bf16*>(prev->v);
+  p.prev_g = static_cast<const __bf16*>(prev->g);
+  p.prev_beta = static_cast<const __bf16*>(prev->beta);
+  p.cur_q = static_cast<const __bf16*>(cur->q);
+  p.cur_k = static_cast<const __bf16*>(cur->k);
+  p.cur_v = static_cast<const __bf16*>(cur->v);
+  p.cur_g = static_cast<const __bf16*>(cur->g);
+  p.cur_beta = static_cast<const __bf16*>(cur->beta);
+  p.cur_z = static_cast<const __bf16*>(cur->z);
+  p.conv_w = conv_w;
+  p.norm_w = norm_w;
+  p.state = state;
+  p.state_acc = state_acc;
+  p.conv_tail = conv_tail;
+  p.o = o;
+  p.out_f32 = out_dtype == KDA_F32 ? 1 : 0;
+  p.scale = scale;
+  p.decay_floor = expf(g_min);
+  p.eps_l2 = eps_l2;
+  p.eps_rms = eps_rms;
+  return launch_status(kda::launch_decode_replay(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -133,17 +133,20 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
   float* sPair = reinterpret_cast<float*>(smem + L::oPair);
 
-  // ---- which (sequence, head, value tile): value tiles of one unit share an XCD
+  // ---- which (sequence, segment, head, state tile): the tiles of one unit share an XCD
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int rest = b >> 3;
   const int vt = rest % p.n_vt;
   const int unit = (rest / p.n_vt) * 8 + xcd;
   if (unit >= p.n_units) return;
-  const int n = unit / p.H;
-  const int h = unit % p.H;
   const int H = p.H;
   const int DV = p.dv;
+  const int h = unit % H;
+  const int sj = unit / H;              // global segment index n * n_seg + j
+  const int n = sj / p.n_seg;
+  const int j = sj % p.n_seg;
+  const int mode = p.mode;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -159,21 +162,40 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     bos = n * p.seq_len;
     eos = bos + p.seq_len;
   }
-
+  if (p.n_seg > 1) {
+    // chunk-aligned contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg)
+    const long long nc = (eos - bos + kChunk - 1) / kChunk;
+    const int c_lo = int((j * nc) / p.n_seg);
+    const int c_hi = int(((j + 1) * nc) / p.n_seg);
+    const int seg_bos = bos + kChunk * c_lo;
+    eos = min(eos, bos + kChunk * c_hi);
+    bos = seg_bos;
+  }
+  // transition mode: tiles [0, DK/64) hold P (zero values, identity start), the rest Q
+  const bool p_tile = mode == kModeTransition && vt < DK / 64;
+  // column of v feeding this tile (P tiles read none; their address stays at column 0)
+  const int vcol0 = p_tile ? 0 : (mode == kModeTransition ? vt - DK / 64 : vt) * VT;
+  const int ldS = mode == kModeTransition ? DK + DV : DV;                // state row stride
   const Tio* __restrict__ gq = reinterpret_cast<const Tio*>(p.q);
   const Tio* __restrict__ gk = reinterpret_cast<const Tio*>(p.k);
   const Tio* __restrict__ gv = reinterpret_cast<const Tio*>(p.v);
   Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
-  const int col0 = vt * VT + 16 * w;   // first value column owned by this wave
+  const int col0 = vt * VT + 16 * w;   // first state column owned by this wave
 
   // ---- entering state in accumulator layout: tile t, register e = row 16t + 4 q4 + e
   f32x4 S[NTD];
+  const float* s_in = nullptr;
+  if (mode == kModeForward && p.h0) s_in = p.h0 + (size_t(n) * H + h) * DK * DV;
+  if (mode == kModeReplay) s_in = p.ws_sin + (size_t(sj) * H + h) * DK * DV;
 #pragma unroll
   for (int t = 0; t < NTD; ++t) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int c = 16 * t + 4 * q4 + e;
-      S[t][e] = p.h0 ? p.h0[((size_t(n) * H + h) * DK + c) * DV + col0 + ln] : 0.f;
+      float x = 0.f;
+      if (s_in) x = s_in[size_t(c) * DV + col0 + ln];
+      if (p_tile) x = (c == col0 + ln) ? 1.f : 0.f;
+      S[t][e] = x;
     }
   }
 
@@ -203,7 +225,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         kk[t][cc] = to_f32(gk[base + cc]);
         qq[t][cc] = to_f32(gq[base + cc]);
       }
-      vv[t] = to_f32(gv[(size_t(tok) * H + h) * DV + vt * VT + lane]);
+      vv[t] = p_tile ? 0.f : to_f32(gv[(size_t(tok) * H + h) * DV + vcol0 + lane]);
     }
     float beta_r = 0.f;
     if (lane < 16) {
@@ -494,13 +516,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     }
+    if (mode != kModeTransition) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * q4 + e;
-        if (r < Lc)
-          go[(size_t(cstart + r) * H + h) * DV + col0 + ln] = from_f32<Tout>(p.scale * O[rb][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * q4 + e;
+          if (r < Lc)
+            go[(size_t(cstart + r) * H + h) * DV + col0 + ln] = from_f32<Tout>(p.scale * O[rb][e]);
+        }
       }
     }
     // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
@@ -524,13 +548,16 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     __syncthreads();
   }
 
-  if (p.ht) {
+  float* s_out = nullptr;
+  if (mode == kModeForward && p.ht) s_out = p.ht + (size_t(n) * H + h) * DK * DV;
+  if (mode == kModeTransition) s_out = p.ws_pq + (size_t(sj) * H + h) * DK * ldS;
+  if (s_out) {
 #pragma unroll
     for (int t = 0; t < NTD; ++t) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 16 * t + 4 * q4 + e;
-        p.ht[((size_t(n) * H + h) * DK + c) * DV + col0 + ln] = S[t][e];
+        s_out[size_t(c) * ldS + col0 + ln] = S[t][e];
       }
     }
   }
@@ -544,8 +571,28 @@ static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Consistency of a launch description with the kernel's index arithmetic: every unit maps to
+// a valid (sequence, segment, head) and every tile to columns inside the state it writes.
+static bool chunk_params_consistent(const ChunkParams& p, int dk) {
+  if (p.H < 1 || p.n_seqs < 1 || p.n_seg < 1 || p.n_vt < 1 || p.dv < 64 || p.dv % 64) return false;
+  if ((long long)p.n_units != (long long)p.n_seqs * p.n_seg * p.H) return false;
+  if (!p.q || !p.k || !p.v || !p.g || !p.beta) return false;
+  if (!p.cu_seqlens && p.seq_len < 0) return false;
+  switch (p.mode) {
+    case kModeForward:
+      return p.n_seg == 1 && p.n_vt == p.dv / 64 && p.o;
+    case kModeTransition:
+      return p.n_vt == (dk + p.dv) / 64 && (dk % 64) == 0 && p.ws_pq;
+    case kModeReplay:
+      return p.n_vt == p.dv / 64 && p.ws_sin && p.o;
+    default:
+      return false;
+  }
+}
+
 hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, int dk,
                             hipStream_t stream) {
+  if (!chunk_params_consistent(p, dk)) return hipErrorInvalidValue;
   if (io_dtype == 1) {
     if (out_dtype == 1) {
       if (dk == 128) return launch_one<PolBF16, __bf16, __bf16, 128>(p, stream);

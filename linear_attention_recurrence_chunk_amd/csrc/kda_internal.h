@@ -7,8 +7,16 @@
 
 namespace kda {
 
-// One launch of the chunk kernel. A "unit" is one (sequence, head) pair; every unit is
-// processed by n_vt workgroups, one per 64-column value tile.
+// What one launch of the chunk kernel computes.
+enum ChunkMode : int {
+  kModeForward = 0,     // outputs o and the final state of whole sequences
+  kModeTransition = 1,  // per segment: (P, Q) with S_out = P S_in + Q, no outputs
+  kModeReplay = 2,      // per segment: outputs o from the segment's entering state
+};
+
+// One launch of the chunk kernel. A "unit" is one (sequence, segment, head) triple (one
+// segment per sequence in forward mode); every unit is processed by n_vt workgroups, one per
+// 64-column tile of its state (d_v columns, or d_k + d_v columns [P | Q] in transition mode).
 struct ChunkParams {
   const void* q;
   const void* k;
@@ -24,10 +32,27 @@ struct ChunkParams {
   int H;
   int dv;                   // full value width (row stride of v / o / states)
   int n_vt;                 // value tiles per unit
-  int n_units;              // n_seqs * H
+  int n_units;              // n_seqs * n_seg * H
+  int n_seg;                // segments per sequence (1 in forward mode)
+  int mode;                 // ChunkMode
+  float* ws_pq;             // transition: [N, n_seg, H, dk, dk + dv]
+  float* ws_sin;            // replay: [N, n_seg, H, dk, dv] entering states
   float scale;
   float g_min;
 };
+
+// Ordered scan over segment summaries: S_in(0) = h0, S_in(j + 1) = P_j S_in(j) + Q_j.
+struct ScanParams {
+  const float* pq;          // [N, n_seg, H, dk, dk + dv]
+  const float* h0;          // [N, H, dk, dv] or null
+  float* sin;               // [N, n_seg, H, dk, dv]
+  float* ht;                // [N, H, dk, dv] or null
+  const int32_t* cu_seqlens;  // device [N + 1] or null (fixed length seq_len)
+  int seq_len;
+  int N, n_seg, H, dv;
+};
+
+hipError_t launch_segment_scan(const ScanParams& p, int dk, hipStream_t stream);
 
 hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, int dk,
                             hipStream_t stream);

@@ -1,0 +1,84 @@
+"""Parity of kda_segment_cp_fwd (HIP, through the C ABI) with the fp64 CPU oracle and with
+kda_chunk_fwd."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_chunk_amd as kda
+from linear_attention_recurrence_chunk_amd import workloads as wl
+from oracle import c_recurrence_fwd
+from kda_testutil import TOL_BF16, TOL_F32, np64, rel_max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, varlen, scale=1.0):
+    cu = inp["cu_seqlens"].numpy() if varlen else None
+    return c_recurrence_fwd(np64(inp["q"]), np64(inp["k"]), np64(inp["v"]), np64(inp["g"]),
+                            np64(inp["beta"]), h0=np64(inp["h0"]), cu_seqlens=cu, scale=scale)
+
+
+def _seg(inp, n_seg, varlen=False, out_dtype=torch.float32, scale=1.0):
+    d = to_dev(inp)
+    o, ht = kda.segment_cp_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                               cu_seqlens=d["cu_seqlens"] if varlen else None,
+                               n_segments=n_seg, out_dtype=out_dtype, scale=scale)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+@pytest.mark.parametrize("T,n_seg", [(1000, 1), (1000, 3), (1000, 7), (4096, 16), (130, 8)])
+def test_segments_match_oracle(T, n_seg):
+    print(f"case segment T={T} n_seg={n_seg}", flush=True)
+    inp = wl.prefill_inputs(T=T, H=2, dk=128, dv=128, dtype="bf16", seed=T + n_seg, h0_std=0.02)
+    o, ht = _seg(inp, n_seg, scale=0.9)
+    o_ref, ht_ref = _oracle(inp, varlen=False, scale=0.9)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_segments_agree_with_chunk_fwd():
+    """Any segment count reaches the same result as the single-pass kernel."""
+    inp = wl.prefill_inputs(T=3000, H=3, dk=128, dv=128, dtype="bf16", seed=8, h0_std=0.02)
+    d = to_dev(inp)
+    o1, h1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                           out_dtype=torch.float32)
+    for n_seg in (2, 5, 47):
+        o2, h2 = _seg(inp, n_seg)
+        e_o = rel_max_err(np64(o2), np64(o1))
+        e_s = rel_max_err(np64(h2), np64(h1))
+        print(f"n_seg={n_seg} vs chunk_fwd: err_o={e_o:.3e} err_state={e_s:.3e}")
+        assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_segments_varlen():
+    lengths = [1, 64, 65, 300, 0, 1000, 129]
+    print(f"case segment varlen {lengths}", flush=True)
+    inp = wl.prefill_inputs(H=2, dk=128, dv=128, dtype="bf16", seed=4, h0_std=0.02,
+                            lengths=lengths)
+    o, ht = _seg(inp, 4, varlen=True)
+    o_ref, ht_ref = _oracle(inp, varlen=True)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    assert torch.equal(ht[4].cpu(), inp["h0"][4])
+
+
+def test_segments_f32():
+    inp = wl.prefill_inputs(T=700, H=2, dk=64, dv=64, dtype="f32", seed=3, h0_std=0.02)
+    o, ht = _seg(inp, 5)
+    o_ref, ht_ref = _oracle(inp, varlen=False)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"f32 err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
+
+
+def test_workspace_too_small_is_rejected():
+    inp = to_dev(wl.prefill_inputs(T=256, H=2, dk=128, dv=128, dtype="bf16", seed=1))
+    need = kda.segment_cp_workspace_size(1, 2, 128, 128, 4)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kda.KDAError) as ei:
+        kda.segment_cp_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], n_segments=4,
+                           workspace=ws)
+    assert ei.value.status == -6
