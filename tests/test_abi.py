@@ -1,0 +1,189 @@
+"""The C ABI without a GPU: every symbol include/kda.h declares is exported, and host-side
+validation returns its status codes before anything is launched. Device pointers here are
+fake addresses: validation never dereferences them, and no case reaches a launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_recurrence_chunk_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, SEQ, WS, UNSUP, LAUNCH, ALIAS, VALUE = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(kda.library_path())
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_segment_cp_fwd", "kda_segment_cp_workspace_size",
+            "kda_decode_replay", "kda_status_string", "kda_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert kda.version() == 1
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, SEQ, WS, UNSUP, LAUNCH, ALIAS, VALUE):
+        s = kda.status_string(code)
+        assert s and s != "unknown status"
+    assert kda.status_string(-99) == "unknown status"
+
+
+# ----------------------------------------------------------------------------- prefill
+BASE = 1 << 40          # fake, 16-byte aligned device addresses far apart
+GiB = 1 << 30
+
+
+def ptrs(n=9):
+    return [ctypes.c_void_p(BASE + i * 64 * GiB) for i in range(n)]
+
+
+def chunk(q=True, k=True, v=True, g=True, beta=True, h0=None, cu=None, cu_host=None, batch=1,
+          seq_len=256, n_seqs=1, H=2, dk=128, dv=128, io=BF16, out=None, scale=1.0,
+          g_min=-5.0, o=True, ht=None, override=None):
+    P = ptrs()
+    args = dict(q=P[0] if q else None, k=P[1] if k else None, v=P[2] if v else None,
+                g=P[3] if g else None, beta=P[4] if beta else None, h0=h0, cu=cu,
+                cu_host=cu_host, o=P[5] if o else None, ht=ht)
+    if override:
+        args.update(override)
+    return kda.library().kda_chunk_fwd(
+        args["q"], args["k"], args["v"], args["g"], args["beta"], args["h0"], args["cu"],
+        args["cu_host"], batch, seq_len, n_seqs, H, dk, dv, io, io if out is None else out,
+        scale, g_min, args["o"], args["ht"], None)
+
+
+def host_cu(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def test_chunk_null_arguments():
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert chunk(**{name: False}) == NULL
+
+
+def test_chunk_dtype_shape_value_checks():
+    assert chunk(io=7) == DTYPE
+    assert chunk(io=F32, out=BF16, dk=64, dv=64) == DTYPE       # bf16 output of fp32 input
+    assert chunk(H=0) == SHAPE
+    assert chunk(seq_len=-1) == SHAPE
+    assert chunk(n_seqs=2) == SHAPE                             # batch 1 without cu_seqlens
+    assert chunk(dk=96, dv=96) == UNSUP
+    assert chunk(dk=128, dv=64) == UNSUP
+    assert chunk(io=F32, dk=128, dv=128) == UNSUP
+    assert chunk(g_min=-6.0) == VALUE
+    assert chunk(g_min=0.5) == VALUE
+    assert chunk(scale=float("nan")) == VALUE
+
+
+def test_chunk_alignment_and_aliasing():
+    P = ptrs()
+    assert chunk(override={"q": ctypes.c_void_p(BASE + 8)}) == ALIGN
+    assert chunk(override={"o": P[0]}) == ALIAS                 # o on top of q
+    assert chunk(override={"o": ctypes.c_void_p(P[1].value + 64)}) == ALIAS  # inside k
+    h0 = ctypes.c_void_p(BASE + 7 * 64 * GiB)
+    ht_bad = ctypes.c_void_p(h0.value + 256)
+    assert chunk(h0=h0, ht=ht_bad) == ALIAS                     # partial overlap of ht and h0
+
+
+def test_chunk_cu_seqlens_checks():
+    dev_cu = ctypes.c_void_p(BASE + 8 * 64 * GiB)
+    arr, cu_host = host_cu([0, 100, 50, 300])                   # decreasing
+    assert chunk(cu=dev_cu, cu_host=cu_host, seq_len=300, n_seqs=3) == SEQ
+    arr, cu_host = host_cu([1, 100, 300])                       # not starting at 0
+    assert chunk(cu=dev_cu, cu_host=cu_host, seq_len=300, n_seqs=2) == SEQ
+    arr, cu_host = host_cu([0, 100, 299])                       # not ending at T
+    assert chunk(cu=dev_cu, cu_host=cu_host, seq_len=300, n_seqs=2) == SEQ
+    arr, cu_host = host_cu([0, 100, 300])
+    assert chunk(cu=dev_cu, cu_host=None, seq_len=300, n_seqs=2) == NULL   # host copy missing
+    assert chunk(cu=dev_cu, cu_host=cu_host, seq_len=300, n_seqs=2, batch=2) == SHAPE
+    assert chunk(cu=ctypes.c_void_p(dev_cu.value + 4), cu_host=cu_host, seq_len=300,
+                 n_seqs=2) == ALIGN
+
+
+def test_segment_workspace_size():
+    lib = kda.library()
+    out = ctypes.c_size_t(0)
+    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 64, ctypes.byref(out)) == OK
+    # [P | Q] summaries plus entering states: N * n_seg * H * d_k * (d_k + 2 d_v) fp32
+    assert out.value == 1 * 64 * 12 * 128 * (128 + 256) * 4
+    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 0, ctypes.byref(out)) == OK
+    assert out.value == 1 * 64 * 12 * 128 * 384 * 4            # automatic choice: 64 segments
+    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 257, ctypes.byref(out)) == SHAPE
+    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 4, None) == NULL
+
+
+def test_segment_workspace_checks():
+    lib = kda.library()
+    P = ptrs()
+    need = 1 * 4 * 2 * 128 * 384 * 4
+    ws = ctypes.c_void_p(BASE + 8 * 64 * GiB)
+
+    def seg(n_seg=4, ws_ptr=ws, ws_bytes=need, o=P[5]):
+        return lib.kda_segment_cp_fwd(P[0], P[1], P[2], P[3], P[4], None, None, None, 1, 256, 1,
+                                      2, 128, 128, BF16, BF16, 1.0, -5.0, o, None, n_seg,
+                                      ws_ptr, ws_bytes, None)
+    assert seg(ws_bytes=need - 1) == WS
+    assert seg(ws_ptr=None) == NULL
+    assert seg(ws_ptr=ctypes.c_void_p(ws.value + 4)) == ALIGN
+    assert seg(ws_ptr=P[0]) == ALIAS                            # workspace on top of q
+    assert seg(n_seg=-1) == SHAPE
+    assert seg(o=None) == NULL
+
+
+# ----------------------------------------------------------------------------- decode
+def window(slots, with_z=True, base=0):
+    P = [ctypes.c_void_p(BASE + (20 + base + i) * 64 * GiB) for i in range(6)]
+    return kda.TokenWindow(P[0], P[1], P[2], P[3], P[4], P[5] if with_z else None, slots)
+
+
+def decode(R=4, H=2, D=128, W=4, n_new=8, prev=None, cur=None, act=1, g_min=-5.0,
+           eps_l2=1e-6, eps_rms=1e-6, out=BF16, override=None):
+    P = [ctypes.c_void_p(BASE + (40 + i) * 64 * GiB) for i in range(7)]
+    a = dict(n_acc=P[0], conv_w=P[1], norm_w=P[2], state=P[3], state_acc=P[4], tail=P[5], o=P[6])
+    if override:
+        a.update(override)
+    prev = prev if prev is not None else window(8, with_z=False)
+    cur = cur if cur is not None else window(8, base=10)
+    return kda.library().kda_decode_replay(
+        R, H, D, D, W, n_new, a["n_acc"], ctypes.byref(prev), ctypes.byref(cur), a["conv_w"],
+        a["norm_w"], 1.0, g_min, eps_l2, eps_rms, act, a["state"], a["state_acc"], a["tail"],
+        a["o"], out, None)
+
+
+def test_decode_checks():
+    assert decode(override={"state": None}) == NULL
+    assert decode(override={"tail": None}) == NULL              # width 4 needs a tail
+    assert decode(cur=window(8, with_z=False, base=10)) == NULL  # z of the current window
+    assert decode(W=5) == SHAPE
+    assert decode(n_new=9) == SHAPE                              # more new tokens than slots
+    assert decode(n_new=0) == SHAPE
+    assert decode(prev=window(17, with_z=False)) == SHAPE
+    assert decode(D=96) == UNSUP
+    assert decode(act=2) == VALUE
+    assert decode(eps_l2=0.0) == VALUE
+    assert decode(g_min=1.0) == VALUE
+    assert decode(out=5) == DTYPE
+    assert decode(override={"o": ctypes.c_void_p(BASE + (40 + 6) * 64 * GiB + 2)}) == ALIGN
+    same = ctypes.c_void_p(BASE + 43 * 64 * GiB)
+    assert decode(override={"state_acc": same}) == ALIAS        # state_acc on top of state
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """No silent fallback: with the shared library absent, a call raises."""
+    monkeypatch.setattr(kda, "_LIB", None)
+    monkeypatch.setattr(kda, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="libkda.so not found"):
+        kda.library()
