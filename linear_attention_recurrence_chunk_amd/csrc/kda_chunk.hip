@@ -43,7 +43,9 @@ namespace kda {
 template <class Pol, int DK>
 struct ChunkLayout {
   using E = typename Pol::E;
-  static constexpr int kPadE = sizeof(E) == 2 ? 8 : 4;
+  // Row strides of 2 dwords modulo 32 banks: the 16 rows read by one 16-lane group of an
+  // MFMA fragment load land on distinct bank pairs (conflict-free 8-byte reads).
+  static constexpr int kPadE = sizeof(E) == 2 ? 4 : 4;
   static constexpr int LDP = DK + kPadE;   // row-major [64 tokens][DK] tiles
   static constexpr int LDT = 64 + kPadE;   // [rows][64 tokens] tiles
   static constexpr int LDA = 64 + 4;       // fp32 A / T working matrix
@@ -95,9 +97,180 @@ __device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E
   if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(x - to_f32(h));
 }
 
-// single-task descriptors of the prologue products: 10 blocks of A, 6 off-diagonal of M
-__constant__ int kTaskI[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 1, 2, 2, 3, 3, 3};
-__constant__ int kTaskJ[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 0, 0, 1, 0, 1, 2};
+// 16 consecutive values (one 16-token column of a transposed tile) with vector stores
+template <class Pol>
+__device__ __forceinline__ void store16(typename Pol::E* dst, const float* x) {
+  if constexpr (sizeof(typename Pol::E) == 2) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<bf16x4*>(dst + e) =
+          bf16x4{(__bf16)x[e], (__bf16)x[e + 1], (__bf16)x[e + 2], (__bf16)x[e + 3]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<f32x4*>(dst + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+  }
+}
+
+template <class Pol>
+__device__ __forceinline__ void store16_split(typename Pol::E* hi, typename Pol::E* lo,
+                                              const float* x) {
+  if constexpr (Pol::kSplit) {
+#pragma unroll
+    for (int e0 = 0; e0 < 16; e0 += 4) {
+      bf16x4 a, c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (__bf16)x[e0 + e];
+        c[e] = (__bf16)(x[e0 + e] - (float)a[e]);
+      }
+      *reinterpret_cast<bf16x4*>(hi + e0) = a;
+      *reinterpret_cast<bf16x4*>(lo + e0) = c;
+    }
+  } else {
+    store16<Pol>(hi, x);
+  }
+}
+
+// CPT consecutive channels of one token row
+template <class Pol, int CPT>
+__device__ __forceinline__ void store_row(typename Pol::E* dst, const float* x) {
+  if constexpr (CPT == 2 && sizeof(typename Pol::E) == 2) {
+    *reinterpret_cast<bf16x2*>(dst) = bf16x2{(__bf16)x[0], (__bf16)x[1]};
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) dst[cc] = from_f32<typename Pol::E>(x[cc]);
+  }
+}
+
+template <class Pol, int CPT>
+__device__ __forceinline__ void store_row_split(typename Pol::E* hi, typename Pol::E* lo,
+                                                const float* x) {
+  if constexpr (Pol::kSplit && CPT == 2) {
+    const bf16x2 h = bf16x2{(__bf16)x[0], (__bf16)x[1]};
+    *reinterpret_cast<bf16x2*>(hi) = h;
+    *reinterpret_cast<bf16x2*>(lo) =
+        bf16x2{(__bf16)(x[0] - (float)h[0]), (__bf16)(x[1] - (float)h[1])};
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) store_split<Pol>(hi, lo, cc, x[cc]);
+  }
+}
+
+// Row-block IA of A and row-block 3 - IA of M for one wave. Column operands: k / rho on the
+// diagonal block, k kappa next to it, k kappa times the decay gap further down.
+template <class Pol, class L, int DK, int IA>
+__device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typename Pol::E* sKd,
+                                        const typename Pol::E* sKdLo, const typename Pol::E* sKc,
+                                        const typename Pol::E* sQr, const typename Pol::E* sQrLo,
+                                        const float* sPair, const float* sBeta, float* sA,
+                                        typename Pol::E* sM, typename Pol::E* sMLo, int ln, int q4) {
+  using Frag = typename Pol::Frag;
+  constexpr int NS = Pol::slices(DK);
+  constexpr int IM = 3 - IA;
+  // gap factor index of a pair (i, j) with i - j >= 2: (2,0) -> 0, (3,1) -> 1, (3,0) -> 2
+  constexpr int gapA0 = IA == 2 ? 0 : 2, gapA1 = 1;
+  constexpr int gapM0 = IM == 2 ? 0 : 2, gapM1 = 1;
+  f32x4 accA[4], accM[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    accA[jb] = zero4();
+    accM[jb] = zero4();
+  }
+#pragma unroll
+  for (int pp = 0; pp < NS; ++pp) {
+    const Frag rowA = Pol::load(sKr, L::LDP, 16 * IA + ln, pp, q4);
+    const Frag rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
+    Frag colA[4], colM[4], dKl, dQl;
+#pragma unroll
+    for (int jb = 0; jb <= IA; ++jb) {
+      if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
+      else if (jb == IA - 1) colA[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
+      else colA[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4,
+                                       sPair + (jb == 0 ? gapA0 : gapA1) * DK);
+    }
+#pragma unroll
+    for (int jb = 0; jb <= IM; ++jb) {
+      if (jb == IM) colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
+      else if (jb == IM - 1) colM[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
+      else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4,
+                                       sPair + (jb == 0 ? gapM0 : gapM1) * DK);
+    }
+    if constexpr (Pol::kSplit) {
+      dKl = Pol::load(sKdLo, L::LDP, 16 * IM + ln, pp, q4);
+      dQl = Pol::load(sQrLo, L::LDP, 16 * IM + ln, pp, q4);
+    }
+#pragma unroll
+    for (int jb = 0; jb <= IA; ++jb) accA[jb] = Pol::mma(colA[jb], rowA, accA[jb]);
+#pragma unroll
+    for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
+    if constexpr (Pol::kSplit) {
+      accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
+      accM[IM] = Pol::mma(colM[IM], dQl, accM[IM]);
+    }
+  }
+  // register e of block (row i, column jb): row 16 i + ln, column 16 jb + 4 q4 + e
+  const int ra = 16 * IA + ln, rm = 16 * IM + ln;
+  const float br = sBeta[ra];
+#pragma unroll
+  for (int jb = 0; jb <= IA; ++jb) {
+    f32x4 outv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 16 * jb + 4 * q4 + e;
+      outv[e] = (jb == IA && s >= ra) ? 0.f : br * accA[jb][e];
+    }
+    *reinterpret_cast<f32x4*>(sA + ra * L::LDA + 16 * jb + 4 * q4) = outv;
+  }
+#pragma unroll
+  for (int jb = 0; jb <= IM; ++jb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 16 * jb + 4 * q4 + e;
+      store_split<Pol>(sM, sMLo, rm * L::LDT + s, (jb == IM && s > rm) ? 0.f : accM[jb][e]);
+    }
+  }
+}
+
+// Raw inputs of one chunk held by one thread: CPT key channels x 16 tokens of its
+// sub-block, one value column x 16 tokens, and (lanes < 16) one beta.
+template <typename Tio, int CPT>
+struct RawChunk {
+  float g[16][CPT];
+  Tio k[16][CPT];
+  Tio q[16][CPT];
+  Tio v[16];
+  float beta;
+};
+
+template <typename Tio, int DK, int CPT>
+__device__ __forceinline__ void load_chunk(RawChunk<Tio, CPT>& x, const ChunkParams& p,
+                                           int cstart, int Lc, int w, int lane, int h,
+                                           int vcol0, bool p_tile) {
+  const Tio* __restrict__ gq = reinterpret_cast<const Tio*>(p.q);
+  const Tio* __restrict__ gk = reinterpret_cast<const Tio*>(p.k);
+  const Tio* __restrict__ gv = reinterpret_cast<const Tio*>(p.v);
+  const int H = p.H;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int r = 16 * w + t;
+    const int tok = cstart + (r < Lc ? r : 0);   // rows past the end read a valid row
+    const size_t base = (size_t(tok) * H + h) * DK + CPT * lane;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      x.g[t][cc] = p.g[base + cc];
+      x.k[t][cc] = gk[base + cc];
+      x.q[t][cc] = gq[base + cc];
+    }
+    x.v[t] = gv[(size_t(tok) * H + h) * p.dv + vcol0 + lane];
+  }
+  x.beta = 0.f;
+  if (lane < 16) {
+    const int r = 16 * w + lane;
+    x.beta = p.beta[size_t(cstart + (r < Lc ? r : 0)) * H + h];
+  }
+  (void)p_tile;
+}
 
 template <class Pol, typename Tio, typename Tout, int DK>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
@@ -176,9 +349,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   // column of v feeding this tile (P tiles read none; their address stays at column 0)
   const int vcol0 = p_tile ? 0 : (mode == kModeTransition ? vt - DK / 64 : vt) * VT;
   const int ldS = mode == kModeTransition ? DK + DV : DV;                // state row stride
-  const Tio* __restrict__ gq = reinterpret_cast<const Tio*>(p.q);
-  const Tio* __restrict__ gk = reinterpret_cast<const Tio*>(p.k);
-  const Tio* __restrict__ gv = reinterpret_cast<const Tio*>(p.v);
   Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
   const int col0 = vt * VT + 16 * w;   // first state column owned by this wave
 
@@ -208,36 +378,17 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
   }
 
+  RawChunk<Tio, CPT> raw;
+
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
     const int Lc = min(kChunk, eos - cstart);
-
-    // ================= prologue 0: loads (all issued up front) ==========================
-    // thread (sub-block w, channels CPT*lane ..): 16 tokens of its sub-block
-    float gg[16][CPT], kk[16][CPT], qq[16][CPT], vv[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int r = 16 * w + t;
-      const int tok = cstart + (r < Lc ? r : 0);
-      const size_t base = (size_t(tok) * H + h) * DK + CPT * lane;
-#pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        gg[t][cc] = p.g[base + cc];
-        kk[t][cc] = to_f32(gk[base + cc]);
-        qq[t][cc] = to_f32(gq[base + cc]);
-      }
-      vv[t] = p_tile ? 0.f : to_f32(gv[(size_t(tok) * H + h) * DV + vcol0 + lane]);
-    }
-    float beta_r = 0.f;
-    if (lane < 16) {
-      const int r = 16 * w + lane;
-      beta_r = p.beta[size_t(cstart + (r < Lc ? r : 0)) * H + h];
-      if (r >= Lc) beta_r = 0.f;
-    }
+    load_chunk<Tio, DK, CPT>(raw, p, cstart, Lc, w, lane, h, vcol0, p_tile);
 
     // ================= prologue 1: decay factors and operand tiles ======================
     // rho = e^{lambda} (decay from the sub-block start to token r, inclusive) <= 1;
     // kappa = P / rho (decay after token r to the sub-block end) <= 1; 1/rho <= e^{16|g_min|}
-    float bp[CPT], rho[16][CPT];
+    float qr[16][CPT], kr[16][CPT], kc[16][CPT], vv[16];
+    float bp[CPT];
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) bp[cc] = 1.f;
 #pragma unroll
@@ -245,35 +396,37 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       const bool valid = 16 * w + t < Lc;
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
-        const float gt = valid ? fmaxf(gg[t][cc], p.g_min) : 0.f;
-        if (!valid) {
-          kk[t][cc] = 0.f;
-          qq[t][cc] = 0.f;
-        }
+        const float gt = valid ? fmaxf(raw.g[t][cc], p.g_min) : 0.f;
         bp[cc] *= __expf(gt);
-        rho[t][cc] = bp[cc];
+        kr[t][cc] = bp[cc];                           // rho, for now
+        kc[t][cc] = valid ? to_f32(raw.k[t][cc]) : 0.f;
+        qr[t][cc] = valid ? to_f32(raw.q[t][cc]) : 0.f;
       }
-      if (!valid) vv[t] = 0.f;
+      vv[t] = (valid && !p_tile) ? to_f32(raw.v[t]) : 0.f;
     }
+    const float beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int r = 16 * w + t;
+      float xq[CPT], xkd[CPT], xkr[CPT], xkc[CPT];
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
-        const int c = CPT * lane + cc;
-        const float rinv = 1.f / rho[t][cc];
-        const float kap = bp[cc] * rinv;
-        const float k0 = kk[t][cc];
-        const float qr = qq[t][cc] * rho[t][cc];
-        const int idx = r * L::LDP + c;
-        store_split<Pol>(sQr, sQrLo, idx, qr);
-        store_split<Pol>(sKd, sKdLo, idx, k0 * rinv);
-        sKr[idx] = from_f32<E>(k0 * rho[t][cc]);
-        sKc[idx] = from_f32<E>(k0 * kap);
-        qq[t][cc] = qr;                  // q rho
-        gg[t][cc] = k0 * kap;            // k kappa
-        kk[t][cc] = k0 * rho[t][cc];     // k rho
+        const float rho = kr[t][cc];
+        const float rinv = __builtin_amdgcn_rcpf(rho);
+        const float k0 = kc[t][cc];
+        xq[cc] = qr[t][cc] * rho;
+        xkd[cc] = k0 * rinv;
+        xkr[cc] = k0 * rho;
+        xkc[cc] = k0 * (bp[cc] * rinv);
+        qr[t][cc] = xq[cc];      // q rho
+        kr[t][cc] = xkr[cc];     // k rho
+        kc[t][cc] = xkc[cc];     // k kappa
       }
+      const int idx = r * L::LDP + CPT * lane;
+      store_row_split<Pol, CPT>(sQr + idx, sQrLo + idx, xq);
+      store_row_split<Pol, CPT>(sKd + idx, sKdLo + idx, xkd);
+      store_row<Pol, CPT>(sKr + idx, xkr);
+      store_row<Pol, CPT>(sKc + idx, xkc);
     }
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) sBP[w * DK + CPT * lane + cc] = bp[cc];
@@ -295,223 +448,229 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
       if (w == 0) {
         sDecay[c] = Pb[0] * Pb[1] * Pb[2] * Pb[3];
-        sPair[c] = Pb[1];               // gap for sub-block pair (2, 0)
-        sPair[DK + c] = Pb[2];          // (3, 1)
+        sPair[c] = Pb[1];                   // gap for sub-block pair (2, 0)
+        sPair[DK + c] = Pb[2];              // (3, 1)
         sPair[2 * DK + c] = Pb[1] * Pb[2];  // (3, 0)
       }
     }
     __syncthreads();
 
     // ================= prologue 2: A (fp32) and M (hi, lo) sub-blocks ====================
-    {
-      // diagonal block w of M from split operands (the largest entries of M)
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int pp = 0; pp < NS; ++pp) {
-        const int rowq = 16 * w + ln;
-        const Frag bh = Pol::load(sQr, L::LDP, rowq, pp, q4);
-        const Frag ah = Pol::load(sKd, L::LDP, rowq, pp, q4);
-        acc = Pol::mma(ah, bh, acc);
-        if constexpr (Pol::kSplit) {
-          acc = Pol::mma(Pol::load(sKdLo, L::LDP, rowq, pp, q4), bh, acc);
-          acc = Pol::mma(ah, Pol::load(sQrLo, L::LDP, rowq, pp, q4), acc);
-        }
-      }
-      // register e: row r = 16 w + ln, column s = 16 w + 4 q4 + e
-      const int r = 16 * w + ln;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = 16 * w + 4 * q4 + e;
-        store_split<Pol>(sM, sMLo, r * L::LDT + s, s > r ? 0.f : acc[e]);
-      }
-    }
-#pragma unroll 1
-    for (int task = 4 * w; task < 4 * w + 4; ++task) {
-      const bool isM = task >= 10;
-      const int bi = kTaskI[task], bj = kTaskJ[task];
-      const E* rowt = isM ? sQr : sKr;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int pp = 0; pp < NS; ++pp) {
-        const Frag bfr = Pol::load(rowt, L::LDP, 16 * bi + ln, pp, q4);
-        Frag afr;
-        if (bi == bj) {
-          afr = Pol::load(sKd, L::LDP, 16 * bj + ln, pp, q4);
-        } else if (bi - bj == 1) {
-          afr = Pol::load(sKc, L::LDP, 16 * bj + ln, pp, q4);
-        } else {
-          const int pi = (bi == 2) ? 0 : (bj == 1 ? 1 : 2);
-          afr = Pol::load_scaled(sKc, L::LDP, 16 * bj + ln, pp, q4, sPair + pi * DK);
-        }
-        acc = Pol::mma(afr, bfr, acc);
-      }
-      // register e: row r = 16 bi + ln, column s = 16 bj + 4 q4 + e
-      const int r = 16 * bi + ln;
-      if (!isM) {
-        const float br = sBeta[r];
-        f32x4 outv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = 16 * bj + 4 * q4 + e;
-          outv[e] = (bi == bj && s >= r) ? 0.f : br * acc[e];
-        }
-        *reinterpret_cast<f32x4*>(sA + r * L::LDA + 16 * bj + 4 * q4) = outv;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          store_split<Pol>(sM, sMLo, r * L::LDT + 16 * bj + 4 * q4 + e, acc[e]);
-      }
+    // wave w: row-block w of A (blocks (w, j <= w)) and row-block 3 - w of M; every wave runs
+    // 28 MFMAs (M's diagonal block uses split operands). The row blocks are compile-time per
+    // wave so each slice's fragment loads issue together.
+    switch (w) {
+      case 0: am_rows<Pol, L, DK, 0>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
+      case 1: am_rows<Pol, L, DK, 1>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
+      case 2: am_rows<Pol, L, DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
+      default: am_rows<Pol, L, DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
     }
     __syncthreads();
 
     // ================= prologue 3: recurrence operand tiles; fp32 inverse =================
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int r = 16 * w + t;
-#pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        const int c = CPT * lane + cc;
-        store_split<Pol>(sQg, sQgLo, r * L::LDP + c, qq[t][cc] * fs[cc]);   // q e^Gamma
-        store_split<Pol>(sKhT, sKhTLo, c * L::LDT + r, gg[t][cc] * fe[cc]); // k e^{GL-Gamma}
-        sKg[r * L::LDP + c] = from_f32<E>(kk[t][cc] * fs[cc]);              // k e^Gamma
-      }
-    }
     if (w == 0) {
-      // diagonal sub-blocks: lane = (block bi, column j), forward substitution in fp32
-      const int bi = lane >> 4, j = lane & 15;
+      // diagonal sub-blocks: lane = (block bi, column jc); right-looking substitution in fp32:
+      // once x_s is final it is removed from every later row
+      const int bi = lane >> 4, jc = lane & 15;
+      const float* Ab = sA + 16 * bi * L::LDA + 16 * bi;
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
 #pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        float acc = 0.f;
+      for (int s = 0; s < 15; ++s) {
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc += sA[(16 * bi + r) * L::LDA + 16 * bi + s] * x[s];
-        if (r > j) x[r] = -acc;
+        for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-Ab[r * L::LDA + s], x[s], x[r]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sA[(16 * bi + r) * L::LDA + 16 * bi + j] = x[r];
+      for (int r = 0; r < 16; ++r) sA[(16 * bi + r) * L::LDA + 16 * bi + jc] = x[r];
+    }
+    {
+      const int c0 = CPT * lane;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = 16 * w + t;
+        float xq[CPT], xk[CPT];
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+          xq[cc] = qr[t][cc] * fs[cc];   // q e^{Gamma}
+          xk[cc] = kr[t][cc] * fs[cc];   // k e^{Gamma}
+        }
+        store_row_split<Pol, CPT>(sQg + r * L::LDP + c0, sQgLo + r * L::LDP + c0, xq);
+        store_row<Pol, CPT>(sKg + r * L::LDP + c0, xk);
+      }
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        float col[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) col[t] = kc[t][cc] * fe[cc];   // k e^{Gamma_L - Gamma}
+        store16_split<Pol>(sKhT + (c0 + cc) * L::LDT + 16 * w, sKhTLo + (c0 + cc) * L::LDT + 16 * w, col);
+      }
     }
     __syncthreads();
-    // off-diagonal sub-blocks T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj on fp32 MFMA (16x16x4).
+    // off-diagonal sub-blocks on fp32 MFMA (16x16x4) in two levels:
+    //   level 1: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22
+    //   level 2: the lower-left 32x32 block -T_[23][23] A_[23][01] T_[01][01], one 16x16 block
+    //   per wave (T_20, T_21, T_30, T_31).
     // T_ij (i > j) is stored in the free upper position (j, i) so that A_ij stays readable.
     auto tblk = [&](int bi, int bj) -> float* {
       return bi == bj ? sA + 16 * bi * L::LDA + 16 * bi : sA + 16 * bj * L::LDA + 16 * bi;
     };
-    auto offdiag = [&](int bi, int bj) {
-      f32x4 X = zero4();
-      for (int m = bj; m < bi; ++m) {
-        const float* Tm = tblk(m, bj);
+    auto ablk = [&](int bi, int bj) -> const float* { return sA + 16 * bi * L::LDA + 16 * bj; };
+    // X += A_blk * T_blk (16x16x16, natural k order)
+    auto mm_acc = [&](f32x4 X, const float* Ab, const float* Tb) -> f32x4 {
 #pragma unroll
-        for (int kk2 = 0; kk2 < 4; ++kk2) {
-          const float a = sA[(16 * bi + ln) * L::LDA + 16 * m + 4 * kk2 + q4];
-          const float bb = Tm[(4 * kk2 + q4) * L::LDA + ln];
-          X = mma_f32(a, bb, X);
-        }
-      }
-      const float* Ti = tblk(bi, bi);
-      f32x4 Y = zero4();
+      for (int kk2 = 0; kk2 < 4; ++kk2)
+        X = mma_f32(Ab[ln * L::LDA + 4 * kk2 + q4], Tb[(4 * kk2 + q4) * L::LDA + ln], X);
+      return X;
+    };
+    // Y += T_blk * X with X in accumulator layout (slice e holds rows 4 q4 + e)
+    auto mm_reg = [&](f32x4 Y, const float* Tb, f32x4 X) -> f32x4 {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Y = mma_f32(Ti[ln * L::LDA + 4 * q4 + e], X[e], Y);
+      for (int e = 0; e < 4; ++e) Y = mma_f32(Tb[ln * L::LDA + 4 * q4 + e], X[e], Y);
+      return Y;
+    };
+    auto put = [&](int bi, int bj, f32x4 Y) {
       float* To = tblk(bi, bj);
 #pragma unroll
       for (int e = 0; e < 4; ++e) To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
     };
-    if (w < 3) offdiag(w + 1, w);
+    if (w < 2) {
+      const int lo = 2 * w;   // (1, 0) or (3, 2)
+      const f32x4 X = mm_acc(zero4(), ablk(lo + 1, lo), tblk(lo, lo));
+      put(lo + 1, lo, mm_reg(zero4(), tblk(lo + 1, lo + 1), X));
+    }
     __syncthreads();
-    if (w < 2) offdiag(w + 2, w);
-    __syncthreads();
-    if (w == 0) offdiag(3, 0);
+    {
+      const int bj = w & 1;          // column block 0 or 1
+      const bool row3 = w >= 2;      // row block 2 or 3
+      f32x4 X2, X3 = zero4();        // X_2j, X_3j = A_[2|3],[01] T_[01],j
+      if (bj == 0) {
+        X2 = mm_acc(mm_acc(zero4(), ablk(2, 0), tblk(0, 0)), ablk(2, 1), tblk(1, 0));
+        if (row3) X3 = mm_acc(mm_acc(zero4(), ablk(3, 0), tblk(0, 0)), ablk(3, 1), tblk(1, 0));
+      } else {
+        X2 = mm_acc(zero4(), ablk(2, 1), tblk(1, 1));
+        if (row3) X3 = mm_acc(zero4(), ablk(3, 1), tblk(1, 1));
+      }
+      f32x4 Y;
+      if (!row3) Y = mm_reg(zero4(), tblk(2, 2), X2);
+      else Y = mm_reg(mm_reg(zero4(), tblk(3, 2), X2), tblk(3, 3), X3);
+      put(row3 ? 3 : 2, bj, Y);
+    }
     __syncthreads();
 
-    // T' = T diag(beta), rounded once complete (hi, lo)
+    // T' = T diag(beta), rounded once complete (hi, lo): thread = (row r, 16 columns)
     {
       const int r = tid >> 2;
       const int s0 = 16 * (tid & 3);
-      const int bi = r >> 4, bj = s0 >> 4;
-      const float* Tb = tblk(bi, bj);
+      const float* Tb = tblk(r >> 4, s0 >> 4) + (r & 15) * L::LDA;
+      float row[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int s = s0 + u;
-        const float val = s <= r ? Tb[(r & 15) * L::LDA + u] * sBeta[s] : 0.f;
-        store_split<Pol>(sT, sTLo, r * L::LDT + s, val);
+      for (int u = 0; u < 16; u += 4) {
+        const f32x4 tv = *reinterpret_cast<const f32x4*>(Tb + u);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(sBeta + s0 + u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) row[u + e] = (s0 + u + e <= r) ? tv[e] * bv[e] : 0.f;
       }
+      store16_split<Pol>(sT + r * L::LDT + s0, sTLo + r * L::LDT + s0, row);
     }
     __syncthreads();
     // value tile, transposed, into region Y (A / T are dead now)
-#pragma unroll
-    for (int t = 0; t < 16; ++t) sVT[lane * L::LDT + 16 * w + t] = from_f32<E>(vv[t]);
+    store16<Pol>(sVT + lane * L::LDT + 16 * w, vv);
     __syncthreads();
 
     // ================= serial step: this wave's 16 value columns ============================
+    // Each product loads a batch of A fragments from LDS first and then issues its MFMAs, so
+    // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
     Frag Sh[NS], Sl[NS];
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
-    // X = V - (K e^Gamma) S, in fp32
+    f32x4 U[4], O[4];
+    // O = (Q e^Gamma) S first, while S is split
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+      Frag qh[4], ql[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        qh[rb] = Pol::load(sQg, L::LDP, 16 * rb + ln, pp, q4);
+        if constexpr (Pol::kSplit) ql[rb] = Pol::load(sQgLo, L::LDP, 16 * rb + ln, pp, q4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        O[rb] = Pol::mma(qh[rb], Sh[pp], pp == 0 ? zero4() : O[rb]);
+        if constexpr (Pol::kSplit) {
+          O[rb] = Pol::mma(ql[rb], Sh[pp], O[rb]);
+          O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
+        }
+      }
+    }
+    // X = (K e^Gamma) S - V, in fp32
     f32x4 X[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+      const E* vsrc = sVT + (16 * w + ln) * L::LDT + 16 * rb + 4 * q4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[rb][e] = -to_f32(sVT[(16 * w + ln) * L::LDT + 16 * rb + 4 * q4 + e]);
+      for (int e = 0; e < 4; ++e) X[rb][e] = -to_f32(vsrc[e]);
     }
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
+      Frag kg[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        X[rb] = Pol::mma(Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4), Sh[pp], X[rb]);
+      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
     }
-    // (X holds K_Gamma S - V; U = T' (V - K_Gamma S) = -T' X)
+    // U = T' (V - K_Gamma S) = -T' X
     Frag Xh[NT], Xl[NT];
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
-    f32x4 U[4], O[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      U[rb] = zero4();
-      O[rb] = zero4();
-    }
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) {
+      Frag th[4], tl[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         if (pp < Pol::slices_blocks(rb + 1)) {
-          const Frag th = Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4);
-          U[rb] = Pol::mma(th, Xh[pp], U[rb]);
+          th[rb] = Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4);
+          if constexpr (Pol::kSplit) tl[rb] = Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
           if constexpr (Pol::kSplit) {
-            U[rb] = Pol::mma(Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4), Xh[pp], U[rb]);
-            U[rb] = Pol::mma(th, Xl[pp], U[rb]);
+            U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
+            U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
           }
         }
       }
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
-    // O = (Q e^Gamma) S + M U
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const Frag qh = Pol::load(sQg, L::LDP, 16 * rb + ln, pp, q4);
-        O[rb] = Pol::mma(qh, Sh[pp], O[rb]);
-        if constexpr (Pol::kSplit) {
-          O[rb] = Pol::mma(Pol::load(sQgLo, L::LDP, 16 * rb + ln, pp, q4), Sh[pp], O[rb]);
-          O[rb] = Pol::mma(qh, Sl[pp], O[rb]);
-        }
-      }
-    }
+    // O += M U
     Frag Uh[NT], Ul[NT];
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(U, pp, Uh[pp], Ul[pp]);
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) {
+      Frag mh[4], ml[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         if (pp < Pol::slices_blocks(rb + 1)) {
-          const Frag mh = Pol::load(sM, L::LDT, 16 * rb + ln, pp, q4);
-          O[rb] = Pol::mma(mh, Uh[pp], O[rb]);
+          mh[rb] = Pol::load(sM, L::LDT, 16 * rb + ln, pp, q4);
+          if constexpr (Pol::kSplit) ml[rb] = Pol::load(sMLo, L::LDT, 16 * rb + ln, pp, q4);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          O[rb] = Pol::mma(mh[rb], Uh[pp], O[rb]);
           if constexpr (Pol::kSplit) {
-            O[rb] = Pol::mma(Pol::load(sMLo, L::LDT, 16 * rb + ln, pp, q4), Uh[pp], O[rb]);
-            O[rb] = Pol::mma(mh, Ul[pp], O[rb]);
+            O[rb] = Pol::mma(ml[rb], Uh[pp], O[rb]);
+            O[rb] = Pol::mma(mh[rb], Ul[pp], O[rb]);
           }
         }
       }
@@ -536,12 +695,21 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) {
 #pragma unroll
-      for (int t = 0; t < NTD; ++t) {
-        const Frag kh = Pol::load(sKhT, L::LDT, 16 * t + ln, pp, q4);
-        S[t] = Pol::mma(kh, Uh[pp], S[t]);
-        if constexpr (Pol::kSplit) {
-          S[t] = Pol::mma(Pol::load(sKhTLo, L::LDT, 16 * t + ln, pp, q4), Uh[pp], S[t]);
-          S[t] = Pol::mma(kh, Ul[pp], S[t]);
+      for (int t0 = 0; t0 < NTD; t0 += 4) {
+        Frag kh[4], kl[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          kh[t] = Pol::load(sKhT, L::LDT, 16 * (t0 + t) + ln, pp, q4);
+          if constexpr (Pol::kSplit) kl[t] = Pol::load(sKhTLo, L::LDT, 16 * (t0 + t) + ln, pp, q4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          S[t0 + t] = Pol::mma(kh[t], Uh[pp], S[t0 + t]);
+          if constexpr (Pol::kSplit) {
+            S[t0 + t] = Pol::mma(kl[t], Uh[pp], S[t0 + t]);
+            S[t0 + t] = Pol::mma(kh[t], Ul[pp], S[t0 + t]);
+          }
         }
       }
     }
