@@ -35,6 +35,8 @@
 // Value columns of S never mix, so each wave owns 16 columns of S in its MFMA accumulators
 // for the whole sequence (the state never leaves registers between chunks). The four waves
 // share the per-chunk prologue through LDS.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -61,30 +63,30 @@ struct ChunkLayout {
   static constexpr size_t oKr = oKdLo + kLo * tP;
   static constexpr size_t oKc = oKr + tP;
   static constexpr size_t kXA = oKc + tP;
-  // ---- region X, recurrence view: Q e^Gamma (hi, lo), (K e^{GL-Gamma})^T (hi, lo),
-  //      K e^Gamma, T diag(beta) (hi, lo)
-  static constexpr size_t oQg = 0;
-  static constexpr size_t oQgLo = oQg + tP;
-  static constexpr size_t oKhT = oQgLo + kLo * tP;
+  // ---- region X, recurrence view: Q e^Gamma (hi, lo) over q rho (hi, lo) and K e^Gamma over
+  //      k / rho, row for row (a thread rewrites in place the elements it reads back), then
+  //      (K e^{GL-Gamma})^T (hi, lo) over k rho and k kappa, which are dead by then
+  static constexpr size_t oQg = oQr;
+  static constexpr size_t oQgLo = oQrLo;
+  static constexpr size_t oKg = oKd;
+  static constexpr size_t oKhT = oKr;
   static constexpr size_t oKhTLo = oKhT + tT;
-  static constexpr size_t oKg = oKhTLo + kLo * tT;
-  static constexpr size_t oT = oKg + tP;
-  static constexpr size_t oTLo = oT + t64;
-  static constexpr size_t kXD = oTLo + kLo * t64;
+  static constexpr size_t kXD = oKhTLo + kLo * tT;
   static constexpr size_t kX = kXA > kXD ? kXA : kXD;
-  // ---- region Y: fp32 A / T, later V^T of the value tile
+  // ---- region Y: fp32 A / T
   static constexpr size_t oA = kX;
-  static constexpr size_t oVT = kX;
-  static constexpr size_t kY = size_t(64) * LDA * 4 > t64 ? size_t(64) * LDA * 4 : t64;
-  // ---- region Z: M (hi, lo)
+  static constexpr size_t kY = size_t(64) * LDA * 4;
+  // ---- region Z: M (hi, lo); region W: T diag(beta) (hi, lo), both written during the prologue
+  //      while region X still holds the prologue tiles
   static constexpr size_t oM = oA + kY;
   static constexpr size_t oMLo = oM + t64;
+  static constexpr size_t oT = oMLo + kLo * t64;
+  static constexpr size_t oTLo = oT + t64;
   // ---- small
-  static constexpr size_t oBeta = oMLo + kLo * t64;
+  static constexpr size_t oBeta = oTLo + kLo * t64;
   static constexpr size_t oBP = oBeta + 64 * 4;        // [4][DK] sub-block decay products
   static constexpr size_t oDecay = oBP + 4 * DK * 4;   // [DK] whole-chunk decay
-  static constexpr size_t oPair = oDecay + DK * 4;     // [3][DK] gaps between sub-blocks
-  static constexpr size_t kBytes = oPair + 3 * DK * 4;
+  static constexpr size_t kBytes = oDecay + DK * 4;
   static_assert(kBytes <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
@@ -97,80 +99,22 @@ __device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E
   if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(x - to_f32(h));
 }
 
-// 16 consecutive values (one 16-token column of a transposed tile) with vector stores
-template <class Pol>
-__device__ __forceinline__ void store16(typename Pol::E* dst, const float* x) {
-  if constexpr (sizeof(typename Pol::E) == 2) {
-#pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *reinterpret_cast<bf16x4*>(dst + e) =
-          bf16x4{(__bf16)x[e], (__bf16)x[e + 1], (__bf16)x[e + 2], (__bf16)x[e + 3]};
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; e += 4)
-      *reinterpret_cast<f32x4*>(dst + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
-  }
-}
-
-template <class Pol>
-__device__ __forceinline__ void store16_split(typename Pol::E* hi, typename Pol::E* lo,
-                                              const float* x) {
-  if constexpr (Pol::kSplit) {
-#pragma unroll
-    for (int e0 = 0; e0 < 16; e0 += 4) {
-      bf16x4 a, c;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = (__bf16)x[e0 + e];
-        c[e] = (__bf16)(x[e0 + e] - (float)a[e]);
-      }
-      *reinterpret_cast<bf16x4*>(hi + e0) = a;
-      *reinterpret_cast<bf16x4*>(lo + e0) = c;
-    }
-  } else {
-    store16<Pol>(hi, x);
-  }
-}
-
-// CPT consecutive channels of one token row
-template <class Pol, int CPT>
-__device__ __forceinline__ void store_row(typename Pol::E* dst, const float* x) {
-  if constexpr (CPT == 2 && sizeof(typename Pol::E) == 2) {
-    *reinterpret_cast<bf16x2*>(dst) = bf16x2{(__bf16)x[0], (__bf16)x[1]};
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) dst[cc] = from_f32<typename Pol::E>(x[cc]);
-  }
-}
-
-template <class Pol, int CPT>
-__device__ __forceinline__ void store_row_split(typename Pol::E* hi, typename Pol::E* lo,
-                                                const float* x) {
-  if constexpr (Pol::kSplit && CPT == 2) {
-    const bf16x2 h = bf16x2{(__bf16)x[0], (__bf16)x[1]};
-    *reinterpret_cast<bf16x2*>(hi) = h;
-    *reinterpret_cast<bf16x2*>(lo) =
-        bf16x2{(__bf16)(x[0] - (float)h[0]), (__bf16)(x[1] - (float)h[1])};
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) store_split<Pol>(hi, lo, cc, x[cc]);
-  }
-}
-
 // Row-block IA of A and row-block 3 - IA of M for one wave. Column operands: k / rho on the
 // diagonal block, k kappa next to it, k kappa times the decay gap further down.
 template <class Pol, class L, int DK, int IA>
 __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typename Pol::E* sKd,
                                         const typename Pol::E* sKdLo, const typename Pol::E* sKc,
                                         const typename Pol::E* sQr, const typename Pol::E* sQrLo,
-                                        const float* sPair, const float* sBeta, float* sA,
-                                        typename Pol::E* sM, typename Pol::E* sMLo, int ln, int q4) {
+                                        const float* sBP, const float* sBeta, float* sA,
+                                        typename Pol::E* sM, typename Pol::E* sMLo,
+                                        typename Pol::E* sT, typename Pol::E* sTLo, int ln, int q4) {
   using Frag = typename Pol::Frag;
   constexpr int NS = Pol::slices(DK);
   constexpr int IM = 3 - IA;
-  // gap factor index of a pair (i, j) with i - j >= 2: (2,0) -> 0, (3,1) -> 1, (3,0) -> 2
-  constexpr int gapA0 = IA == 2 ? 0 : 2, gapA1 = 1;
-  constexpr int gapM0 = IM == 2 ? 0 : 2, gapM1 = 1;
+  // gap between sub-blocks i and j (i - j >= 2): the whole-sub-block decays strictly between
+  // them, (2, 0) -> P_1, (3, 1) -> P_2, (3, 0) -> P_1 P_2 (sBP row b holds P_b per channel)
+  const float* P1 = sBP + DK;
+  const float* P2 = sBP + 2 * DK;
   f32x4 accA[4], accM[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
@@ -186,15 +130,15 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     for (int jb = 0; jb <= IA; ++jb) {
       if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == IA - 1) colA[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
-      else colA[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4,
-                                       sPair + (jb == 0 ? gapA0 : gapA1) * DK);
+      else if (jb == 0 && IA == 3) colA[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
+      else colA[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
     }
 #pragma unroll
     for (int jb = 0; jb <= IM; ++jb) {
       if (jb == IM) colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == IM - 1) colM[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
-      else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4,
-                                       sPair + (jb == 0 ? gapM0 : gapM1) * DK);
+      else if (jb == 0 && IM == 3) colM[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
+      else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
     }
     if constexpr (Pol::kSplit) {
       dKl = Pol::load(sKdLo, L::LDP, 16 * IM + ln, pp, q4);
@@ -230,46 +174,184 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       store_split<Pol>(sM, sMLo, rm * L::LDT + s, (jb == IM && s > rm) ? 0.f : accM[jb][e]);
     }
   }
+  // Diagonal block IA of T = (I + A)^{-1} in fp32, by right-looking substitution: the quad of
+  // lanes 4 jc .. 4 jc + 3 solves column jc, lane part pp holding rows pp, pp + 4, pp + 8,
+  // pp + 12. Once x_s is final its owner broadcasts it inside the quad and it is removed from
+  // every row (the block is zero on and above its diagonal, so later rows only). The block
+  // was written just above by other lanes of this wave: a wave-scope fence orders those LDS
+  // writes before the reads.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  {
+    const int lane = 16 * q4 + ln;
+    const int jc = lane >> 2, pp = lane & 3;
+    const float* Ab = sA + 16 * IA * L::LDA + 16 * IA;
+    f32x4 arow[4][4];   // rows pp + 4 i, columns 4 m .. 4 m + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        arow[i][m] = *reinterpret_cast<const f32x4*>(Ab + (pp + 4 * i) * L::LDA + 4 * m);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (pp + 4 * i == jc) ? 1.f : 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 15; ++s2) {
+      float xs;
+      switch (s2 & 3) {
+        case 0: xs = quad_bcast<0>(x[s2 >> 2]); break;
+        case 1: xs = quad_bcast<1>(x[s2 >> 2]); break;
+        case 2: xs = quad_bcast<2>(x[s2 >> 2]); break;
+        default: xs = quad_bcast<3>(x[s2 >> 2]); break;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = fmaf(-arow[i][s2 >> 2][s2 & 3], xs, x[i]);
+    }
+    const float bj = sBeta[16 * IA + jc];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * IA + pp + 4 * i;
+      sA[r * L::LDA + 16 * IA + jc] = x[i];
+      store_split<Pol>(sT, sTLo, r * L::LDT + 16 * IA + jc, x[i] * bj);
+    }
+  }
 }
 
-// Raw inputs of one chunk held by one thread: CPT key channels x 16 tokens of its
-// sub-block, one value column x 16 tokens, and (lanes < 16) one beta.
-template <typename Tio, int CPT>
+// N input elements of one thread, bf16 ones two to a register
+template <typename T, int N>
+struct Packed {
+  T x[N];
+  __device__ __forceinline__ float get(int i) const { return to_f32(x[i]); }
+  __device__ __forceinline__ void set(int i, T a) { x[i] = a; }
+};
+template <int N>
+struct Packed<__bf16, N> {
+  bf16x2 x[N / 2];
+  __device__ __forceinline__ float get(int i) const { return (float)x[i >> 1][i & 1]; }
+  __device__ __forceinline__ void set(int i, __bf16 a) { x[i >> 1][i & 1] = a; }
+};
+
+// four consecutive elements of one input row (one vector load)
+template <typename T> struct Quad;
+template <> struct Quad<__bf16> { using type = bf16x4; };
+template <> struct Quad<float> { using type = f32x4; };
+
+// Prologue thread mapping: wave w owns the 16-token sub-block w; inside it, lane = (token group
+// grp, channel quad c4) with DK / 4 lanes per token row, so each thread holds DK / 16
+// consecutive tokens (16 w + grp DK / 16 + t) of four consecutive key channels (4 c4 ..).
+template <int DK>
+struct ProMap {
+  static constexpr int kLPT = DK / 4;      // lanes per token row
+  static constexpr int kNG = 64 / kLPT;    // token groups per sub-block
+  static constexpr int kTPT = DK / 16;     // tokens per thread
+};
+
+// Raw inputs of one chunk held by one thread: g, k, q of its prologue elements; for each of
+// the four 16-token row blocks rb, four value columns 16 w + 4 (lane % 16 / 4) .. + 3 of token
+// 16 rb + 4 (lane / 16) + lane % 4 (a quad transpose turns them into MFMA accumulator layout);
+// and (lanes < 16) the beta of token 16 w + lane.
+template <typename Tio, int DK>
 struct RawChunk {
-  float g[16][CPT];
-  Tio k[16][CPT];
-  Tio q[16][CPT];
-  Tio v[16];
+  static constexpr int kTPT = ProMap<DK>::kTPT;
+  f32x4 g[kTPT];
+  typename Quad<Tio>::type k[kTPT], q[kTPT], v[4];
   float beta;
 };
 
-template <typename Tio, int DK, int CPT>
-__device__ __forceinline__ void load_chunk(RawChunk<Tio, CPT>& x, const ChunkParams& p,
-                                           int cstart, int Lc, int w, int lane, int h,
-                                           int vcol0, bool p_tile) {
-  const Tio* __restrict__ gq = reinterpret_cast<const Tio*>(p.q);
-  const Tio* __restrict__ gk = reinterpret_cast<const Tio*>(p.k);
-  const Tio* __restrict__ gv = reinterpret_cast<const Tio*>(p.v);
+// Loads of one chunk. Token offsets are wave-uniform (scalar address arithmetic) and each lane
+// adds a fixed 32-bit byte offset. With kFull false (the last, ragged chunk of a sequence)
+// rows past its end read the chunk's first row instead, which always exists.
+// Address of a lane's element: base + uniform_elems + lane_elems (elements of type E), read
+// as type T; with kFull false and !ok, base + fallback_elems instead.
+template <bool kFull, typename E, typename T>
+__device__ __forceinline__ const T* lane_ptr(const void* base, size_t uniform_elems,
+                                             uint32_t lane_elems, bool ok, size_t fallback_elems) {
+  const E* b = reinterpret_cast<const E*>(base);
+  const char* u = reinterpret_cast<const char*>(b + uniform_elems);
+  const char* a = u + lane_elems * uint32_t(sizeof(E));
+  if constexpr (!kFull) a = ok ? a : reinterpret_cast<const char*>(b + fallback_elems);
+  return reinterpret_cast<const T*>(a);
+}
+
+// Pieces of a chunk's raw inputs, loaded separately so that their issue can be spread over
+// the previous chunk: kind G, K or Q for the thread's tokens [kLo, kHi) out of eight (scaled to
+// its token count), or V (values and beta).
+enum : int { kLoadG = 1, kLoadK = 2, kLoadQ = 4, kLoadV = 8, kLoadAll = 15 };
+
+template <bool kFull, int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8>
+__device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkParams& p, int cstart,
+                                           int Lc, int w, int lane, int h, int vcol0) {
+  using M = ProMap<DK>;
+  using Q4 = typename Quad<Tio>::type;
   const int H = p.H;
+  const int grp = lane / M::kLPT;
+  const int c0 = 4 * (lane % M::kLPT);
+  const size_t row = size_t(H) * DK;                 // elements from one token to the next
+  // prologue elements: token cstart + 16 w + grp kTPT + t, channels c0 .. c0 + 3
+  const uint32_t lk = uint32_t((grp * M::kTPT * H + h) * DK + c0);
+  const size_t fk = (size_t(cstart) * H + h) * DK + c0;   // fallback: the chunk's first row
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int r = 16 * w + t;
-    const int tok = cstart + (r < Lc ? r : 0);   // rows past the end read a valid row
-    const size_t base = (size_t(tok) * H + h) * DK + CPT * lane;
+  for (int t = kLo * M::kTPT / 8; t < kHi * M::kTPT / 8; ++t) {
+    const bool ok = 16 * w + grp * M::kTPT + t < Lc;
+    const size_t u = size_t(cstart + 16 * w + t) * row;
+    if constexpr ((kParts & kLoadG) != 0) x.g[t] = *lane_ptr<kFull, float, f32x4>(p.g, u, lk, ok, fk);
+    if constexpr ((kParts & kLoadK) != 0) x.k[t] = *lane_ptr<kFull, Tio, Q4>(p.k, u, lk, ok, fk);
+    if constexpr ((kParts & kLoadQ) != 0) x.q[t] = *lane_ptr<kFull, Tio, Q4>(p.q, u, lk, ok, fk);
+  }
+  if constexpr ((kParts & kLoadV) == 0) return;
+  // values: token cstart + 16 rb + 4 q4 + lane % 4, columns vcol0 + 16 w + 4 (ln / 4) .. + 3
+  const int q4 = lane >> 4, ln = lane & 15;
+  const int vc = vcol0 + 16 * w + 4 * (ln >> 2);
+  const uint32_t lv = uint32_t(((4 * q4 + (ln & 3)) * H + h) * p.dv + vc);
+  const size_t fv = (size_t(cstart) * H + h) * p.dv + vc;
+  const size_t vrow = size_t(H) * p.dv;
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      x.g[t][cc] = p.g[base + cc];
-      x.k[t][cc] = gk[base + cc];
-      x.q[t][cc] = gq[base + cc];
-    }
-    x.v[t] = gv[(size_t(tok) * H + h) * p.dv + vcol0 + lane];
+  for (int rb = 0; rb < 4; ++rb) {
+    const bool ok = 16 * rb + 4 * q4 + (ln & 3) < Lc;
+    x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, size_t(cstart + 16 * rb) * vrow, lv, ok, fv);
   }
   x.beta = 0.f;
   if (lane < 16) {
-    const int r = 16 * w + lane;
-    x.beta = p.beta[size_t(cstart + (r < Lc ? r : 0)) * H + h];
+    const bool ok = 16 * w + lane < Lc;
+    const uint32_t lb = uint32_t((16 * w + lane) * H + h);
+    const size_t fb = size_t(cstart) * H + h;
+    x.beta = *lane_ptr<kFull, float, float>(p.beta, size_t(cstart) * H, lb, ok, fb);
   }
-  (void)p_tile;
+}
+
+template <int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8>
+__device__ __forceinline__ void load_chunk_any(RawChunk<Tio, DK>& x, const ChunkParams& p,
+                                               int cstart, int Lc, int w, int lane, int h,
+                                               int vcol0) {
+  if (Lc == kChunk) load_chunk<true, kParts, Tio, DK, kLo, kHi>(x, p, cstart, Lc, w, lane, h, vcol0);
+  else load_chunk<false, kParts, Tio, DK, kLo, kHi>(x, p, cstart, Lc, w, lane, h, vcol0);
+}
+
+// four consecutive elements (8 bytes for bf16, 16 for fp32) and their hi / lo split
+template <class Pol>
+__device__ __forceinline__ void store4(typename Pol::E* dst, const float* x) {
+  if constexpr (sizeof(typename Pol::E) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  else
+    *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+}
+
+template <class Pol>
+__device__ __forceinline__ void store4_split(typename Pol::E* hi, typename Pol::E* lo,
+                                             const float* x) {
+  if constexpr (Pol::kSplit) {
+    bf16x4 a, c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (__bf16)x[e];
+      c[e] = (__bf16)(x[e] - (float)a[e]);
+    }
+    *reinterpret_cast<bf16x4*>(hi) = a;
+    *reinterpret_cast<bf16x4*>(lo) = c;
+  } else {
+    store4<Pol>(hi, x);
+  }
 }
 
 template <class Pol, typename Tio, typename Tout, int DK>
@@ -277,7 +359,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using L = ChunkLayout<Pol, DK>;
   using E = typename Pol::E;
   using Frag = typename Pol::Frag;
-  constexpr int CPT = DK / 64;             // key channels per thread in the prologue
+  using PM = ProMap<DK>;
+  constexpr int TPT = PM::kTPT;            // tokens per thread in the prologue
   constexpr int NS = Pol::slices(DK);      // k-slices over key channels
   constexpr int NT = Pol::slices(64);      // k-slices over the chunk's tokens
   constexpr int NTD = DK / 16;             // 16-row tiles of S per wave
@@ -298,13 +381,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   E* sT = reinterpret_cast<E*>(smem + L::oT);
   E* sTLo = reinterpret_cast<E*>(smem + L::oTLo);
   float* sA = reinterpret_cast<float*>(smem + L::oA);
-  E* sVT = reinterpret_cast<E*>(smem + L::oVT);
   E* sM = reinterpret_cast<E*>(smem + L::oM);
   E* sMLo = reinterpret_cast<E*>(smem + L::oMLo);
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
   float* sBP = reinterpret_cast<float*>(smem + L::oBP);
   float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
-  float* sPair = reinterpret_cast<float*>(smem + L::oPair);
 
   // ---- which (sequence, segment, head, state tile): the tiles of one unit share an XCD
   const int b = blockIdx.x;
@@ -322,7 +403,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int mode = p.mode;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int q4 = lane >> 4;   // k-group of the lane inside an MFMA fragment
   const int ln = lane & 15;   // row / column of the lane inside a 16x16 tile
@@ -369,149 +450,185 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
   }
 
-  // strictly upper sub-blocks of M stay zero for the whole sequence
+  // strictly upper sub-blocks of M and T' stay zero for the whole sequence
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, s = idx & 63;
     if ((s >> 4) > (r >> 4)) {
       sM[r * L::LDT + s] = from_f32<E>(0.f);
-      if constexpr (Pol::kSplit) sMLo[r * L::LDT + s] = from_f32<E>(0.f);
+      sT[r * L::LDT + s] = from_f32<E>(0.f);
+      if constexpr (Pol::kSplit) {
+        sMLo[r * L::LDT + s] = from_f32<E>(0.f);
+        sTLo[r * L::LDT + s] = from_f32<E>(0.f);
+      }
     }
   }
 
-  RawChunk<Tio, CPT> raw;
+  RawChunk<Tio, DK> raw;
 
+  if (bos < eos)
+    load_chunk_any<kLoadAll, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+
+  const int lane0 = lane, q4_0 = q4, ln0 = ln;
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
     const int Lc = min(kChunk, eos - cstart);
-    load_chunk<Tio, DK, CPT>(raw, p, cstart, Lc, w, lane, h, vcol0, p_tile);
+    // lane coordinates re-derived per chunk: the LDS addresses built from them are then
+    // recomputed in the loop (a few integer ops) instead of being hoisted out of it, where
+    // dozens of them would stay live in registers for the whole sequence
+    int lane = lane0, q4 = q4_0, ln = ln0;
+    asm volatile("" : "+v"(lane), "+v"(q4), "+v"(ln));
+    // the next chunk's raw inputs are loaded in small pieces spread over this chunk, once the
+    // prologue has consumed the current ones: issuing them never waits on a full memory
+    // pipeline and their HBM latency is covered
+    const bool more = cstart + kChunk < eos;
+    const int nstart = cstart + kChunk, nLc = min(kChunk, eos - nstart);
+#define KDA_PREFETCH(parts, lo, hi) \
+  if (more) load_chunk_any<parts, Tio, DK, lo, hi>(raw, p, nstart, nLc, w, lane, h, vcol0)
 
     // ================= prologue 1: decay factors and operand tiles ======================
     // rho = e^{lambda} (decay from the sub-block start to token r, inclusive) <= 1;
     // kappa = P / rho (decay after token r to the sub-block end) <= 1; 1/rho <= e^{16|g_min|}
-    float qr[16][CPT], kr[16][CPT], kc[16][CPT], vv[16];
-    float bp[CPT];
+    const int grp = lane / PM::kLPT;
+    const int c0 = 4 * (lane % PM::kLPT);
+    const int rb0 = 16 * w + grp * TPT;   // first token row of this thread
+    float rho[TPT][4], qv[TPT][4], kv[TPT][4];
+    float lp[4] = {1.f, 1.f, 1.f, 1.f};   // running decay over this thread's tokens
+    // rows past the end of a ragged last chunk count as zero keys and queries with no decay
+    auto raw_in = [&](auto full) {
+      constexpr bool kFull = decltype(full)::value;
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) bp[cc] = 1.f;
+      for (int t = 0; t < TPT; ++t) {
+        const bool valid = kFull || rb0 + t < Lc;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const bool valid = 16 * w + t < Lc;
-#pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        const float gt = valid ? fmaxf(raw.g[t][cc], p.g_min) : 0.f;
-        bp[cc] *= __expf(gt);
-        kr[t][cc] = bp[cc];                           // rho, for now
-        kc[t][cc] = valid ? to_f32(raw.k[t][cc]) : 0.f;
-        qr[t][cc] = valid ? to_f32(raw.q[t][cc]) : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          const float gt = valid ? fmaxf(raw.g[t][c], p.g_min) : 0.f;
+          lp[c] *= __expf(gt);
+          rho[t][c] = lp[c];
+          kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
+          qv[t][c] = valid ? to_f32(raw.q[t][c]) : 0.f;
+        }
       }
-      vv[t] = (valid && !p_tile) ? to_f32(raw.v[t]) : 0.f;
+    };
+    if (Lc == kChunk) raw_in(std::true_type{});
+    else raw_in(std::false_type{});
+    // decay of the earlier token groups of the sub-block (exclusive prefix product across
+    // lanes) and of the whole sub-block; every lane of a channel gets the same bits
+    float bp[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float pre;
+      if constexpr (PM::kNG == 2) {
+        const float o = __shfl_xor(lp[c], 32);
+        pre = grp ? o : 1.f;
+        bp[c] = lp[c] * o;
+      } else {
+        static_assert(PM::kNG == 4, "token groups per sub-block");
+        const float a = __shfl_xor(lp[c], 16);
+        const float pair = lp[c] * a;
+        const float b2 = __shfl_xor(pair, 32);
+        pre = ((grp & 2) ? b2 : 1.f) * ((grp & 1) ? a : 1.f);
+        bp[c] = pair * b2;
+      }
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) rho[t][c] *= pre;
     }
     const float beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int r = 16 * w + t;
-      float xq[CPT], xkd[CPT], xkr[CPT], xkc[CPT];
+    for (int t = 0; t < TPT; ++t) {
+      float xq[4], xkd[4], xkr[4], xkc[4];
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        const float rho = kr[t][cc];
-        const float rinv = __builtin_amdgcn_rcpf(rho);
-        const float k0 = kc[t][cc];
-        xq[cc] = qr[t][cc] * rho;
-        xkd[cc] = k0 * rinv;
-        xkr[cc] = k0 * rho;
-        xkc[cc] = k0 * (bp[cc] * rinv);
-        qr[t][cc] = xq[cc];      // q rho
-        kr[t][cc] = xkr[cc];     // k rho
-        kc[t][cc] = xkc[cc];     // k kappa
+      for (int c = 0; c < 4; ++c) {
+        const float rh = rho[t][c];
+        const float rinv = __builtin_amdgcn_rcpf(rh);
+        const float k0 = kv[t][c];
+        xq[c] = qv[t][c] * rh;
+        xkd[c] = k0 * rinv;
+        xkr[c] = k0 * rh;
+        xkc[c] = k0 * (bp[c] * rinv);
+        qv[t][c] = xq[c];    // q rho
+        kv[t][c] = xkr[c];   // k rho
+        rho[t][c] = xkc[c];  // k kappa
       }
-      const int idx = r * L::LDP + CPT * lane;
-      store_row_split<Pol, CPT>(sQr + idx, sQrLo + idx, xq);
-      store_row_split<Pol, CPT>(sKd + idx, sKdLo + idx, xkd);
-      store_row<Pol, CPT>(sKr + idx, xkr);
-      store_row<Pol, CPT>(sKc + idx, xkc);
+      const int idx = (rb0 + t) * L::LDP + c0;
+      store4_split<Pol>(sQr + idx, sQrLo + idx, xq);
+      store4_split<Pol>(sKd + idx, sKdLo + idx, xkd);
+      store4<Pol>(sKr + idx, xkr);
+      store4<Pol>(sKc + idx, xkc);
     }
-#pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) sBP[w * DK + CPT * lane + cc] = bp[cc];
+    if (grp == 0) *reinterpret_cast<f32x4*>(sBP + w * DK + c0) = f32x4{bp[0], bp[1], bp[2], bp[3]};
     if (lane < 16) sBeta[16 * w + lane] = beta_r;
     __syncthreads();
 
-    // ---- chunk-level factors from the four sub-block products of each channel
-    float fs[CPT], fe[CPT];
+    // ---- chunk-level factors from the four sub-block products of each channel (read-only
+    //      here; the whole-chunk decay is first read after two more barriers)
+    float fs[4], fe[4];
+    {
+      f32x4 Pb[4];
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int c = CPT * lane + cc;
-      const float Pb[4] = {sBP[c], sBP[DK + c], sBP[2 * DK + c], sBP[3 * DK + c]};
-      fs[cc] = 1.f;
-      fe[cc] = 1.f;
+      for (int bb = 0; bb < 4; ++bb) Pb[bb] = *reinterpret_cast<const f32x4*>(sBP + bb * DK + c0);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        if (bb < w) fs[cc] *= Pb[bb];
-        if (bb > w) fe[cc] *= Pb[bb];
+      for (int c = 0; c < 4; ++c) {
+        fs[c] = 1.f;
+        fe[c] = 1.f;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          if (bb < w) fs[c] *= Pb[bb][c];
+          if (bb > w) fe[c] *= Pb[bb][c];
+        }
       }
-      if (w == 0) {
-        sDecay[c] = Pb[0] * Pb[1] * Pb[2] * Pb[3];
-        sPair[c] = Pb[1];                   // gap for sub-block pair (2, 0)
-        sPair[DK + c] = Pb[2];              // (3, 1)
-        sPair[2 * DK + c] = Pb[1] * Pb[2];  // (3, 0)
-      }
+      if (w == 0 && grp == 0)
+        *reinterpret_cast<f32x4*>(sDecay + c0) = Pb[0] * Pb[1] * Pb[2] * Pb[3];
     }
-    __syncthreads();
+
+    KDA_PREFETCH(kLoadG, 0, 2);
 
     // ================= prologue 2: A (fp32) and M (hi, lo) sub-blocks ====================
     // wave w: row-block w of A (blocks (w, j <= w)) and row-block 3 - w of M; every wave runs
     // 28 MFMAs (M's diagonal block uses split operands). The row blocks are compile-time per
     // wave so each slice's fragment loads issue together.
     switch (w) {
-      case 0: am_rows<Pol, L, DK, 0>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
-      case 1: am_rows<Pol, L, DK, 1>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
-      case 2: am_rows<Pol, L, DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
-      default: am_rows<Pol, L, DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sPair, sBeta, sA, sM, sMLo, ln, q4); break;
+      case 0: am_rows<Pol, L, DK, 0>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      case 1: am_rows<Pol, L, DK, 1>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      case 2: am_rows<Pol, L, DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      default: am_rows<Pol, L, DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
     }
+    KDA_PREFETCH(kLoadG, 2, 4);
     __syncthreads();
 
-    // ================= prologue 3: recurrence operand tiles; fp32 inverse =================
-    if (w == 0) {
-      // diagonal sub-blocks: lane = (block bi, column jc); right-looking substitution in fp32:
-      // once x_s is final it is removed from every later row
-      const int bi = lane >> 4, jc = lane & 15;
-      const float* Ab = sA + 16 * bi * L::LDA + 16 * bi;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < 15; ++s) {
-#pragma unroll
-        for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-Ab[r * L::LDA + s], x[s], x[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sA[(16 * bi + r) * L::LDA + 16 * bi + jc] = x[r];
-    }
+    // ================= prologue 3: recurrence operand tiles; off-diagonal inverse ===========
     {
-      const int c0 = CPT * lane;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int r = 16 * w + t;
-        float xq[CPT], xk[CPT];
+      for (int t = 0; t < TPT; ++t) {
+        const int idx = (rb0 + t) * L::LDP + c0;
+        float xq[4], xk[4];
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-          xq[cc] = qr[t][cc] * fs[cc];   // q e^{Gamma}
-          xk[cc] = kr[t][cc] * fs[cc];   // k e^{Gamma}
+        for (int c = 0; c < 4; ++c) {
+          xq[c] = qv[t][c] * fs[c];   // q e^{Gamma}
+          xk[c] = kv[t][c] * fs[c];   // k e^{Gamma}
         }
-        store_row_split<Pol, CPT>(sQg + r * L::LDP + c0, sQgLo + r * L::LDP + c0, xq);
-        store_row<Pol, CPT>(sKg + r * L::LDP + c0, xk);
+        store4_split<Pol>(sQg + idx, sQgLo + idx, xq);
+        store4<Pol>(sKg + idx, xk);
       }
+      KDA_PREFETCH(kLoadG, 4, 6);
+      // (K e^{Gamma_L - Gamma})^T: channel rows, this thread's TPT consecutive tokens
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        float col[16];
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) col[t] = kc[t][cc] * fe[cc];   // k e^{Gamma_L - Gamma}
-        store16_split<Pol>(sKhT + (c0 + cc) * L::LDT + 16 * w, sKhTLo + (c0 + cc) * L::LDT + 16 * w, col);
+        for (int t4 = 0; t4 < TPT; t4 += 4) {
+          float col[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) col[e] = rho[t4 + e][c] * fe[c];
+          const int idx = (c0 + c) * L::LDT + rb0 + t4;
+          store4_split<Pol>(sKhT + idx, sKhTLo + idx, col);
+        }
       }
+      KDA_PREFETCH(kLoadG, 6, 8);
     }
-    __syncthreads();
-    // off-diagonal sub-blocks on fp32 MFMA (16x16x4) in two levels:
-    //   level 1: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22
-    //   level 2: the lower-left 32x32 block -T_[23][23] A_[23][01] T_[01][01], one 16x16 block
-    //   per wave (T_20, T_21, T_30, T_31).
-    // T_ij (i > j) is stored in the free upper position (j, i) so that A_ij stays readable.
+    // T = (I + A)^{-1} in fp32, by 16x16 blocks. The diagonal blocks came with A (one per
+    // wave); waves 1 and 3 now run level 1 on fp32 MFMA (16x16x4): T_10 = -T_11 A_10 T_00,
+    // T_32 = -T_33 A_32 T_22. After a barrier, level 2 fills the lower-left 32x32 block
+    // -T_[23][23] A_[23][01] T_[01][01], one 16x16 block per wave (T_20, T_21, T_30, T_31).
+    // T_ij (i > j) is stored in the free upper position (j, i) so that A_ij stays readable;
+    // every block also goes out as T'_ij = T_ij diag(beta) (hi, lo) for the serial step.
     auto tblk = [&](int bi, int bj) -> float* {
       return bi == bj ? sA + 16 * bi * L::LDA + 16 * bi : sA + 16 * bj * L::LDA + 16 * bi;
     };
@@ -529,17 +646,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       for (int e = 0; e < 4; ++e) Y = mma_f32(Tb[ln * L::LDA + 4 * q4 + e], X[e], Y);
       return Y;
     };
+    // T_ij = -Y into sA (fp32, for later blocks) and T'_ij = T_ij diag(beta) into sT (hi, lo)
     auto put = [&](int bi, int bj, f32x4 Y) {
       float* To = tblk(bi, bj);
+      const float bcol = sBeta[16 * bj + ln];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
+      for (int e = 0; e < 4; ++e) {
+        To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
+        store_split<Pol>(sT, sTLo, (16 * bi + 4 * q4 + e) * L::LDT + 16 * bj + ln, -Y[e] * bcol);
+      }
     };
-    if (w < 2) {
-      const int lo = 2 * w;   // (1, 0) or (3, 2)
+    if (w & 1) {
+      const int lo = w - 1;   // diagonal pair (lo, lo + 1)
       const f32x4 X = mm_acc(zero4(), ablk(lo + 1, lo), tblk(lo, lo));
       put(lo + 1, lo, mm_reg(zero4(), tblk(lo + 1, lo + 1), X));
     }
     __syncthreads();
+    KDA_PREFETCH(kLoadK, 0, 4);
     {
       const int bj = w & 1;          // column block 0 or 1
       const bool row3 = w >= 2;      // row block 2 or 3
@@ -556,36 +679,42 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       else Y = mm_reg(mm_reg(zero4(), tblk(3, 2), X2), tblk(3, 3), X3);
       put(row3 ? 3 : 2, bj, Y);
     }
+    KDA_PREFETCH(kLoadK, 4, 8);
     __syncthreads();
 
-    // T' = T diag(beta), rounded once complete (hi, lo): thread = (row r, 16 columns)
-    {
-      const int r = tid >> 2;
-      const int s0 = 16 * (tid & 3);
-      const float* Tb = tblk(r >> 4, s0 >> 4) + (r & 15) * L::LDA;
-      float row[16];
-#pragma unroll
-      for (int u = 0; u < 16; u += 4) {
-        const f32x4 tv = *reinterpret_cast<const f32x4*>(Tb + u);
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(sBeta + s0 + u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) row[u + e] = (s0 + u + e <= r) ? tv[e] * bv[e] : 0.f;
-      }
-      store16_split<Pol>(sT + r * L::LDT + s0, sTLo + r * L::LDT + s0, row);
-    }
-    __syncthreads();
-    // value tile, transposed, into region Y (A / T are dead now)
-    store16<Pol>(sVT + lane * L::LDT + 16 * w, vv);
-    __syncthreads();
 
     // ================= serial step: this wave's 16 value columns ============================
+
     // Each product loads a batch of A fragments from LDS first and then issues its MFMAs, so
     // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
     Frag Sh[NS], Sl[NS];
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
+    // X = (K e^Gamma) S - V, in fp32
+    // (the values stay packed in the raw registers until here)
+    f32x4 X[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float vx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
+      quad_transpose(vx, lane);   // now token 16 rb + 4 q4 + e, column 16 w + ln
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc && !p_tile) ? -vx[e] : 0.f;
+    }
+    KDA_PREFETCH(kLoadV, 0, 8);
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+      Frag kg[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
+    }
+    KDA_PREFETCH(kLoadQ, 0, 4);
     f32x4 U[4], O[4];
-    // O = (Q e^Gamma) S first, while S is split
+    // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
       Frag qh[4], ql[4];
@@ -604,23 +733,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     }
-    // X = (K e^Gamma) S - V, in fp32
-    f32x4 X[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const E* vsrc = sVT + (16 * w + ln) * L::LDT + 16 * rb + 4 * q4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) X[rb][e] = -to_f32(vsrc[e]);
-    }
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-      Frag kg[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
-    }
+    KDA_PREFETCH(kLoadQ, 4, 8);
     // U = T' (V - K_Gamma S) = -T' X
     Frag Xh[NT], Xl[NT];
 #pragma unroll
@@ -675,17 +788,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     }
-    if (mode != kModeTransition) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * q4 + e;
-          if (r < Lc)
-            go[(size_t(cstart + r) * H + h) * DV + col0 + ln] = from_f32<Tout>(p.scale * O[rb][e]);
-        }
-      }
-    }
     // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
 #pragma unroll
     for (int t = 0; t < NTD; ++t) {
@@ -713,7 +815,29 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     }
+    // output, after the state update so that the last O products complete under it: a quad
+    // transpose gives each lane four consecutive columns of token 16 rb + 4 q4 + lane % 4
+    if (mode != kModeTransition) {
+      const int tq = 4 * q4 + (ln & 3);
+      const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        float ox[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ox[e] = p.scale * O[rb][e];
+        quad_transpose(ox, lane);
+        Tout* row = go + size_t(cstart + 16 * rb) * H * DV;
+        if (16 * rb + tq < Lc) {
+          if constexpr (sizeof(Tout) == 2)
+            *reinterpret_cast<bf16x4*>(row + lo_el) =
+                bf16x4{(__bf16)ox[0], (__bf16)ox[1], (__bf16)ox[2], (__bf16)ox[3]};
+          else
+            *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[0], ox[1], ox[2], ox[3]};
+        }
+      }
+    }
     __syncthreads();
+#undef KDA_PREFETCH
   }
 
   float* s_out = nullptr;

@@ -68,6 +68,26 @@ struct PolBF16 {
     }
     return r;
   }
+  // as load_scaled with the per-channel factor fac1 * fac2
+  __device__ static __forceinline__ Frag load_scaled2(const E* tile, int ld, int row, int p,
+                                                      int q, const float* fac1,
+                                                      const float* fac2) {
+    const E* base = tile + row * ld + 32 * p + 4 * q;
+    const int o = 32 * p + 4 * q;
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(base);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16);
+    f32x4 alo = *reinterpret_cast<const f32x4*>(fac1 + o);
+    f32x4 ahi = *reinterpret_cast<const f32x4*>(fac1 + o + 16);
+    f32x4 blo = *reinterpret_cast<const f32x4*>(fac2 + o);
+    f32x4 bhi = *reinterpret_cast<const f32x4*>(fac2 + o + 16);
+    Frag r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = (__bf16)((float)lo[e] * (alo[e] * blo[e]));
+      r[e + 4] = (__bf16)((float)hi[e] * (ahi[e] * bhi[e]));
+    }
+    return r;
+  }
   // B fragment of slice p from accumulator tiles acc[2p] and acc[2p + 1]
   __device__ static __forceinline__ Frag from_acc(const f32x4* acc, int p) {
     Frag r;
@@ -110,6 +130,12 @@ struct PolF32 {
     const int kk = 16 * (p >> 2) + 4 * q + (p & 3);
     return tile[row * ld + kk] * fac[kk];
   }
+  __device__ static __forceinline__ Frag load_scaled2(const E* tile, int ld, int row, int p,
+                                                      int q, const float* fac1,
+                                                      const float* fac2) {
+    const int kk = 16 * (p >> 2) + 4 * q + (p & 3);
+    return tile[row * ld + kk] * (fac1[kk] * fac2[kk]);
+  }
   __device__ static __forceinline__ Frag from_acc(const f32x4* acc, int p) {
     return acc[p >> 2][p & 3];
   }
@@ -126,5 +152,37 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Cross-lane moves inside each quad of four lanes (DPP quad_perm: lane i of the quad reads
+// lane sel[i]).
+template <int kCtrl>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl,
+                                                            0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;   // [2, 3, 0, 1]
+template <int kSrc>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return quad_perm<kSrc * 0x55>(v);   // [kSrc, kSrc, kSrc, kSrc]
+}
+
+// 4 x 4 transpose across a quad: lane a of the quad holds row a in x[0..3] and afterwards
+// holds column a (two exchange stages: 2 x 2 blocks, then the off-diagonal pair of blocks).
+__device__ __forceinline__ void quad_transpose(float x[4], int lane) {
+  const bool odd = (lane & 1) != 0, up = (lane & 2) != 0;
+  float r0 = quad_perm<kQuadXor1>(odd ? x[0] : x[1]);
+  float r1 = quad_perm<kQuadXor1>(odd ? x[2] : x[3]);
+  x[0] = odd ? r0 : x[0];
+  x[1] = odd ? x[1] : r0;
+  x[2] = odd ? r1 : x[2];
+  x[3] = odd ? x[3] : r1;
+  r0 = quad_perm<kQuadXor2>(up ? x[0] : x[2]);
+  r1 = quad_perm<kQuadXor2>(up ? x[1] : x[3]);
+  x[0] = up ? r0 : x[0];
+  x[1] = up ? r1 : x[1];
+  x[2] = up ? x[2] : r0;
+  x[3] = up ? x[3] : r1;
+}
 
 }  // namespace kda
