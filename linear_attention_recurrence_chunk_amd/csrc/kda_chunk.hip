@@ -633,18 +633,39 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       return bi == bj ? sA + 16 * bi * L::LDA + 16 * bi : sA + 16 * bj * L::LDA + 16 * bi;
     };
     auto ablk = [&](int bi, int bj) -> const float* { return sA + 16 * bi * L::LDA + 16 * bj; };
-    // X += A_blk * T_blk (16x16x16, natural k order)
-    auto mm_acc = [&](f32x4 X, const float* Ab, const float* Tb) -> f32x4 {
+    // X += A_blk * T_blk (16x16x16, natural k order: k-step kk2 takes k = 4 kk2 + q4) and
+    // Y += T_blk * X with X in accumulator layout (k-step e takes rows 4 q4 + e).
+    // Two independent accumulations issued alternately, so that consecutive MFMAs never wait
+    // on each other: Xa += A1 T1 and Xb += A2 T2; a single product A T split over its k range
+    // (Xa: k < 8, Xb: k >= 8); and the same for products with a register operand.
+    auto mm_acc2 = [&](f32x4& Xa, const float* A1, const float* T1, f32x4& Xb, const float* A2,
+                       const float* T2) {
 #pragma unroll
-      for (int kk2 = 0; kk2 < 4; ++kk2)
-        X = mma_f32(Ab[ln * L::LDA + 4 * kk2 + q4], Tb[(4 * kk2 + q4) * L::LDA + ln], X);
-      return X;
+      for (int kk2 = 0; kk2 < 4; ++kk2) {
+        Xa = mma_f32(A1[ln * L::LDA + 4 * kk2 + q4], T1[(4 * kk2 + q4) * L::LDA + ln], Xa);
+        Xb = mma_f32(A2[ln * L::LDA + 4 * kk2 + q4], T2[(4 * kk2 + q4) * L::LDA + ln], Xb);
+      }
     };
-    // Y += T_blk * X with X in accumulator layout (slice e holds rows 4 q4 + e)
-    auto mm_reg = [&](f32x4 Y, const float* Tb, f32x4 X) -> f32x4 {
+    auto mm_acc_split = [&](f32x4& Xa, f32x4& Xb, const float* Ab, const float* Tb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Y = mma_f32(Tb[ln * L::LDA + 4 * q4 + e], X[e], Y);
-      return Y;
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        Xa = mma_f32(Ab[ln * L::LDA + 4 * kk2 + q4], Tb[(4 * kk2 + q4) * L::LDA + ln], Xa);
+        Xb = mma_f32(Ab[ln * L::LDA + 4 * kk2 + 8 + q4], Tb[(4 * kk2 + 8 + q4) * L::LDA + ln], Xb);
+      }
+    };
+    auto mm_reg2 = [&](f32x4& Ya, const float* T1, f32x4 X1, f32x4& Yb, const float* T2, f32x4 X2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Ya = mma_f32(T1[ln * L::LDA + 4 * q4 + e], X1[e], Ya);
+        Yb = mma_f32(T2[ln * L::LDA + 4 * q4 + e], X2[e], Yb);
+      }
+    };
+    auto mm_reg_split = [&](f32x4& Ya, f32x4& Yb, const float* Tb, f32x4 X) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Ya = mma_f32(Tb[ln * L::LDA + 4 * q4 + e], X[e], Ya);
+        Yb = mma_f32(Tb[ln * L::LDA + 4 * q4 + e + 2], X[e + 2], Yb);
+      }
     };
     // T_ij = -Y into sA (fp32, for later blocks) and T'_ij = T_ij diag(beta) into sT (hi, lo)
     auto put = [&](int bi, int bj, f32x4 Y) {
@@ -658,26 +679,29 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     };
     if (w & 1) {
       const int lo = w - 1;   // diagonal pair (lo, lo + 1)
-      const f32x4 X = mm_acc(zero4(), ablk(lo + 1, lo), tblk(lo, lo));
-      put(lo + 1, lo, mm_reg(zero4(), tblk(lo + 1, lo + 1), X));
+      f32x4 Xa = zero4(), Xb = zero4(), Ya = zero4(), Yb = zero4();
+      mm_acc_split(Xa, Xb, ablk(lo + 1, lo), tblk(lo, lo));
+      mm_reg_split(Ya, Yb, tblk(lo + 1, lo + 1), Xa + Xb);
+      put(lo + 1, lo, Ya + Yb);
     }
     __syncthreads();
     KDA_PREFETCH(kLoadK, 0, 4);
     {
       const int bj = w & 1;          // column block 0 or 1
       const bool row3 = w >= 2;      // row block 2 or 3
-      f32x4 X2, X3 = zero4();        // X_2j, X_3j = A_[2|3],[01] T_[01],j
+      // X_2j, X_3j = A_[2|3],[01] T_[01],j, each accumulated in two halves
+      f32x4 X2a = zero4(), X2b = zero4(), X3a = zero4(), X3b = zero4();
       if (bj == 0) {
-        X2 = mm_acc(mm_acc(zero4(), ablk(2, 0), tblk(0, 0)), ablk(2, 1), tblk(1, 0));
-        if (row3) X3 = mm_acc(mm_acc(zero4(), ablk(3, 0), tblk(0, 0)), ablk(3, 1), tblk(1, 0));
+        mm_acc2(X2a, ablk(2, 0), tblk(0, 0), X2b, ablk(2, 1), tblk(1, 0));
+        if (row3) mm_acc2(X3a, ablk(3, 0), tblk(0, 0), X3b, ablk(3, 1), tblk(1, 0));
       } else {
-        X2 = mm_acc(zero4(), ablk(2, 1), tblk(1, 1));
-        if (row3) X3 = mm_acc(zero4(), ablk(3, 1), tblk(1, 1));
+        mm_acc_split(X2a, X2b, ablk(2, 1), tblk(1, 1));
+        if (row3) mm_acc_split(X3a, X3b, ablk(3, 1), tblk(1, 1));
       }
-      f32x4 Y;
-      if (!row3) Y = mm_reg(zero4(), tblk(2, 2), X2);
-      else Y = mm_reg(mm_reg(zero4(), tblk(3, 2), X2), tblk(3, 3), X3);
-      put(row3 ? 3 : 2, bj, Y);
+      f32x4 Ya = zero4(), Yb = zero4();
+      if (!row3) mm_reg_split(Ya, Yb, tblk(2, 2), X2a + X2b);
+      else mm_reg2(Ya, tblk(3, 2), X2a + X2b, Yb, tblk(3, 3), X3a + X3b);
+      put(row3 ? 3 : 2, bj, Ya + Yb);
     }
     KDA_PREFETCH(kLoadK, 4, 8);
     __syncthreads();
@@ -724,13 +748,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         if constexpr (Pol::kSplit) ql[rb] = Pol::load(sQgLo, L::LDP, 16 * rb + ln, pp, q4);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the three split products of one accumulator are issued four MFMAs apart (one pass per
+      // term over the row blocks), so consecutive MFMAs never wait on each other
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        O[rb] = Pol::mma(qh[rb], Sh[pp], pp == 0 ? zero4() : O[rb]);
-        if constexpr (Pol::kSplit) {
-          O[rb] = Pol::mma(ql[rb], Sh[pp], O[rb]);
-          O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
-        }
+      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sh[pp], pp == 0 ? zero4() : O[rb]);
+      if constexpr (Pol::kSplit) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(ql[rb], Sh[pp], O[rb]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
       }
     }
     KDA_PREFETCH(kLoadQ, 4, 8);
@@ -750,14 +776,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
-          if constexpr (Pol::kSplit) {
-            U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
-            U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
-          }
-        }
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
+      if constexpr (Pol::kSplit) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
       }
     }
 #pragma unroll
@@ -778,14 +805,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          O[rb] = Pol::mma(mh[rb], Uh[pp], O[rb]);
-          if constexpr (Pol::kSplit) {
-            O[rb] = Pol::mma(ml[rb], Uh[pp], O[rb]);
-            O[rb] = Pol::mma(mh[rb], Ul[pp], O[rb]);
-          }
-        }
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(mh[rb], Uh[pp], O[rb]);
+      if constexpr (Pol::kSplit) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(ml[rb], Uh[pp], O[rb]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(mh[rb], Ul[pp], O[rb]);
       }
     }
     // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
@@ -806,12 +834,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          S[t0 + t] = Pol::mma(kh[t], Uh[pp], S[t0 + t]);
-          if constexpr (Pol::kSplit) {
-            S[t0 + t] = Pol::mma(kl[t], Uh[pp], S[t0 + t]);
-            S[t0 + t] = Pol::mma(kh[t], Ul[pp], S[t0 + t]);
-          }
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kh[t], Uh[pp], S[t0 + t]);
+        if constexpr (Pol::kSplit) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kl[t], Uh[pp], S[t0 + t]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kh[t], Ul[pp], S[t0 + t]);
         }
       }
     }
