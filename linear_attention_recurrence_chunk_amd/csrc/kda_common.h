@@ -167,6 +167,35 @@ __device__ __forceinline__ float quad_bcast(float v) {
   return quad_perm<kSrc * 0x55>(v);   // [kSrc, kSrc, kSrc, kSrc]
 }
 
+// Sums across lanes without LDS traffic (DPP and the gfx950 row-swap instructions). Each
+// returns x + x' where x' is the value of the partner lane named; both partners get the same
+// bits (fp32 addition commutes).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_xor1(float x) { return x + quad_perm<0xB1>(x); }
+__device__ __forceinline__ float sum_xor2(float x) { return x + quad_perm<0x4E>(x); }
+// partner 7 - l inside each group of eight (after sum_xor1 and sum_xor2 this completes the
+// sum over the eight lanes)
+__device__ __forceinline__ float sum_mirror8(float x) { return x + dpp_mov<0x141>(x); }
+// partner l ^ 8 inside each row of sixteen (row rotation by eight)
+__device__ __forceinline__ float sum_xor8(float x) { return x + dpp_mov<0x128>(x); }
+// partner l ^ 16: v_permlane16_swap exchanges the odd rows of one copy with the even rows of
+// the other, so the two results hold x[l] and x[l ^ 16] in row order in every lane
+__device__ __forceinline__ float sum_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
+}
+// partner l ^ 32, with v_permlane32_swap on the two halves of the wave
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, unsigned(r[0])) + __builtin_bit_cast(float, unsigned(r[1]));
+}
+
 // 4 x 4 transpose across a quad: lane a of the quad holds row a in x[0..3] and afterwards
 // holds column a (two exchange stages: 2 x 2 blocks, then the off-diagonal pair of blocks).
 __device__ __forceinline__ void quad_transpose(float x[4], int lane) {

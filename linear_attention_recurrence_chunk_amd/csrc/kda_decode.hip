@@ -10,108 +10,89 @@
 // and walk the same tokens in order.)
 //
 // Work decomposition: one workgroup (4 waves) per (request, head). The head's fp32 state
-// (d_k x d_v) is read from HBM once, lives in registers for every token of the loop (wave w
-// owns value columns [32w, 32w + 32); lane (row group rg = lane / 8, column group cg =
-// lane % 8) holds rows 16 rg .. 16 rg + 15 of columns 4 cg .. 4 cg + 3), and is written back
-// twice: after the replayed drafts (state_acc) and after the bonus token (state, in place).
-// Column sums over the 128 key rows are reduced inside the wave (lanes that share cg), so the
-// recurrence needs no LDS traffic and no barrier.
+// (d_k x d_v) is read from HBM once, lives in registers for every token (wave w owns value
+// columns [D/4 w, D/4 (w + 1)); lane (row group rg = lane / 8, column group cg = lane % 8)
+// holds rows D/8 rg .. + D/8 - 1 of its D/32 columns), and is written back twice: after the
+// replayed drafts (state_acc) and after the bonus token (state, in place).
 //
-// Per token, with the state columns independent:
+// Tokens go in blocks of eight. The whole block's projected inputs are loaded one block
+// ahead; the block's input stage (causal convolution, SiLU, decay and output gates, L2 norms
+// of q and k) runs for all its tokens at once, parallel over channels and tokens; each wave
+// then replays its columns through the block's tokens with no barrier (column sums over the
+// key rows are reduced inside the wave); the block's outputs get their RMS normalisation
+// together at the end. Per token, with the state columns independent:
 //   k_s = sum_i (a_i k_i) S_ij,  q_s = sum_i (a_i q_i) S_ij     (both on the old state)
 //   e_j = v_j - k_s;  S_ij <- a_i S_ij + (beta k_i) e_j;  o_j = q_s + beta (q . k) e_j
-// which equals decaying first, correcting, then reading out S^T q. The operation order is
-// fixed and identical for replayed, bonus and draft tokens, so a replayed state is
-// bit-identical to the state the same tokens reach one launch at a time.
+// which equals decaying first, correcting, then reading out S^T q. Every per-token quantity is
+// computed by the same operations in the same order whatever the token's position in its
+// block, so a replayed state is bit-identical to the state the same tokens reach one launch
+// at a time.
 #include "kda_common.h"
 #include "kda_decode.h"
 
 namespace kda {
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
-
-struct RawToken {
-  float a, b, g, z, beta;
-};
-
-// Raw inputs a thread needs for token t of its request: replay slots 1..n_acc of the
-// previous window, then slots 0..n_new-1 of the current one. Threads of the q/k role read
-// q and k of their channel, threads of the v role read v, g, z and (channel 0) beta.
-template <int D>
-__device__ __forceinline__ RawToken load_raw(const DecodeParams& p, int r, int t, int n_acc,
-                                             int ch, bool role_qk, bool role_v) {
-  const bool replay = t < n_acc;
-  const int slot = replay ? t + 1 : t - n_acc;
-  const int slots = replay ? p.prev_slots : p.cur_slots;
-  const size_t tok = (size_t(r) * slots + slot) * p.H + blockIdx.x % p.H;
-  RawToken x = {0.f, 0.f, 0.f, 0.f, 0.f};
-  if (role_qk) {
-    x.a = (float)(replay ? p.prev_q : p.cur_q)[tok * D + ch];
-    x.b = (float)(replay ? p.prev_k : p.cur_k)[tok * D + ch];
-  } else if (role_v) {
-    x.a = (float)(replay ? p.prev_v : p.cur_v)[tok * D + ch];
-    x.g = (float)(replay ? p.prev_g : p.cur_g)[tok * D + ch];
-    if (!replay) x.z = (float)p.cur_z[tok * D + ch];
-    if (ch == 0) x.beta = (float)(replay ? p.prev_beta : p.cur_beta)[tok];
-  }
-  return x;
+// sigmoid with the hardware exponential and reciprocal (a few ulp; saturates correctly: an
+// overflowing exponential gives 0, a vanishing one 1)
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
 template <int D, int W, typename Tout>
-__global__ __launch_bounds__(256) void decode_replay_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dimension");
   static_assert(W >= 1 && W <= 4, "convolution width");
+  constexpr int NB = 8;               // tokens per block
   constexpr int RPL = D / 8;          // rows of S per lane
   constexpr int CPW = D / 4;          // value columns per wave
   constexpr int CPL = CPW / 8;        // value columns per lane
   constexpr int C3 = 3 * D;           // convolved channels q, k, v
+  constexpr int CPG = D / 32;         // channels per thread in the 32-thread token groups
 
   const int rh = blockIdx.x;
   const int r = rh / p.H;
   const int h = rh % p.H;
   const int H = p.H;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int rg = lane >> 3;
   const int cg = lane & 7;
   const int col0 = CPW * w + CPL * cg;   // first value column of this lane
   const int row0 = RPL * rg;             // first key row of this lane
 
-  // per-token values shared through LDS, double-buffered by token parity
-  __shared__ float s_q[2][D], s_k[2][D], s_a[2][D], s_v[2][D], s_z[2][D];
-  __shared__ float s_red[2][4][3];      // per wave: sum q^2, sum k^2, sum q k
-  __shared__ float s_beta[2];
-  __shared__ float s_osq[2][4];         // per wave: sum o^2 over its columns
+  // one block's per-token vectors: convolved q, k (then a q^, a k^ with the L2-normalised
+  // q^, k^), v, decay a, beta k^, output gate, pre-norm output
+  __shared__ __attribute__((aligned(16))) float s_q[NB][D], s_k[NB][D], s_v[NB][D], s_a[NB][D];
+  __shared__ __attribute__((aligned(16))) float s_bk[NB][D], s_z[NB][D], s_o[NB][D];
+  __shared__ float s_beta[NB];
+  // one block's projected inputs as loaded (q, k, v, g, z rows of each token) and its betas
+  constexpr int kRows = 5;
+  __shared__ __attribute__((aligned(16))) __bf16 s_raw[NB][kRows][D];
+  __shared__ float s_rbeta[NB];
+  __shared__ float s_nrm[NB][3];        // 1/|q|, 1/|k|, (q . k) of the normalised vectors
+  __shared__ float s_osq[NB][4];        // per wave: sum of o^2 over its columns
 
-  // ---- state tile into registers
-  const size_t sbase = (size_t(r) * H + h) * D * D;
-  float S[RPL][CPL];
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const float* src = p.state + sbase + size_t(row0 + i) * D + col0;
-    if constexpr (CPL == 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = x[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) S[i][j] = src[j];
-    }
-  }
+  // Loads are issued in the order their data is needed: the request's accepted count, the
+  // convolution tails and taps, the first block of inputs, then the state (first read by
+  // the recurrence, after the block's input stage).
+  int n_acc = p.n_acc[r];
+  n_acc = n_acc < 0 ? 0 : (n_acc > p.prev_slots - 1 ? p.prev_slots - 1 : n_acc);
+  const int n_tok = n_acc + p.n_new;
 
-  // ---- input-stage role: threads [0, D) own q and k channel tid; [D, 2D) own v, g and z
-  // channel tid - D. Each keeps the causal-convolution tail of its channels in registers.
-  const bool role_qk = tid < D;
-  const bool role_v = tid >= D && tid < 2 * D;
+  // ---- input-stage role (whole waves): threads [0, D) own q and k channel tid; [D, 2D) own
+  // v, g and z channel tid - D. Each keeps the causal-convolution tail of its channels in
+  // registers.
+  const bool role_qk = w < D / 64;
+  const bool role_v = w >= D / 64 && w < 2 * D / 64;
   const int ch = role_qk ? tid : tid - D;
   float tail_a[3] = {0.f, 0.f, 0.f}, tail_b[3] = {0.f, 0.f, 0.f};
   float wa[4] = {0.f, 0.f, 0.f, 0.f}, wb[4] = {0.f, 0.f, 0.f, 0.f};
   const size_t tbase = (size_t(r) * H + h) * C3 * (W - 1);
   const size_t wbase = size_t(h) * C3 * W;
+  const int ca = role_qk ? ch : 2 * D + ch;   // q channel or v channel
+  const int cb = ch + D;                      // k channel (q/k role only)
   if (role_qk || role_v) {
-    const int ca = role_qk ? ch : 2 * D + ch;   // q channel or v channel
-    const int cb = ch + D;                      // k channel (q/k role only)
 #pragma unroll
     for (int m = 0; m < W - 1; ++m) {
       tail_a[m] = p.conv_tail[tbase + size_t(ca) * (W - 1) + m];
@@ -124,189 +105,309 @@ __global__ __launch_bounds__(256) void decode_replay_kernel(DecodeParams p) {
     }
   }
 
-  int n_acc = p.n_acc[r];
-  n_acc = n_acc < 0 ? 0 : (n_acc > p.prev_slots - 1 ? p.prev_slots - 1 : n_acc);
-  const int n_tok = n_acc + p.n_new;
 
-  if (n_acc == 0 && p.state_acc) {
-    // no accepted drafts: the accepted state is the committed entering state
+
+  // ---- projected inputs of one block: replay slots 1..n_acc of the previous window, then
+  // slots 0..n_new-1 of the current one. They are fetched one block ahead in 16-byte pieces
+  // (thread tid takes pieces tid, tid + 256, ...) into registers and written to s_raw once
+  // the block before has been replayed.
+  constexpr int kPPR = D * 2 / 16;                  // 16-byte pieces per row
+  constexpr int kPieces = NB * kRows * kPPR;        // per block
+  constexpr int kPPT = (kPieces + 255) / 256;       // per thread
+  bf16x8 praw[kPPT];
+  float pbeta = 0.f;
+  auto token_row = [&](int t) -> size_t {
+    const bool replay = t < n_acc;
+    const int slot = replay ? t + 1 : t - n_acc;
+    const int slots = replay ? p.prev_slots : p.cur_slots;
+    return (size_t(r) * slots + slot) * H + h;
+  };
+  auto fetch_block = [&](int tb) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      float* dst = p.state_acc + sbase + size_t(row0 + i) * D + col0;
+    for (int m = 0; m < kPPT; ++m) {
+      const int c = tid + 256 * m;
+      if (c >= kPieces) break;
+      const int i = c / (kRows * kPPR), f = (c / kPPR) % kRows, part = c % kPPR;
+      const int t = tb + i;
+      const bool replay = t < n_acc;
+      // rows past the end, and z of replayed tokens (never used), read a present row
+      const bool use = t < n_tok && !(f == 4 && replay);
+      const __bf16* base;
+      switch (f) {
+        case 0: base = replay ? p.prev_q : p.cur_q; break;
+        case 1: base = replay ? p.prev_k : p.cur_k; break;
+        case 2: base = replay ? p.prev_v : p.cur_v; break;
+        case 3: base = replay ? p.prev_g : p.cur_g; break;
+        default: base = p.cur_z; break;
+      }
+      const size_t row = use ? token_row(t) : size_t(0);
+      if (!use) base = p.cur_q;
+      praw[m] = *reinterpret_cast<const bf16x8*>(base + row * D + 8 * part);
+    }
+    if (tid < NB && tb + tid < n_tok) {
+      const int t = tb + tid;
+      pbeta = (float)(t < n_acc ? p.prev_beta : p.cur_beta)[token_row(t)];
+    }
+  };
+  auto stage_block = [&]() {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) dst[j] = S[i][j];
+    for (int m = 0; m < kPPT; ++m) {
+      const int c = tid + 256 * m;
+      if (c >= kPieces) break;
+      const int i = c / (kRows * kPPR), f = (c / kPPR) % kRows, part = c % kPPR;
+      *reinterpret_cast<bf16x8*>(&s_raw[i][f][8 * part]) = praw[m];
+    }
+    if (tid < NB) s_rbeta[tid] = pbeta;
+  };
+  fetch_block(0);
+
+  // ---- state tile into registers
+  const size_t sbase = (size_t(r) * H + h) * D * D;
+  float S[RPL][CPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    const float* src = p.state + sbase + size_t(row0 + i) * D + col0;
+    if constexpr (CPL == 4) {
+      // read once: a streaming (non-temporal) load
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[i][j] = x[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) S[i][j] = src[j];
     }
   }
 
-  RawToken nx = {0.f, 0.f, 0.f, 0.f, 0.f};
-  if (n_tok > 0) nx = load_raw<D>(p, r, 0, n_acc, ch, role_qk, role_v);
 
-  for (int t = 0; t < n_tok; ++t) {
-    const int buf = t & 1;
-    const bool replay = t < n_acc;
-    const bool output = !replay;
-    const float xa = nx.a, xb = nx.b, xg = nx.g, xz = nx.z, xbeta = nx.beta;
-    if (t + 1 < n_tok) nx = load_raw<D>(p, r, t + 1, n_acc, ch, role_qk, role_v);
+  stage_block();
+  __syncthreads();
 
-    // ---------------- input stage: causal conv, SiLU, gates -------------------------------
-    float sq = 0.f, sk = 0.f, sqk = 0.f;
-    if (role_qk) {
-      float ya = wa[W - 1] * xa, yb = wb[W - 1] * xb;
-#pragma unroll
-      for (int m = 0; m < W - 1; ++m) {
-        ya += wa[m] * tail_a[m];
-        yb += wb[m] * tail_b[m];
-      }
-#pragma unroll
-      for (int m = 0; m + 1 < W - 1; ++m) {
-        tail_a[m] = tail_a[m + 1];
-        tail_b[m] = tail_b[m + 1];
-      }
-      if constexpr (W > 1) {
-        tail_a[W - 2] = xa;
-        tail_b[W - 2] = xb;
-      }
-      if (p.act) {
-        ya = ya * sigmoidf_(ya);
-        yb = yb * sigmoidf_(yb);
-      }
-      s_q[buf][ch] = ya;
-      s_k[buf][ch] = yb;
-      sq = ya * ya;
-      sk = yb * yb;
-      sqk = ya * yb;
-    } else if (role_v) {
-      float ya = wa[W - 1] * xa;
-#pragma unroll
-      for (int m = 0; m < W - 1; ++m) ya += wa[m] * tail_a[m];
-#pragma unroll
-      for (int m = 0; m + 1 < W - 1; ++m) tail_a[m] = tail_a[m + 1];
-      if constexpr (W > 1) tail_a[W - 2] = xa;
-      if (p.act) ya = ya * sigmoidf_(ya);
-      s_v[buf][ch] = ya;
-      // exp(max(-softplus(x), g_min)) = max(sigmoid(-x), e^{g_min})
-      s_a[buf][ch] = fmaxf(1.f / (1.f + expf(xg)), p.decay_floor);
-      s_z[buf][ch] = output ? sigmoidf_(xz) : 0.f;
-      if (ch == 0) s_beta[buf] = sigmoidf_(xbeta);
-    }
-    // norms of q and k: reduce inside the wave, one partial per wave
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      sq += __shfl_xor(sq, off);
-      sk += __shfl_xor(sk, off);
-      sqk += __shfl_xor(sqk, off);
-    }
-    if (lane == 0) {
-      s_red[buf][w][0] = sq;
-      s_red[buf][w][1] = sk;
-      s_red[buf][w][2] = sqk;
-    }
-    __syncthreads();
+  for (int tb = 0; tb < n_tok; tb += NB) {
+    const int nb = min(NB, n_tok - tb);
+    // lane coordinates re-derived per block: the LDS and global addresses built from them are
+    // recomputed here (a few integer ops) instead of being hoisted out of the loop and kept
+    // live across it
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, rg = lane >> 3, cg = lane & 7;
+    const int col0 = CPW * w + CPL * cg, row0 = RPL * rg;
+    const int ch = role_qk ? tid : tid - D;
 
-    // ---------------- recurrence on this lane's block of S --------------------------------
-    const float nq2 = s_red[buf][0][0] + s_red[buf][1][0] + s_red[buf][2][0] + s_red[buf][3][0];
-    const float nk2 = s_red[buf][0][1] + s_red[buf][1][1] + s_red[buf][2][1] + s_red[buf][3][1];
-    const float nqk = s_red[buf][0][2] + s_red[buf][1][2] + s_red[buf][2][2] + s_red[buf][3][2];
-    const float iq = 1.f / sqrtf(nq2 + p.eps_l2);
-    const float ik = 1.f / sqrtf(nk2 + p.eps_l2);
-    const float beta = s_beta[buf];
-    const float qk = nqk * iq * ik;    // (q . k) of the normalised vectors
-    float ak[RPL], aq[RPL], bk[RPL], av[RPL];
+    // ---------------- input stage of the block: causal conv, SiLU, gates -----------------
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const float a = s_a[buf][row0 + i];
-      const float kn = s_k[buf][row0 + i] * ik;
-      av[i] = a;
-      ak[i] = a * kn;
-      aq[i] = a * (s_q[buf][row0 + i] * iq);
-      bk[i] = beta * kn;
-    }
-    float ks[CPL], qs[CPL];
+    for (int i = 0; i < NB; ++i) {
+      if (i >= nb) continue;
+      const int t = tb + i;
+      if (role_qk) {
+        const float xa = (float)s_raw[i][0][ch], xb = (float)s_raw[i][1][ch];
+        float ya = wa[W - 1] * xa, yb = wb[W - 1] * xb;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      ks[j] = 0.f;
-      qs[j] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        ks[j] = fmaf(ak[i], S[i][j], ks[j]);
-        qs[j] = fmaf(aq[i], S[i][j], qs[j]);
-      }
-    }
-    // sum over the 8 row groups (lanes cg, cg + 8, ..., cg + 56), fixed butterfly order
-#pragma unroll
-    for (int off = 8; off <= 32; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        ks[j] += __shfl_xor(ks[j], off);
-        qs[j] += __shfl_xor(qs[j], off);
-      }
-    }
-    float e[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) e[j] = s_v[buf][col0 + j] - ks[j];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) S[i][j] = fmaf(bk[i], e[j], av[i] * S[i][j]);
-    }
-
-    float ov[CPL];
-    if (output) {
-      float osq = 0.f;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        ov[j] = p.scale * fmaf(beta * qk, e[j], qs[j]);
-        osq += ov[j] * ov[j];
-      }
-      // each column is held by 8 lanes; count it once (row group 0)
-      osq = rg == 0 ? osq : 0.f;
-#pragma unroll
-      for (int off = 1; off <= 4; off <<= 1) osq += __shfl_xor(osq, off);
-      if (lane == 0) s_osq[buf][w] = osq;
-    }
-    if (replay && t == n_acc - 1 && p.state_acc) {
-      // state after the accepted drafts
-#pragma unroll
-      for (int i = 0; i < RPL; ++i) {
-        float* dst = p.state_acc + sbase + size_t(row0 + i) * D + col0;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) dst[j] = S[i][j];
-      }
-    }
-    __syncthreads();
-
-    if (output) {
-      const float tot = s_osq[buf][0] + s_osq[buf][1] + s_osq[buf][2] + s_osq[buf][3];
-      const float rinv = 1.f / sqrtf(tot / float(D) + p.eps_rms);
-      if (rg == 0) {
-        const int j_out = t - n_acc;
-        Tout* dst = reinterpret_cast<Tout*>(p.o) + ((size_t(r) * p.n_new + j_out) * H + h) * D + col0;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          dst[j] = from_f32<Tout>(ov[j] * rinv * p.norm_w[col0 + j] * s_z[buf][col0 + j]);
-      }
-      if (t == n_acc) {
-        // bonus token: the new committed state and convolution tail
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-          float* dst = p.state + sbase + size_t(row0 + i) * D + col0;
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) dst[j] = S[i][j];
+        for (int m = 0; m < W - 1; ++m) {
+          ya += wa[m] * tail_a[m];
+          yb += wb[m] * tail_b[m];
         }
-        if (role_qk || role_v) {
-          const int ca = role_qk ? ch : 2 * D + ch;
-          const int cb = ch + D;
 #pragma unroll
-          for (int m = 0; m < W - 1; ++m) {
-            p.conv_tail[tbase + size_t(ca) * (W - 1) + m] = tail_a[m];
-            if (role_qk) p.conv_tail[tbase + size_t(cb) * (W - 1) + m] = tail_b[m];
+        for (int m = 0; m + 1 < W - 1; ++m) {
+          tail_a[m] = tail_a[m + 1];
+          tail_b[m] = tail_b[m + 1];
+        }
+        if constexpr (W > 1) {
+          tail_a[W - 2] = xa;
+          tail_b[W - 2] = xb;
+        }
+        if (p.act) {
+          ya = ya * sigmoidf_(ya);
+          yb = yb * sigmoidf_(yb);
+        }
+        s_q[i][ch] = ya;
+        s_k[i][ch] = yb;
+      } else if (role_v) {
+        const float xa = (float)s_raw[i][2][ch], xg = (float)s_raw[i][3][ch];
+        const float xz = (float)s_raw[i][4][ch];
+        float ya = wa[W - 1] * xa;
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) ya += wa[m] * tail_a[m];
+#pragma unroll
+        for (int m = 0; m + 1 < W - 1; ++m) tail_a[m] = tail_a[m + 1];
+        if constexpr (W > 1) tail_a[W - 2] = xa;
+        if (p.act) ya = ya * sigmoidf_(ya);
+        s_v[i][ch] = ya;
+        // exp(max(-softplus(x), g_min)) = max(sigmoid(-x), e^{g_min})
+        s_a[i][ch] = fmaxf(sigmoidf_(-xg), p.decay_floor);
+        s_z[i][ch] = t >= n_acc ? sigmoidf_(xz) : 0.f;
+      }
+      if (t == n_acc && (role_qk || role_v)) {
+        // bonus token: the convolution tail it leaves is the new committed tail
+#pragma unroll
+        for (int m = 0; m < W - 1; ++m) {
+          p.conv_tail[tbase + size_t(ca) * (W - 1) + m] = tail_a[m];
+          if (role_qk) p.conv_tail[tbase + size_t(cb) * (W - 1) + m] = tail_b[m];
+        }
+      }
+    }
+    if (tid < nb) s_beta[tid] = sigmoidf_(s_rbeta[tid]);
+    __syncthreads();
+
+    // the next block's inputs load while this block is replayed
+    const bool more = tb + NB < n_tok;
+    if (more) fetch_block(tb + NB);
+
+    // L2 norms of q and k and their dot product: 32 threads per token, fixed order
+    {
+      const int i = tid >> 5, l = tid & 31;
+      float sq = 0.f, sk = 0.f, sqk = 0.f;
+      if (i < nb) {
+#pragma unroll
+        for (int m = 0; m < CPG; ++m) {
+          const float qv = s_q[i][l + 32 * m], kv = s_k[i][l + 32 * m];
+          sq = fmaf(qv, qv, sq);
+          sk = fmaf(kv, kv, sk);
+          sqk = fmaf(qv, kv, sqk);
+        }
+      }
+      // sums over the 32 lanes of the group (lanes 0-7, then 8 and 16 apart)
+      sq = sum_xor16(sum_xor8(sum_mirror8(sum_xor2(sum_xor1(sq)))));
+      sk = sum_xor16(sum_xor8(sum_mirror8(sum_xor2(sum_xor1(sk)))));
+      sqk = sum_xor16(sum_xor8(sum_mirror8(sum_xor2(sum_xor1(sqk)))));
+      if (l == 0 && i < nb) {
+        const float iq = 1.f / sqrtf(sq + p.eps_l2);
+        const float ik = 1.f / sqrtf(sk + p.eps_l2);
+        s_nrm[i][0] = iq;
+        s_nrm[i][1] = ik;
+        s_nrm[i][2] = sqk * iq * ik;
+      }
+    }
+    __syncthreads();
+    // per-row factors of the recurrence, once per token and channel
+#pragma unroll
+    for (int idx = tid; idx < NB * D; idx += 256) {
+      const int i = idx / D, c = idx % D;
+      if (i < nb) {
+        const float a = s_a[i][c];
+        const float kn = s_k[i][c] * s_nrm[i][1];
+        s_k[i][c] = a * kn;
+        s_q[i][c] = a * (s_q[i][c] * s_nrm[i][0]);
+        s_bk[i][c] = s_beta[i] * kn;
+      }
+    }
+    __syncthreads();
+
+    if (tb == 0 && n_acc == 0 && p.state_acc) {
+      // no accepted drafts: the accepted state is the committed entering state
+#pragma unroll
+      for (int ii = 0; ii < RPL; ++ii) {
+        float* dst = p.state_acc + sbase + size_t(row0 + ii) * D + col0;
+        if constexpr (CPL == 4) {
+          __builtin_nontemporal_store(f32x4{S[ii][0], S[ii][1], S[ii][2], S[ii][3]},
+                                      reinterpret_cast<f32x4*>(dst));
+        } else {
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) dst[j] = S[ii][j];
+        }
+      }
+    }
+    // ---------------- recurrence: this wave's columns through the block's tokens ----------
+#pragma unroll 1
+    for (int i = 0; i < nb; ++i) {
+      const int t = tb + i;
+      const bool output = t >= n_acc;
+      const float qk = s_nrm[i][2];
+      const float beta = s_beta[i];
+      float ks[CPL], qs[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        ks[j] = 0.f;
+        qs[j] = 0.f;
+      }
+      // row factors four at a time (16-byte reads; few registers in flight)
+#pragma unroll
+      for (int i4 = 0; i4 < RPL; i4 += 4) {
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(&s_k[i][row0 + i4]);
+        const f32x4 aq = *reinterpret_cast<const f32x4*>(&s_q[i][row0 + i4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            ks[j] = fmaf(ak[u], S[i4 + u][j], ks[j]);
+            qs[j] = fmaf(aq[u], S[i4 + u][j], qs[j]);
+          }
+      }
+      // sum over the 8 row groups (lanes cg, cg + 8, ..., cg + 56), fixed butterfly order
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        ks[j] = sum_xor32(sum_xor16(sum_xor8(ks[j])));
+        qs[j] = sum_xor32(sum_xor16(sum_xor8(qs[j])));
+      }
+      float e[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) e[j] = s_v[i][col0 + j] - ks[j];
+#pragma unroll
+      for (int i4 = 0; i4 < RPL; i4 += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&s_a[i][row0 + i4]);
+        const f32x4 bk = *reinterpret_cast<const f32x4*>(&s_bk[i][row0 + i4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) S[i4 + u][j] = fmaf(bk[u], e[j], a[u] * S[i4 + u][j]);
+      }
+      if (output) {
+        float osq = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const float ov = p.scale * fmaf(beta * qk, e[j], qs[j]);
+          if (rg == 0) s_o[i][col0 + j] = ov;
+          osq += ov * ov;
+        }
+        // each column is held by 8 lanes; count it once (row group 0)
+        osq = sum_mirror8(sum_xor2(sum_xor1(osq)));   // over the 8 lanes of row group 0
+        if (lane == 0) s_osq[i][w] = osq;
+      }
+      float* dst_state = nullptr;
+      if (t == n_acc - 1) dst_state = p.state_acc;   // after the accepted drafts
+      if (t == n_acc) dst_state = p.state;           // after the bonus token
+      if (dst_state) {
+#pragma unroll
+        for (int ii = 0; ii < RPL; ++ii) {
+          float* dst = dst_state + sbase + size_t(row0 + ii) * D + col0;
+          if constexpr (CPL == 4) {
+            // written once, read by a later launch: streaming (non-temporal) stores
+            __builtin_nontemporal_store(f32x4{S[ii][0], S[ii][1], S[ii][2], S[ii][3]},
+                                        reinterpret_cast<f32x4*>(dst));
+          } else {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) dst[j] = S[ii][j];
           }
         }
       }
     }
+    if (more) stage_block();   // s_raw of this block was last read before the first barrier
+    __syncthreads();
+
+    // ---------------- gated RMS normalisation of the block's outputs ----------------------
+    {
+      const int i = tid >> 5, l = tid & 31;
+      const int t = tb + i;
+      if (i < nb && t >= n_acc) {
+        const float tot = s_osq[i][0] + s_osq[i][1] + s_osq[i][2] + s_osq[i][3];
+        const float rinv = 1.f / sqrtf(tot / float(D) + p.eps_rms);
+        Tout* dst = reinterpret_cast<Tout*>(p.o) + ((size_t(r) * p.n_new + (t - n_acc)) * H + h) * D;
+        // CPG consecutive channels per thread, one vector store
+        const int c0 = CPG * l;
+        float ov[CPG];
+#pragma unroll
+        for (int m = 0; m < CPG; ++m)
+          ov[m] = s_o[i][c0 + m] * rinv * p.norm_w[c0 + m] * s_z[i][c0 + m];
+        if constexpr (CPG == 4 && sizeof(Tout) == 2)
+          *reinterpret_cast<bf16x4*>(dst + c0) =
+              bf16x4{(__bf16)ov[0], (__bf16)ov[1], (__bf16)ov[2], (__bf16)ov[3]};
+        else if constexpr (CPG == 4)
+          *reinterpret_cast<f32x4*>(dst + c0) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+        else if constexpr (CPG == 2 && sizeof(Tout) == 2)
+          *reinterpret_cast<bf16x2*>(dst + c0) = bf16x2{(__bf16)ov[0], (__bf16)ov[1]};
+        else
+          *reinterpret_cast<f32x2*>(dst + c0) = f32x2{ov[0], ov[1]};
+      }
+    }
+    if (more) __syncthreads();   // the next block rewrites the shared vectors
   }
 }
 
