@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark of the KDA prefill hot path (kda_chunk_fwd) on one MI355X.
+"""Benchmark of the KDA hot path on one MI355X.
 
 One step = one kda_chunk_fwd over the 8192-token, 96-head, d = 128 prefill (bf16 q, k, v;
 fp32 g, beta and state; entering state h0 ~ N(0, 0.02^2); bf16 output plus fp32 final
-state), inputs resident in HBM before the timed region. Prints ONE JSON line.
+state), inputs resident in HBM before the timed region: that is the line's ``value``. Two
+more legs ride on the same line: ``decode`` (kda_decode_replay on the 256-request, 96-head
+speculative verify: window of 7 drafts plus the bonus token, HBM GB/s and latency) and
+``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill).
+Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs ...]
 
-The line carries the roofline of the kernel (algorithmic bytes per launch over the average
-launch time measured with HIP events on the launch stream), the MFMA rate, the fp64 CPU
-oracle timed on the host cores, and, when they were taken on the current kernel source, the
-HBM bytes read and written per launch from rocprofv3 counters (profiles/).
+The line carries the roofline of the prefill kernel (algorithmic bytes per launch over the
+average launch time measured with HIP events on the launch stream), the MFMA rate, the fp64
+CPU oracle timed on the host cores, and, when they were taken on the current kernel source,
+the HBM bytes read and written per launch from rocprofv3 counters (profiles/).
 """
 
 import argparse
@@ -26,8 +30,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc", "kda_chunk.hip")
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "kda_chunk.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_8k_counters.txt")
+DECODE_SRC = os.path.join(CSRC, "kda_decode.hip")
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_replay_verify_counters.txt")
 
 
 def algorithmic_bytes(T, H, dk, dv, io_bytes, out_bytes, n_seqs=1):
@@ -44,23 +51,23 @@ def algorithmic_flops(T, H, dk, dv):
     return T * H * (6 * dk * dv + CHUNK * (3 * dk + 2 * dv))
 
 
-def source_digest():
-    with open(KERNEL_SRC, "rb") as f:
+def source_digest(path=KERNEL_SRC):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+def counter_traffic(counters=COUNTERS, source=KERNEL_SRC):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
     kernel source changed since the counters were taken."""
-    if not os.path.exists(COUNTERS):
+    if not os.path.exists(counters):
         return None
     vals = {}
-    with open(COUNTERS) as f:
+    with open(counters) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_sha256") != source_digest():
+    if vals.get("kernel_source_sha256") != source_digest(source):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -95,12 +102,128 @@ def cpu_baseline(inp, scale):
                       f"{dt:.2f} s on {threads} threads, {cpu_model})"}
 
 
+def timed_launches(fn, stream, steps, warmup, before=None):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream; ``before``
+    runs untimed ahead of every launch (e.g. restoring state updated in place)."""
+    import torch
+    for _ in range(warmup):
+        if before:
+            before()
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        if before:
+            before()
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(starts, ends)]
+
+
+def decode_bytes(R, H, D, W, n_new, n_acc_total, out_bytes):
+    """Bytes the fused verify must move: the fp32 state read once and written twice (accepted
+    and bonus states), the convolution tail read and written, the bf16 projected inputs of the
+    tokens it replays (q, k, v, g, beta of n_acc accepted drafts per request) and of the new
+    window (q, k, v, g, z, beta), the outputs, the taps and the norm weight."""
+    state = 3 * R * H * D * D * 4
+    tail = 2 * R * H * 3 * D * (W - 1) * 4
+    inputs = n_acc_total * H * (4 * D + 1) * 2 + R * n_new * H * (5 * D + 1) * 2
+    return state + tail + inputs + R * n_new * H * D * out_bytes + H * 3 * D * W * 4 + D * 4
+
+
+def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
+    cfg = wl.CONFIGS["decode_verify"]
+    R, H, D, W, n_new = cfg["R"], cfg["H"], cfg["dk"], cfg["conv_width"], cfg["n_new"]
+    w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=W, n_new=n_new, window=cfg["window"],
+                         seed=cfg["seed"], device=dev)
+    state = w.state.clone()
+    tail = w.conv_tail.clone()
+    acc = torch.empty_like(state)
+    o = torch.empty(R, n_new, H, D, dtype=torch.bfloat16, device=dev)
+
+    def restore():
+        state.copy_(w.state)
+        tail.copy_(w.conv_tail)
+
+    def launch():
+        kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
+                          state_acc=acc, o=o, stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup, before=restore)
+    avg = sum(ms) / len(ms)
+    n_acc_total = int(w.n_acc.sum().item())
+    nbytes = decode_bytes(R, H, D, W, n_new, n_acc_total, 2)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    out = {"workload": f"decode_verify: {R} requests x {H} heads, d_k=d_v={D}, fp32 state, "
+                       f"window of {cfg['window'] - 1} drafts + 1 bonus, accepted drafts "
+                       f"uniform in 0..{cfg['window'] - 1} (mean {n_acc_total / R:.2f}), "
+                       f"conv width {W}, bf16 inputs and output",
+           "latency_ms": avg, "min_latency_ms": min(ms),
+           "verified_tokens_per_s": R * n_new / (avg * 1e-3),
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": counter_traffic(DECODE_COUNTERS, DECODE_SRC)},
+           "algorithmic_bytes_per_launch": nbytes, "kernel": "decode_replay_kernel"}
+    if cpu_baseline:
+        import numpy as np
+        from oracle import kda_oracle as ko
+        rs = list(range(4))
+        host = lambda x: None if x is None else x[rs].double().cpu().numpy()
+        t0 = time.perf_counter()
+        ko.decode_replay(host(w.state), host(w.conv_tail), w.n_acc[rs].cpu().numpy(),
+                         {k: host(v) for k, v in w.prev.items()},
+                         {k: host(v) for k, v in w.new.items()},
+                         w.conv_w.double().cpu().numpy(), w.norm_w.double().cpu().numpy())
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": len(rs) * n_new / dt, "unit": "verified tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{len(rs)} requests x {H} heads of the same workload "
+                                         f"(fp64 NumPy oracle, {dt:.2f} s)"}
+        del np
+    return out
+
+
+def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
+    cfg = wl.CONFIGS["ultralong_256k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device=dev)
+    q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    ht = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    n_seg = 0   # the library's automatic choice
+    ws = torch.empty(kda.segment_cp_workspace_size(1, H, dk, dv, n_seg), dtype=torch.uint8,
+                     device=dev)
+
+    def launch():
+        kda.segment_cp_fwd(q, k, v, g, beta, o=o, ht=ht, n_segments=n_seg, workspace=ws,
+                           stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup)
+    avg = sum(ms) / len(ms)
+    nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2)
+    del inp, q, k, v, g, beta, o, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"ultralong_256k: B=1, T={T}, H={H}, d_k=d_v={dk}, bf16 q/k/v and "
+                        "output, fp32 g/beta/state, automatic segment count",
+            "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "algorithmic_bytes_per_call": nbytes,
+            "kernels": "transition (chunk kernel), ordered scan, replay (chunk kernel)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="prefill,decode,segment",
+                    help="comma-separated legs to run besides the prefill line "
+                         "(decode, segment); the prefill leg always runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -193,6 +316,16 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
+    legs = set(args.legs.split(","))
+    if "decode" in legs or "segment" in legs:
+        del inp, q, k, v, g, beta, h0, o, ht
+        torch.cuda.empty_cache()
+    if "decode" in legs:
+        line["decode"] = bench_decode(kda, wl, torch, dev, stream, args.steps, args.warmup,
+                                      not args.no_cpu_baseline)
+    if "segment" in legs:
+        line["segment_cp"] = bench_segment(kda, wl, torch, dev, stream,
+                                           max(3, args.steps // 4), min(args.warmup, 2))
     print(json.dumps(line), flush=True)
 
 
