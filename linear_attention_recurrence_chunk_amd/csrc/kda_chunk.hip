@@ -99,9 +99,9 @@ __device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E
   if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(x - to_f32(h));
 }
 
-// Row-block IA of A and row-block 3 - IA of M for one wave. Column operands: k / rho on the
-// diagonal block, k kappa next to it, k kappa times the decay gap further down.
-template <class Pol, class L, int DK, int IA>
+// Row-block IA of A and (kM) row-block 3 - IA of M for one wave. Column operands: k / rho on
+// the diagonal block, k kappa next to it, k kappa times the decay gap further down.
+template <class Pol, class L, int DK, int IA, bool kM>
 __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typename Pol::E* sKd,
                                         const typename Pol::E* sKdLo, const typename Pol::E* sKc,
                                         const typename Pol::E* sQr, const typename Pol::E* sQrLo,
@@ -124,8 +124,8 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
 #pragma unroll
   for (int pp = 0; pp < NS; ++pp) {
     const Frag rowA = Pol::load(sKr, L::LDP, 16 * IA + ln, pp, q4);
-    const Frag rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
-    Frag colA[4], colM[4], dKl, dQl;
+    Frag rowM, colA[4], colM[4], dKl, dQl;
+    if constexpr (kM) rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
 #pragma unroll
     for (int jb = 0; jb <= IA; ++jb) {
       if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
@@ -135,22 +135,25 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     }
 #pragma unroll
     for (int jb = 0; jb <= IM; ++jb) {
+      if constexpr (!kM) break;
       if (jb == IM) colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == IM - 1) colM[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == 0 && IM == 3) colM[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
       else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
     }
-    if constexpr (Pol::kSplit) {
+    if constexpr (Pol::kSplit && kM) {
       dKl = Pol::load(sKdLo, L::LDP, 16 * IM + ln, pp, q4);
       dQl = Pol::load(sQrLo, L::LDP, 16 * IM + ln, pp, q4);
     }
 #pragma unroll
     for (int jb = 0; jb <= IA; ++jb) accA[jb] = Pol::mma(colA[jb], rowA, accA[jb]);
+    if constexpr (kM) {
 #pragma unroll
-    for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
-    if constexpr (Pol::kSplit) {
-      accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
-      accM[IM] = Pol::mma(colM[IM], dQl, accM[IM]);
+      for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
+      if constexpr (Pol::kSplit) {
+        accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
+        accM[IM] = Pol::mma(colM[IM], dQl, accM[IM]);
+      }
     }
   }
   // register e of block (row i, column jb): row 16 i + ln, column 16 jb + 4 q4 + e
@@ -168,6 +171,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
   }
 #pragma unroll
   for (int jb = 0; jb <= IM; ++jb) {
+    if constexpr (!kM) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = 16 * jb + 4 * q4 + e;
@@ -354,7 +358,9 @@ __device__ __forceinline__ void store4_split(typename Pol::E* hi, typename Pol::
   }
 }
 
-template <class Pol, typename Tio, typename Tout, int DK>
+// kOut false: the transition pass of the segment-parallel path, which keeps only the state
+// (no M, no Q e^Gamma tile, no output products, q is never read).
+template <class Pol, typename Tio, typename Tout, int DK, bool kOut>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using L = ChunkLayout<Pol, DK>;
   using E = typename Pol::E;
@@ -466,7 +472,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   RawChunk<Tio, DK> raw;
 
   if (bos < eos)
-    load_chunk_any<kLoadAll, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+    load_chunk_any<kOut ? kLoadAll : kLoadAll & ~kLoadQ, Tio, DK>(raw, p, bos, min(kChunk, eos - bos),
+                                                                w, lane, h, vcol0);
 
   const int lane0 = lane, q4_0 = q4, ln0 = ln;
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
@@ -504,7 +511,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           lp[c] *= __expf(gt);
           rho[t][c] = lp[c];
           kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
-          qv[t][c] = valid ? to_f32(raw.q[t][c]) : 0.f;
+          qv[t][c] = (kOut && valid) ? to_f32(raw.q[t][c]) : 0.f;
         }
       }
     };
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         rho[t][c] = xkc[c];  // k kappa
       }
       const int idx = (rb0 + t) * L::LDP + c0;
-      store4_split<Pol>(sQr + idx, sQrLo + idx, xq);
+      if constexpr (kOut) store4_split<Pol>(sQr + idx, sQrLo + idx, xq);
       store4_split<Pol>(sKd + idx, sKdLo + idx, xkd);
       store4<Pol>(sKr + idx, xkr);
       store4<Pol>(sKc + idx, xkc);
@@ -586,10 +593,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     // 28 MFMAs (M's diagonal block uses split operands). The row blocks are compile-time per
     // wave so each slice's fragment loads issue together.
     switch (w) {
-      case 0: am_rows<Pol, L, DK, 0>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
-      case 1: am_rows<Pol, L, DK, 1>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
-      case 2: am_rows<Pol, L, DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
-      default: am_rows<Pol, L, DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      case 0: am_rows<Pol, L, DK, 0, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      case 1: am_rows<Pol, L, DK, 1, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      case 2: am_rows<Pol, L, DK, 2, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
+      default: am_rows<Pol, L, DK, 3, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
     }
     KDA_PREFETCH(kLoadG, 2, 4);
     __syncthreads();
@@ -605,7 +612,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           xq[c] = qv[t][c] * fs[c];   // q e^{Gamma}
           xk[c] = kv[t][c] * fs[c];   // k e^{Gamma}
         }
-        store4_split<Pol>(sQg + idx, sQgLo + idx, xq);
+        if constexpr (kOut) store4_split<Pol>(sQg + idx, sQgLo + idx, xq);
         store4<Pol>(sKg + idx, xk);
       }
       KDA_PREFETCH(kLoadG, 4, 6);
@@ -736,11 +743,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
     }
-    KDA_PREFETCH(kLoadQ, 0, 4);
+    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 0, 4);
     f32x4 U[4], O[4];
     // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
+      if constexpr (!kOut) break;
       Frag qh[4], ql[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -759,7 +767,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
       }
     }
-    KDA_PREFETCH(kLoadQ, 4, 8);
+    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 4, 8);
     // U = T' (V - K_Gamma S) = -T' X
     Frag Xh[NT], Xl[NT];
 #pragma unroll
@@ -795,6 +803,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(U, pp, Uh[pp], Ul[pp]);
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) {
+      if constexpr (!kOut) break;
       Frag mh[4], ml[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
@@ -845,7 +854,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
     // output, after the state update so that the last O products complete under it: a quad
     // transpose gives each lane four consecutive columns of token 16 rb + 4 q4 + lane % 4
-    if (mode != kModeTransition) {
+    if constexpr (kOut) {
       const int tq = 4 * q4 + (ln & 3);
       const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
 #pragma unroll
@@ -887,7 +896,10 @@ template <class Pol, typename Tio, typename Tout, int DK>
 static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   const int groups = (p.n_units + 7) / 8;
   const dim3 grid(groups * 8 * p.n_vt);
-  hipLaunchKernelGGL((chunk_fwd_kernel<Pol, Tio, Tout, DK>), grid, dim3(256), 0, stream, p);
+  if (p.mode == kModeTransition)
+    hipLaunchKernelGGL((chunk_fwd_kernel<Pol, Tio, Tout, DK, false>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_fwd_kernel<Pol, Tio, Tout, DK, true>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
