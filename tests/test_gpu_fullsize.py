@@ -1,0 +1,139 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+Each test runs the entry point on the whole workload exactly as the benchmark does (bf16
+output), runs it again with fp32 output, and checks:
+  * the bf16 output is bit-for-bit the round-to-nearest-even of the fp32 output (so the timed
+    launch carries the verified arithmetic);
+  * the fp32 output and the final states match the fp64 oracle, element by element, on a
+    sample of heads / sequences / requests the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_chunk_amd as kda
+from linear_attention_recurrence_chunk_amd import workloads as wl
+from oracle import c_recurrence_fwd
+from oracle import kda_oracle as ko
+from kda_testutil import TOL_BF16, np64, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL = 1e-5
+
+
+def _host_heads(x, heads):
+    return x[:, heads].detach().to("cpu", torch.float32).numpy()
+
+
+def _check_rounding(o16, o32):
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+
+
+def test_prefill_8k_full():
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    print(f"case prefill_8k T={T} H={H} d={dk}", flush=True)
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device="cuda")
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    o16, ht16 = kda.chunk_fwd(*args, h0=inp["h0"])
+    o32, ht32 = kda.chunk_fwd(*args, h0=inp["h0"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_rounding(o16, o32)
+    assert torch.equal(ht16, ht32)
+    heads = [0, 47, 95]
+    o_ref, ht_ref = c_recurrence_fwd(*[_host_heads(x, heads) for x in args],
+                                     h0=_host_heads(inp["h0"], heads))
+    e_o = rel_max_err(_host_heads(o32, heads), o_ref)
+    e_s = rel_max_err(_host_heads(ht32, heads), ht_ref)
+    print(f"heads {heads}: err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_ultralong_256k_segment_cp_full():
+    cfg = wl.CONFIGS["ultralong_256k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    print(f"case ultralong_256k T={T} H={H} d={dk} (automatic segments)", flush=True)
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device="cuda")
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    o16, ht16 = kda.segment_cp_fwd(*args)
+    o32, ht32 = kda.segment_cp_fwd(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_rounding(o16, o32)
+    assert torch.equal(ht16, ht32)
+    heads = [5]
+    o_ref, ht_ref = c_recurrence_fwd(*[_host_heads(x, heads) for x in args])
+    e_o = rel_max_err(_host_heads(o32, heads), o_ref)
+    e_s = rel_max_err(_host_heads(ht32, heads), ht_ref)
+    print(f"head {heads}: err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_varlen_64_full():
+    cfg = wl.CONFIGS["varlen_64"]
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    lengths = wl.varlen_lengths(cfg["n_seqs"], cfg["len_lo"], cfg["len_hi"], cfg["seed"])
+    print(f"case varlen_64 {len(lengths)} sequences, {sum(lengths)} tokens, H={H}", flush=True)
+    inp = wl.prefill_inputs(H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], lengths=lengths, device="cuda")
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    cu = inp["cu_seqlens"]
+    o32, ht32 = kda.chunk_fwd(*args, h0=inp["h0"], cu_seqlens=cu, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cu_h = cu.tolist()
+    # the shortest and the longest sequence and two in between, two heads each
+    order = np.argsort(lengths)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 7})
+    heads = [3, 90]
+    for n in seqs:
+        a, b = cu_h[n], cu_h[n + 1]
+        sl = [x[a:b] for x in args]
+        o_ref, ht_ref = c_recurrence_fwd(*[_host_heads(x, heads) for x in sl],
+                                         h0=_host_heads(inp["h0"][n:n + 1], heads))
+        e_o = rel_max_err(_host_heads(o32[a:b], heads), o_ref)
+        e_s = rel_max_err(_host_heads(ht32[n:n + 1], heads), ht_ref)
+        print(f"seq {n} (length {b - a}) heads {heads}: err_o={e_o:.3e} err_state={e_s:.3e}")
+        assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    del o32
+    torch.cuda.empty_cache()
+    o16, ht16 = kda.chunk_fwd(*args, h0=inp["h0"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(ht16, ht32)
+
+
+def test_decode_verify_full():
+    cfg = wl.CONFIGS["decode_verify"]
+    R, H, D, W, n_new = cfg["R"], cfg["H"], cfg["dk"], cfg["conv_width"], cfg["n_new"]
+    print(f"case decode_verify R={R} H={H} d={D}", flush=True)
+    w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=W, n_new=n_new, window=cfg["window"],
+                         seed=cfg["seed"], device="cuda")
+    outs = {}
+    for odt in (torch.bfloat16, torch.float32):
+        state, tail = w.state.clone(), w.conv_tail.clone()
+        o, acc = kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
+                                   out_dtype=odt)
+        torch.cuda.synchronize()
+        outs[odt] = (o, state, acc, tail)
+    o16, s16, a16, t16 = outs[torch.bfloat16]
+    o32, s32, a32, t32 = outs[torch.float32]
+    _check_rounding(o16, o32)
+    assert torch.equal(s16, s32) and torch.equal(a16, a32) and torch.equal(t16, t32)
+    n_acc = w.n_acc.cpu()
+    # requests with no, some and all accepted drafts
+    rs = sorted({int(torch.argmin(n_acc)), int(torch.argmax(n_acc)), 100, 255})
+    host = lambda x: None if x is None else x[rs].double().cpu().numpy()
+    ref = ko.decode_replay(host(w.state), host(w.conv_tail), n_acc[rs].numpy(),
+                           {k: host(v) for k, v in w.prev.items()},
+                           {k: host(v) for k, v in w.new.items()},
+                           w.conv_w.double().cpu().numpy(), w.norm_w.double().cpu().numpy())
+    e_state = np.abs(np64(s32[rs]) - ref["state"]).max()
+    e_acc = np.abs(np64(a32[rs]) - ref["state_acc"]).max()
+    e_tail = np.abs(np64(t32[rs]) - ref["conv_tail"]).max()
+    e_o = rel_max_err(np64(o32[rs]), ref["o"])
+    print(f"requests {rs} (n_acc {n_acc[rs].tolist()}): err_state={e_state:.2e} "
+          f"err_acc={e_acc:.2e} err_tail={e_tail:.2e} err_o={e_o:.2e}")
+    assert e_state <= STATE_TOL and e_acc <= STATE_TOL and e_tail <= STATE_TOL
+    assert e_o <= TOL_BF16
