@@ -693,6 +693,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
     __syncthreads();
     KDA_PREFETCH(kLoadK, 0, 4);
+    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 0, 4);
     {
       const int bj = w & 1;          // column block 0 or 1
       const bool row3 = w >= 2;      // row block 2 or 3
@@ -711,6 +712,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       put(row3 ? 3 : 2, bj, Ya + Yb);
     }
     KDA_PREFETCH(kLoadK, 4, 8);
+    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 4, 8);
     __syncthreads();
 
 
@@ -743,7 +745,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
     }
-    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 0, 4);
     f32x4 U[4], O[4];
     // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
 #pragma unroll
@@ -767,7 +768,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
       }
     }
-    if constexpr (kOut) KDA_PREFETCH(kLoadQ, 4, 8);
     // U = T' (V - K_Gamma S) = -T' X
     Frag Xh[NT], Xl[NT];
 #pragma unroll
