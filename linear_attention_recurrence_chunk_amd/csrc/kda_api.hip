@@ -107,6 +107,43 @@ int launch_status(hipError_t err) {
   return KDA_OK;
 }
 
+// Compute units of the current device (one query per process and device).
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Automatic segment count (at most kAutoSegments, the size the workspace query assumes): the
+// one minimising a cost in units of one chunk step of the chunk kernel, with the passes
+// running in rounds of one workgroup per compute unit. A transition step costs ~0.75 of a
+// replay step (no output products) and a scan step ~0.9. One segment means the plain
+// forward kernel (no transition, no scan).
+int auto_segments(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
+  auto rounds = [&](int64_t wgs) { return double((wgs + cus - 1) / cus); };
+  double best = rounds(int64_t(N) * H * (dv / 64)) * double(max_chunks);
+  int best_n = 1;
+  const int hi = int(max_chunks < kAutoSegments ? max_chunks : kAutoSegments);
+  for (int n = 2; n <= hi; ++n) {
+    const double per_seg = double((max_chunks + n - 1) / n);
+    const double cost = rounds(int64_t(N) * n * H * ((dk + dv) / 64)) * per_seg * 0.75 +
+                        0.9 * n + rounds(int64_t(N) * n * H * (dv / 64)) * per_seg;
+    if (cost < best) {
+      best = cost;
+      best_n = n;
+    }
+  }
+  return best_n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,7 +248,6 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   }
   if (N == 0) return KDA_OK;
   if (n_segments == 0) {
-    // automatic: no more segments than the longest sequence has chunks
     int64_t max_len = 0;
     if (cu_seqlens_host) {
       for (int i = 0; i < N; ++i) {
@@ -221,12 +257,35 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
     } else {
       max_len = seq_len;
     }
-    const int64_t max_chunks = (max_len + 63) / 64;
-    if (max_chunks < ns) ns = max_chunks < 1 ? 1 : int(max_chunks);
+    ns = auto_segments(N, num_heads, d_k, d_v, (max_len + 63) / 64, compute_units());
   }
   float* ws_pq = static_cast<float*>(workspace);
   float* ws_sin = ws_pq + size_t(N) * ns * num_heads * d_k * (d_k + d_v);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ns == 1 && n_segments == 0) {
+    // one segment: the entering state is h0, so the forward pass is the whole job
+    kda::ChunkParams f{};
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.g = g;
+    f.beta = beta;
+    f.h0 = h0;
+    f.cu_seqlens = cu_seqlens;
+    f.o = o;
+    f.ht = ht;
+    f.seq_len = cu_seqlens ? 0 : seq_len;
+    f.n_seqs = N;
+    f.H = num_heads;
+    f.dv = d_v;
+    f.n_vt = d_v / 64;
+    f.n_seg = 1;
+    f.n_units = N * num_heads;
+    f.scale = scale;
+    f.g_min = g_min;
+    f.mode = kda::kModeForward;
+    return launch_status(kda::launch_chunk_fwd(f, io_dtype, out_dtype, d_k, s));
+  }
 
   kda::ChunkParams p{};
   p.q = q;

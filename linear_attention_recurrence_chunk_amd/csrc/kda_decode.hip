@@ -279,7 +279,8 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
     __syncthreads();
     // per-row factors of the recurrence, once per token and channel
 #pragma unroll
-    for (int idx = tid; idx < NB * D; idx += 256) {
+    for (int m = 0; m < NB * D / 256; ++m) {
+      const int idx = tid + 256 * m;
       const int i = idx / D, c = idx % D;
       if (i < nb) {
         const float a = s_a[i][c];
