@@ -315,10 +315,12 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
     const bool ok = 16 * rb + 4 * q4 + (ln & 3) < Lc;
     x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, size_t(cstart + 16 * rb) * vrow, lv, ok, fv);
   }
-  x.beta = 0.f;
-  if (lane < 16) {
-    const bool ok = 16 * w + lane < Lc;
-    const uint32_t lb = uint32_t((16 * w + lane) * H + h);
+  // beta of token 16 w + lane % 16 (every lane loads, so that the register is only ever
+  // written by loads; lanes 16-63 repeat lanes 0-15 and are not used)
+  {
+    const int bl = lane & 15;
+    const bool ok = 16 * w + bl < Lc;
+    const uint32_t lb = uint32_t((16 * w + bl) * H + h);
     const size_t fb = size_t(cstart) * H + h;
     x.beta = *lane_ptr<kFull, float, float>(p.beta, size_t(cstart) * H, lb, ok, fb);
   }
