@@ -82,3 +82,25 @@ def test_workspace_too_small_is_rejected():
         kda.segment_cp_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], n_segments=4,
                            workspace=ws)
     assert ei.value.status == -6
+
+
+def test_automatic_segment_count():
+    """n_segments = 0: the library picks the count from its cost model (a few segments for
+    two heads of 1000 tokens) and matches the oracle."""
+    inp = wl.prefill_inputs(T=1000, H=2, dk=128, dv=128, dtype="bf16", seed=21, h0_std=0.02)
+    o, ht = _seg(inp, 0)
+    o_ref, ht_ref = _oracle(inp, varlen=False)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"auto: err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_automatic_single_segment_is_the_forward_pass():
+    """With enough heads to fill the device the model picks one segment, which runs the
+    forward kernel itself: the result equals kda_chunk_fwd bit for bit."""
+    inp = wl.prefill_inputs(T=300, H=96, dk=128, dv=128, dtype="bf16", seed=22, h0_std=0.02)
+    d = to_dev(inp)
+    o1, h1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                           out_dtype=torch.float32)
+    o2, h2 = _seg(inp, 0)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
