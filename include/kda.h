@@ -105,8 +105,12 @@ int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v,
  * section 5: group summaries, ordered scan, parallel replay).
  *
  * Same tensors, conventions and supported sizes as kda_chunk_fwd. Every sequence is cut into
- * up to n_segments contiguous, chunk-aligned segments (n_segments = 0: automatic, otherwise
- * 1..256). Three launches on `stream`: (1) each segment's affine summary (P, Q) with
+ * up to n_segments contiguous, chunk-aligned segments (1..256). With n_segments = 0 the
+ * library picks at most 64 from a cost model over the device's compute units and the longest
+ * sequence; when that choice is one segment (the heads alone fill the device) it runs the
+ * forward kernel once, exactly as kda_chunk_fwd, and leaves the workspace untouched (the
+ * workspace query still returns the size for 64 segments). Otherwise there are three
+ * launches on `stream`: (1) each segment's affine summary (P, Q) with
  * S_out = P S_in + Q, computed without its entering state; (2) an ordered scan that composes
  * the summaries into every segment's exact entering state and the final state; (3) all
  * segments replay their tokens in parallel from those states. The result equals
