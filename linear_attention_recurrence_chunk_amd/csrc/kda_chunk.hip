@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
     Frag Sh[NS], Sl[NS];
 #pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
+    for (int pp = 0; pp < NS; ++pp) Sh[pp] = Pol::from_acc(S, pp);   // lo halves after X
     // X = (K e^Gamma) S - V, in fp32
     // (the values stay packed in the raw registers until here)
     f32x4 X[4];
@@ -747,6 +747,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
     }
+    // the lo halves of S, computed while the X products run
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) Sl[pp] = Pol::lo_from_acc(S, pp, Sh[pp]);
     f32x4 U[4], O[4];
     // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
 #pragma unroll

@@ -108,6 +108,12 @@ struct PolBF16 {
       hi[e] = xh;
       lo[e] = (__bf16)(x - (float)xh);
     }
+  }  // the lo half of from_acc_split, given the hi half from from_acc
+  __device__ static __forceinline__ Frag lo_from_acc(const f32x4* acc, int p, Frag hi) {
+    Frag lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo[e] = (__bf16)(acc[2 * p + (e >> 2)][e & 3] - (float)hi[e]);
+    return lo;
   }
 };
 
@@ -143,7 +149,7 @@ struct PolF32 {
                                                         Frag& lo) {
     hi = acc[p >> 2][p & 3];
     lo = 0.f;
-  }
+  }  __device__ static __forceinline__ Frag lo_from_acc(const f32x4*, int, Frag) { return 0.f; }
 };
 
 // fp32 MFMA on a natural k-order (used by the triangular inverse): slice s holds k = 4s + q.
