@@ -25,11 +25,16 @@
 // Precision. The inverse is fp32 end to end (fp32 inputs, fp32 16x16x4 MFMA accumulation)
 // and rounded only once complete. The model's outputs are heavy-tailed (a read-out is a sum
 // of products of near-Gaussian factors, max |o| ~ 10-30 x RMS), so a single bf16 rounding of
-// a dominant factor would cost up to ~2.5% of the output RMS. Every factor on the dominant
-// paths (T diag(beta), the diagonal blocks of M and their operands, M, U, V - K_Gamma S,
-// Q e^Gamma, S in the read-out, K e^{Gamma_L - Gamma}) is therefore carried as a hi + lo pair
-// of bf16 values and multiplied with three bf16 MFMAs (hi*hi + lo*hi + hi*lo): ~16 mantissa
-// bits on matrix cores at 3/16 of the cost of fp32 MFMA.
+// a dominant factor would cost up to ~2.5% of the output RMS. Two kinds of operands avoid it:
+//  * factors bounded well inside the fp16 range go to fp16 MFMAs (11-bit significand, one
+//    MFMA): Q e^Gamma and K e^Gamma (at most 1 for unit-norm q, k) and the state S in the
+//    products with them. With unit keys, beta in [0, 1] and g <= 0 a token adds at most
+//    v_c^2 to the squared norm of state column c, so |S| stays below
+//    sqrt(|h0 column|^2 + sum_t v_{t,c}^2), far inside fp16's 65504;
+//  * the other factors on the dominant paths (T diag(beta), the diagonal blocks of M and
+//    their operands, M, U, V - K_Gamma S, K e^{Gamma_L - Gamma}) can be large or tiny and
+//    are carried as a hi + lo pair of bf16 values, multiplied with three bf16 MFMAs
+//    (hi*hi + lo*hi + hi*lo): ~16 mantissa bits at 3/16 of the cost of fp32 MFMA.
 //
 // Work decomposition: one workgroup (4 waves) per (sequence, head, 64-wide value tile).
 // Value columns of S never mix, so each wave owns 16 columns of S in its MFMA accumulators
@@ -63,11 +68,10 @@ struct ChunkLayout {
   static constexpr size_t oKr = oKdLo + kLo * tP;
   static constexpr size_t oKc = oKr + tP;
   static constexpr size_t kXA = oKc + tP;
-  // ---- region X, recurrence view: Q e^Gamma (hi, lo) over q rho (hi, lo) and K e^Gamma over
+  // ---- region X, recurrence view: Q e^Gamma (fp16) over q rho and K e^Gamma (fp16) over
   //      k / rho, row for row (a thread rewrites in place the elements it reads back), then
   //      (K e^{GL-Gamma})^T (hi, lo) over k rho and k kappa, which are dead by then
   static constexpr size_t oQg = oQr;
-  static constexpr size_t oQgLo = oQrLo;
   static constexpr size_t oKg = oKd;
   static constexpr size_t oKhT = oKr;
   static constexpr size_t oKhTLo = oKhT + tT;
@@ -343,6 +347,15 @@ __device__ __forceinline__ void store4(typename Pol::E* dst, const float* x) {
     *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
 }
 
+// four consecutive elements as read-out operands (fp16 for bf16 inputs)
+template <class Pol>
+__device__ __forceinline__ void store4r(typename Pol::ER* dst, const float* x) {
+  if constexpr (sizeof(typename Pol::ER) == 2)
+    *reinterpret_cast<f16x4*>(dst) = __builtin_convertvector((f32x4{x[0], x[1], x[2], x[3]}), f16x4);
+  else
+    *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+}
+
 template <class Pol>
 __device__ __forceinline__ void store4_split(typename Pol::E* hi, typename Pol::E* lo,
                                              const float* x) {
@@ -367,6 +380,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using L = ChunkLayout<Pol, DK>;
   using E = typename Pol::E;
   using Frag = typename Pol::Frag;
+  using ER = typename Pol::ER;
+  using FragR = typename Pol::FragR;
   using PM = ProMap<DK>;
   constexpr int TPT = PM::kTPT;            // tokens per thread in the prologue
   constexpr int NS = Pol::slices(DK);      // k-slices over key channels
@@ -381,11 +396,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   E* sKdLo = reinterpret_cast<E*>(smem + L::oKdLo);
   E* sKr = reinterpret_cast<E*>(smem + L::oKr);
   E* sKc = reinterpret_cast<E*>(smem + L::oKc);
-  E* sQg = reinterpret_cast<E*>(smem + L::oQg);
-  E* sQgLo = reinterpret_cast<E*>(smem + L::oQgLo);
+  ER* sQg = reinterpret_cast<ER*>(smem + L::oQg);
   E* sKhT = reinterpret_cast<E*>(smem + L::oKhT);
   E* sKhTLo = reinterpret_cast<E*>(smem + L::oKhTLo);
-  E* sKg = reinterpret_cast<E*>(smem + L::oKg);
+  ER* sKg = reinterpret_cast<ER*>(smem + L::oKg);
   E* sT = reinterpret_cast<E*>(smem + L::oT);
   E* sTLo = reinterpret_cast<E*>(smem + L::oTLo);
   float* sA = reinterpret_cast<float*>(smem + L::oA);
@@ -614,8 +628,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           xq[c] = qv[t][c] * fs[c];   // q e^{Gamma}
           xk[c] = kv[t][c] * fs[c];   // k e^{Gamma}
         }
-        if constexpr (kOut) store4_split<Pol>(sQg + idx, sQgLo + idx, xq);
-        store4<Pol>(sKg + idx, xk);
+        if constexpr (kOut) store4r<Pol>(sQg + idx, xq);
+        store4r<Pol>(sKg + idx, xk);
       }
       KDA_PREFETCH(kLoadG, 4, 6);
       // (K e^{Gamma_L - Gamma})^T: channel rows, this thread's TPT consecutive tokens
@@ -722,9 +736,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 
     // Each product loads a batch of A fragments from LDS first and then issues its MFMAs, so
     // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
-    Frag Sh[NS], Sl[NS];
+    // S as fp16 B fragments, shared by the two products with decayed keys and queries
+    FragR Sr[NS];
 #pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Sh[pp] = Pol::from_acc(S, pp);   // lo halves after X
+    for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
     // X = (K e^Gamma) S - V, in fp32
     // (the values stay packed in the raw registers until here)
     f32x4 X[4];
@@ -740,38 +755,24 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     KDA_PREFETCH(kLoadV, 0, 8);
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
-      Frag kg[4];
+      FragR kg[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load(sKg, L::LDP, 16 * rb + ln, pp, q4);
+      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load_r(sKg, L::LDP, 16 * rb + ln, pp, q4);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma(kg[rb], Sh[pp], X[rb]);
+      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(kg[rb], Sr[pp], X[rb]);
     }
-    // the lo halves of S, computed while the X products run
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Sl[pp] = Pol::lo_from_acc(S, pp, Sh[pp]);
     f32x4 U[4], O[4];
     // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
       if constexpr (!kOut) break;
-      Frag qh[4], ql[4];
+      FragR qg[4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        qh[rb] = Pol::load(sQg, L::LDP, 16 * rb + ln, pp, q4);
-        if constexpr (Pol::kSplit) ql[rb] = Pol::load(sQgLo, L::LDP, 16 * rb + ln, pp, q4);
-      }
+      for (int rb = 0; rb < 4; ++rb) qg[rb] = Pol::load_r(sQg, L::LDP, 16 * rb + ln, pp, q4);
       __builtin_amdgcn_sched_barrier(0);
-      // the three split products of one accumulator are issued four MFMAs apart (one pass per
-      // term over the row blocks), so consecutive MFMAs never wait on each other
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sh[pp], pp == 0 ? zero4() : O[rb]);
-      if constexpr (Pol::kSplit) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(ql[rb], Sh[pp], O[rb]);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma(qh[rb], Sl[pp], O[rb]);
-      }
+      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(qg[rb], Sr[pp], pp == 0 ? zero4() : O[rb]);
     }
     // U = T' (V - K_Gamma S) = -T' X
     Frag Xh[NT], Xl[NT];

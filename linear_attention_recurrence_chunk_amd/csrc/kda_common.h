@@ -11,6 +11,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kChunk = 64;   // tokens per chunk
@@ -108,12 +110,25 @@ struct PolBF16 {
       hi[e] = xh;
       lo[e] = (__bf16)(x - (float)xh);
     }
-  }  // the lo half of from_acc_split, given the hi half from from_acc
-  __device__ static __forceinline__ Frag lo_from_acc(const f32x4* acc, int p, Frag hi) {
-    Frag lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lo[e] = (__bf16)(acc[2 * p + (e >> 2)][e & 3] - (float)hi[e]);
-    return lo;
+  }
+  // fp16 operands (v_mfma_f32_16x16x32_f16, same k-order) for the products whose factors are
+  // bounded well inside the fp16 range: an 11-bit significand in one MFMA, where a single
+  // bf16 (8 bits) would need a hi + lo pair and three MFMAs
+  using ER = _Float16;
+  using FragR = f16x8;
+  __device__ static __forceinline__ f32x4 mma_r(FragR a, FragR b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ FragR load_r(const ER* tile, int ld, int row, int p, int q) {
+    const ER* base = tile + row * ld + 32 * p + 4 * q;
+    f16x4 lo = *reinterpret_cast<const f16x4*>(base);
+    f16x4 hi = *reinterpret_cast<const f16x4*>(base + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ static __forceinline__ FragR from_acc_r(const f32x4* acc, int p) {
+    const f32x4 a = acc[2 * p], b = acc[2 * p + 1];
+    const f16x4 ra = __builtin_convertvector(a, f16x4), rb = __builtin_convertvector(b, f16x4);
+    return __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
 
@@ -149,7 +164,14 @@ struct PolF32 {
                                                         Frag& lo) {
     hi = acc[p >> 2][p & 3];
     lo = 0.f;
-  }  __device__ static __forceinline__ Frag lo_from_acc(const f32x4*, int, Frag) { return 0.f; }
+  }
+  using ER = float;
+  using FragR = float;
+  __device__ static __forceinline__ f32x4 mma_r(FragR a, FragR b, f32x4 c) { return mma(a, b, c); }
+  __device__ static __forceinline__ FragR load_r(const ER* tile, int ld, int row, int p, int q) {
+    return load(tile, ld, row, p, q);
+  }
+  __device__ static __forceinline__ FragR from_acc_r(const f32x4* acc, int p) { return from_acc(acc, p); }
 };
 
 // fp32 MFMA on a natural k-order (used by the triangular inverse): slice s holds k = 4s + q.

@@ -27,6 +27,7 @@ PINS = [
     ("heads and columns independent", pins.test_heads_and_value_columns_independent, ()),
     ("varlen and empty sequence", pins.test_varlen_packing_equals_separate_runs_and_empty_sequence, ()),
     ("contraction", pins.test_token_transition_is_a_contraction, ()),
+    ("state energy bound", pins.test_state_column_energy_bound, ()),
     ("decode elementary functions", pins.test_decode_elementary_functions, ()),
     ("conv = np.convolve", pins.test_causal_conv_matches_numpy_convolve, ()),
     ("decode single token", pins.test_decode_single_token_is_one_recurrence_step, ()),

@@ -257,6 +257,34 @@ def test_token_transition_is_a_contraction():
         assert np.linalg.norm(A, 2) <= 1.0 + 1e-12
 
 
+def test_state_column_energy_bound():
+    """Unit keys, beta in [0, 1], g <= 0: one token adds at most v_c^2 to the squared norm of
+    state column c, so ||S_T[:, c]||^2 <= ||S_0[:, c]||^2 + sum_t v_{t,c}^2 (with the decay
+    first, the correction e = v - S'^T k changes the component along k only). Equality holds
+    for beta = 1, g = 0, keys orthonormal to each other and to the entering columns."""
+    rng = np.random.default_rng(12)
+    dk, dv = 12, 5
+    for trial in range(6):
+        T = 40 + 13 * trial
+        q, k, v, g, beta = _rand_inputs(rng, T, 1, dk, dv, g_scale=0.5)
+        g *= 0.05                     # decays near 1: the state keeps most of its past
+        v *= 1.0 + 3.0 * rng.random((T, 1, 1))
+        h0 = rng.standard_normal((1, 1, dk, dv))
+        for L in (1, T // 3, T):
+            _, ht = ko.recurrence_fwd(q[:L], k[:L], v[:L], g[:L], beta[:L], h0=h0)
+            lhs = np.sum(ht[0, 0] ** 2, axis=0)
+            rhs = np.sum(h0[0, 0] ** 2, axis=0) + np.sum(v[:L, 0] ** 2, axis=0)
+            assert np.all(lhs <= rhs * (1 + 1e-12)), (trial, L, lhs, rhs)
+    # equality case: orthonormal keys, overwrite, zero entering state
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Qm[:, :8].T
+    V = rng.standard_normal((8, dv))
+    _, ht = ko.recurrence_fwd(K[:, None], K[:, None], V[:, None], np.zeros((8, 1, dk)),
+                              np.ones((8, 1)))
+    np.testing.assert_allclose(np.sum(ht[0, 0] ** 2, axis=0), np.sum(V ** 2, axis=0),
+                               rtol=1e-12)
+
+
 # ------------------------------------------------------------------ C oracle twin
 @pytest.mark.parametrize("shape", [(256, 2, 64, 64), (70, 3, 16, 24)])
 def test_c_oracle_matches_numpy(shape):
