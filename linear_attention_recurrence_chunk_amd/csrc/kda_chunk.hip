@@ -299,10 +299,11 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
   // prologue elements: token cstart + 16 w + grp kTPT + t, channels c0 .. c0 + 3
   const uint32_t lk = uint32_t((grp * M::kTPT * H + h) * DK + c0);
   const size_t fk = (size_t(cstart) * H + h) * DK + c0;   // fallback: the chunk's first row
+  const size_t u0 = size_t(cstart + 16 * w) * row;
 #pragma unroll
   for (int t = kLo * M::kTPT / 8; t < kHi * M::kTPT / 8; ++t) {
     const bool ok = 16 * w + grp * M::kTPT + t < Lc;
-    const size_t u = size_t(cstart + 16 * w + t) * row;
+    const size_t u = u0 + size_t(t) * row;
     if constexpr ((kParts & kLoadG) != 0) x.g[t] = *lane_ptr<kFull, float, f32x4>(p.g, u, lk, ok, fk);
     if constexpr ((kParts & kLoadK) != 0) x.k[t] = *lane_ptr<kFull, Tio, Q4>(p.k, u, lk, ok, fk);
     if constexpr ((kParts & kLoadQ) != 0) x.q[t] = *lane_ptr<kFull, Tio, Q4>(p.q, u, lk, ok, fk);
@@ -314,10 +315,11 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
   const uint32_t lv = uint32_t(((4 * q4 + (ln & 3)) * H + h) * p.dv + vc);
   const size_t fv = (size_t(cstart) * H + h) * p.dv + vc;
   const size_t vrow = size_t(H) * p.dv;
+  const size_t v0 = size_t(cstart) * vrow;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const bool ok = 16 * rb + 4 * q4 + (ln & 3) < Lc;
-    x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, size_t(cstart + 16 * rb) * vrow, lv, ok, fv);
+    x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, v0 + size_t(16 * rb) * vrow, lv, ok, fv);
   }
   // beta of token 16 w + lane % 16 (every lane loads, so that the register is only ever
   // written by loads; lanes 16-63 repeat lanes 0-15 and are not used)
@@ -515,6 +517,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     const int rb0 = 16 * w + grp * TPT;   // first token row of this thread
     float rho[TPT][4], qv[TPT][4], kv[TPT][4];
     float lp[4] = {1.f, 1.f, 1.f, 1.f};   // running decay over this thread's tokens
+    // e^{max(g, g_min)} = 2^{max(g log2 e, g_min log2 e)}: scaling by log2 e first makes the
+    // floor a single max (the product needs no NaN quieting) and feeds v_exp_f32 directly
+    const float gmin2 = p.g_min * kLog2e;
     // rows past the end of a ragged last chunk count as zero keys and queries with no decay
     auto raw_in = [&](auto full) {
       constexpr bool kFull = decltype(full)::value;
@@ -523,8 +528,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         const bool valid = kFull || rb0 + t < Lc;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float gt = valid ? fmaxf(raw.g[t][c], p.g_min) : 0.f;
-          lp[c] *= __expf(gt);
+          const float gt = valid ? fmaxf(raw.g[t][c] * kLog2e, gmin2) : 0.f;
+          lp[c] *= __builtin_amdgcn_exp2f(gt);
           rho[t][c] = lp[c];
           kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
           qv[t][c] = (kOut && valid) ? to_f32(raw.q[t][c]) : 0.f;
@@ -749,8 +754,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
       quad_transpose(vx, lane);   // now token 16 rb + 4 q4 + e, column 16 w + ln
+      if (Lc == kChunk && !p_tile) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc && !p_tile) ? -vx[e] : 0.f;
+        for (int e = 0; e < 4; ++e) X[rb][e] = -vx[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc && !p_tile) ? -vx[e] : 0.f;
+      }
     }
     KDA_PREFETCH(kLoadV, 0, 8);
 #pragma unroll

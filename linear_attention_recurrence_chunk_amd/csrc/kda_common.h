@@ -14,6 +14,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kLog2e = 1.44269504088896340736f;   // log2(e), rounded to fp32
 constexpr int kWave = 64;
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kSub = 16;     // tokens per sub-block (one MFMA tile edge)
