@@ -86,11 +86,13 @@ typedef enum kda_dtype {
  * g values above 0 are accepted but are not decays. o must not overlap any input; ht may
  * alias h0 (in-place state update).
  *
- * Numeric range (KDA_BF16): the products of the state with the decayed queries and keys run
- * on fp16 operands (max 65504). They stay in range in the method's regime: q and k of unit
- * L2 norm per token and head, beta in [0, 1], g <= 0. There every token adds at most v_c^2
- * to the squared norm of state column c, so |S| <= sqrt(|h0 column c|^2 + sum_t v_{t,c}^2);
- * keys or queries far from unit norm, or a sum above ~4e9, can give non-finite outputs.
+ * Numeric range (KDA_BF16): several of the chunk's matrix products take fp16 operands (max
+ * 65504): the decayed queries and keys, the state, the tokens' weighted errors
+ * beta (v - S'^T k) and the in-chunk attention scores. They stay in range in the method's
+ * regime: q and k of unit L2 norm per token and head, beta in [0, 1], g <= 0. There every
+ * token adds at most v_c^2 to the squared norm of state column c, so
+ * |S| <= sqrt(|h0 column c|^2 + sum_t v_{t,c}^2) and each error is at most |v| + that bound;
+ * keys or queries far from unit norm, or a sum above ~1e9, can give non-finite outputs.
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,

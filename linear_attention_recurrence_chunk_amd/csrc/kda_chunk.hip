@@ -25,16 +25,19 @@
 // Precision. The inverse is fp32 end to end (fp32 inputs, fp32 16x16x4 MFMA accumulation)
 // and rounded only once complete. The model's outputs are heavy-tailed (a read-out is a sum
 // of products of near-Gaussian factors, max |o| ~ 10-30 x RMS), so a single bf16 rounding of
-// a dominant factor would cost up to ~2.5% of the output RMS. Two kinds of operands avoid it:
-//  * factors bounded well inside the fp16 range go to fp16 MFMAs (11-bit significand, one
-//    MFMA): Q e^Gamma and K e^Gamma (at most 1 for unit-norm q, k) and the state S in the
-//    products with them. With unit keys, beta in [0, 1] and g <= 0 a token adds at most
-//    v_c^2 to the squared norm of state column c, so |S| stays below
+// a dominant factor would cost up to ~2.5% of the output RMS. Three kinds of operands avoid it:
+//  * fp16 (11-bit significand, one MFMA) for factors bounded well inside the fp16 range:
+//    Q e^Gamma, K e^Gamma and K e^{Gamma_L - Gamma} (at most 1 for unit-norm q, k) and the
+//    state S in its products with them. With unit keys, beta in [0, 1] and g <= 0 a token adds
+//    at most v_c^2 to the squared norm of state column c, so |S| stays below
 //    sqrt(|h0 column|^2 + sum_t v_{t,c}^2), far inside fp16's 65504;
-//  * the other factors on the dominant paths (T diag(beta), the diagonal blocks of M and
-//    their operands, M, U, V - K_Gamma S, K e^{Gamma_L - Gamma}) can be large or tiny and
-//    are carried as a hi + lo pair of bf16 values, multiplied with three bf16 MFMAs
-//    (hi*hi + lo*hi + hi*lo): ~16 mantissa bits at 3/16 of the cost of fp32 MFMA.
+//  * fp16 hi + lo pairs (~22 bits, two or three MFMAs) for M (at most 1) and U, whose rows are
+//    the tokens' weighted errors beta (v - S'^T k), bounded like S;
+//  * bf16 hi + lo pairs (~16 bits, three MFMAs: hi*hi + lo*hi + hi*lo) where a factor can be
+//    large or tiny: T diag(beta), V - K_Gamma S, and the operands of M's diagonal blocks,
+//    whose in-block decay ratios reach e^{16 |g_min|}.
+// A itself takes single bf16 operands (with an fp32 accumulation and an fp32 inverse); the
+// emulation of every rounding point showed no gain from splitting them.
 //
 // Work decomposition: one workgroup (4 waves) per (sequence, head, 64-wide value tile).
 // Value columns of S never mix, so each wave owns 16 columns of S in its MFMA accumulators
@@ -70,17 +73,16 @@ struct ChunkLayout {
   static constexpr size_t kXA = oKc + tP;
   // ---- region X, recurrence view: Q e^Gamma (fp16) over q rho and K e^Gamma (fp16) over
   //      k / rho, row for row (a thread rewrites in place the elements it reads back), then
-  //      (K e^{GL-Gamma})^T (hi, lo) over k rho and k kappa, which are dead by then
+  //      (K e^{GL-Gamma})^T (fp16) over k rho, which is dead by then
   static constexpr size_t oQg = oQr;
   static constexpr size_t oKg = oKd;
   static constexpr size_t oKhT = oKr;
-  static constexpr size_t oKhTLo = oKhT + tT;
-  static constexpr size_t kXD = oKhTLo + kLo * tT;
+  static constexpr size_t kXD = oKhT + tT;
   static constexpr size_t kX = kXA > kXD ? kXA : kXD;
   // ---- region Y: fp32 A / T
   static constexpr size_t oA = kX;
   static constexpr size_t kY = size_t(64) * LDA * 4;
-  // ---- region Z: M (hi, lo); region W: T diag(beta) (hi, lo), both written during the prologue
+  // ---- region Z: M (fp16 hi, lo); region W: T diag(beta) (bf16 hi, lo), both written during the prologue
   //      while region X still holds the prologue tiles
   static constexpr size_t oM = oA + kY;
   static constexpr size_t oMLo = oM + t64;
@@ -93,6 +95,16 @@ struct ChunkLayout {
   static constexpr size_t kBytes = oDecay + DK * 4;
   static_assert(kBytes <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
+
+// one element as an fp16 hi + lo pair (fp32 for fp32 inputs)
+template <class Pol>
+__device__ __forceinline__ void store_split_r(typename Pol::ER* hi, typename Pol::ER* lo, int idx,
+                                              float x) {
+  using R = typename Pol::ER;
+  const R h = R(x);
+  hi[idx] = h;
+  if constexpr (Pol::kSplit) lo[idx] = R(x - float(h));
+}
 
 template <class Pol>
 __device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E* lo, int idx,
@@ -110,7 +122,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
                                         const typename Pol::E* sKdLo, const typename Pol::E* sKc,
                                         const typename Pol::E* sQr, const typename Pol::E* sQrLo,
                                         const float* sBP, const float* sBeta, float* sA,
-                                        typename Pol::E* sM, typename Pol::E* sMLo,
+                                        typename Pol::ER* sM, typename Pol::ER* sMLo,
                                         typename Pol::E* sT, typename Pol::E* sTLo, int ln, int q4) {
   using Frag = typename Pol::Frag;
   constexpr int NS = Pol::slices(DK);
@@ -156,7 +168,10 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
       if constexpr (Pol::kSplit) {
         accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
-        accM[IM] = Pol::mma(colM[IM], dQl, accM[IM]);
+        // the lo half of q rho on every block of the row: the single bf16 rounding of q rho
+        // is the largest error source of the outputs otherwise
+#pragma unroll
+        for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], dQl, accM[jb]);
       }
     }
   }
@@ -179,7 +194,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = 16 * jb + 4 * q4 + e;
-      store_split<Pol>(sM, sMLo, rm * L::LDT + s, (jb == IM && s > rm) ? 0.f : accM[jb][e]);
+      store_split_r<Pol>(sM, sMLo, rm * L::LDT + s, (jb == IM && s > rm) ? 0.f : accM[jb][e]);
     }
   }
   // Diagonal block IA of T = (I + A)^{-1} in fp32, by right-looking substitution: the quad of
@@ -399,14 +414,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   E* sKr = reinterpret_cast<E*>(smem + L::oKr);
   E* sKc = reinterpret_cast<E*>(smem + L::oKc);
   ER* sQg = reinterpret_cast<ER*>(smem + L::oQg);
-  E* sKhT = reinterpret_cast<E*>(smem + L::oKhT);
-  E* sKhTLo = reinterpret_cast<E*>(smem + L::oKhTLo);
+  ER* sKhT = reinterpret_cast<ER*>(smem + L::oKhT);
   ER* sKg = reinterpret_cast<ER*>(smem + L::oKg);
   E* sT = reinterpret_cast<E*>(smem + L::oT);
   E* sTLo = reinterpret_cast<E*>(smem + L::oTLo);
   float* sA = reinterpret_cast<float*>(smem + L::oA);
-  E* sM = reinterpret_cast<E*>(smem + L::oM);
-  E* sMLo = reinterpret_cast<E*>(smem + L::oMLo);
+  ER* sM = reinterpret_cast<ER*>(smem + L::oM);
+  ER* sMLo = reinterpret_cast<ER*>(smem + L::oMLo);
   float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
   float* sBP = reinterpret_cast<float*>(smem + L::oBP);
   float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
@@ -478,10 +492,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, s = idx & 63;
     if ((s >> 4) > (r >> 4)) {
-      sM[r * L::LDT + s] = from_f32<E>(0.f);
+      sM[r * L::LDT + s] = ER(0.f);
       sT[r * L::LDT + s] = from_f32<E>(0.f);
       if constexpr (Pol::kSplit) {
-        sMLo[r * L::LDT + s] = from_f32<E>(0.f);
+        sMLo[r * L::LDT + s] = ER(0.f);
         sTLo[r * L::LDT + s] = from_f32<E>(0.f);
       }
     }
@@ -610,9 +624,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     KDA_PREFETCH(kLoadG, 0, 2);
 
     // ================= prologue 2: A (fp32) and M (hi, lo) sub-blocks ====================
-    // wave w: row-block w of A (blocks (w, j <= w)) and row-block 3 - w of M; every wave runs
-    // 28 MFMAs (M's diagonal block uses split operands). The row blocks are compile-time per
-    // wave so each slice's fragment loads issue together.
+    // wave w: row-block w of A (blocks (w, j <= w)) and row-block 3 - w of M, 40 - 4 w MFMAs
+    // (M takes the lo half of q rho on every block, and of k / rho on its diagonal block). The
+    // row blocks are compile-time per wave so each slice's fragment loads issue together.
     switch (w) {
       case 0: am_rows<Pol, L, DK, 0, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
       case 1: am_rows<Pol, L, DK, 1, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) col[e] = rho[t4 + e][c] * fe[c];
           const int idx = (c0 + c) * L::LDT + rb0 + t4;
-          store4_split<Pol>(sKhT + idx, sKhTLo + idx, col);
+          store4r<Pol>(sKhT + idx, col);
         }
       }
       KDA_PREFETCH(kLoadG, 6, 8);
@@ -813,32 +827,33 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
-    // O += M U
-    Frag Uh[NT], Ul[NT];
+    // O += M U and S += K^T U with fp16 operands: U as an fp16 hi + lo pair, M as one too,
+    // K e^{Gamma_L - Gamma} (at most 1) as a single fp16
+    FragR Uh[NT], Ul[NT];
 #pragma unroll
-    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(U, pp, Uh[pp], Ul[pp]);
+    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split_r(U, pp, Uh[pp], Ul[pp]);
 #pragma unroll
     for (int pp = 0; pp < NT; ++pp) {
       if constexpr (!kOut) break;
-      Frag mh[4], ml[4];
+      FragR mh[4], ml[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         if (pp < Pol::slices_blocks(rb + 1)) {
-          mh[rb] = Pol::load(sM, L::LDT, 16 * rb + ln, pp, q4);
-          if constexpr (Pol::kSplit) ml[rb] = Pol::load(sMLo, L::LDT, 16 * rb + ln, pp, q4);
+          mh[rb] = Pol::load_r(sM, L::LDT, 16 * rb + ln, pp, q4);
+          if constexpr (Pol::kSplit) ml[rb] = Pol::load_r(sMLo, L::LDT, 16 * rb + ln, pp, q4);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(mh[rb], Uh[pp], O[rb]);
+        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Uh[pp], O[rb]);
       if constexpr (Pol::kSplit) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(ml[rb], Uh[pp], O[rb]);
+          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(ml[rb], Uh[pp], O[rb]);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma(mh[rb], Ul[pp], O[rb]);
+          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Ul[pp], O[rb]);
       }
     }
     // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
@@ -851,20 +866,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     for (int pp = 0; pp < NT; ++pp) {
 #pragma unroll
       for (int t0 = 0; t0 < NTD; t0 += 4) {
-        Frag kh[4], kl[4];
+        FragR kh[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          kh[t] = Pol::load(sKhT, L::LDT, 16 * (t0 + t) + ln, pp, q4);
-          if constexpr (Pol::kSplit) kl[t] = Pol::load(sKhTLo, L::LDT, 16 * (t0 + t) + ln, pp, q4);
-        }
+        for (int t = 0; t < 4; ++t) kh[t] = Pol::load_r(sKhT, L::LDT, 16 * (t0 + t) + ln, pp, q4);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kh[t], Uh[pp], S[t0 + t]);
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Uh[pp], S[t0 + t]);
         if constexpr (Pol::kSplit) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kl[t], Uh[pp], S[t0 + t]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma(kh[t], Ul[pp], S[t0 + t]);
+          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Ul[pp], S[t0 + t]);
         }
       }
     }

@@ -131,6 +131,17 @@ struct PolBF16 {
     const f16x4 ra = __builtin_convertvector(a, f16x4), rb = __builtin_convertvector(b, f16x4);
     return __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // fp16 hi + lo pair (~22 significant bits): hi = fp16(x), lo = fp16(x - hi)
+  __device__ static __forceinline__ void from_acc_split_r(const f32x4* acc, int p, FragR& hi,
+                                                          FragR& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = acc[2 * p + (e >> 2)][e & 3];
+      const _Float16 xh = (_Float16)x;
+      hi[e] = xh;
+      lo[e] = (_Float16)(x - (float)xh);
+    }
+  }
 };
 
 // fp32 operands, v_mfma_f32_16x16x4_f32. Slice p covers rows {16 (p/4) + 4q + p%4 : q}.
@@ -173,6 +184,10 @@ struct PolF32 {
     return load(tile, ld, row, p, q);
   }
   __device__ static __forceinline__ FragR from_acc_r(const f32x4* acc, int p) { return from_acc(acc, p); }
+  __device__ static __forceinline__ void from_acc_split_r(const f32x4* acc, int p, FragR& hi,
+                                                          FragR& lo) {
+    from_acc_split(acc, p, hi, lo);
+  }
 };
 
 // fp32 MFMA on a natural k-order (used by the triangular inverse): slice s holds k = 4s + q.
