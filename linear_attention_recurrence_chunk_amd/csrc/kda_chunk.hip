@@ -530,6 +530,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     const int c0 = 4 * (lane % PM::kLPT);
     const int rb0 = 16 * w + grp * TPT;   // first token row of this thread
     float rho[TPT][4], qv[TPT][4], kv[TPT][4];
+    float ex[TPT][4];                      // per-token decays e^{max(g, g_min)}
     float lp[4] = {1.f, 1.f, 1.f, 1.f};   // running decay over this thread's tokens
     // e^{max(g, g_min)} = 2^{max(g log2 e, g_min log2 e)}: scaling by log2 e first makes the
     // floor a single max (the product needs no NaN quieting) and feeds v_exp_f32 directly
@@ -543,7 +544,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float gt = valid ? fmaxf(raw.g[t][c] * kLog2e, gmin2) : 0.f;
-          lp[c] *= __builtin_amdgcn_exp2f(gt);
+          ex[t][c] = __builtin_amdgcn_exp2f(gt);
+          lp[c] *= ex[t][c];
           rho[t][c] = lp[c];
           kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
           qv[t][c] = (kOut && valid) ? to_f32(raw.q[t][c]) : 0.f;
@@ -574,18 +576,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       for (int t = 0; t < TPT; ++t) rho[t][c] *= pre;
     }
     const float beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
+    // 1 / rho from one reciprocal per channel: 1/rho_t = (1/rho_last) x the decays after t
+    float rinv_next[4];
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) {
+    for (int c = 0; c < 4; ++c) rinv_next[c] = __builtin_amdgcn_rcpf(rho[TPT - 1][c]);
+#pragma unroll
+    for (int t = TPT - 1; t >= 0; --t) {
       float xq[4], xkd[4], xkr[4], xkc[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float rh = rho[t][c];
-        const float rinv = __builtin_amdgcn_rcpf(rh);
+        const float rinv = rinv_next[c];
+        if (t > 0) rinv_next[c] = rinv * ex[t][c];
         const float k0 = kv[t][c];
         xq[c] = qv[t][c] * rh;
         xkd[c] = k0 * rinv;
         xkr[c] = k0 * rh;
-        xkc[c] = k0 * (bp[c] * rinv);
+        xkc[c] = xkd[c] * bp[c];
         qv[t][c] = xq[c];    // q rho
         kv[t][c] = xkr[c];   // k rho
         rho[t][c] = xkc[c];  // k kappa
