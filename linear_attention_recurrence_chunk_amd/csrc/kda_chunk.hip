@@ -628,7 +628,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         *reinterpret_cast<f32x4*>(sDecay + c0) = Pb[0] * Pb[1] * Pb[2] * Pb[3];
     }
 
-    KDA_PREFETCH(kLoadG, 0, 2);
 
     // ================= prologue 2: A (fp32) and M (hi, lo) sub-blocks ====================
     // wave w: row-block w of A (blocks (w, j <= w)) and row-block 3 - w of M, 40 - 4 w MFMAs
@@ -640,7 +639,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       case 2: am_rows<Pol, L, DK, 2, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
       default: am_rows<Pol, L, DK, 3, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
     }
-    KDA_PREFETCH(kLoadG, 2, 4);
+    KDA_PREFETCH(kLoadG, 0, 4);
     __syncthreads();
 
     // ================= prologue 3: recurrence operand tiles; off-diagonal inverse ===========
