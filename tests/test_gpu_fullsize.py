@@ -52,24 +52,43 @@ def test_prefill_8k_full():
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
 
 
-def test_ultralong_256k_segment_cp_full():
+_ULTRALONG = {}
+
+
+def _ultralong_inputs_and_oracle(heads):
+    """The ultralong workload on the device and the oracle on the sampled heads, computed
+    once for the segment counts below."""
+    if not _ULTRALONG:
+        cfg = wl.CONFIGS["ultralong_256k"]
+        inp = wl.prefill_inputs(T=cfg["T"], H=cfg["H"], dk=cfg["dk"], dv=cfg["dv"],
+                                dtype=cfg["dtype"], seed=cfg["seed"], h0_std=cfg["h0_std"],
+                                device="cuda")
+        args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+        _ULTRALONG["args"] = args
+        _ULTRALONG["ref"] = c_recurrence_fwd(*[_host_heads(x, heads) for x in args])
+    return _ULTRALONG["args"], _ULTRALONG["ref"]
+
+
+@pytest.mark.parametrize("n_segments", [0, 64, 256])
+def test_ultralong_256k_segment_cp_full(n_segments):
+    """T = 262144, H = 12 through the segment-parallel path: the automatic segment count (as
+    the benchmark runs it) and the two ends of the 64..256 range of the workload."""
     cfg = wl.CONFIGS["ultralong_256k"]
-    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
-    print(f"case ultralong_256k T={T} H={H} d={dk} (automatic segments)", flush=True)
-    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
-                            h0_std=cfg["h0_std"], device="cuda")
-    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
-    o16, ht16 = kda.segment_cp_fwd(*args)
-    o32, ht32 = kda.segment_cp_fwd(*args, out_dtype=torch.float32)
+    print(f"case ultralong_256k T={cfg['T']} H={cfg['H']} d={cfg['dk']} "
+          f"n_segments={n_segments or 'automatic'}", flush=True)
+    heads = [5]
+    args, (o_ref, ht_ref) = _ultralong_inputs_and_oracle(heads)
+    o16, ht16 = kda.segment_cp_fwd(*args, n_segments=n_segments)
+    o32, ht32 = kda.segment_cp_fwd(*args, n_segments=n_segments, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _check_rounding(o16, o32)
     assert torch.equal(ht16, ht32)
-    heads = [5]
-    o_ref, ht_ref = c_recurrence_fwd(*[_host_heads(x, heads) for x in args])
     e_o = rel_max_err(_host_heads(o32, heads), o_ref)
     e_s = rel_max_err(_host_heads(ht32, heads), ht_ref)
     print(f"head {heads}: err_o={e_o:.3e} err_state={e_s:.3e}")
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+    del o16, o32
+    torch.cuda.empty_cache()
 
 
 def test_varlen_64_full():
