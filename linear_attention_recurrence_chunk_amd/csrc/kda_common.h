@@ -91,17 +91,8 @@ struct PolBF16 {
     }
     return r;
   }
-  // B fragment of slice p from accumulator tiles acc[2p] and acc[2p + 1]
-  __device__ static __forceinline__ Frag from_acc(const f32x4* acc, int p) {
-    Frag r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      r[e] = (__bf16)acc[2 * p][e];
-      r[e + 4] = (__bf16)acc[2 * p + 1][e];
-    }
-    return r;
-  }
-  // same, as a hi + lo pair: hi = bf16(x), lo = bf16(x - hi)
+  // B fragment of slice p from accumulator tiles acc[2p] and acc[2p + 1], as a hi + lo pair:
+  // hi = bf16(x), lo = bf16(x - hi)
   __device__ static __forceinline__ void from_acc_split(const f32x4* acc, int p, Frag& hi,
                                                         Frag& lo) {
 #pragma unroll
