@@ -59,6 +59,20 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
   }
   const long long nc = (eos - bos + 63) / 64;
 
+  // P_j is read one step ahead into registers (16-byte pieces of the thread's rows), so its
+  // HBM latency hides under the previous step.
+  constexpr int kPPT = DK * DK / (4 * 256);   // f32x4 pieces of P per thread
+  f32x4 pr[kPPT];
+  auto fetch = [&](int j) {
+    const float* pq = p.pq + ((size_t(n) * p.n_seg + j) * p.H + h) * DK * ldpq;
+#pragma unroll
+    for (int i = 0; i < kPPT; ++i) {
+      const int idx = (tid + 256 * i) * 4;
+      pr[i] = *reinterpret_cast<const f32x4*>(pq + size_t(idx / DK) * ldpq + idx % DK);
+    }
+  };
+  if (p.n_seg > 0) fetch(0);
+
   for (int j = 0; j < p.n_seg; ++j) {
     const size_t seg = (size_t(n) * p.n_seg + j) * p.H + h;
     // entering state of segment j
@@ -68,18 +82,22 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sin[size_t(16 * t + 4 * q4 + e) * DV + col] = S[t][e];
     // a segment without tokens is the identity map: the state passes through unchanged
-    if ((j * nc) / p.n_seg == ((j + 1) * nc) / p.n_seg) continue;
+    // (its summary was never written; the registers are refilled with the next one)
+    if ((j * nc) / p.n_seg == ((j + 1) * nc) / p.n_seg) {
+      if (j + 1 < p.n_seg) fetch(j + 1);
+      continue;
+    }
 
     // P_j into LDS as (hi, lo) bf16, row = key channel
-    const float* pq = p.pq + seg * DK * ldpq;
-    for (int idx = tid * 4; idx < DK * DK; idx += 256 * 4) {
+#pragma unroll
+    for (int i = 0; i < kPPT; ++i) {
+      const int idx = (tid + 256 * i) * 4;
       const int r = idx / DK, c = idx % DK;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(pq + size_t(r) * ldpq + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = (__bf16)x[e];
+        const __bf16 hi = (__bf16)pr[i][e];
         sPh[r * LDP + c + e] = hi;
-        sPl[r * LDP + c + e] = (__bf16)(x[e] - (float)hi);
+        sPl[r * LDP + c + e] = (__bf16)(pr[i][e] - (float)hi);
       }
     }
     __syncthreads();
@@ -88,10 +106,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
     Frag Sh[NS], Sl[NS];
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
+    const float* q = p.pq + seg * DK * ldpq + DK;
 #pragma unroll
     for (int t = 0; t < NTD; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] = pq[size_t(16 * t + 4 * q4 + e) * ldpq + DK + col];
+      for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
+    if (j + 1 < p.n_seg) fetch(j + 1);
 #pragma unroll
     for (int pp = 0; pp < NS; ++pp) {
 #pragma unroll
