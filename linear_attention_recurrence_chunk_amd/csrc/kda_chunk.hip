@@ -116,7 +116,9 @@ __device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E
 }
 
 // Row-block IA of A and (kM) row-block 3 - IA of M for one wave. Column operands: k / rho on
-// the diagonal block, k kappa next to it, k kappa times the decay gap further down.
+// the diagonal block, k kappa next to it, k kappa times the decay gap further down. Without M
+// (the transition pass) block (3, 0) moves from wave 3 to wave 0, so the waves run 8, 8, 12
+// and 12 MFMAs instead of 4 to 16.
 template <class Pol, class L, int DK, int IA, bool kM>
 __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typename Pol::E* sKd,
                                         const typename Pol::E* sKdLo, const typename Pol::E* sKc,
@@ -127,11 +129,13 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
   using Frag = typename Pol::Frag;
   constexpr int NS = Pol::slices(DK);
   constexpr int IM = 3 - IA;
+  constexpr bool kTake30 = !kM && IA == 0;   // this wave also computes A block (3, 0)
+  constexpr int kJ0 = (!kM && IA == 3) ? 1 : 0;   // first column block of the row
   // gap between sub-blocks i and j (i - j >= 2): the whole-sub-block decays strictly between
   // them, (2, 0) -> P_1, (3, 1) -> P_2, (3, 0) -> P_1 P_2 (sBP row b holds P_b per channel)
   const float* P1 = sBP + DK;
   const float* P2 = sBP + 2 * DK;
-  f32x4 accA[4], accM[4];
+  f32x4 accA[4], accM[4], acc30 = zero4();
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
     accA[jb] = zero4();
@@ -143,7 +147,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     Frag rowM, colA[4], colM[4], dKl, dQl;
     if constexpr (kM) rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
 #pragma unroll
-    for (int jb = 0; jb <= IA; ++jb) {
+    for (int jb = kJ0; jb <= IA; ++jb) {
       if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == IA - 1) colA[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
       else if (jb == 0 && IA == 3) colA[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
@@ -162,7 +166,11 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       dQl = Pol::load(sQrLo, L::LDP, 16 * IM + ln, pp, q4);
     }
 #pragma unroll
-    for (int jb = 0; jb <= IA; ++jb) accA[jb] = Pol::mma(colA[jb], rowA, accA[jb]);
+    for (int jb = kJ0; jb <= IA; ++jb) accA[jb] = Pol::mma(colA[jb], rowA, accA[jb]);
+    if constexpr (kTake30) {
+      const Frag row3 = Pol::load(sKr, L::LDP, 48 + ln, pp, q4);
+      acc30 = Pol::mma(Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2), row3, acc30);
+    }
     if constexpr (kM) {
 #pragma unroll
       for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
@@ -179,7 +187,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
   const int ra = 16 * IA + ln, rm = 16 * IM + ln;
   const float br = sBeta[ra];
 #pragma unroll
-  for (int jb = 0; jb <= IA; ++jb) {
+  for (int jb = kJ0; jb <= IA; ++jb) {
     f32x4 outv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -187,6 +195,10 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       outv[e] = (jb == IA && s >= ra) ? 0.f : br * accA[jb][e];
     }
     *reinterpret_cast<f32x4*>(sA + ra * L::LDA + 16 * jb + 4 * q4) = outv;
+  }
+  if constexpr (kTake30) {
+    const float b3 = sBeta[48 + ln];
+    *reinterpret_cast<f32x4*>(sA + (48 + ln) * L::LDA + 4 * q4) = b3 * acc30;
   }
 #pragma unroll
   for (int jb = 0; jb <= IM; ++jb) {
