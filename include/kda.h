@@ -93,12 +93,40 @@ typedef enum kda_dtype {
  * token adds at most v_c^2 to the squared norm of state column c, so
  * |S| <= sqrt(|h0 column c|^2 + sum_t v_{t,c}^2) and each error is at most |v| + that bound;
  * keys or queries far from unit norm, or a sum above ~1e9, can give non-finite outputs.
+ *
+ * Workspace and launches. With workspace == NULL the call is one launch: each workgroup owns
+ * one (sequence, head, 64-column state tile) and computes every chunk's token-parallel
+ * prologue and then its serial step. With a workspace (KDA_BF16 only) the call is two
+ * launches, the split of a token-parallel stage from the serial recurrence that the AMD blog
+ * describes in section 5: (1) the prologue of every (chunk, head) runs in parallel over the
+ * whole device and stores the serial step's operands (about 73 KiB per chunk and head at
+ * d_k = 128) in the workspace; (2) the serial walk per (sequence, head, state tile) reads
+ * them back. Both paths give bit-identical o and ht. The workspace must hold at least
+ * kda_chunk_fwd_workspace_size(..., KDA_CHUNK_WS_TWO_PASS, ...) bytes, be 16-byte aligned and
+ * overlap no other argument; its contents on entry are ignored and on return are undefined.
+ * KDA_F32 ignores the workspace.
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
                   const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                   int num_heads, int d_k, int d_v, int io_dtype, int out_dtype, float scale,
-                  float g_min, void* o, float* ht, void* stream);
+                  float g_min, void* o, float* ht, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Policies of kda_chunk_fwd_workspace_size. */
+#define KDA_CHUNK_WS_AUTO 0     /* size of the path the library recommends: 0 when one launch */
+#define KDA_CHUNK_WS_TWO_PASS 1 /* size the two-launch path needs, whatever the shape */
+
+/*
+ * Bytes of workspace kda_chunk_fwd uses for the given sizes (same batch / seq_len / n_seqs
+ * conventions as kda_chunk_fwd: seq_len is T_total when sequences are packed). With
+ * KDA_CHUNK_WS_AUTO it returns 0 when one launch is expected to be faster: a KDA_F32 call, or
+ * enough (sequence, head, state tile) workgroups to fill every compute unit of the current
+ * device, where the one-launch path keeps HBM traffic at the algorithmic bytes. Otherwise it
+ * returns the two-launch size: (T_total / 64 + N + 1) chunk slots x num_heads x the slot size.
+ */
+int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                 int d_v, int io_dtype, int policy, size_t* bytes);
 
 /*
  * Bytes of device workspace kda_segment_cp_fwd needs for the given sizes (n_segments = 0

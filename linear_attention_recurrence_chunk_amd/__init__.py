@@ -4,8 +4,8 @@ Argument marshalling only: torch tensors are turned into device pointers and the
 HIP stream, and every step runs in the library's HIP kernels. There is no fallback: if
 libkda.so is missing or fails to load, every call raises.
 
-Entry points mirror include/kda.h: ``chunk_fwd``, ``segment_cp_fwd``,
-``segment_cp_workspace_size``, ``decode_replay``.
+Entry points mirror include/kda.h: ``chunk_fwd``, ``chunk_fwd_workspace_size``,
+``segment_cp_fwd``, ``segment_cp_workspace_size``, ``decode_replay``.
 """
 
 from __future__ import annotations
@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["KDAError", "library", "library_path", "chunk_fwd", "segment_cp_fwd",
+__all__ = ["KDAError", "library", "library_path", "chunk_fwd", "chunk_fwd_workspace_size",
+           "segment_cp_fwd",
            "segment_cp_workspace_size", "decode_replay", "status_string", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -21,6 +22,8 @@ _LIB = None
 
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_CHUNK_WS_AUTO = 0
+KDA_CHUNK_WS_TWO_PASS = 1
 
 
 class KDAError(RuntimeError):
@@ -50,8 +53,12 @@ def library():
                            "`python -m linear_attention_recurrence_chunk_amd.build`")
     lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, P]
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, P,
+                                  ctypes.c_size_t, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_fwd_workspace_size.restype = I
     lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_segment_cp_workspace_size.restype = I
     lib.kda_segment_cp_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P,
@@ -169,18 +176,42 @@ def _cu_host_ptr(cu_host):
 
 
 # ------------------------------------------------------------------------------ entry points
+def chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF16,
+                             policy=KDA_CHUNK_WS_AUTO):
+    """kda_chunk_fwd_workspace_size: bytes of workspace for the two-launch path (0 under the
+    automatic policy when one launch is recommended)."""
+    out = ctypes.c_size_t(0)
+    st = library().kda_chunk_fwd_workspace_size(int(batch), int(seq_len), int(n_seqs), int(H),
+                                                int(dk), int(dv), int(io_dtype), int(policy),
+                                                ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_workspace_size")
+    return int(out.value)
+
+
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0, o=None,
-              ht=None, output_final_state=True, out_dtype=None, stream=None):
+              ht=None, output_final_state=True, out_dtype=None, workspace="auto", stream=None):
     """kda_chunk_fwd. q, k: [B, T, H, d_k] or packed [T, H, d_k]; v: [.., d_v];
     g: same shape as k (fp32); beta: [.., H] (fp32); h0: [N, H, d_k, d_v] fp32 or None;
     cu_seqlens: [N + 1] int32 (any device) for packed varlen input; out_dtype: None (same as
-    q) or torch.float32. Returns (o, ht)."""
+    q) or torch.float32. workspace: "auto" (the library's recommended path, allocating the
+    workspace it asks for), None (one launch), "two_pass" (two launches whatever the shape)
+    or a uint8 device tensor (two launches). Returns (o, ht)."""
     a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
+    T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
+    if isinstance(workspace, str):
+        if workspace not in ("auto", "two_pass"):
+            raise ValueError(f"unknown workspace policy {workspace!r}")
+        policy = KDA_CHUNK_WS_AUTO if workspace == "auto" else KDA_CHUNK_WS_TWO_PASS
+        need = chunk_fwd_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"],
+                                        a["dv"], a["io"], policy)
+        workspace = (_torch().empty(need, dtype=_torch().uint8, device=q.device)
+                     if need > 0 else None)
     st = library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
-        _cu_host_ptr(a["cu_host"]), a["batch"], a["seq_len"] if a["cu_dev"] is None
-        else int(a["cu_host"][-1]), a["n_seqs"], a["H"], a["dk"], a["dv"], a["io"], a["out"],
-        float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]), _stream(stream))
+        _cu_host_ptr(a["cu_host"]), a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
+        a["io"], a["out"], float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
     return a["o"], a["ht"]

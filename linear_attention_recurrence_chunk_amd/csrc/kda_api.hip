@@ -144,6 +144,48 @@ int auto_segments(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
   return best_n;
 }
 
+// Two-pass prefill: chunks per workgroup of the prep pass (its loop prefetches each chunk's
+// inputs during the previous one)
+constexpr int kPrepChunks = 8;
+
+size_t two_pass_workspace_bytes(int64_t T, int64_t N, int H, int dk) {
+  return size_t(kda::op_slot_count(T, N)) * size_t(H) * kda::op_slot_bytes(dk);
+}
+
+// The one-launch path leaves compute units idle when its (sequence, head, state tile)
+// workgroups do not fill them; its per-chunk prologue then sits on every workgroup's serial
+// chain, which the two-launch path takes off it.
+bool two_pass_wanted(int64_t N, int H, int dv) {
+  return N * H * (dv / 64) <= int64_t(compute_units());
+}
+
+int64_t max_seq_len(const int32_t* cu_seqlens_host, int N, int seq_len) {
+  if (!cu_seqlens_host) return seq_len;
+  int64_t m = 0;
+  for (int i = 0; i < N; ++i) {
+    const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+    m = len > m ? len : m;
+  }
+  return m;
+}
+
+int check_workspace_aliasing(const void* ws, size_t need, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, const float* h0,
+                             const void* o, const float* ht, int64_t T, int N, int H, int dk,
+                             int dv, int io_dtype, int out_dtype) {
+  const size_t es = dsize(io_dtype);
+  const Range rws = range_of(ws, need);
+  const Range all[] = {
+      range_of(q, size_t(T) * H * dk * es), range_of(k, size_t(T) * H * dk * es),
+      range_of(v, size_t(T) * H * dv * es), range_of(g, size_t(T) * H * dk * 4),
+      range_of(beta, size_t(T) * H * 4), range_of(h0, h0 ? size_t(N) * H * dk * dv * 4 : 0),
+      range_of(o, size_t(T) * H * dv * dsize(out_dtype)),
+      range_of(ht, ht ? size_t(N) * H * dk * dv * 4 : 0)};
+  for (Range x : all)
+    if (overlaps(rws, x)) return KDA_ERR_ALIASING;
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,17 +211,45 @@ const char* kda_status_string(int status) {
   }
 }
 
+int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                 int d_v, int io_dtype, int policy, size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_ARG;
+  if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (policy != KDA_CHUNK_WS_AUTO && policy != KDA_CHUNK_WS_TWO_PASS) return KDA_ERR_BAD_VALUE;
+  if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+    return KDA_ERR_BAD_SHAPE;
+  *bytes = 0;
+  if (io_dtype != KDA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_OK;
+  // packed sequences: batch 1, seq_len = T_total; otherwise n_seqs = batch
+  const int64_t T = batch == 1 && n_seqs != 1 ? int64_t(seq_len) : int64_t(batch) * seq_len;
+  const int64_t N = batch == 1 && n_seqs != 1 ? n_seqs : batch;
+  if (policy == KDA_CHUNK_WS_AUTO && two_pass_wanted(N, num_heads, d_v) == false) return KDA_OK;
+  *bytes = two_pass_workspace_bytes(T, N, num_heads, d_k);
+  return KDA_OK;
+}
+
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
                   const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                   int num_heads, int d_k, int d_v, int io_dtype, int out_dtype, float scale,
-                  float g_min, void* o, float* ht, void* stream) {
+                  float g_min, void* o, float* ht, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   int N = 0;
   int64_t T = 0;
   const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
                                   seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
                                   g_min, o, ht, &N, &T);
   if (st != KDA_OK) return st;
+  const bool two_pass = workspace != nullptr && io_dtype == KDA_BF16;
+  size_t need = 0;
+  if (two_pass) {
+    need = two_pass_workspace_bytes(T, N, num_heads, d_k);
+    if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    const int rc = check_workspace_aliasing(workspace, need, q, k, v, g, beta, h0, o, ht, T, N,
+                                            num_heads, d_k, d_v, io_dtype, out_dtype);
+    if (rc != KDA_OK) return rc;
+  }
   if (N == 0) return KDA_OK;
   kda::ChunkParams p{};
   p.q = q;
@@ -201,6 +271,14 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   p.n_units = N * num_heads;
   p.scale = scale;
   p.g_min = g_min;
+  if (two_pass) {
+    p.mode = kda::kModeWalk;
+    p.ws_ops = static_cast<char*>(workspace);
+    const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
+    const int groups = int((max_chunks + kPrepChunks - 1) / kPrepChunks);
+    return launch_status(kda::launch_chunk_two_pass(p, groups < 1 ? 1 : groups, out_dtype, d_k,
+                                                    static_cast<hipStream_t>(stream)));
+  }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
 }

@@ -311,8 +311,8 @@ __device__ __forceinline__ const T* lane_ptr(const void* base, size_t uniform_el
 
 // Pieces of a chunk's raw inputs, loaded separately so that their issue can be spread over
 // the previous chunk: kind G, K or Q for the thread's tokens [kLo, kHi) out of eight (scaled to
-// its token count), or V (values and beta).
-enum : int { kLoadG = 1, kLoadK = 2, kLoadQ = 4, kLoadV = 8, kLoadAll = 15 };
+// its token count), V (values) or B (beta).
+enum : int { kLoadG = 1, kLoadK = 2, kLoadQ = 4, kLoadV = 8, kLoadB = 16, kLoadAll = 31 };
 
 template <bool kFull, int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8>
 __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkParams& p, int cstart,
@@ -335,19 +335,21 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
     if constexpr ((kParts & kLoadK) != 0) x.k[t] = *lane_ptr<kFull, Tio, Q4>(p.k, u, lk, ok, fk);
     if constexpr ((kParts & kLoadQ) != 0) x.q[t] = *lane_ptr<kFull, Tio, Q4>(p.q, u, lk, ok, fk);
   }
-  if constexpr ((kParts & kLoadV) == 0) return;
-  // values: token cstart + 16 rb + 4 q4 + lane % 4, columns vcol0 + 16 w + 4 (ln / 4) .. + 3
-  const int q4 = lane >> 4, ln = lane & 15;
-  const int vc = vcol0 + 16 * w + 4 * (ln >> 2);
-  const uint32_t lv = uint32_t(((4 * q4 + (ln & 3)) * H + h) * p.dv + vc);
-  const size_t fv = (size_t(cstart) * H + h) * p.dv + vc;
-  const size_t vrow = size_t(H) * p.dv;
-  const size_t v0 = size_t(cstart) * vrow;
+  if constexpr ((kParts & kLoadV) != 0) {
+    // values: token cstart + 16 rb + 4 q4 + lane % 4, columns vcol0 + 16 w + 4 (ln / 4) .. + 3
+    const int q4 = lane >> 4, ln = lane & 15;
+    const int vc = vcol0 + 16 * w + 4 * (ln >> 2);
+    const uint32_t lv = uint32_t(((4 * q4 + (ln & 3)) * H + h) * p.dv + vc);
+    const size_t fv = (size_t(cstart) * H + h) * p.dv + vc;
+    const size_t vrow = size_t(H) * p.dv;
+    const size_t v0 = size_t(cstart) * vrow;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const bool ok = 16 * rb + 4 * q4 + (ln & 3) < Lc;
-    x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, v0 + size_t(16 * rb) * vrow, lv, ok, fv);
+    for (int rb = 0; rb < 4; ++rb) {
+      const bool ok = 16 * rb + 4 * q4 + (ln & 3) < Lc;
+      x.v[rb] = *lane_ptr<kFull, Tio, Q4>(p.v, v0 + size_t(16 * rb) * vrow, lv, ok, fv);
+    }
   }
+  if constexpr ((kParts & kLoadB) == 0) return;
   // beta of token 16 w + lane % 16 (every lane loads, so that the register is only ever
   // written by loads; lanes 16-63 repeat lanes 0-15 and are not used)
   {
@@ -402,9 +404,69 @@ __device__ __forceinline__ void store4_split(typename Pol::E* hi, typename Pol::
   }
 }
 
+// One chunk-head's serial-step operands, written by the prep pass of the two-pass prefill and
+// read by its walk: MFMA fragments in lane order (64 lanes x 16 bytes = 1 KiB per fragment),
+// so a wave moves one fragment as one contiguous block, and the walk's LDS reads of them are
+// conflict-free without padding. The last block holds the whole-chunk decay (DK fp32).
+template <int DK>
+struct OpSlot {
+  static constexpr int NS = DK / 32;    // k-slices over key channels
+  static constexpr int NTD = DK / 16;   // 16-row tiles over key channels
+  static constexpr int fKg = 0;         // K e^Gamma (fp16), fragment (rb, pp) at rb NS + pp
+  static constexpr int fQg = 4 * NS;    // Q e^Gamma (fp16), same order
+  static constexpr int fT = 8 * NS;     // T diag(beta) hi (bf16): the 6 lower fragments
+  static constexpr int fTLo = fT + 6;   //   and lo
+  static constexpr int fM = fT + 12;    // M hi (fp16): the 6 lower fragments
+  static constexpr int fMLo = fT + 18;  //   and lo
+  static constexpr int fKh = fT + 24;   // (K e^{Gamma_L - Gamma})^T (fp16), (t, pp) at 2 t + pp
+  static constexpr int kDecay = fKh + 2 * NTD;
+  static constexpr int kBlocks = kDecay + 1;
+  static constexpr size_t kBytes = size_t(kBlocks) * 1024;
+  static_assert(DK * 4 <= 1024, "the decay fits one block");
+  // the lower fragments of a 64 x 64 operand in slice order: row block rb takes slices
+  // pp < (rb + 2) / 2, i.e. (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+  static constexpr __device__ int tri(int rb, int pp) { return (rb == 3 ? 4 : rb) + pp; }
+};
+
+// Prep pass: copy one chunk's serial-step operands from their LDS tiles to its slot, in
+// fragment order (wave w writes fragments w, w + 4, ...; one 16-byte store per lane each).
+template <class Pol, class L, int DK>
+__device__ __forceinline__ void prep_store(char* slot, const typename Pol::ER* sKg,
+                                           const typename Pol::ER* sQg, const typename Pol::E* sT,
+                                           const typename Pol::E* sTLo, const typename Pol::ER* sM,
+                                           const typename Pol::ER* sMLo,
+                                           const typename Pol::ER* sKhT, const float* sDecay,
+                                           int w, int lane, int ln, int q4) {
+  using OS = OpSlot<DK>;
+  constexpr int NS = OS::NS;
+  auto put = [&](int f, auto frag) {
+    static_assert(sizeof(frag) == 16, "one 16-byte fragment per lane");
+    *reinterpret_cast<decltype(frag)*>(slot + size_t(f) * 1024 + lane * 16) = frag;
+  };
+  for (int f = w; f < 4 * NS; f += 4) {
+    put(OS::fKg + f, Pol::load_r(sKg, L::LDP, 16 * (f / NS) + ln, f % NS, q4));
+    put(OS::fQg + f, Pol::load_r(sQg, L::LDP, 16 * (f / NS) + ln, f % NS, q4));
+  }
+  for (int i = w; i < 6; i += 4) {
+    const int rb = i < 2 ? i : (i < 4 ? 2 : 3), pp = i < 2 ? 0 : (i & 1);
+    put(OS::fT + i, Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4));
+    put(OS::fTLo + i, Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4));
+    put(OS::fM + i, Pol::load_r(sM, L::LDT, 16 * rb + ln, pp, q4));
+    put(OS::fMLo + i, Pol::load_r(sMLo, L::LDT, 16 * rb + ln, pp, q4));
+  }
+  for (int f = w; f < 2 * OS::NTD; f += 4)
+    put(OS::fKh + f, Pol::load_r(sKhT, L::LDT, 16 * (f / 2) + ln, f % 2, q4));
+  if (w == 0 && lane < DK / 4)
+    *reinterpret_cast<f32x4*>(slot + size_t(OS::kDecay) * 1024 + lane * 16) =
+        *reinterpret_cast<const f32x4*>(sDecay + 4 * lane);
+}
+
 // kOut false: the transition pass of the segment-parallel path, which keeps only the state
 // (no M, no Q e^Gamma tile, no output products, q is never read).
-template <class Pol, typename Tio, typename Tout, int DK, bool kOut>
+// kPrep true: pass 1 of the two-pass prefill. One workgroup per (sequence, group of chunks,
+// head) runs the prologue of each chunk and stores the serial step's operands to the chunk's
+// slot instead of running the step (no state, values or outputs).
+template <class Pol, typename Tio, typename Tout, int DK, bool kOut, bool kPrep = false>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using L = ChunkLayout<Pol, DK>;
   using E = typename Pol::E;
@@ -466,6 +528,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     bos = n * p.seq_len;
     eos = bos + p.seq_len;
   }
+  // operand slot of the sequence's first chunk (prep pass)
+  const long long seq_slot0 = (long long)(bos >> 6) + n;
+  const int seq_bos = bos;
   if (p.n_seg > 1) {
     // chunk-aligned contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg)
     const long long nc = (eos - bos + kChunk - 1) / kChunk;
@@ -490,6 +555,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   if (mode == kModeReplay) s_in = p.ws_sin + (size_t(sj) * H + h) * DK * DV;
 #pragma unroll
   for (int t = 0; t < NTD; ++t) {
+    if constexpr (kPrep) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int c = 16 * t + 4 * q4 + e;
@@ -516,8 +582,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   RawChunk<Tio, DK> raw;
 
   if (bos < eos)
-    load_chunk_any<kOut ? kLoadAll : kLoadAll & ~kLoadQ, Tio, DK>(raw, p, bos, min(kChunk, eos - bos),
-                                                                w, lane, h, vcol0);
+    load_chunk_any<kPrep ? kLoadAll & ~kLoadV : (kOut ? kLoadAll : kLoadAll & ~kLoadQ), Tio, DK>(
+        raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
 
   const int lane0 = lane, q4_0 = q4, ln0 = ln;
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
@@ -769,151 +835,158 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     __syncthreads();
 
 
-    // ================= serial step: this wave's 16 value columns ============================
+    if constexpr (kPrep) {
+      char* slot = p.ws_ops + (size_t(seq_slot0 + (cstart - seq_bos) / kChunk) * H + h) *
+                                  OpSlot<DK>::kBytes;
+      prep_store<Pol, L, DK>(slot, sKg, sQg, sT, sTLo, sM, sMLo, sKhT, sDecay, w, lane, ln, q4);
+      KDA_PREFETCH(kLoadB, 0, 8);
+    } else {
+      // ================= serial step: this wave's 16 value columns ============================
 
-    // Each product loads a batch of A fragments from LDS first and then issues its MFMAs, so
-    // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
-    // S as fp16 B fragments, shared by the two products with decayed keys and queries
-    FragR Sr[NS];
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
-    // X = (K e^Gamma) S - V, in fp32
-    // (the values stay packed in the raw registers until here)
-    f32x4 X[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      float vx[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
-      quad_transpose(vx, lane);   // now token 16 rb + 4 q4 + e, column 16 w + ln
-      if (Lc == kChunk && !p_tile) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = -vx[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc && !p_tile) ? -vx[e] : 0.f;
-      }
-    }
-    KDA_PREFETCH(kLoadV, 0, 8);
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-      FragR kg[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load_r(sKg, L::LDP, 16 * rb + ln, pp, q4);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(kg[rb], Sr[pp], X[rb]);
-    }
-    f32x4 U[4], O[4];
-    // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-      if constexpr (!kOut) break;
-      FragR qg[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) qg[rb] = Pol::load_r(sQg, L::LDP, 16 * rb + ln, pp, q4);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(qg[rb], Sr[pp], pp == 0 ? zero4() : O[rb]);
-    }
-    // U = T' (V - K_Gamma S) = -T' X
-    Frag Xh[NT], Xl[NT];
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-      Frag th[4], tl[4];
-#pragma unroll
+      // Each product loads a batch of A fragments from LDS first and then issues its MFMAs, so
+      // several LDS reads are in flight per wave (one wave per SIMD hides nothing otherwise).
+      // S as fp16 B fragments, shared by the two products with decayed keys and queries
+      FragR Sr[NS];
+  #pragma unroll
+      for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
+      // X = (K e^Gamma) S - V, in fp32
+      // (the values stay packed in the raw registers until here)
+      f32x4 X[4];
+  #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          th[rb] = Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4);
-          if constexpr (Pol::kSplit) tl[rb] = Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4);
+        float vx[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
+        quad_transpose(vx, lane);   // now token 16 rb + 4 q4 + e, column 16 w + ln
+        if (Lc == kChunk && !p_tile) {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) X[rb][e] = -vx[e];
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc && !p_tile) ? -vx[e] : 0.f;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
-      if constexpr (Pol::kSplit) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
-    // O += M U and S += K^T U with fp16 operands: U as an fp16 hi + lo pair, M as one too,
-    // K e^{Gamma_L - Gamma} (at most 1) as a single fp16
-    FragR Uh[NT], Ul[NT];
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split_r(U, pp, Uh[pp], Ul[pp]);
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-      if constexpr (!kOut) break;
-      FragR mh[4], ml[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          mh[rb] = Pol::load_r(sM, L::LDT, 16 * rb + ln, pp, q4);
-          if constexpr (Pol::kSplit) ml[rb] = Pol::load_r(sMLo, L::LDT, 16 * rb + ln, pp, q4);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Uh[pp], O[rb]);
-      if constexpr (Pol::kSplit) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(ml[rb], Uh[pp], O[rb]);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Ul[pp], O[rb]);
-      }
-    }
-    // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
-#pragma unroll
-    for (int t = 0; t < NTD; ++t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] *= sDecay[16 * t + 4 * q4 + e];
-    }
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-#pragma unroll
-      for (int t0 = 0; t0 < NTD; t0 += 4) {
-        FragR kh[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) kh[t] = Pol::load_r(sKhT, L::LDT, 16 * (t0 + t) + ln, pp, q4);
+      KDA_PREFETCH(kLoadV | kLoadB, 0, 8);
+  #pragma unroll
+      for (int pp = 0; pp < NS; ++pp) {
+        FragR kg[4];
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) kg[rb] = Pol::load_r(sKg, L::LDP, 16 * rb + ln, pp, q4);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Uh[pp], S[t0 + t]);
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(kg[rb], Sr[pp], X[rb]);
+      }
+      f32x4 U[4], O[4];
+      // O = (Q e^Gamma) S, independent of X: its MFMAs cover the latency of the X products
+  #pragma unroll
+      for (int pp = 0; pp < NS; ++pp) {
+        if constexpr (!kOut) break;
+        FragR qg[4];
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) qg[rb] = Pol::load_r(sQg, L::LDP, 16 * rb + ln, pp, q4);
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(qg[rb], Sr[pp], pp == 0 ? zero4() : O[rb]);
+      }
+      // U = T' (V - K_Gamma S) = -T' X
+      Frag Xh[NT], Xl[NT];
+  #pragma unroll
+      for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
+  #pragma unroll
+      for (int pp = 0; pp < NT; ++pp) {
+        Frag th[4], tl[4];
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          if (pp < Pol::slices_blocks(rb + 1)) {
+            th[rb] = Pol::load(sT, L::LDT, 16 * rb + ln, pp, q4);
+            if constexpr (Pol::kSplit) tl[rb] = Pol::load(sTLo, L::LDT, 16 * rb + ln, pp, q4);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
         if constexpr (Pol::kSplit) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Ul[pp], S[t0 + t]);
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
         }
       }
-    }
-    // output, after the state update so that the last O products complete under it: a quad
-    // transpose gives each lane four consecutive columns of token 16 rb + 4 q4 + lane % 4
-    if constexpr (kOut) {
-      const int tq = 4 * q4 + (ln & 3);
-      const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        float ox[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ox[e] = p.scale * O[rb][e];
-        quad_transpose(ox, lane);
-        Tout* row = go + size_t(cstart + 16 * rb) * H * DV;
-        if (16 * rb + tq < Lc) {
-          if constexpr (sizeof(Tout) == 2)
-            *reinterpret_cast<bf16x4*>(row + lo_el) =
-                bf16x4{(__bf16)ox[0], (__bf16)ox[1], (__bf16)ox[2], (__bf16)ox[3]};
-          else
-            *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[0], ox[1], ox[2], ox[3]};
+  #pragma unroll
+      for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
+      // O += M U and S += K^T U with fp16 operands: U as an fp16 hi + lo pair, M as one too,
+      // K e^{Gamma_L - Gamma} (at most 1) as a single fp16
+      FragR Uh[NT], Ul[NT];
+  #pragma unroll
+      for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split_r(U, pp, Uh[pp], Ul[pp]);
+  #pragma unroll
+      for (int pp = 0; pp < NT; ++pp) {
+        if constexpr (!kOut) break;
+        FragR mh[4], ml[4];
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          if (pp < Pol::slices_blocks(rb + 1)) {
+            mh[rb] = Pol::load_r(sM, L::LDT, 16 * rb + ln, pp, q4);
+            if constexpr (Pol::kSplit) ml[rb] = Pol::load_r(sMLo, L::LDT, 16 * rb + ln, pp, q4);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Uh[pp], O[rb]);
+        if constexpr (Pol::kSplit) {
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(ml[rb], Uh[pp], O[rb]);
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Ul[pp], O[rb]);
+        }
+      }
+      // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
+  #pragma unroll
+      for (int t = 0; t < NTD; ++t) {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) S[t][e] *= sDecay[16 * t + 4 * q4 + e];
+      }
+  #pragma unroll
+      for (int pp = 0; pp < NT; ++pp) {
+  #pragma unroll
+        for (int t0 = 0; t0 < NTD; t0 += 4) {
+          FragR kh[4];
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) kh[t] = Pol::load_r(sKhT, L::LDT, 16 * (t0 + t) + ln, pp, q4);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Uh[pp], S[t0 + t]);
+          if constexpr (Pol::kSplit) {
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Ul[pp], S[t0 + t]);
+          }
+        }
+      }
+      // output, after the state update so that the last O products complete under it: a quad
+      // transpose gives each lane four consecutive columns of token 16 rb + 4 q4 + lane % 4
+      if constexpr (kOut) {
+        const int tq = 4 * q4 + (ln & 3);
+        const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
+  #pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          float ox[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) ox[e] = p.scale * O[rb][e];
+          quad_transpose(ox, lane);
+          Tout* row = go + size_t(cstart + 16 * rb) * H * DV;
+          if (16 * rb + tq < Lc) {
+            if constexpr (sizeof(Tout) == 2)
+              *reinterpret_cast<bf16x4*>(row + lo_el) =
+                  bf16x4{(__bf16)ox[0], (__bf16)ox[1], (__bf16)ox[2], (__bf16)ox[3]};
+            else
+              *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[0], ox[1], ox[2], ox[3]};
+          }
         }
       }
     }
@@ -921,6 +994,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #undef KDA_PREFETCH
   }
 
+  if constexpr (kPrep) return;
   float* s_out = nullptr;
   if (mode == kModeForward && p.ht) s_out = p.ht + (size_t(n) * H + h) * DK * DV;
   if (mode == kModeTransition) s_out = p.ws_pq + (size_t(sj) * H + h) * DK * ldS;
@@ -936,6 +1010,260 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
+// Pass 2 of the two-pass prefill: the serial walk over the chunks of one (sequence, head,
+// 64-column state tile), with the prologue's operands read from the chunks' slots. The step is
+// the chunk kernel's serial step, operation for operation, so the two paths agree bit for bit.
+// Slots stream into two LDS buffers by direct global-to-LDS loads: the next chunk's slot is in
+// flight while the current one is consumed, and the next chunk's values load into registers.
+// A chunk's outputs are stored at the start of the following chunk, so the wait for the slot
+// before the barrier never waits on recent stores.
+template <typename Tio, typename Tout, int DK>
+__global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
+  using Pol = PolBF16;
+  using Frag = typename Pol::Frag;
+  using FragR = typename Pol::FragR;
+  using OS = OpSlot<DK>;
+  constexpr int NS = OS::NS;
+  constexpr int NT = Pol::slices(64);
+  constexpr int NTD = OS::NTD;
+  constexpr int VT = 64;
+  static_assert(2 * OS::kBytes <= 160 * 1024, "two slots fit the LDS of one compute unit");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * OS::kBytes];
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int rest = b >> 3;
+  const int vt = rest % p.n_vt;
+  const int unit = (rest / p.n_vt) * 8 + xcd;
+  if (unit >= p.n_units) return;
+  const int H = p.H;
+  const int DV = p.dv;
+  const int h = unit % H;
+  const int n = unit / H;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int q4 = lane >> 4;
+  const int ln = lane & 15;
+
+  int bos, eos;
+  if (p.cu_seqlens) {
+    bos = p.cu_seqlens[n];
+    eos = p.cu_seqlens[n + 1];
+  } else {
+    bos = n * p.seq_len;
+    eos = bos + p.seq_len;
+  }
+  const int nchunks = (eos - bos + kChunk - 1) / kChunk;
+  const char* ws_head = p.ws_ops + (size_t((long long)(bos >> 6) + n) * H + h) * OS::kBytes;
+  const size_t slot_stride = size_t(H) * OS::kBytes;   // from one chunk's slot to the next
+  const int vcol0 = vt * VT;
+  const int col0 = vcol0 + 16 * w;
+  Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
+
+  f32x4 S[NTD];
+  if (p.h0) {
+    // all 32 loads in flight together
+    const float* s_in = p.h0 + (size_t(n) * H + h) * DK * DV + col0 + ln;
+#pragma unroll
+    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[t][e] = s_in[size_t(16 * t + 4 * q4 + e) * DV];
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) S[t] = zero4();
+  }
+
+  // wave w moves blocks w, w + 4, ... of chunk ci's slot into buffer dst
+  auto fetch_slot = [&](int ci, char* dst) {
+    const char* src = ws_head + size_t(ci) * slot_stride + lane * 16;
+#pragma unroll
+    for (int i = 0; i < (OS::kBlocks + 3) / 4; ++i) {
+      const int f = w + 4 * i;
+      if (f < OS::kBlocks)
+        __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024, dst + f * 1024, 16, 0, 0);
+    }
+  };
+  auto frag_r = [&](const char* buf, int f) {
+    return *reinterpret_cast<const FragR*>(buf + f * 1024 + lane * 16);
+  };
+  auto frag = [&](const char* buf, int f) {
+    return *reinterpret_cast<const Frag*>(buf + f * 1024 + lane * 16);
+  };
+
+  RawChunk<Tio, DK> raw;
+  if (nchunks > 0) {
+    fetch_slot(0, smem);
+    load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+
+  // outputs of the previous chunk, transposed (lane: token 16 rb + tq, four columns)
+  const int tq = 4 * q4 + (ln & 3);
+  const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
+  float ox[4][4];
+  auto store_out = [&](int cst, int L) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      Tout* row = go + size_t(cst + 16 * rb) * H * DV;
+      if (16 * rb + tq < L) {
+        if constexpr (sizeof(Tout) == 2)
+          *reinterpret_cast<bf16x4*>(row + lo_el) =
+              bf16x4{(__bf16)ox[rb][0], (__bf16)ox[rb][1], (__bf16)ox[rb][2], (__bf16)ox[rb][3]};
+        else
+          *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[rb][0], ox[rb][1], ox[rb][2], ox[rb][3]};
+      }
+    }
+  };
+
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int cstart = bos + ci * kChunk;
+    const int Lc = min(kChunk, eos - cstart);
+    const char* cur = smem + (ci & 1) * OS::kBytes;
+    const bool more = ci + 1 < nchunks;
+    if (more) fetch_slot(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
+    if (ci > 0) store_out(cstart - kChunk, kChunk);
+
+    FragR Sr[NS];
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
+    // X = (K e^Gamma) S - V, in fp32
+    f32x4 X[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float vx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
+      quad_transpose(vx, lane);   // token 16 rb + 4 q4 + e, column 16 w + ln
+      if (Lc == kChunk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[rb][e] = -vx[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc) ? -vx[e] : 0.f;
+      }
+    }
+    if (more) {
+      const int nstart = cstart + kChunk;
+      load_chunk_any<kLoadV, Tio, DK>(raw, p, nstart, min(kChunk, eos - nstart), w, lane, h, vcol0);
+    }
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+      FragR kg[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) kg[rb] = frag_r(cur, OS::fKg + rb * NS + pp);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(kg[rb], Sr[pp], X[rb]);
+    }
+    f32x4 U[4], O[4];
+    // O = (Q e^Gamma) S
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) {
+      FragR qg[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) qg[rb] = frag_r(cur, OS::fQg + rb * NS + pp);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(qg[rb], Sr[pp], pp == 0 ? zero4() : O[rb]);
+    }
+    // U = T' (V - K_Gamma S) = -T' X
+    Frag Xh[NT], Xl[NT];
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+      Frag th[4], tl[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          th[rb] = frag(cur, OS::fT + OS::tri(rb, pp));
+          tl[rb] = frag(cur, OS::fTLo + OS::tri(rb, pp));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
+    // O += M U and S += K^T U (fp16 operands; U and M as hi + lo pairs)
+    FragR Uh[NT], Ul[NT];
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split_r(U, pp, Uh[pp], Ul[pp]);
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+      FragR mh[4], ml[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (pp < Pol::slices_blocks(rb + 1)) {
+          mh[rb] = frag_r(cur, OS::fM + OS::tri(rb, pp));
+          ml[rb] = frag_r(cur, OS::fMLo + OS::tri(rb, pp));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Uh[pp], O[rb]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(ml[rb], Uh[pp], O[rb]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Ul[pp], O[rb]);
+    }
+    // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
+    const float* decay = reinterpret_cast<const float*>(cur + OS::kDecay * 1024);
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[t][e] *= decay[16 * t + 4 * q4 + e];
+    }
+#pragma unroll
+    for (int pp = 0; pp < NT; ++pp) {
+#pragma unroll
+      for (int t0 = 0; t0 < NTD; t0 += 4) {
+        FragR kh[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kh[t] = frag_r(cur, OS::fKh + 2 * (t0 + t) + pp);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Uh[pp], S[t0 + t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Ul[pp], S[t0 + t]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ox[rb][e] = p.scale * O[rb][e];
+      quad_transpose(ox[rb], lane);
+    }
+    if (ci + 1 == nchunks) store_out(cstart, Lc);
+    // the next slot (and values) must have landed before any wave reads them
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (p.ht) {
+    float* s_out = p.ht + (size_t(n) * H + h) * DK * DV;
+#pragma unroll
+    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_out[size_t(16 * t + 4 * q4 + e) * DV + col0 + ln] = S[t][e];
+  }
+}
+
 template <class Pol, typename Tio, typename Tout, int DK>
 static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   const int groups = (p.n_units + 7) / 8;
@@ -945,6 +1273,44 @@ static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((chunk_fwd_kernel<Pol, Tio, Tout, DK, true>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename Tout, int DK>
+static hipError_t launch_two_pass(const ChunkParams& walk, int prep_groups, hipStream_t stream) {
+  ChunkParams prep = walk;
+  prep.mode = kModePrep;
+  prep.n_seg = prep_groups;
+  prep.n_vt = 1;
+  prep.n_units = walk.n_seqs * prep_groups * walk.H;
+  prep.o = nullptr;
+  prep.ht = nullptr;
+  prep.h0 = nullptr;
+  {
+    const dim3 grid((prep.n_units + 7) / 8 * 8);
+    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, DK, true, true>), grid, dim3(256),
+                       0, stream, prep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((walk.n_units + 7) / 8 * 8 * walk.n_vt);
+  hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK>), grid, dim3(256), 0, stream, walk);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_two_pass(const ChunkParams& p, int prep_groups, int out_dtype, int dk,
+                                 hipStream_t stream) {
+  if (p.mode != kModeWalk || !p.ws_ops || !p.o || !p.q || !p.k || !p.v || !p.g || !p.beta)
+    return hipErrorInvalidValue;
+  if (p.H < 1 || p.n_seqs < 1 || p.n_seg != 1 || prep_groups < 1 || p.dv != dk ||
+      p.n_vt != p.dv / 64 || (long long)p.n_units != (long long)p.n_seqs * p.H)
+    return hipErrorInvalidValue;
+  if (op_slot_bytes(dk) != (dk == 128 ? OpSlot<128>::kBytes : OpSlot<64>::kBytes))
+    return hipErrorInvalidValue;
+  if (dk == 128) return out_dtype == 1 ? launch_two_pass<__bf16, 128>(p, prep_groups, stream)
+                                       : launch_two_pass<float, 128>(p, prep_groups, stream);
+  if (dk == 64) return out_dtype == 1 ? launch_two_pass<__bf16, 64>(p, prep_groups, stream)
+                                      : launch_two_pass<float, 64>(p, prep_groups, stream);
+  return hipErrorInvalidValue;
 }
 
 // Consistency of a launch description with the kernel's index arithmetic: every unit maps to

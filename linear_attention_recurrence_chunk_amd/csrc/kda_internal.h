@@ -12,6 +12,9 @@ enum ChunkMode : int {
   kModeForward = 0,     // outputs o and the final state of whole sequences
   kModeTransition = 1,  // per segment: (P, Q) with S_out = P S_in + Q, no outputs
   kModeReplay = 2,      // per segment: outputs o from the segment's entering state
+  kModePrep = 3,        // two-pass prefill, pass 1: per chunk and head, the serial step's
+                        // operands into ws_ops (no state, no values, no outputs)
+  kModeWalk = 4,        // two-pass prefill, pass 2: the serial chunk walk from ws_ops
 };
 
 // One launch of the chunk kernel. A "unit" is one (sequence, segment, head) triple (one
@@ -37,6 +40,7 @@ struct ChunkParams {
   int mode;                 // ChunkMode
   float* ws_pq;             // transition: [N, n_seg, H, dk, dk + dv]
   float* ws_sin;            // replay: [N, n_seg, H, dk, dv] entering states
+  char* ws_ops;             // prep / walk: operand slots [chunk slot][H] (see op_slot_count)
   float scale;
   float g_min;
 };
@@ -56,5 +60,20 @@ hipError_t launch_segment_scan(const ScanParams& p, int dk, hipStream_t stream);
 
 hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, int dk,
                             hipStream_t stream);
+
+// Two-pass prefill (bf16 inputs): prep over (sequence, group of chunks, head), then the walk
+// over (sequence, head, value tile). p describes the walk (forward-mode fields plus ws_ops);
+// prep_groups is the number of chunk groups per sequence of the prep pass.
+hipError_t launch_chunk_two_pass(const ChunkParams& p, int prep_groups, int out_dtype, int dk,
+                                 hipStream_t stream);
+
+// Operand slots: chunk c of sequence n (bos_n its first token) uses slot (bos_n / 64) + n + c,
+// so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them.
+inline long long op_slot_count(long long total_tokens, long long n_seqs) {
+  return total_tokens / 64 + n_seqs + 1;
+}
+// bytes of one (slot, head) operand block for key width dk (MFMA fragments of 1 KiB each plus
+// one block for the whole-chunk decay)
+inline size_t op_slot_bytes(int dk) { return size_t(8 * (dk / 32) + 24 + 2 * (dk / 16) + 1) * 1024; }
 
 }  // namespace kda

@@ -26,7 +26,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(kda.library_path())
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_segment_cp_fwd", "kda_segment_cp_workspace_size",
+    assert {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_segment_cp_fwd",
+            "kda_segment_cp_workspace_size",
             "kda_decode_replay", "kda_status_string", "kda_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -61,7 +62,7 @@ def chunk(q=True, k=True, v=True, g=True, beta=True, h0=None, cu=None, cu_host=N
     return kda.library().kda_chunk_fwd(
         args["q"], args["k"], args["v"], args["g"], args["beta"], args["h0"], args["cu"],
         args["cu_host"], batch, seq_len, n_seqs, H, dk, dv, io, io if out is None else out,
-        scale, g_min, args["o"], args["ht"], None)
+        scale, g_min, args["o"], args["ht"], args.get("ws"), args.get("ws_bytes", 0), None)
 
 
 def host_cu(vals):
@@ -111,6 +112,46 @@ def test_chunk_cu_seqlens_checks():
     assert chunk(cu=dev_cu, cu_host=cu_host, seq_len=300, n_seqs=2, batch=2) == SHAPE
     assert chunk(cu=ctypes.c_void_p(dev_cu.value + 4), cu_host=cu_host, seq_len=300,
                  n_seqs=2) == ALIGN
+
+
+def chunk_ws_size(batch=1, seq_len=8192, n_seqs=1, H=96, dk=128, dv=128, io=BF16, policy=1):
+    out = ctypes.c_size_t(123)
+    st = kda.library().kda_chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io,
+                                                    policy, ctypes.byref(out))
+    return st, out.value
+
+
+def test_chunk_workspace_size():
+    """Two-launch workspace: (T / 64 + N + 1) chunk slots x heads x one slot, a slot being
+    the MFMA fragments of one chunk's serial-step operands (1 KiB each) plus its decay."""
+    slot128 = (8 * 4 + 24 + 2 * 8 + 1) * 1024
+    slot64 = (8 * 2 + 24 + 2 * 4 + 1) * 1024
+    assert chunk_ws_size() == (OK, (8192 // 64 + 1 + 1) * 96 * slot128)
+    # packed sequences: seq_len is the token total, n_seqs the sequence count
+    assert chunk_ws_size(seq_len=1000, n_seqs=5, H=3) == (OK, (1000 // 64 + 5 + 1) * 3 * slot128)
+    assert chunk_ws_size(batch=4, seq_len=300, n_seqs=4, H=2, dk=64, dv=64) == (
+        OK, (1200 // 64 + 4 + 1) * 2 * slot64)
+    # fp32 and unsupported widths never take the two-launch path
+    assert chunk_ws_size(io=F32, dk=64, dv=64) == (OK, 0)
+    assert chunk_ws_size(io=F32, dk=64, dv=64, policy=0) == (OK, 0)
+    assert chunk_ws_size(dk=96, dv=96) == (OK, 0)
+    assert chunk_ws_size(policy=2)[0] == VALUE
+    assert chunk_ws_size(io=5)[0] == DTYPE
+    assert chunk_ws_size(H=0)[0] == SHAPE
+    assert kda.library().kda_chunk_fwd_workspace_size(1, 64, 1, 2, 128, 128, BF16, 1,
+                                                      None) == NULL
+
+
+def test_chunk_workspace_checks():
+    P = ptrs()
+    _, need = chunk_ws_size(seq_len=256, H=2)
+    ws = ctypes.c_void_p(BASE + 20 * 64 * GiB)
+    assert chunk(override=dict(ws=ctypes.c_void_p(ws.value + 8), ws_bytes=need)) == ALIGN
+    assert chunk(override=dict(ws=ws, ws_bytes=need - 16)) == WS
+    assert chunk(override=dict(ws=P[2], ws_bytes=need)) == ALIAS          # overlaps v
+    assert chunk(override=dict(ws=ctypes.c_void_p(P[5].value - 1024), ws_bytes=need)) == ALIAS
+    # an fp32 call ignores the workspace, as documented
+    assert chunk(io=F32, dk=64, dv=64, q=False, override=dict(ws=ws, ws_bytes=0)) == NULL
 
 
 def test_segment_workspace_size():
