@@ -50,6 +50,15 @@
 
 namespace kda {
 
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <class Pol, int DK>
 struct ChunkLayout {
   using E = typename Pol::E;
@@ -425,7 +434,7 @@ struct OpSlot {
   static_assert(DK * 4 <= 1024, "the decay fits one block");
   // the lower fragments of a 64 x 64 operand in slice order: row block rb takes slices
   // pp < (rb + 2) / 2, i.e. (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-  static constexpr __device__ int tri(int rb, int pp) { return (rb == 3 ? 4 : rb) + pp; }
+  static constexpr __host__ __device__ int tri(int rb, int pp) { return (rb == 3 ? 4 : rb) + pp; }
 };
 
 // Prep pass: copy one chunk's serial-step operands from their LDS tiles to its slot, in
@@ -1010,13 +1019,64 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
+// The walk's products as a fixed sequence of stages, each one group of operand fragments
+// (at most eight) and the MFMAs that consume them, in an order that keeps the state's chain
+// (X, its split, U, its split, the state update) short: the products with decayed queries
+// (O) fill the MFMA unit while the splits run. Every accumulator sees its products in the
+// same order as in the chunk kernel's serial step.
+template <int DK>
+struct WalkPlan {
+  using OS = OpSlot<DK>;
+  static constexpr int NS = OS::NS;
+  static constexpr int NTD = OS::NTD;
+  enum : int { kK, kQ, kT, kKh, kM };
+  static constexpr int kQ1 = NS / 2;                    // Q stages before the X split
+  // K 0..NS-1 | Q 0..kQ1-1 | T 0,1 | Q kQ1..NS-1 | Kh (pp, t0) | M 0,1
+  static constexpr int kStages = NS + kQ1 + 2 + (NS - kQ1) + 2 * (NTD / 4) + 2;
+  static constexpr int kAfterK = NS - 1;                // stream the next chunk in
+  static constexpr int kAfterQ1 = NS + kQ1 - 1;         // split X
+  static constexpr int kAfterQ2 = 2 * NS + 1;           // negate and split U
+  static constexpr __host__ __device__ int kind(int s) {
+    return s < NS ? kK
+         : s < NS + kQ1 ? kQ
+         : s < NS + kQ1 + 2 ? kT
+         : s < 2 * NS + 2 ? kQ
+         : s < 2 * NS + 2 + 2 * (NTD / 4) ? kKh
+         : kM;
+  }
+  // slice of the stage (the k-slice for K and Q, the token slice for T, M and Kh)
+  static constexpr __host__ __device__ int pp(int s) {
+    return s < NS ? s
+         : s < NS + kQ1 ? s - NS
+         : s < NS + kQ1 + 2 ? s - NS - kQ1
+         : s < 2 * NS + 2 ? s - 2 - NS
+         : s < 2 * NS + 2 + 2 * (NTD / 4) ? (s - 2 * NS - 2) / (NTD / 4)
+         : s - 2 * NS - 2 - 2 * (NTD / 4);
+  }
+  // first 16-row tile of the state updated by a Kh stage
+  static constexpr __host__ __device__ int t0(int s) { return 4 * ((s - 2 * NS - 2) % (NTD / 4)); }
+  static constexpr __host__ __device__ int count(int s) {
+    return (kind(s) == kT || kind(s) == kM) ? (pp(s) == 0 ? 8 : 4) : 4;
+  }
+  // fragment k of stage s
+  static constexpr __host__ __device__ int frag(int s, int k) {
+    const int kd = kind(s), p = pp(s);
+    if (kd == kK) return OS::fKg + k * NS + p;
+    if (kd == kQ) return OS::fQg + k * NS + p;
+    if (kd == kKh) return OS::fKh + 2 * (t0(s) + k) + p;
+    // T and M: hi of the stage's row blocks, then lo
+    const int nr = p == 0 ? 4 : 2, rb0 = p == 0 ? 0 : 2;
+    const int hi = kd == kT ? OS::fT : OS::fM, lo = kd == kT ? OS::fTLo : OS::fMLo;
+    const int i = k < nr ? k : k - nr;
+    return (k < nr ? hi : lo) + OS::tri(rb0 + i, p);
+  }
+};
+
 // Pass 2 of the two-pass prefill: the serial walk over the chunks of one (sequence, head,
 // 64-column state tile), with the prologue's operands read from the chunks' slots. The step is
 // the chunk kernel's serial step, operation for operation, so the two paths agree bit for bit.
 // Slots stream into two LDS buffers by direct global-to-LDS loads: the next chunk's slot is in
 // flight while the current one is consumed, and the next chunk's values load into registers.
-// A chunk's outputs are stored at the start of the following chunk, so the wait for the slot
-// before the barrier never waits on recent stores.
 template <typename Tio, typename Tout, int DK>
 __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
   using Pol = PolBF16;
@@ -1086,172 +1146,166 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
         __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024, dst + f * 1024, 16, 0, 0);
     }
   };
-  auto frag_r = [&](const char* buf, int f) {
-    return *reinterpret_cast<const FragR*>(buf + f * 1024 + lane * 16);
-  };
-  auto frag = [&](const char* buf, int f) {
-    return *reinterpret_cast<const Frag*>(buf + f * 1024 + lane * 16);
-  };
 
   RawChunk<Tio, DK> raw;
-  if (nchunks > 0) {
-    fetch_slot(0, smem);
-    load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-
-  // outputs of the previous chunk, transposed (lane: token 16 rb + tq, four columns)
+  // values of the chunk about to start, in accumulator layout and negated: the initial X
   const int tq = 4 * q4 + (ln & 3);
-  const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
-  float ox[4][4];
-  auto store_out = [&](int cst, int L) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      Tout* row = go + size_t(cst + 16 * rb) * H * DV;
-      if (16 * rb + tq < L) {
-        if constexpr (sizeof(Tout) == 2)
-          *reinterpret_cast<bf16x4*>(row + lo_el) =
-              bf16x4{(__bf16)ox[rb][0], (__bf16)ox[rb][1], (__bf16)ox[rb][2], (__bf16)ox[rb][3]};
-        else
-          *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[rb][0], ox[rb][1], ox[rb][2], ox[rb][3]};
-      }
-    }
-  };
-
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int cstart = bos + ci * kChunk;
-    const int Lc = min(kChunk, eos - cstart);
-    const char* cur = smem + (ci & 1) * OS::kBytes;
-    const bool more = ci + 1 < nchunks;
-    if (more) fetch_slot(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
-    if (ci > 0) store_out(cstart - kChunk, kChunk);
-
-    FragR Sr[NS];
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
-    // X = (K e^Gamma) S - V, in fp32
-    f32x4 X[4];
+  f32x4 X0[4];
+  auto values_to_x0 = [&](int L) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       float vx[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
       quad_transpose(vx, lane);   // token 16 rb + 4 q4 + e, column 16 w + ln
-      if (Lc == kChunk) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = -vx[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[rb][e] = (16 * rb + 4 * q4 + e < Lc) ? -vx[e] : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) X0[rb][e] = (16 * rb + 4 * q4 + e < L) ? -vx[e] : 0.f;
     }
-    if (more) {
-      const int nstart = cstart + kChunk;
-      load_chunk_any<kLoadV, Tio, DK>(raw, p, nstart, min(kChunk, eos - nstart), w, lane, h, vcol0);
-    }
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-      FragR kg[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) kg[rb] = frag_r(cur, OS::fKg + rb * NS + pp);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(kg[rb], Sr[pp], X[rb]);
-    }
-    f32x4 U[4], O[4];
-    // O = (Q e^Gamma) S
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
-      FragR qg[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) qg[rb] = frag_r(cur, OS::fQg + rb * NS + pp);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(qg[rb], Sr[pp], pp == 0 ? zero4() : O[rb]);
-    }
-    // U = T' (V - K_Gamma S) = -T' X
-    Frag Xh[NT], Xl[NT];
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split(X, pp, Xh[pp], Xl[pp]);
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-      Frag th[4], tl[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          th[rb] = frag(cur, OS::fT + OS::tri(rb, pp));
-          tl[rb] = frag(cur, OS::fTLo + OS::tri(rb, pp));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xh[pp], pp == 0 ? zero4() : U[rb]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(tl[rb], Xh[pp], U[rb]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) U[rb] = Pol::mma(th[rb], Xl[pp], U[rb]);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
-    // O += M U and S += K^T U (fp16 operands; U and M as hi + lo pairs)
-    FragR Uh[NT], Ul[NT];
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) Pol::from_acc_split_r(U, pp, Uh[pp], Ul[pp]);
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-      FragR mh[4], ml[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (pp < Pol::slices_blocks(rb + 1)) {
-          mh[rb] = frag_r(cur, OS::fM + OS::tri(rb, pp));
-          ml[rb] = frag_r(cur, OS::fMLo + OS::tri(rb, pp));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Uh[pp], O[rb]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(ml[rb], Uh[pp], O[rb]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        if (pp < Pol::slices_blocks(rb + 1)) O[rb] = Pol::mma_r(mh[rb], Ul[pp], O[rb]);
-    }
-    // S <- diag(e^{Gamma_L}) S + (K e^{Gamma_L - Gamma})^T U
-    const float* decay = reinterpret_cast<const float*>(cur + OS::kDecay * 1024);
-#pragma unroll
-    for (int t = 0; t < NTD; ++t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] *= decay[16 * t + 4 * q4 + e];
-    }
-#pragma unroll
-    for (int pp = 0; pp < NT; ++pp) {
-#pragma unroll
-      for (int t0 = 0; t0 < NTD; t0 += 4) {
-        FragR kh[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) kh[t] = frag_r(cur, OS::fKh + 2 * (t0 + t) + pp);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Uh[pp], S[t0 + t]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(kh[t], Ul[pp], S[t0 + t]);
-      }
-    }
+  };
+  if (nchunks > 0) {
+    fetch_slot(0, smem);
+    load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    values_to_x0(min(kChunk, eos - bos));
+  }
+  __syncthreads();
+
+  // outputs of a chunk, transposed (lane: token 16 rb + tq, four consecutive columns)
+  const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
+  auto store_out = [&](const f32x4* Oc, int cst, int L) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+      float ox[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ox[rb][e] = p.scale * O[rb][e];
-      quad_transpose(ox[rb], lane);
+      for (int e = 0; e < 4; ++e) ox[e] = p.scale * Oc[rb][e];
+      quad_transpose(ox, lane);
+      Tout* row = go + size_t(cst + 16 * rb) * H * DV;
+      if (16 * rb + tq < L) {
+        if constexpr (sizeof(Tout) == 2)
+          *reinterpret_cast<bf16x4*>(row + lo_el) =
+              bf16x4{(__bf16)ox[0], (__bf16)ox[1], (__bf16)ox[2], (__bf16)ox[3]};
+        else
+          *reinterpret_cast<f32x4*>(row + lo_el) = f32x4{ox[0], ox[1], ox[2], ox[3]};
+      }
     }
-    if (ci + 1 == nchunks) store_out(cstart, Lc);
-    // the next slot (and values) must have landed before any wave reads them
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  using Plan = WalkPlan<DK>;
+  using V16 = int __attribute__((ext_vector_type(4)));
+  f32x4 O[4];
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int cstart = bos + ci * kChunk;
+    const int Lc = min(kChunk, eos - cstart);
+    const char* cur = smem + (ci & 1) * OS::kBytes;
+    const bool more = ci + 1 < nchunks;
+    // the next slot streams in behind this chunk (issued first: it has the whole chunk to land)
+    if (more) fetch_slot(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
+
+    // the state as fp16 B fragments (both products with decayed keys and queries), then its
+    // decay for the update: S is not read again before S += K^T U
+    FragR Sr[NS];
+#pragma unroll
+    for (int pp = 0; pp < NS; ++pp) Sr[pp] = Pol::from_acc_r(S, pp);
+    {
+      const float* decay = reinterpret_cast<const float*>(cur + OS::kDecay * 1024);
+#pragma unroll
+      for (int t = 0; t < NTD; ++t) {
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(decay + 16 * t + 4 * q4);
+        S[t] *= dv4;
+      }
+    }
+
+    // The products run as a fixed sequence of stages (Plan): each stage's fragments are read
+    // from LDS two stages ahead of its MFMAs, into three rotating register buffers.
+    V16 fb[3][8];
+    auto load_stage = [&](int st, V16* dst) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < Plan::count(st))
+          dst[k] = *reinterpret_cast<const V16*>(cur + Plan::frag(st, k) * 1024 + lane * 16);
+    };
+    auto R = [](V16 x) { return __builtin_bit_cast(FragR, x); };
+    auto B = [](V16 x) { return __builtin_bit_cast(Frag, x); };
+    f32x4 X[4], U[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) X[rb] = X0[rb];
+    Frag Xh[NT], Xl[NT];
+    FragR Uh[NT], Ul[NT];
+    load_stage(0, fb[0]);
+    load_stage(1, fb[1]);
+    static_for<0, Plan::kStages>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      if constexpr (st + 2 < Plan::kStages) load_stage(st + 2, fb[(st + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      V16* f = fb[st % 3];
+      constexpr int kind = Plan::kind(st), pp = Plan::pp(st);
+      if constexpr (kind == Plan::kK) {
+        // X = (K e^Gamma) S - V
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) X[rb] = Pol::mma_r(R(f[rb]), Sr[pp], X[rb]);
+      } else if constexpr (kind == Plan::kQ) {
+        // O = (Q e^Gamma) S
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) O[rb] = Pol::mma_r(R(f[rb]), Sr[pp], pp == 0 ? zero4() : O[rb]);
+      } else if constexpr (kind == Plan::kT) {
+        // U = T' (V - K_Gamma S) = -T' X; stage pp holds hi then lo of row blocks rb0..3
+        constexpr int kMax = 4;
+        const int rb0 = pp == 0 ? 0 : 2, nr = pp == 0 ? 4 : 2;
+#pragma unroll
+        for (int i = 0; i < kMax; ++i)
+          if (i < nr) U[rb0 + i] = Pol::mma(B(f[i]), Xh[pp], pp == 0 ? zero4() : U[rb0 + i]);
+#pragma unroll
+        for (int i = 0; i < kMax; ++i)
+          if (i < nr) U[rb0 + i] = Pol::mma(B(f[nr + i]), Xh[pp], U[rb0 + i]);
+#pragma unroll
+        for (int i = 0; i < kMax; ++i)
+          if (i < nr) U[rb0 + i] = Pol::mma(B(f[i]), Xl[pp], U[rb0 + i]);
+      } else if constexpr (kind == Plan::kKh) {
+        // S += (K e^{Gamma_L - Gamma})^T U, U as an fp16 hi + lo pair
+        const int t0 = Plan::t0(st);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(R(f[t]), Uh[pp], S[t0 + t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t0 + t] = Pol::mma_r(R(f[t]), Ul[pp], S[t0 + t]);
+      } else {
+        // O += M U, M and U as fp16 hi + lo pairs
+        const int rb0 = pp == 0 ? 0 : 2, nr = pp == 0 ? 4 : 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nr) O[rb0 + i] = Pol::mma_r(R(f[i]), Uh[pp], O[rb0 + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nr) O[rb0 + i] = Pol::mma_r(R(f[nr + i]), Uh[pp], O[rb0 + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nr) O[rb0 + i] = Pol::mma_r(R(f[i]), Ul[pp], O[rb0 + i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // work off the state's chain, placed where the products above keep the MFMA unit busy
+      if constexpr (st == Plan::kAfterK) {
+        // the next chunk's values
+        if (more) {
+          const int nstart = cstart + kChunk;
+          load_chunk_any<kLoadV, Tio, DK>(raw, p, nstart, min(kChunk, eos - nstart), w, lane, h,
+                                          vcol0);
+        }
+      } else if constexpr (st == Plan::kAfterQ1) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q) Pol::from_acc_split(X, q, Xh[q], Xl[q]);
+      } else if constexpr (st == Plan::kAfterQ2) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) Pol::from_acc_split_r(U, q, Uh[q], Ul[q]);
+      }
+    });
+    if (more) {
+      // the next slot (and values) must have landed before any wave reads them; this
+      // chunk's output stores are issued after the wait, so it never waits on them
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      values_to_x0(min(kChunk, eos - cstart - kChunk));
+    }
+    store_out(O, cstart, Lc);
     __syncthreads();
   }
 
