@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc")
 KERNEL_SRC = os.path.join(CSRC, "kda_chunk.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "chunk_fwd_prefill_8k_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "chunk_two_pass_prefill_8k_counters.txt")
 DECODE_SRC = os.path.join(CSRC, "kda_decode.hip")
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_replay_verify_counters.txt")
 
@@ -59,8 +59,8 @@ def source_digest(path=KERNEL_SRC):
 
 
 def counter_traffic(counters=COUNTERS, source=KERNEL_SRC):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
-    kernel source changed since the counters were taken."""
+    """HBM bytes per step (every launch of one call) from a committed rocprofv3 counter
+    summary, or None when the kernel source changed since the counters were taken."""
     if not os.path.exists(counters):
         return None
     vals = {}
@@ -297,7 +297,8 @@ def main():
     nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2)
     nflops = algorithmic_flops(T, H, dk, dv)
     achieved_gbs = nbytes / (avg_ms * 1e-3) / 1e9
-    traffic = counter_traffic()
+    # the committed counters cover the two-launch path
+    traffic = counter_traffic() if ws is not None else None
     line = {
         "metric": "KDA prefill tokens/s (kda_chunk_fwd)",
         "value": T / (ms_per_step * 1e-3),
