@@ -197,8 +197,8 @@ def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
     o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
     ht = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
     n_seg = 0   # the library's automatic choice
-    ws = torch.empty(kda.segment_cp_workspace_size(1, H, dk, dv, n_seg), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(kda.segment_cp_workspace_size(1, T, 1, H, dk, dv, kda.KDA_BF16, n_seg),
+                     dtype=torch.uint8, device=dev)
 
     def launch():
         kda.segment_cp_fwd(q, k, v, g, beta, o=o, ht=ht, n_segments=n_seg, workspace=ws,
@@ -214,7 +214,7 @@ def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
             "algorithmic_bytes_per_call": nbytes,
-            "kernels": "transition (chunk kernel), ordered scan, replay (chunk kernel)"}
+            "kernels": "prep pass (chunk kernel), transition walk, ordered scan, replay walk"}
 
 
 def main():

@@ -129,11 +129,14 @@ int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs, int num_hea
                                  int d_v, int io_dtype, int policy, size_t* bytes);
 
 /*
- * Bytes of device workspace kda_segment_cp_fwd needs for the given sizes (n_segments = 0
- * asks for the automatic choice). Returns KDA_OK and writes *bytes, or a negative status.
+ * Bytes of device workspace kda_segment_cp_fwd needs for the given sizes (batch / seq_len /
+ * n_seqs as in kda_chunk_fwd; n_segments = 0 asks for the automatic choice). For KDA_BF16
+ * inputs with d_k = d_v in {64, 128} the size includes the operand slots of the two-launch
+ * form (see kda_chunk_fwd); for KDA_F32 it is the segment summaries and entering states only.
+ * Returns KDA_OK and writes *bytes, or a negative status.
  */
-int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v,
-                                  int n_segments, size_t* bytes);
+int kda_segment_cp_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                  int d_v, int io_dtype, int n_segments, size_t* bytes);
 
 /*
  * kda_segment_cp_fwd: segment-parallel prefill for few heads over long sequences
@@ -143,16 +146,20 @@ int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v,
  * Same tensors, conventions and supported sizes as kda_chunk_fwd. Every sequence is cut into
  * up to n_segments contiguous, chunk-aligned segments (1..256). With n_segments = 0 the
  * library picks at most 64 from a cost model over the device's compute units and the longest
- * sequence; when that choice is one segment (the heads alone fill the device) it runs the
- * forward kernel once, exactly as kda_chunk_fwd, and leaves the workspace untouched (the
- * workspace query still returns the size for 64 segments). Otherwise there are three
- * launches on `stream`: (1) each segment's affine summary (P, Q) with
- * S_out = P S_in + Q, computed without its entering state; (2) an ordered scan that composes
- * the summaries into every segment's exact entering state and the final state; (3) all
- * segments replay their tokens in parallel from those states. The result equals
- * kda_chunk_fwd up to rounding. `workspace` is device memory of at least
- * kda_segment_cp_workspace_size(...) bytes, owned by the caller; its contents on entry are
- * ignored.
+ * sequence; when that choice is one segment (the heads alone fill the device) the call is
+ * the plain forward pass, exactly as kda_chunk_fwd (the workspace query still returns the
+ * size for 64 segments). Otherwise the steps on `stream` are: (1) each segment's affine
+ * summary (P, Q) with S_out = P S_in + Q, computed without its entering state; (2) an ordered
+ * scan that composes the summaries into every segment's exact entering state and the final
+ * state; (3) all segments replay their tokens in parallel from those states. The result
+ * equals kda_chunk_fwd up to rounding.
+ *
+ * `workspace` is caller-owned device memory, 16-byte aligned, overlapping no other argument;
+ * its contents on entry are ignored. With at least kda_segment_cp_workspace_size(...) bytes
+ * and bf16 inputs, the steps use the two-launch form: one prep pass over every chunk and head
+ * writes the chunks' operand slots, and (1) and (3) are walks over those slots. With less,
+ * but at least the size the query returns for KDA_F32 inputs, (1) and (3) run the one-launch
+ * kernel, which recomputes each chunk's prologue for every state tile.
  */
 int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const float* h0, const int32_t* cu_seqlens,

@@ -59,7 +59,8 @@ def library():
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_workspace_size.restype = I
-    lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_segment_cp_workspace_size.restype = I
     lib.kda_segment_cp_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P,
                                        P, I, P, ctypes.c_size_t, P]
@@ -217,9 +218,12 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     return a["o"], a["ht"]
 
 
-def segment_cp_workspace_size(n_seqs, H, dk, dv, n_segments=0):
+def segment_cp_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF16,
+                              n_segments=0):
+    """kda_segment_cp_workspace_size (batch / seq_len / n_seqs as in kda_chunk_fwd)."""
     out = ctypes.c_size_t(0)
-    st = library().kda_segment_cp_workspace_size(int(n_seqs), int(H), int(dk), int(dv),
+    st = library().kda_segment_cp_workspace_size(int(batch), int(seq_len), int(n_seqs), int(H),
+                                                  int(dk), int(dv), int(io_dtype),
                                                   int(n_segments), ctypes.byref(out))
     if st != 0:
         raise KDAError(st, "kda_segment_cp_workspace_size")
@@ -233,7 +237,9 @@ def segment_cp_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=
     tensor of at least segment_cp_workspace_size(...) bytes; allocated here if None."""
     torch = _torch()
     a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
-    need = segment_cp_workspace_size(a["n_seqs"], a["H"], a["dk"], a["dv"], n_segments)
+    T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
+    need = segment_cp_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
+                                     a["io"], n_segments)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = library().kda_segment_cp_fwd(

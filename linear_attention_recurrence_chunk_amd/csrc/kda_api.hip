@@ -169,6 +169,38 @@ int64_t max_seq_len(const int32_t* cu_seqlens_host, int N, int seq_len) {
   return m;
 }
 
+// chunk groups per sequence of the prep pass
+int prep_groups(const int32_t* cu_seqlens_host, int N, int seq_len) {
+  const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
+  const int64_t groups = (max_chunks + kPrepChunks - 1) / kPrepChunks;
+  return groups < 1 ? 1 : int(groups);
+}
+
+// Automatic segment count of the two-launch segment path (at most kAutoSegments), in units
+// of one walk chunk step: the prep pass is the same for every count; a transition step
+// (no output products) costs ~0.7 of a replay step and a scan step ~1.5.
+int auto_segments_two_pass(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
+  auto rounds = [&](int64_t wgs) { return double((wgs + cus - 1) / cus); };
+  double best = rounds(int64_t(N) * H * (dv / 64)) * double(max_chunks);
+  int best_n = 1;
+  const int hi = int(max_chunks < kAutoSegments ? max_chunks : kAutoSegments);
+  for (int n = 2; n <= hi; ++n) {
+    const double per_seg = double((max_chunks + n - 1) / n);
+    const double cost = rounds(int64_t(N) * n * H * ((dk + dv) / 64)) * per_seg * 0.7 +
+                        1.5 * n + rounds(int64_t(N) * n * H * (dv / 64)) * per_seg;
+    if (cost < best) {
+      best = cost;
+      best_n = n;
+    }
+  }
+  return best_n;
+}
+
+// the two-launch form needs bf16 inputs and equal key and value widths of 64 or 128
+bool two_pass_supported(int io_dtype, int dk, int dv) {
+  return io_dtype == KDA_BF16 && dk == dv && (dk == 64 || dk == 128);
+}
+
 int check_workspace_aliasing(const void* ws, size_t need, const void* q, const void* k,
                              const void* v, const float* g, const float* beta, const float* h0,
                              const void* o, const float* ht, int64_t T, int N, int H, int dk,
@@ -274,22 +306,28 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   if (two_pass) {
     p.mode = kda::kModeWalk;
     p.ws_ops = static_cast<char*>(workspace);
-    const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
-    const int groups = int((max_chunks + kPrepChunks - 1) / kPrepChunks);
-    return launch_status(kda::launch_chunk_two_pass(p, groups < 1 ? 1 : groups, out_dtype, d_k,
-                                                    static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rc = launch_status(
+        kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s));
+    if (rc != KDA_OK) return rc;
+    return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s));
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
 }
 
-int kda_segment_cp_workspace_size(int n_seqs, int num_heads, int d_k, int d_v, int n_segments,
-                                  size_t* bytes) {
+int kda_segment_cp_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                  int d_v, int io_dtype, int n_segments, size_t* bytes) {
   if (!bytes) return KDA_ERR_NULL_ARG;
-  if (n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_BAD_SHAPE;
+  if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+    return KDA_ERR_BAD_SHAPE;
   if (n_segments < 0 || n_segments > kMaxSegments) return KDA_ERR_BAD_SHAPE;
   const int ns = n_segments == 0 ? kAutoSegments : n_segments;
-  *bytes = segment_workspace_bytes(n_seqs, num_heads, d_k, d_v, ns);
+  const int64_t T = batch == 1 && n_seqs != 1 ? int64_t(seq_len) : int64_t(batch) * seq_len;
+  const int64_t N = batch == 1 && n_seqs != 1 ? n_seqs : batch;
+  *bytes = segment_workspace_bytes(int(N), num_heads, d_k, d_v, ns);
+  if (two_pass_supported(io_dtype, d_k, d_v)) *bytes += two_pass_workspace_bytes(T, N, num_heads, d_k);
   return KDA_OK;
 }
 
@@ -308,62 +346,28 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   if (n_segments < 0 || n_segments > kMaxSegments) return KDA_ERR_BAD_SHAPE;
   int ns = n_segments == 0 ? kAutoSegments : n_segments;
   const size_t need = segment_workspace_bytes(N, num_heads, d_k, d_v, ns);
+  const size_t need_ops = two_pass_supported(io_dtype, d_k, d_v)
+                              ? two_pass_workspace_bytes(T, N, num_heads, d_k) : 0;
   if (!workspace) return KDA_ERR_NULL_ARG;
   if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // a workspace that also holds the operand slots runs the two-launch form
+  const bool two_pass = need_ops > 0 && workspace_bytes >= need + need_ops;
   {
-    const size_t es = dsize(io_dtype);
-    const Range rws = range_of(workspace, need);
-    const Range all[] = {
-        range_of(q, size_t(T) * num_heads * d_k * es), range_of(k, size_t(T) * num_heads * d_k * es),
-        range_of(v, size_t(T) * num_heads * d_v * es), range_of(g, size_t(T) * num_heads * d_k * 4),
-        range_of(beta, size_t(T) * num_heads * 4),
-        range_of(h0, h0 ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
-        range_of(o, size_t(T) * num_heads * d_v * dsize(out_dtype)),
-        range_of(ht, ht ? size_t(N) * num_heads * d_k * d_v * 4 : 0)};
-    for (Range x : all)
-      if (overlaps(rws, x)) return KDA_ERR_ALIASING;
+    const int rc = check_workspace_aliasing(workspace, two_pass ? need + need_ops : need, q, k, v,
+                                            g, beta, h0, o, ht, T, N, num_heads, d_k, d_v,
+                                            io_dtype, out_dtype);
+    if (rc != KDA_OK) return rc;
   }
   if (N == 0) return KDA_OK;
-  if (n_segments == 0) {
-    int64_t max_len = 0;
-    if (cu_seqlens_host) {
-      for (int i = 0; i < N; ++i) {
-        const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
-        max_len = len > max_len ? len : max_len;
-      }
-    } else {
-      max_len = seq_len;
-    }
-    ns = auto_segments(N, num_heads, d_k, d_v, (max_len + 63) / 64, compute_units());
-  }
+  const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
+  if (n_segments == 0)
+    ns = two_pass ? auto_segments_two_pass(N, num_heads, d_k, d_v, max_chunks, compute_units())
+                  : auto_segments(N, num_heads, d_k, d_v, max_chunks, compute_units());
   float* ws_pq = static_cast<float*>(workspace);
   float* ws_sin = ws_pq + size_t(N) * ns * num_heads * d_k * (d_k + d_v);
+  char* ws_ops = static_cast<char*>(workspace) + need;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ns == 1 && n_segments == 0) {
-    // one segment: the entering state is h0, so the forward pass is the whole job
-    kda::ChunkParams f{};
-    f.q = q;
-    f.k = k;
-    f.v = v;
-    f.g = g;
-    f.beta = beta;
-    f.h0 = h0;
-    f.cu_seqlens = cu_seqlens;
-    f.o = o;
-    f.ht = ht;
-    f.seq_len = cu_seqlens ? 0 : seq_len;
-    f.n_seqs = N;
-    f.H = num_heads;
-    f.dv = d_v;
-    f.n_vt = d_v / 64;
-    f.n_seg = 1;
-    f.n_units = N * num_heads;
-    f.scale = scale;
-    f.g_min = g_min;
-    f.mode = kda::kModeForward;
-    return launch_status(kda::launch_chunk_fwd(f, io_dtype, out_dtype, d_k, s));
-  }
 
   kda::ChunkParams p{};
   p.q = q;
@@ -379,16 +383,37 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   p.n_seqs = N;
   p.H = num_heads;
   p.dv = d_v;
+  p.scale = scale;
+  p.g_min = g_min;
+  p.ws_ops = two_pass ? ws_ops : nullptr;
+  if (two_pass) {
+    // one prep pass serves every walk below
+    const int rc = launch_status(
+        kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s));
+    if (rc != KDA_OK) return rc;
+  }
+  if (ns == 1 && n_segments == 0) {
+    // one segment: the entering state is h0, so the forward pass is the whole job
+    p.ht = ht;
+    p.n_vt = d_v / 64;
+    p.n_seg = 1;
+    p.n_units = N * num_heads;
+    if (two_pass) {
+      p.mode = kda::kModeWalk;
+      return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s));
+    }
+    p.mode = kda::kModeForward;
+    return launch_status(kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
+  }
   p.n_seg = ns;
   p.n_units = N * ns * num_heads;
   p.ws_pq = ws_pq;
   p.ws_sin = ws_sin;
-  p.scale = scale;
-  p.g_min = g_min;
   // (1) segment summaries [P | Q] over the widened state, without entering states
   p.mode = kda::kModeTransition;
   p.n_vt = (d_k + d_v) / 64;
-  int rc = launch_status(kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
+  int rc = launch_status(two_pass ? kda::launch_chunk_walk(p, out_dtype, d_k, s)
+                                  : kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
   if (rc != KDA_OK) return rc;
   // (2) ordered scan: every segment's entering state and the final state
   kda::ScanParams sp{};
@@ -407,7 +432,8 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   // (3) all segments replay their tokens in parallel
   p.mode = kda::kModeReplay;
   p.n_vt = d_v / 64;
-  return launch_status(kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
+  return launch_status(two_pass ? kda::launch_chunk_walk(p, out_dtype, d_k, s)
+                                : kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
 }
 
 int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_width,

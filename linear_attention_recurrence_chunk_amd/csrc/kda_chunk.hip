@@ -1024,37 +1024,38 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 // (X, its split, U, its split, the state update) short: the products with decayed queries
 // (O) fill the MFMA unit while the splits run. Every accumulator sees its products in the
 // same order as in the chunk kernel's serial step.
-template <int DK>
+template <int DK, bool kOut = true>
 struct WalkPlan {
   using OS = OpSlot<DK>;
   static constexpr int NS = OS::NS;
   static constexpr int NTD = OS::NTD;
   enum : int { kK, kQ, kT, kKh, kM };
-  static constexpr int kQ1 = NS / 2;                    // Q stages before the X split
-  // K 0..NS-1 | Q 0..kQ1-1 | T 0,1 | Q kQ1..NS-1 | Kh (pp, t0) | M 0,1
-  static constexpr int kStages = NS + kQ1 + 2 + (NS - kQ1) + 2 * (NTD / 4) + 2;
-  static constexpr int kAfterK = NS - 1;                // stream the next chunk in
-  static constexpr int kAfterQ1 = NS + kQ1 - 1;         // split X
-  static constexpr int kAfterQ2 = 2 * NS + 1;           // negate and split U
+  // K 0..NS-1 | Q 0..kQ1-1 | T 0,1 | Q kQ1..NS-1 | Kh (pp, t0) | M 0,1; without outputs there
+  // are no Q and M stages
+  static constexpr int kQ1 = kOut ? NS / 2 : 0;        // Q stages before the X split
+  static constexpr int sQ1 = NS;
+  static constexpr int sT = sQ1 + kQ1;
+  static constexpr int sQ2 = sT + 2;
+  static constexpr int sKh = sQ2 + (kOut ? NS - kQ1 : 0);
+  static constexpr int sM = sKh + 2 * (NTD / 4);
+  static constexpr int kStages = sM + (kOut ? 2 : 0);
+  static constexpr int kAfterK = NS - 1;                // load the next chunk's values
+  static constexpr int kAfterQ1 = sT - 1;               // split X
+  static constexpr int kAfterQ2 = sKh - 1;              // negate and split U
   static constexpr __host__ __device__ int kind(int s) {
-    return s < NS ? kK
-         : s < NS + kQ1 ? kQ
-         : s < NS + kQ1 + 2 ? kT
-         : s < 2 * NS + 2 ? kQ
-         : s < 2 * NS + 2 + 2 * (NTD / 4) ? kKh
-         : kM;
+    return s < sQ1 ? kK : s < sT ? kQ : s < sQ2 ? kT : s < sKh ? kQ : s < sM ? kKh : kM;
   }
   // slice of the stage (the k-slice for K and Q, the token slice for T, M and Kh)
   static constexpr __host__ __device__ int pp(int s) {
-    return s < NS ? s
-         : s < NS + kQ1 ? s - NS
-         : s < NS + kQ1 + 2 ? s - NS - kQ1
-         : s < 2 * NS + 2 ? s - 2 - NS
-         : s < 2 * NS + 2 + 2 * (NTD / 4) ? (s - 2 * NS - 2) / (NTD / 4)
-         : s - 2 * NS - 2 - 2 * (NTD / 4);
+    return s < sQ1 ? s
+         : s < sT ? s - sQ1
+         : s < sQ2 ? s - sT
+         : s < sKh ? kQ1 + s - sQ2
+         : s < sM ? (s - sKh) / (NTD / 4)
+         : s - sM;
   }
   // first 16-row tile of the state updated by a Kh stage
-  static constexpr __host__ __device__ int t0(int s) { return 4 * ((s - 2 * NS - 2) % (NTD / 4)); }
+  static constexpr __host__ __device__ int t0(int s) { return 4 * ((s - sKh) % (NTD / 4)); }
   static constexpr __host__ __device__ int count(int s) {
     return (kind(s) == kT || kind(s) == kM) ? (pp(s) == 0 ? 8 : 4) : 4;
   }
@@ -1077,7 +1078,7 @@ struct WalkPlan {
 // the chunk kernel's serial step, operation for operation, so the two paths agree bit for bit.
 // Slots stream into two LDS buffers by direct global-to-LDS loads: the next chunk's slot is in
 // flight while the current one is consumed, and the next chunk's values load into registers.
-template <typename Tio, typename Tout, int DK>
+template <typename Tio, typename Tout, int DK, bool kOut>
 __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
   using Pol = PolBF16;
   using Frag = typename Pol::Frag;
@@ -1091,6 +1092,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
 
   __shared__ __attribute__((aligned(16))) char smem[2 * OS::kBytes];
 
+  // ---- which (sequence, segment, head, state tile): the tiles of one unit share an XCD
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int rest = b >> 3;
@@ -1100,7 +1102,10 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
   const int H = p.H;
   const int DV = p.dv;
   const int h = unit % H;
-  const int n = unit / H;
+  const int sj = unit / H;              // global segment index n * n_seg + j
+  const int n = sj / p.n_seg;
+  const int j = sj % p.n_seg;
+  const int mode = p.mode;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1116,34 +1121,64 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
     bos = n * p.seq_len;
     eos = bos + p.seq_len;
   }
+  // operand slot of the sequence's first chunk, then the segment's chunk range (chunk-aligned
+  // contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg))
+  long long slot0 = (long long)(bos >> 6) + n;
+  if (p.n_seg > 1) {
+    const long long nc = (eos - bos + kChunk - 1) / kChunk;
+    const int c_lo = int((j * nc) / p.n_seg);
+    const int c_hi = int(((j + 1) * nc) / p.n_seg);
+    slot0 += c_lo;
+    const int seg_bos = bos + kChunk * c_lo;
+    eos = min(eos, bos + kChunk * c_hi);
+    bos = seg_bos;
+  }
   const int nchunks = (eos - bos + kChunk - 1) / kChunk;
-  const char* ws_head = p.ws_ops + (size_t((long long)(bos >> 6) + n) * H + h) * OS::kBytes;
+  const char* ws_head = p.ws_ops + (size_t(slot0) * H + h) * OS::kBytes;
   const size_t slot_stride = size_t(H) * OS::kBytes;   // from one chunk's slot to the next
-  const int vcol0 = vt * VT;
-  const int col0 = vcol0 + 16 * w;
+  // transition: tiles [0, DK/64) hold P (zero values, identity start), the rest Q
+  const bool p_tile = !kOut && vt < DK / 64;
+  const int vcol0 = p_tile ? 0 : (kOut ? vt : vt - DK / 64) * VT;   // column of v feeding the tile
+  const int col0 = vt * VT + 16 * w;   // first state column owned by this wave
+  const int ldS = kOut ? DV : DK + DV;   // row stride of the state this tile writes
   Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
 
+  // ---- entering state in accumulator layout: tile t, register e = row 16t + 4 q4 + e
   f32x4 S[NTD];
-  if (p.h0) {
-    // all 32 loads in flight together
-    const float* s_in = p.h0 + (size_t(n) * H + h) * DK * DV + col0 + ln;
+  const float* s_in = nullptr;
+  if (mode == kModeWalk && p.h0) s_in = p.h0 + (size_t(n) * H + h) * DK * DV;
+  if (mode == kModeReplay) s_in = p.ws_sin + (size_t(sj) * H + h) * DK * DV;
+  if (s_in) {
+    // all loads in flight together
+    const float* src = s_in + col0 + ln;
 #pragma unroll
     for (int t = 0; t < NTD; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] = s_in[size_t(16 * t + 4 * q4 + e) * DV];
+      for (int e = 0; e < 4; ++e) S[t][e] = src[size_t(16 * t + 4 * q4 + e) * DV];
   } else {
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) S[t] = zero4();
+    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[t][e] = (p_tile && 16 * t + 4 * q4 + e == col0 + ln) ? 1.f : 0.f;
   }
 
-  // wave w moves blocks w, w + 4, ... of chunk ci's slot into buffer dst
-  auto fetch_slot = [&](int ci, char* dst) {
-    const char* src = ws_head + size_t(ci) * slot_stride + lane * 16;
+  // wave w moves blocks w, w + 4, ... of the fragment ranges the walk reads (without outputs:
+  // no Q e^Gamma and no M) of chunk ci's slot into buffer dst
+  auto fetch_range = [&](const char* src, char* dst, int f0, int f1) {
 #pragma unroll
     for (int i = 0; i < (OS::kBlocks + 3) / 4; ++i) {
-      const int f = w + 4 * i;
-      if (f < OS::kBlocks)
-        __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024, dst + f * 1024, 16, 0, 0);
+      const int f = f0 + w + 4 * i;
+      if (f < f1) __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024, dst + f * 1024, 16, 0, 0);
+    }
+  };
+  auto fetch_slot = [&](int ci, char* dst) {
+    const char* src = ws_head + size_t(ci) * slot_stride + lane * 16;
+    if constexpr (kOut) {
+      fetch_range(src, dst, 0, OS::kBlocks);
+    } else {
+      fetch_range(src, dst, OS::fKg, OS::fKg + 4 * NS);
+      fetch_range(src, dst, OS::fT, OS::fTLo + 6);
+      fetch_range(src, dst, OS::fKh, OS::kBlocks);
     }
   };
 
@@ -1159,12 +1194,13 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
       for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
       quad_transpose(vx, lane);   // token 16 rb + 4 q4 + e, column 16 w + ln
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X0[rb][e] = (16 * rb + 4 * q4 + e < L) ? -vx[e] : 0.f;
+      for (int e = 0; e < 4; ++e) X0[rb][e] = (16 * rb + 4 * q4 + e < L && !p_tile) ? -vx[e] : 0.f;
     }
   };
   if (nchunks > 0) {
     fetch_slot(0, smem);
-    load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+    if (!p_tile)
+      load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     values_to_x0(min(kChunk, eos - bos));
   }
@@ -1190,7 +1226,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
     }
   };
 
-  using Plan = WalkPlan<DK>;
+  using Plan = WalkPlan<DK, kOut>;
   using V16 = int __attribute__((ext_vector_type(4)));
   f32x4 O[4];
   for (int ci = 0; ci < nchunks; ++ci) {
@@ -1284,15 +1320,17 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
       // work off the state's chain, placed where the products above keep the MFMA unit busy
       if constexpr (st == Plan::kAfterK) {
         // the next chunk's values
-        if (more) {
+        if (more && !p_tile) {
           const int nstart = cstart + kChunk;
           load_chunk_any<kLoadV, Tio, DK>(raw, p, nstart, min(kChunk, eos - nstart), w, lane, h,
                                           vcol0);
         }
-      } else if constexpr (st == Plan::kAfterQ1) {
+      }
+      if constexpr (st == Plan::kAfterQ1) {
 #pragma unroll
         for (int q = 0; q < NT; ++q) Pol::from_acc_split(X, q, Xh[q], Xl[q]);
-      } else if constexpr (st == Plan::kAfterQ2) {
+      }
+      if constexpr (st == Plan::kAfterQ2) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) U[rb] = -U[rb];
 #pragma unroll
@@ -1305,16 +1343,18 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       values_to_x0(min(kChunk, eos - cstart - kChunk));
     }
-    store_out(O, cstart, Lc);
+    if constexpr (kOut) store_out(O, cstart, Lc);
     __syncthreads();
   }
 
-  if (p.ht) {
-    float* s_out = p.ht + (size_t(n) * H + h) * DK * DV;
+  float* s_out = nullptr;
+  if (mode == kModeWalk && p.ht) s_out = p.ht + (size_t(n) * H + h) * DK * DV;
+  if (mode == kModeTransition) s_out = p.ws_pq + (size_t(sj) * H + h) * DK * ldS;
+  if (s_out) {
 #pragma unroll
     for (int t = 0; t < NTD; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_out[size_t(16 * t + 4 * q4 + e) * DV + col0 + ln] = S[t][e];
+      for (int e = 0; e < 4; ++e) s_out[size_t(16 * t + 4 * q4 + e) * ldS + col0 + ln] = S[t][e];
   }
 }
 
@@ -1329,41 +1369,67 @@ static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename Tout, int DK>
-static hipError_t launch_two_pass(const ChunkParams& walk, int prep_groups, hipStream_t stream) {
-  ChunkParams prep = walk;
-  prep.mode = kModePrep;
-  prep.n_seg = prep_groups;
-  prep.n_vt = 1;
-  prep.n_units = walk.n_seqs * prep_groups * walk.H;
-  prep.o = nullptr;
-  prep.ht = nullptr;
-  prep.h0 = nullptr;
-  {
-    const dim3 grid((prep.n_units + 7) / 8 * 8);
-    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, DK, true, true>), grid, dim3(256),
-                       0, stream, prep);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const dim3 grid((walk.n_units + 7) / 8 * 8 * walk.n_vt);
-  hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK>), grid, dim3(256), 0, stream, walk);
-  return hipGetLastError();
-}
-
-hipError_t launch_chunk_two_pass(const ChunkParams& p, int prep_groups, int out_dtype, int dk,
-                                 hipStream_t stream) {
-  if (p.mode != kModeWalk || !p.ws_ops || !p.o || !p.q || !p.k || !p.v || !p.g || !p.beta)
-    return hipErrorInvalidValue;
-  if (p.H < 1 || p.n_seqs < 1 || p.n_seg != 1 || prep_groups < 1 || p.dv != dk ||
-      p.n_vt != p.dv / 64 || (long long)p.n_units != (long long)p.n_seqs * p.H)
+hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
+                             hipStream_t stream) {
+  if (!base.ws_ops || !base.q || !base.k || !base.g || !base.beta || base.H < 1 ||
+      base.n_seqs < 1 || prep_groups < 1 || (!base.cu_seqlens && base.seq_len < 0))
     return hipErrorInvalidValue;
   if (op_slot_bytes(dk) != (dk == 128 ? OpSlot<128>::kBytes : OpSlot<64>::kBytes))
     return hipErrorInvalidValue;
-  if (dk == 128) return out_dtype == 1 ? launch_two_pass<__bf16, 128>(p, prep_groups, stream)
-                                       : launch_two_pass<float, 128>(p, prep_groups, stream);
-  if (dk == 64) return out_dtype == 1 ? launch_two_pass<__bf16, 64>(p, prep_groups, stream)
-                                      : launch_two_pass<float, 64>(p, prep_groups, stream);
+  ChunkParams prep = base;
+  prep.mode = kModePrep;
+  prep.n_seg = prep_groups;
+  prep.n_vt = 1;
+  prep.n_units = base.n_seqs * prep_groups * base.H;
+  prep.o = nullptr;
+  prep.ht = nullptr;
+  prep.h0 = nullptr;
+  prep.ws_pq = nullptr;
+  prep.ws_sin = nullptr;
+  const dim3 grid((prep.n_units + 7) / 8 * 8);
+  if (dk == 128)
+    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true>), grid,
+                       dim3(256), 0, stream, prep);
+  else if (dk == 64)
+    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 64, true, true>), grid,
+                       dim3(256), 0, stream, prep);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename Tout, int DK>
+static hipError_t launch_walk(const ChunkParams& p, hipStream_t stream) {
+  const dim3 grid((p.n_units + 7) / 8 * 8 * p.n_vt);
+  if (p.mode == kModeTransition)
+    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, false>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, true>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream) {
+  if (!p.ws_ops || !p.v || p.H < 1 || p.n_seqs < 1 || p.n_seg < 1 || p.dv != dk ||
+      (long long)p.n_units != (long long)p.n_seqs * p.n_seg * p.H ||
+      (!p.cu_seqlens && p.seq_len < 0))
+    return hipErrorInvalidValue;
+  switch (p.mode) {
+    case kModeWalk:
+      if (p.n_seg != 1 || p.n_vt != p.dv / 64 || !p.o) return hipErrorInvalidValue;
+      break;
+    case kModeTransition:
+      if (p.n_vt != (dk + p.dv) / 64 || !p.ws_pq) return hipErrorInvalidValue;
+      break;
+    case kModeReplay:
+      if (p.n_vt != p.dv / 64 || !p.ws_sin || !p.o) return hipErrorInvalidValue;
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  if (dk == 128) return out_dtype == 1 ? launch_walk<__bf16, 128>(p, stream)
+                                       : launch_walk<float, 128>(p, stream);
+  if (dk == 64) return out_dtype == 1 ? launch_walk<__bf16, 64>(p, stream)
+                                      : launch_walk<float, 64>(p, stream);
   return hipErrorInvalidValue;
 }
 

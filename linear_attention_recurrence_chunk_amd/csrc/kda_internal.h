@@ -61,11 +61,14 @@ hipError_t launch_segment_scan(const ScanParams& p, int dk, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, int dk,
                             hipStream_t stream);
 
-// Two-pass prefill (bf16 inputs): prep over (sequence, group of chunks, head), then the walk
-// over (sequence, head, value tile). p describes the walk (forward-mode fields plus ws_ops);
-// prep_groups is the number of chunk groups per sequence of the prep pass.
-hipError_t launch_chunk_two_pass(const ChunkParams& p, int prep_groups, int out_dtype, int dk,
-                                 hipStream_t stream);
+// Two-pass prefill (bf16 inputs). The prep pass runs over (sequence, group of chunks, head),
+// prep_groups groups per sequence, and fills the operand slots in base.ws_ops from q, k, g,
+// beta (no other field of base is read). A walk then runs over (sequence, segment, head,
+// state tile) in mode kModeWalk (whole sequences: o and ht), kModeTransition (segment
+// summaries [P | Q] into ws_pq) or kModeReplay (o from the entering states in ws_sin).
+hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
+                             hipStream_t stream);
+hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream);
 
 // Operand slots: chunk c of sequence n (bos_n its first token) uses slot (bos_n / 64) + n + c,
 // so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them.

@@ -157,13 +157,20 @@ def test_chunk_workspace_checks():
 def test_segment_workspace_size():
     lib = kda.library()
     out = ctypes.c_size_t(0)
-    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 64, ctypes.byref(out)) == OK
+
+    def size(n_seg, io=F32, batch=1, seq_len=262144, n_seqs=1, H=12):
+        st = lib.kda_segment_cp_workspace_size(batch, seq_len, n_seqs, H, 128, 128, io, n_seg,
+                                               ctypes.byref(out))
+        return st, out.value
     # [P | Q] summaries plus entering states: N * n_seg * H * d_k * (d_k + 2 d_v) fp32
-    assert out.value == 1 * 64 * 12 * 128 * (128 + 256) * 4
-    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 0, ctypes.byref(out)) == OK
-    assert out.value == 1 * 64 * 12 * 128 * 384 * 4            # automatic choice: 64 segments
-    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 257, ctypes.byref(out)) == SHAPE
-    assert lib.kda_segment_cp_workspace_size(1, 12, 128, 128, 4, None) == NULL
+    seg64 = 1 * 64 * 12 * 128 * (128 + 256) * 4
+    assert size(64) == (OK, seg64)
+    assert size(0) == (OK, seg64)                              # automatic choice: 64 segments
+    # bf16 inputs add the two-launch operand slots: (T / 64 + N + 1) x H x 74752 B
+    assert size(64, io=BF16) == (OK, seg64 + (262144 // 64 + 2) * 12 * 74752)
+    assert size(257)[0] == SHAPE
+    assert size(4, io=9)[0] == DTYPE
+    assert lib.kda_segment_cp_workspace_size(1, 256, 1, 12, 128, 128, F32, 4, None) == NULL
 
 
 def test_segment_workspace_checks():

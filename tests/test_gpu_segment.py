@@ -76,7 +76,9 @@ def test_segments_f32():
 
 def test_workspace_too_small_is_rejected():
     inp = to_dev(wl.prefill_inputs(T=256, H=2, dk=128, dv=128, dtype="bf16", seed=1))
-    need = kda.segment_cp_workspace_size(1, 2, 128, 128, 4)
+    # below the segment summaries themselves (the size the query gives for fp32 inputs)
+    need = kda.segment_cp_workspace_size(1, 256, 1, 2, 128, 128, io_dtype=kda.KDA_F32,
+                                         n_segments=4)
     ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(kda.KDAError) as ei:
         kda.segment_cp_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], n_segments=4,
@@ -104,3 +106,38 @@ def test_automatic_single_segment_is_the_forward_pass():
                            out_dtype=torch.float32)
     o2, h2 = _seg(inp, 0)
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("n_segments,lengths", [(4, None), (0, None), (3, [100, 0, 700, 64, 1])])
+def test_two_launch_form_is_bit_identical(n_segments, lengths):
+    """A workspace holding the operand slots runs the prep pass and the transition and
+    replay walks; one holding only the segment summaries runs the one-launch kernel for both.
+    The two forms compute the same products in the same order: identical o and final state."""
+    print(f"case segment two-launch vs one-launch n_segments={n_segments} lengths={lengths}",
+          flush=True)
+    if lengths is None:
+        inp = wl.prefill_inputs(T=1500, H=3, dk=128, dv=128, dtype="bf16", seed=33, h0_std=0.02)
+    else:
+        inp = wl.prefill_inputs(H=2, dk=128, dv=128, dtype="bf16", seed=34, h0_std=0.02,
+                                lengths=lengths)
+    d = to_dev(inp)
+    cu = d["cu_seqlens"] if lengths is not None else None
+    T = int(d["q"].shape[0])
+    N = len(lengths) if lengths is not None else 1
+    H = int(d["q"].shape[1])
+    full = kda.segment_cp_workspace_size(1, T, N, H, 128, 128, kda.KDA_BF16, n_segments)
+    small = kda.segment_cp_workspace_size(1, T, N, H, 128, 128, kda.KDA_F32, n_segments)
+    assert full > small
+    res = []
+    for nbytes in (full, small):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        res.append(kda.segment_cp_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"],
+                                      cu_seqlens=cu, n_segments=n_segments, workspace=ws,
+                                      out_dtype=torch.float32))
+        torch.cuda.synchronize()
+    (o1, h1), (o2, h2) = res
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    o_ref, ht_ref = _oracle(inp, varlen=lengths is not None)
+    e_o, e_s = rel_max_err(np64(o1), o_ref), rel_max_err(np64(h1), ht_ref)
+    print(f"err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
