@@ -196,6 +196,14 @@ int auto_segments_two_pass(int N, int H, int dk, int dv, int64_t max_chunks, int
   return best_n;
 }
 
+// State tiles per walk workgroup. One tile (four waves, one per SIMD) keeps the serial chain
+// shortest and wins while the workgroups fit on the compute units in one round; beyond that
+// two tiles per workgroup (eight waves, two per SIMD, sharing every slot load) finish the
+// rounds sooner.
+int walk_tiles_per_wg(int64_t units, int n_vt) {
+  return (n_vt % 2 == 0 && units * n_vt > int64_t(compute_units())) ? 2 : 1;
+}
+
 // the two-launch form needs bf16 inputs and equal key and value widths of 64 or 128
 bool two_pass_supported(int io_dtype, int dk, int dv) {
   return io_dtype == KDA_BF16 && dk == dv && (dk == 64 || dk == 128);
@@ -310,6 +318,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
     const int rc = launch_status(
         kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s));
     if (rc != KDA_OK) return rc;
+    p.walk_tpw = walk_tiles_per_wg(p.n_units, p.n_vt);
     return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s));
   }
   return launch_status(
@@ -400,6 +409,7 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
     p.n_units = N * num_heads;
     if (two_pass) {
       p.mode = kda::kModeWalk;
+      p.walk_tpw = walk_tiles_per_wg(p.n_units, p.n_vt);
       return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s));
     }
     p.mode = kda::kModeForward;
@@ -412,6 +422,7 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   // (1) segment summaries [P | Q] over the widened state, without entering states
   p.mode = kda::kModeTransition;
   p.n_vt = (d_k + d_v) / 64;
+  p.walk_tpw = walk_tiles_per_wg(p.n_units, p.n_vt);
   int rc = launch_status(two_pass ? kda::launch_chunk_walk(p, out_dtype, d_k, s)
                                   : kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
   if (rc != KDA_OK) return rc;
@@ -432,6 +443,7 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   // (3) all segments replay their tokens in parallel
   p.mode = kda::kModeReplay;
   p.n_vt = d_v / 64;
+  p.walk_tpw = walk_tiles_per_wg(p.n_units, p.n_vt);
   return launch_status(two_pass ? kda::launch_chunk_walk(p, out_dtype, d_k, s)
                                 : kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, s));
 }

@@ -41,6 +41,7 @@ struct ChunkParams {
   float* ws_pq;             // transition: [N, n_seg, H, dk, dk + dv]
   float* ws_sin;            // replay: [N, n_seg, H, dk, dv] entering states
   char* ws_ops;             // prep / walk: operand slots [chunk slot][H] (see op_slot_count)
+  int walk_tpw;             // walk: state tiles per workgroup, 1 or 2 (2 needs n_vt even)
   float scale;
   float g_min;
 };

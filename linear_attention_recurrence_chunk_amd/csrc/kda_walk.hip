@@ -5,9 +5,6 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
-#ifndef KDA_WALK_AHEAD
-#define KDA_WALK_AHEAD 2
-#endif
 
 namespace kda {
 
@@ -70,8 +67,8 @@ struct WalkPlan {
 // the chunk kernel's serial step, operation for operation, so the two paths agree bit for bit.
 // Slots stream into two LDS buffers by direct global-to-LDS loads: the next chunk's slot is in
 // flight while the current one is consumed, and the next chunk's values load into registers.
-template <typename Tio, typename Tout, int DK, bool kOut>
-__global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
+template <typename Tio, typename Tout, int DK, bool kOut, int kTPW>
+__global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   using Pol = PolBF16;
   using Frag = typename Pol::Frag;
   using FragR = typename Pol::FragR;
@@ -84,12 +81,14 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
 
   __shared__ __attribute__((aligned(16))) char smem[2 * OS::kBytes];
 
-  // ---- which (sequence, segment, head, state tile): the tiles of one unit share an XCD
+  // ---- which (sequence, segment, head) and which kTPW state tiles of it (four waves per
+  //      tile): the workgroups of one unit share an XCD
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int rest = b >> 3;
-  const int vt = rest % p.n_vt;
-  const int unit = (rest / p.n_vt) * 8 + xcd;
+  const int n_groups = p.n_vt / kTPW;
+  const int vg = rest % n_groups;
+  const int unit = (rest / n_groups) * 8 + xcd;
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int DV = p.dv;
@@ -100,7 +99,9 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
   const int mode = p.mode;
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave in the workgroup
+  const int w = wid & 3;                                       // wave in its state tile
+  const int vt = vg * kTPW + (wid >> 2);
   const int lane = tid & 63;
   const int q4 = lane >> 4;
   const int ln = lane & 15;
@@ -154,17 +155,20 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
       for (int e = 0; e < 4; ++e) S[t][e] = (p_tile && 16 * t + 4 * q4 + e == col0 + ln) ? 1.f : 0.f;
   }
 
-  // wave w moves blocks w, w + 4, ... of the fragment ranges the walk reads (without outputs:
+  // wave wid moves blocks wid, wid + 4 kTPW, ... of the fragment ranges the walk reads (without outputs:
   // no Q e^Gamma and no M) of chunk ci's slot into buffer dst
+  // (the global address is a wave-uniform block address plus the lane's 16-byte offset)
   auto fetch_range = [&](const char* src, char* dst, int f0, int f1) {
 #pragma unroll
-    for (int i = 0; i < (OS::kBlocks + 3) / 4; ++i) {
-      const int f = f0 + w + 4 * i;
-      if (f < f1) __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024, dst + f * 1024, 16, 0, 0);
+    for (int i = 0; i < (OS::kBlocks + 4 * kTPW - 1) / (4 * kTPW); ++i) {
+      const int f = f0 + wid + 4 * kTPW * i;
+      if (f < f1)
+        __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024 + lane * 16, dst + f * 1024, 16,
+                                         0, 0);
     }
   };
   auto fetch_slot = [&](int ci, char* dst) {
-    const char* src = ws_head + size_t(ci) * slot_stride + lane * 16;
+    const char* src = ws_head + size_t(ci) * slot_stride;
     if constexpr (kOut) {
       fetch_range(src, dst, 0, OS::kBlocks);
     } else {
@@ -185,8 +189,13 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) vx[e] = to_f32(raw.v[rb][e]);
       quad_transpose(vx, lane);   // token 16 rb + 4 q4 + e, column 16 w + ln
+      if (L == kChunk && !p_tile) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X0[rb][e] = (16 * rb + 4 * q4 + e < L && !p_tile) ? -vx[e] : 0.f;
+        for (int e = 0; e < 4; ++e) X0[rb][e] = -vx[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X0[rb][e] = (16 * rb + 4 * q4 + e < L && !p_tile) ? -vx[e] : 0.f;
+      }
     }
   };
   if (nchunks > 0) {
@@ -245,7 +254,9 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
 
     // The products run as a fixed sequence of stages (Plan): each stage's fragments are read
     // from LDS two stages ahead of its MFMAs, into three rotating register buffers.
-    constexpr int kAhead = KDA_WALK_AHEAD;   // stages of fragment look-ahead
+    // stages of fragment look-ahead: two with one wave per SIMD; one with two waves per SIMD
+    // (both waves' registers fit the SIMD's file only then)
+    constexpr int kAhead = kTPW == 1 ? 2 : 1;
     V16 fb[kAhead + 1][8];
     auto load_stage = [&](int st, V16* dst) {
 #pragma unroll
@@ -350,14 +361,21 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkParams p) {
   }
 }
 
+template <typename Tout, int DK, int kTPW>
+static hipError_t launch_walk_tpw(const ChunkParams& p, hipStream_t stream) {
+  const dim3 grid((p.n_units + 7) / 8 * 8 * (p.n_vt / kTPW));
+  const dim3 block(256 * kTPW);
+  if (p.mode == kModeTransition)
+    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, false, kTPW>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, true, kTPW>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename Tout, int DK>
 static hipError_t launch_walk(const ChunkParams& p, hipStream_t stream) {
-  const dim3 grid((p.n_units + 7) / 8 * 8 * p.n_vt);
-  if (p.mode == kModeTransition)
-    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, false>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, true>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (p.walk_tpw == 2) return launch_walk_tpw<Tout, DK, 2>(p, stream);
+  return launch_walk_tpw<Tout, DK, 1>(p, stream);
 }
 
 hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream) {
@@ -365,6 +383,7 @@ hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStr
       (long long)p.n_units != (long long)p.n_seqs * p.n_seg * p.H ||
       (!p.cu_seqlens && p.seq_len < 0))
     return hipErrorInvalidValue;
+  if ((p.walk_tpw != 1 && p.walk_tpw != 2) || p.n_vt % p.walk_tpw != 0) return hipErrorInvalidValue;
   switch (p.mode) {
     case kModeWalk:
       if (p.n_seg != 1 || p.n_vt != p.dv / 64 || !p.o) return hipErrorInvalidValue;

@@ -113,3 +113,34 @@ def test_automatic_path_choice():
     if 96 * 2 <= cus:
         assert n_small == kda.chunk_fwd_workspace_size(
             1, 8192, 1, 96, 128, 128, policy=kda.KDA_CHUNK_WS_TWO_PASS) > 0
+
+
+def test_two_tiles_per_workgroup_bit_identical():
+    """With more (sequence, head, tile) units than compute units the walk packs both value
+    tiles of a head into one eight-wave workgroup: still the same bits as the one-launch
+    kernel (3 sequences x 96 heads x 2 tiles = 576 tiles)."""
+    lengths = [200, 64, 130]
+    print(f"case two tiles per workgroup lengths={lengths} H=96", flush=True)
+    inp = wl.prefill_inputs(H=96, dk=128, dv=128, dtype="bf16", seed=55, h0_std=0.02,
+                            lengths=lengths)
+    (o1, h1), (o2, h2) = _both(inp, varlen=True)
+    assert torch.equal(o1, o2)
+    assert torch.equal(h1, h2)
+
+
+def test_segment_walks_two_tiles_per_workgroup_bit_identical():
+    """The segment path's transition walk (96 heads x 2 segments x 4 tiles) and replay walk
+    (x 2 tiles) with eight-wave workgroups, against the one-launch passes."""
+    print("case segment walks with two tiles per workgroup T=256 H=96 n_segments=2", flush=True)
+    inp = wl.prefill_inputs(T=256, H=96, dk=128, dv=128, dtype="bf16", seed=56, h0_std=0.02)
+    d = to_dev(inp)
+    full = kda.segment_cp_workspace_size(1, 256, 1, 96, 128, 128, kda.KDA_BF16, 2)
+    small = kda.segment_cp_workspace_size(1, 256, 1, 96, 128, 128, kda.KDA_F32, 2)
+    res = []
+    for nbytes in (full, small):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        res.append(kda.segment_cp_fwd(*_args(d), h0=d["h0"], n_segments=2, workspace=ws,
+                                      out_dtype=torch.float32))
+        torch.cuda.synchronize()
+    (o1, h1), (o2, h2) = res
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
