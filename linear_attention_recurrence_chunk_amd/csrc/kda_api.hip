@@ -176,18 +176,28 @@ int prep_groups(const int32_t* cu_seqlens_host, int N, int seq_len) {
   return groups < 1 ? 1 : int(groups);
 }
 
-// Automatic segment count of the two-launch segment path (at most kAutoSegments), in units
-// of one walk chunk step: the prep pass is the same for every count; a transition step
-// (no output products) costs ~0.7 of a replay step and a scan step ~1.5.
+// Automatic segment count of the two-launch segment path (at most kAutoSegments): the count
+// minimising a cost in units of one walk chunk step with one state tile per workgroup
+// (~3.7 us on MI355X). The prep pass is the same for every count. A walk runs in rounds of
+// one workgroup per compute unit (its LDS holds two operand slots); a step of a two-tile
+// workgroup costs 1.13 units, a transition step 0.85 of the corresponding output step, and
+// the ordered scan 1.5 units per segment (fitted to measured launch times).
+double walk_cost(int64_t units, int n_vt, int64_t chunks, bool transition, int cus) {
+  const int tpw = (n_vt % 2 == 0 && units * n_vt > int64_t(cus)) ? 2 : 1;
+  const int64_t wgs = units * n_vt / tpw;
+  const double rounds = double((wgs + cus - 1) / cus);
+  return rounds * double(chunks) * (tpw == 2 ? 1.13 : 1.0) * (transition ? 0.85 : 1.0);
+}
+
 int auto_segments_two_pass(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
-  auto rounds = [&](int64_t wgs) { return double((wgs + cus - 1) / cus); };
-  double best = rounds(int64_t(N) * H * (dv / 64)) * double(max_chunks);
+  double best = walk_cost(int64_t(N) * H, dv / 64, max_chunks, false, cus);
   int best_n = 1;
   const int hi = int(max_chunks < kAutoSegments ? max_chunks : kAutoSegments);
   for (int n = 2; n <= hi; ++n) {
-    const double per_seg = double((max_chunks + n - 1) / n);
-    const double cost = rounds(int64_t(N) * n * H * ((dk + dv) / 64)) * per_seg * 0.7 +
-                        1.5 * n + rounds(int64_t(N) * n * H * (dv / 64)) * per_seg;
+    const int64_t per_seg = (max_chunks + n - 1) / n;
+    const int64_t units = int64_t(N) * n * H;
+    const double cost = walk_cost(units, (dk + dv) / 64, per_seg, true, cus) + 1.5 * n +
+                        walk_cost(units, dv / 64, per_seg, false, cus);
     if (cost < best) {
       best = cost;
       best_n = n;
