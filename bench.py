@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 CHUNK = 64
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc")
-KERNEL_SRC = os.path.join(CSRC, "kda_chunk.hip")
+KERNEL_SRC = (os.path.join(CSRC, "kda_chunk.hip"), os.path.join(CSRC, "kda_walk.hip"),
+              os.path.join(CSRC, "kda_chunk_io.h"))
 COUNTERS = os.path.join(ROOT, "profiles", "chunk_two_pass_prefill_8k_counters.txt")
 DECODE_SRC = os.path.join(CSRC, "kda_decode.hip")
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_replay_verify_counters.txt")
@@ -53,9 +54,13 @@ def algorithmic_flops(T, H, dk, dv):
     return T * H * (6 * dk * dv + CHUNK * (3 * dk + 2 * dv))
 
 
-def source_digest(path=KERNEL_SRC):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths=KERNEL_SRC):
+    """sha256 of the kernel source file, or of the concatenated files of a tuple."""
+    h = hashlib.sha256()
+    for path in ((paths,) if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counter_traffic(counters=COUNTERS, source=KERNEL_SRC):
