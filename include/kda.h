@@ -105,13 +105,23 @@ typedef enum kda_dtype {
  * kda_chunk_fwd_workspace_size(..., KDA_CHUNK_WS_TWO_PASS, ...) bytes, be 16-byte aligned and
  * overlap no other argument; its contents on entry are ignored and on return are undefined.
  * KDA_F32 ignores the workspace.
+ *
+ * State checkpoints (prefix-cache resume points; the prefill hands states on to later
+ * requests, "Inférence : cache KV, décodage, quantification", prefill/decode disaggregation):
+ * with ckpt_every > 0 (a multiple of 64) the state after every ckpt_every tokens of each
+ * sequence is written to ckpt_states, fp32 [floor(T_total / ckpt_every), H, d_k, d_v]: the
+ * state after the first (j + 1) * ckpt_every tokens of sequence n (n-th sequence starting at
+ * token bos_n) goes to slot floor(bos_n / ckpt_every) + j. Slots of different sequences never
+ * collide; slots no sequence reaches are left untouched. Passing a checkpoint as h0 for the
+ * rest of its sequence reproduces the rest of the original call's o and ht bit for bit.
+ * ckpt_every = 0 writes none (ckpt_states may be NULL).
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
                   const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                   int num_heads, int d_k, int d_v, int io_dtype, int out_dtype, float scale,
-                  float g_min, void* o, float* ht, void* workspace, size_t workspace_bytes,
-                  void* stream);
+                  float g_min, void* o, float* ht, int ckpt_every, float* ckpt_states,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Policies of kda_chunk_fwd_workspace_size. */
 #define KDA_CHUNK_WS_AUTO 0     /* size of the path the library recommends: 0 when one launch */

@@ -53,8 +53,8 @@ def library():
                            "`python -m linear_attention_recurrence_chunk_amd.build`")
     lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, P,
-                                  ctypes.c_size_t, P]
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, I,
+                                  P, P, ctypes.c_size_t, P]
     lib.kda_chunk_fwd.restype = I
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
@@ -191,13 +191,17 @@ def chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF1
 
 
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0, o=None,
-              ht=None, output_final_state=True, out_dtype=None, workspace="auto", stream=None):
+              ht=None, output_final_state=True, out_dtype=None, workspace="auto", ckpt_every=0,
+              ckpt=None, stream=None):
     """kda_chunk_fwd. q, k: [B, T, H, d_k] or packed [T, H, d_k]; v: [.., d_v];
     g: same shape as k (fp32); beta: [.., H] (fp32); h0: [N, H, d_k, d_v] fp32 or None;
     cu_seqlens: [N + 1] int32 (any device) for packed varlen input; out_dtype: None (same as
     q) or torch.float32. workspace: "auto" (the library's recommended path, allocating the
     workspace it asks for), None (one launch), "two_pass" (two launches whatever the shape)
-    or a uint8 device tensor (two launches). Returns (o, ht)."""
+    or a uint8 device tensor (two launches). ckpt_every > 0 (a multiple of 64) also returns
+    the states after every ckpt_every tokens of each sequence, [T // ckpt_every, H, d_k, d_v]
+    fp32 (slot floor(bos_n / ckpt_every) + j for sequence n): (o, ht, ckpt). Returns (o, ht)
+    otherwise."""
     a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
     T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
     if isinstance(workspace, str):
@@ -208,13 +212,21 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
                                         a["dv"], a["io"], policy)
         workspace = (_torch().empty(need, dtype=_torch().uint8, device=q.device)
                      if need > 0 else None)
+    if ckpt_every and ckpt is None:
+        total = a["batch"] * T_arg if a["cu_dev"] is None else T_arg
+        ckpt = _torch().empty(total // ckpt_every, a["H"], a["dk"], a["dv"],
+                              dtype=_torch().float32, device=q.device)
+    _check(ckpt, "ckpt", _torch().float32, q.device)
     st = library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
         _cu_host_ptr(a["cu_host"]), a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
         a["io"], a["out"], float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]),
+        int(ckpt_every), _ptr(ckpt) if ckpt_every else None,
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
+    if ckpt_every:
+        return a["o"], a["ht"], ckpt
     return a["o"], a["ht"]
 
 

@@ -282,14 +282,32 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
                   const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                   int num_heads, int d_k, int d_v, int io_dtype, int out_dtype, float scale,
-                  float g_min, void* o, float* ht, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  float g_min, void* o, float* ht, int ckpt_every, float* ckpt_states,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   int N = 0;
   int64_t T = 0;
   const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
                                   seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
                                   g_min, o, ht, &N, &T);
   if (st != KDA_OK) return st;
+  if (ckpt_every < 0 || ckpt_every % 64 != 0) return KDA_ERR_BAD_SHAPE;
+  if (ckpt_every > 0 && T / ckpt_every == 0) ckpt_every = 0;   // no sequence reaches a slot
+  if (ckpt_every > 0) {
+    if (!ckpt_states) return KDA_ERR_NULL_ARG;
+    if (!aligned16(ckpt_states)) return KDA_ERR_MISALIGNED;
+    const size_t es = dsize(io_dtype);
+    const Range rc = range_of(ckpt_states, size_t(T / ckpt_every) * num_heads * d_k * d_v * 4);
+    const Range all[] = {
+        range_of(q, size_t(T) * num_heads * d_k * es), range_of(k, size_t(T) * num_heads * d_k * es),
+        range_of(v, size_t(T) * num_heads * d_v * es), range_of(g, size_t(T) * num_heads * d_k * 4),
+        range_of(beta, size_t(T) * num_heads * 4),
+        range_of(h0, h0 ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
+        range_of(o, size_t(T) * num_heads * d_v * dsize(out_dtype)),
+        range_of(ht, ht ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
+        range_of(workspace, workspace ? workspace_bytes : 0)};
+    for (Range x : all)
+      if (overlaps(rc, x)) return KDA_ERR_ALIASING;
+  }
   const bool two_pass = workspace != nullptr && io_dtype == KDA_BF16;
   size_t need = 0;
   if (two_pass) {
@@ -321,6 +339,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   p.n_units = N * num_heads;
   p.scale = scale;
   p.g_min = g_min;
+  p.ckpt = ckpt_every > 0 ? ckpt_states : nullptr;
+  p.ckpt_every = ckpt_every > 0 ? ckpt_every : 64;
   if (two_pass) {
     p.mode = kda::kModeWalk;
     p.ws_ops = static_cast<char*>(workspace);

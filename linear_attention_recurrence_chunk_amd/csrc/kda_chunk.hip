@@ -851,6 +851,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     }
+    if constexpr (!kPrep)
+      if (mode == kModeForward)
+        write_checkpoint<DK, NTD>(p, S, seq_bos, cstart + Lc, Lc, h, col0, q4, ln);
     __syncthreads();
 #undef KDA_PREFETCH
   }
@@ -899,6 +902,7 @@ hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
   prep.h0 = nullptr;
   prep.ws_pq = nullptr;
   prep.ws_sin = nullptr;
+  prep.ckpt = nullptr;
   const dim3 grid((prep.n_units + 7) / 8 * 8);
   if (dk == 128)
     hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true>), grid,

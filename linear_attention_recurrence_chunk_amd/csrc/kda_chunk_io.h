@@ -159,4 +159,21 @@ struct OpSlot {
   static constexpr __host__ __device__ int tri(int rb, int pp) { return (rb == 3 ? 4 : rb) + pp; }
 };
 
+// Checkpoint of the state after a full chunk that ends a multiple of p.ckpt_every tokens into
+// its sequence (forward mode; seq_bos is the sequence's first token). S holds this wave's 16
+// columns (from col0) in MFMA accumulator layout.
+template <int DK, int NTD>
+__device__ __forceinline__ void write_checkpoint(const ChunkParams& p, const f32x4 (&S)[NTD],
+                                                 int seq_bos, int cend, int Lc, int h, int col0,
+                                                 int q4, int ln) {
+  const int done = cend - seq_bos;   // tokens of the sequence processed so far
+  if (!p.ckpt || Lc != kChunk || done % p.ckpt_every != 0) return;
+  const size_t slot = size_t(seq_bos / p.ckpt_every + done / p.ckpt_every - 1);
+  float* dst = p.ckpt + (slot * p.H + h) * size_t(DK) * p.dv + col0 + ln;
+#pragma unroll
+  for (int t = 0; t < NTD; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[size_t(16 * t + 4 * q4 + e) * p.dv] = S[t][e];
+}
+
 }  // namespace kda

@@ -42,6 +42,11 @@ struct ChunkParams {
   float* ws_sin;            // replay: [N, n_seg, H, dk, dv] entering states
   char* ws_ops;             // prep / walk: operand slots [chunk slot][H] (see op_slot_count)
   int walk_tpw;             // walk: state tiles per workgroup, 1 or 2 (2 needs n_vt even)
+  // forward / walk mode: states at every ckpt_every tokens of each sequence (a multiple of
+  // 64; 0 for none). The state after token bos_n + (j + 1) ckpt_every - 1 of sequence n goes
+  // to [floor(bos_n / ckpt_every) + j, H, dk, dv] of ckpt.
+  float* ckpt;
+  int ckpt_every;
   float scale;
   float g_min;
 };

@@ -340,6 +340,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
         for (int q = 0; q < NT; ++q) Pol::from_acc_split_r(U, q, Uh[q], Ul[q]);
       }
     });
+    if (mode == kModeWalk) write_checkpoint<DK, NTD>(p, S, bos, cstart + Lc, Lc, h, col0, q4, ln);
     if (more) {
       // the next slot (and values) must have landed before any wave reads them; this
       // chunk's output stores are issued after the wait, so it never waits on them

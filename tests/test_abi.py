@@ -62,7 +62,8 @@ def chunk(q=True, k=True, v=True, g=True, beta=True, h0=None, cu=None, cu_host=N
     return kda.library().kda_chunk_fwd(
         args["q"], args["k"], args["v"], args["g"], args["beta"], args["h0"], args["cu"],
         args["cu_host"], batch, seq_len, n_seqs, H, dk, dv, io, io if out is None else out,
-        scale, g_min, args["o"], args["ht"], args.get("ws"), args.get("ws_bytes", 0), None)
+        scale, g_min, args["o"], args["ht"], args.get("ckpt_every", 0), args.get("ckpt"),
+        args.get("ws"), args.get("ws_bytes", 0), None)
 
 
 def host_cu(vals):
@@ -152,6 +153,17 @@ def test_chunk_workspace_checks():
     assert chunk(override=dict(ws=ctypes.c_void_p(P[5].value - 1024), ws_bytes=need)) == ALIAS
     # an fp32 call ignores the workspace, as documented
     assert chunk(io=F32, dk=64, dv=64, q=False, override=dict(ws=ws, ws_bytes=0)) == NULL
+
+
+def test_chunk_checkpoint_checks():
+    P = ptrs()
+    ck = ctypes.c_void_p(BASE + 30 * 64 * GiB)
+    assert chunk(override=dict(ckpt_every=100, ckpt=ck)) == SHAPE        # not a multiple of 64
+    assert chunk(override=dict(ckpt_every=-64, ckpt=ck)) == SHAPE
+    assert chunk(override=dict(ckpt_every=128, ckpt=None)) == NULL
+    assert chunk(override=dict(ckpt_every=128, ckpt=ctypes.c_void_p(ck.value + 4))) == ALIGN
+    assert chunk(override=dict(ckpt_every=128, ckpt=P[3])) == ALIAS       # on top of g
+    assert chunk(override=dict(ckpt_every=128, ckpt=ctypes.c_void_p(P[5].value + 64))) == ALIAS
 
 
 def test_segment_workspace_size():
