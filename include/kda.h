@@ -208,8 +208,10 @@ typedef struct kda_token_window {
  *   2. state_acc[r, h] <- S (skipped when state_acc is NULL);
  *   3. slot 0 of `cur` (the bonus token), output o[r, 0, h]; state[r, h] <- S and
  *      conv_tail[r, h] <- tail (the new committed values);
- *   4. slots 1 .. n_new - 1 of `cur` (the next draft window), outputs o[r, j, h]; their
- *      states are never written.
+ *   4. slots 1 .. n_r - 1 of `cur` (the next draft window), outputs o[r, j, h]; their
+ *      states are never written. n_r = n_new, or n_new_per_request[r] clamped to
+ *      [1, n_new] when that array is given (irregular batches: requests whose draft windows
+ *      differ in length; rows j >= n_r of o[r] are left untouched).
  * Each token: depthwise causal convolution of width conv_width over the raw q, k, v
  * channels with the tail of the last conv_width - 1 raw inputs; SiLU if act == 1;
  * q and k scaled by 1 / sqrt(sum x^2 + eps_l2); beta = sigmoid; g = max(-softplus, g_min);
@@ -218,6 +220,7 @@ typedef struct kda_token_window {
  * replayed state is bit-identical to the state the same tokens reach one launch at a time.
  *
  *   n_acc      [R] int32 device, clamped to [0, prev->slots - 1]
+ *   n_new_per_request  [R] int32 device or NULL (all requests take n_new tokens)
  *   conv_w     [H, 2 d_k + d_v, conv_width] fp32, channel order q, k, v; tap conv_width - 1
  *              multiplies the current token
  *   norm_w     [d_v] fp32, shared by all heads
@@ -232,7 +235,8 @@ typedef struct kda_token_window {
  * prev->slots in 1..16, act in {0, 1}, eps_l2 > 0, eps_rms >= 0.
  */
 int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_width,
-                      int n_new, const int32_t* n_acc, const kda_token_window* prev,
+                      int n_new, const int32_t* n_acc, const int32_t* n_new_per_request,
+                      const kda_token_window* prev,
                       const kda_token_window* cur, const float* conv_w, const float* norm_w,
                       float scale, float g_min, float eps_l2, float eps_rms, int act,
                       float* state, float* state_acc, float* conv_tail, void* o,

@@ -65,7 +65,7 @@ def library():
     lib.kda_segment_cp_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P,
                                        P, I, P, ctypes.c_size_t, P]
     lib.kda_segment_cp_fwd.restype = I
-    lib.kda_decode_replay.argtypes = [I, I, I, I, I, I, P, ctypes.POINTER(TokenWindow),
+    lib.kda_decode_replay.argtypes = [I, I, I, I, I, I, P, P, ctypes.POINTER(TokenWindow),
                                       ctypes.POINTER(TokenWindow), P, P, F, F, F, F, I, P, P, P,
                                       P, I, P]
     lib.kda_decode_replay.restype = I
@@ -272,10 +272,12 @@ def _window(win, slots):
 
 def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None, scale=1.0,
                   g_min=-5.0, eps_l2=1e-6, eps_rms=1e-6, act=1, state_acc=None, o=None,
-                  write_state_acc=True, out_dtype=None, stream=None):
+                  write_state_acc=True, out_dtype=None, n_new_per_request=None, stream=None):
     """kda_decode_replay. ``state`` [R, H, d_k, d_v] and ``conv_tail`` are updated in place;
     prev / new are dicts of bf16 tensors q, k, v, g, beta (and z for new), each
     [R, slots, H, ...]. out_dtype: None (bf16) or torch.float32.
+    n_new_per_request: optional [R] int32 device tensor of new tokens per request (clamped
+    to [1, n_new]; rows past a request's count are left untouched).
     Returns (o [R, n_new, H, d_v], state_acc or None)."""
     torch = _torch()
     R, H, dk, dv = state.shape
@@ -288,6 +290,7 @@ def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None
     _check(conv_w, "conv_w", torch.float32, dev)
     _check(norm_w, "norm_w", torch.float32, dev)
     _check(n_acc, "n_acc", torch.int32, dev)
+    _check(n_new_per_request, "n_new_per_request", torch.int32, dev)
     for win, nm in ((prev, "prev"), (new, "new")):
         for key in ("q", "k", "v", "g", "beta", "z"):
             if win.get(key) is not None:
@@ -304,7 +307,8 @@ def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, n_new=None
     pw = _window(prev, prev["q"].shape[1])
     nw = _window(new, new["q"].shape[1])
     st = library().kda_decode_replay(
-        R, H, dk, dv, conv_width, int(n_new), _ptr(n_acc), ctypes.byref(pw), ctypes.byref(nw),
+        R, H, dk, dv, conv_width, int(n_new), _ptr(n_acc), _ptr(n_new_per_request),
+        ctypes.byref(pw), ctypes.byref(nw),
         _ptr(conv_w), _ptr(norm_w), float(scale), float(g_min), float(eps_l2), float(eps_rms),
         int(act), _ptr(state), _ptr(state_acc),
         _ptr(conv_tail) if conv_tail.numel() else None, _ptr(o), _io_dtype(o), _stream(stream))

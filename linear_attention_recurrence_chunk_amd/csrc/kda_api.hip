@@ -479,7 +479,8 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
 }
 
 int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_width,
-                      int n_new, const int32_t* n_acc, const kda_token_window* prev,
+                      int n_new, const int32_t* n_acc, const int32_t* n_new_per_request,
+                      const kda_token_window* prev,
                       const kda_token_window* cur, const float* conv_w, const float* norm_w,
                       float scale, float g_min, float eps_l2, float eps_rms, int act,
                       float* state, float* state_acc, float* conv_tail, void* o,
@@ -500,7 +501,8 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
   if (!isfinite(scale) || !isfinite(g_min) || g_min > 0.f || !(eps_l2 > 0.f) ||
       !(eps_rms >= 0.f) || !isfinite(eps_l2) || !isfinite(eps_rms))
     return KDA_ERR_BAD_VALUE;
-  const void* ptrs[] = {n_acc,    prev->q, prev->k, prev->v, prev->g, prev->beta, cur->q,
+  const void* ptrs[] = {n_acc, n_new_per_request, prev->q, prev->k, prev->v, prev->g,
+                        prev->beta, cur->q,
                         cur->k,   cur->v,  cur->g,  cur->beta, cur->z, conv_w,   norm_w,
                         state,    state_acc, conv_tail, o};
   for (const void* ptr : ptrs)
@@ -512,7 +514,7 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
   const Range rtail = range_of(conv_tail, R * H * C3 * size_t(conv_width - 1) * 4);
   const Range ro = range_of(o, R * size_t(n_new) * H * D * dsize(out_dtype));
   const Range ins[] = {
-      range_of(n_acc, R * 4),
+      range_of(n_acc, R * 4), range_of(n_new_per_request, n_new_per_request ? R * 4 : 0),
       range_of(prev->q, R * prev->slots * H * D * 2), range_of(prev->k, R * prev->slots * H * D * 2),
       range_of(prev->v, R * prev->slots * H * D * 2), range_of(prev->g, R * prev->slots * H * D * 2),
       range_of(prev->beta, R * prev->slots * H * 2),
@@ -538,6 +540,7 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
   p.cur_slots = cur->slots;
   p.act = act;
   p.n_acc = n_acc;
+  p.n_new_r = n_new_per_request;
   p.prev_q = static_cast<const __bf16*>(prev->q);
   p.prev_k = static_cast<const __bf16*>(prev->k);
   p.prev_v = static_cast<const __bf16*>(prev->v);

@@ -9,6 +9,7 @@ namespace kda {
 struct DecodeParams {
   int R, H, D, conv_width, n_new, prev_slots, cur_slots, act;
   const int32_t* n_acc;     // [R]
+  const int32_t* n_new_r;   // [R] new tokens per request (clamped to [1, n_new]) or null
   const __bf16* prev_q;     // [R, prev_slots, H, D] ...
   const __bf16* prev_k;
   const __bf16* prev_v;
@@ -25,7 +26,7 @@ struct DecodeParams {
   float* state;             // [R, H, D, D] in: committed, out: after the bonus token
   float* state_acc;         // [R, H, D, D] or null
   float* conv_tail;         // [R, H, 3D, W - 1]
-  void* o;                  // [R, n_new, H, D] bf16 or fp32
+  void* o;                  // [R, n_new, H, D] bf16 or fp32 (n_new: the most per request)
   int out_f32;
   float scale, decay_floor, eps_l2, eps_rms;
 };

@@ -78,7 +78,12 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
   // the recurrence, after the block's input stage).
   int n_acc = p.n_acc[r];
   n_acc = n_acc < 0 ? 0 : (n_acc > p.prev_slots - 1 ? p.prev_slots - 1 : n_acc);
-  const int n_tok = n_acc + p.n_new;
+  int n_new = p.n_new;
+  if (p.n_new_r) {
+    n_new = p.n_new_r[r];
+    n_new = n_new < 1 ? 1 : (n_new > p.n_new ? p.n_new : n_new);
+  }
+  const int n_tok = n_acc + n_new;
 
   // ---- input-stage role (whole waves): threads [0, D) own q and k channel tid; [D, 2D) own
   // v, g and z channel tid - D. Each keeps the causal-convolution tail of its channels in

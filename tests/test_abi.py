@@ -218,7 +218,8 @@ def decode(R=4, H=2, D=128, W=4, n_new=8, prev=None, cur=None, act=1, g_min=-5.0
     prev = prev if prev is not None else window(8, with_z=False)
     cur = cur if cur is not None else window(8, base=10)
     return kda.library().kda_decode_replay(
-        R, H, D, D, W, n_new, a["n_acc"], ctypes.byref(prev), ctypes.byref(cur), a["conv_w"],
+        R, H, D, D, W, n_new, a["n_acc"], a.get("n_new_r"), ctypes.byref(prev), ctypes.byref(cur),
+        a["conv_w"],
         a["norm_w"], 1.0, g_min, eps_l2, eps_rms, act, a["state"], a["state_acc"], a["tail"],
         a["o"], out, None)
 
@@ -239,6 +240,9 @@ def test_decode_checks():
     assert decode(override={"o": ctypes.c_void_p(BASE + (40 + 6) * 64 * GiB + 2)}) == ALIGN
     same = ctypes.c_void_p(BASE + 43 * 64 * GiB)
     assert decode(override={"state_acc": same}) == ALIAS        # state_acc on top of state
+    # per-request new-token counts: aligned, and never written over by an output
+    assert decode(override={"n_new_r": ctypes.c_void_p(BASE + 50 * 64 * GiB + 4)}) == ALIGN
+    assert decode(override={"n_new_r": ctypes.c_void_p(BASE + (40 + 6) * 64 * GiB)}) == ALIAS
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

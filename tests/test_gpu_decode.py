@@ -137,3 +137,40 @@ def test_decode_bf16_output_is_rounded_fp32_output():
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o32.to(torch.bfloat16), o16)
     assert torch.equal(s32, s16) and torch.equal(a32, a16) and torch.equal(t32, t16)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_irregular_draft_windows(D):
+    """Requests with different new-token counts in one launch: each request's outputs match
+    the oracle run over its own window, rows past its count stay untouched, and the
+    committed states equal those of the uniform launch bit for bit (they only depend on the
+    accepted drafts and the bonus token)."""
+    R, H = 6, 3
+    w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=4, n_new=8, window=8, seed=70 + D)
+    nn = torch.tensor([1, 8, 3, 5, 2, 7], dtype=torch.int32)
+    print(f"case irregular windows D={D} n_acc={w.n_acc.tolist()} n_new={nn.tolist()}",
+          flush=True)
+    state, tail = w.state.cuda().clone(), w.conv_tail.cuda().clone()
+    o = torch.full((R, 8, H, D), float("nan"), device="cuda")
+    _, acc = kda.decode_replay(state, tail, w.n_acc.cuda(), _dev_window(w.prev),
+                               _dev_window(w.new), w.conv_w.cuda(), w.norm_w.cuda(), o=o,
+                               n_new_per_request=nn.cuda())
+    torch.cuda.synchronize()
+    o_u, state_u, acc_u, tail_u = _run_gpu(w)
+    assert torch.equal(state, state_u) and torch.equal(acc, acc_u) and torch.equal(tail, tail_u)
+    for r in range(R):
+        k = int(nn[r])
+        assert torch.equal(o[r, :k], o_u[r, :k])
+        assert torch.isnan(o[r, k:]).all()
+        ref = ko.decode_replay(np64(w.state[r:r + 1]), np64(w.conv_tail[r:r + 1]),
+                               w.n_acc[r:r + 1].numpy(),
+                               {x: (np64(v[r:r + 1]) if v is not None else None)
+                                for x, v in w.prev.items()},
+                               {x: (np64(v[r:r + 1, :k]) if v is not None else None)
+                                for x, v in w.new.items()},
+                               np64(w.conv_w), np64(w.norm_w))
+        e_o = rel_max_err(np64(o[r:r + 1, :k]), ref["o"])
+        e_s = np.abs(np64(state[r:r + 1]) - ref["state"]).max()
+        print(f"request {r} (n_acc {int(w.n_acc[r])}, n_new {k}): err_o={e_o:.2e} "
+              f"err_state={e_s:.2e}")
+        assert e_o <= TOL_BF16 and e_s <= STATE_TOL
