@@ -101,10 +101,13 @@ typedef enum kda_dtype {
  * describes in section 5: (1) the prologue of every (chunk, head) runs in parallel over the
  * whole device and stores the serial step's operands (about 73 KiB per chunk and head at
  * d_k = 128) in the workspace; (2) the serial walk per (sequence, head, state tile) reads
- * them back. Both paths give bit-identical o and ht. The workspace must hold at least
- * kda_chunk_fwd_workspace_size(..., KDA_CHUNK_WS_TWO_PASS, ...) bytes, be 16-byte aligned and
- * overlap no other argument; its contents on entry are ignored and on return are undefined.
- * KDA_F32 ignores the workspace.
+ * them back. Both paths give bit-identical o and ht. A workspace of at least
+ * kda_chunk_fwd_workspace_size(..., KDA_CHUNK_WS_TWO_PASS, ...) bytes takes the whole batch
+ * in one prep and one walk; a smaller one (at least the KDA_CHUNK_WS_MIN size: the longest
+ * sequence's slots) takes consecutive groups of whole sequences that fit, two launches per
+ * group, with the same results. The workspace must be 16-byte aligned and overlap no other
+ * argument; its contents on entry are ignored and on return are undefined. KDA_F32 ignores
+ * the workspace.
  *
  * State checkpoints (prefix-cache resume points; the prefill hands states on to later
  * requests, "Inférence : cache KV, décodage, quantification", prefill/decode disaggregation):
@@ -124,18 +127,24 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Policies of kda_chunk_fwd_workspace_size. */
-#define KDA_CHUNK_WS_AUTO 0     /* size of the path the library recommends: 0 when one launch */
-#define KDA_CHUNK_WS_TWO_PASS 1 /* size the two-launch path needs, whatever the shape */
+#define KDA_CHUNK_WS_AUTO 0     /* size of the path the library recommends (0: one launch) */
+#define KDA_CHUNK_WS_TWO_PASS 1 /* the whole batch in one prep and one walk */
+#define KDA_CHUNK_WS_MIN 2      /* the least the two-launch path accepts (longest sequence) */
 
 /*
- * Bytes of workspace kda_chunk_fwd uses for the given sizes (same batch / seq_len / n_seqs
- * conventions as kda_chunk_fwd: seq_len is T_total when sequences are packed). With
- * KDA_CHUNK_WS_AUTO it returns 0 when one launch is expected to be faster: a KDA_F32 call, or
- * enough (sequence, head, state tile) workgroups to fill every compute unit of the current
- * device, where the one-launch path keeps HBM traffic at the algorithmic bytes. Otherwise it
- * returns the two-launch size: (T_total / 64 + N + 1) chunk slots x num_heads x the slot size.
+ * Bytes of workspace kda_chunk_fwd uses for the given sizes (same batch / seq_len / n_seqs /
+ * cu_seqlens_host conventions as kda_chunk_fwd; cu_seqlens_host may be NULL, then packed
+ * sequences are sized as if one of them held every token). Slots: a batch or group of
+ * sequences with T tokens and N sequences needs (T / 64 + N + 1) x num_heads slots of
+ * 74,752 B (d_k = 128) or 50,176 B (d_k = 64). 0 for KDA_F32 and unsupported widths.
+ * KDA_CHUNK_WS_AUTO returns the whole-batch size while the one-launch workgroups
+ * (sequences x heads x d_v / 64) do not exceed the current device's compute units (the
+ * prologue then sits on every serial chain); beyond that, min(whole batch, max(8 GiB, longest
+ * sequence)): groups of sequences, which measured faster than one launch on a 64-sequence
+ * varlen batch as well.
  */
-int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
+                                 const int32_t* cu_seqlens_host, int num_heads, int d_k,
                                  int d_v, int io_dtype, int policy, size_t* bytes);
 
 /*

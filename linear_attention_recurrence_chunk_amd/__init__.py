@@ -24,6 +24,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_CHUNK_WS_AUTO = 0
 KDA_CHUNK_WS_TWO_PASS = 1
+KDA_CHUNK_WS_MIN = 2
 
 
 class KDAError(RuntimeError):
@@ -56,7 +57,7 @@ def library():
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, I,
                                   P, P, ctypes.c_size_t, P]
     lib.kda_chunk_fwd.restype = I
-    lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, P, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_workspace_size.restype = I
     lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
@@ -178,13 +179,17 @@ def _cu_host_ptr(cu_host):
 
 # ------------------------------------------------------------------------------ entry points
 def chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF16,
-                             policy=KDA_CHUNK_WS_AUTO):
+                             policy=KDA_CHUNK_WS_AUTO, cu_seqlens_host=None):
     """kda_chunk_fwd_workspace_size: bytes of workspace for the two-launch path (0 under the
-    automatic policy when one launch is recommended)."""
+    automatic policy when one launch is recommended). cu_seqlens_host: optional int32 CPU
+    tensor of packed-sequence offsets."""
+    cu = None
+    if cu_seqlens_host is not None:
+        cu = cu_seqlens_host.detach().to("cpu", _torch().int32).contiguous()
     out = ctypes.c_size_t(0)
-    st = library().kda_chunk_fwd_workspace_size(int(batch), int(seq_len), int(n_seqs), int(H),
-                                                int(dk), int(dv), int(io_dtype), int(policy),
-                                                ctypes.byref(out))
+    st = library().kda_chunk_fwd_workspace_size(int(batch), int(seq_len), int(n_seqs),
+                                                _cu_host_ptr(cu), int(H), int(dk), int(dv),
+                                                int(io_dtype), int(policy), ctypes.byref(out))
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd_workspace_size")
     return int(out.value)
@@ -197,19 +202,21 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     g: same shape as k (fp32); beta: [.., H] (fp32); h0: [N, H, d_k, d_v] fp32 or None;
     cu_seqlens: [N + 1] int32 (any device) for packed varlen input; out_dtype: None (same as
     q) or torch.float32. workspace: "auto" (the library's recommended path, allocating the
-    workspace it asks for), None (one launch), "two_pass" (two launches whatever the shape)
-    or a uint8 device tensor (two launches). ckpt_every > 0 (a multiple of 64) also returns
+    workspace it asks for), None (one launch), "two_pass" (two launches over the whole batch),
+    "min" (two launches per group of sequences, the smallest workspace) or a uint8 device
+    tensor (two launches, grouped when it is smaller than the whole batch needs). ckpt_every > 0 (a multiple of 64) also returns
     the states after every ckpt_every tokens of each sequence, [T // ckpt_every, H, d_k, d_v]
     fp32 (slot floor(bos_n / ckpt_every) + j for sequence n): (o, ht, ckpt). Returns (o, ht)
     otherwise."""
     a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
     T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
     if isinstance(workspace, str):
-        if workspace not in ("auto", "two_pass"):
+        policies = {"auto": KDA_CHUNK_WS_AUTO, "two_pass": KDA_CHUNK_WS_TWO_PASS,
+                    "min": KDA_CHUNK_WS_MIN}
+        if workspace not in policies:
             raise ValueError(f"unknown workspace policy {workspace!r}")
-        policy = KDA_CHUNK_WS_AUTO if workspace == "auto" else KDA_CHUNK_WS_TWO_PASS
         need = chunk_fwd_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"],
-                                        a["dv"], a["io"], policy)
+                                        a["dv"], a["io"], policies[workspace], a["cu_host"])
         workspace = (_torch().empty(need, dtype=_torch().uint8, device=q.device)
                      if need > 0 else None)
     if ckpt_every and ckpt is None:

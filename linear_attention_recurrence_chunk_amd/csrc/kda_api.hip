@@ -147,6 +147,8 @@ int auto_segments(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
 // Two-pass prefill: chunks per workgroup of the prep pass (its loop prefetches each chunk's
 // inputs during the previous one)
 constexpr int kPrepChunks = 8;
+// workspace the automatic policy asks for when the batch runs in groups of sequences
+constexpr size_t kGroupedWorkspace = size_t(8) << 30;
 
 size_t two_pass_workspace_bytes(int64_t T, int64_t N, int H, int dk) {
   return size_t(kda::op_slot_count(T, N)) * size_t(H) * kda::op_slot_bytes(dk);
@@ -261,20 +263,40 @@ const char* kda_status_string(int status) {
   }
 }
 
-int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
-                                 int d_v, int io_dtype, int policy, size_t* bytes) {
+int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
+                                 const int32_t* cu_seqlens_host, int num_heads, int d_k, int d_v,
+                                 int io_dtype, int policy, size_t* bytes) {
   if (!bytes) return KDA_ERR_NULL_ARG;
   if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
-  if (policy != KDA_CHUNK_WS_AUTO && policy != KDA_CHUNK_WS_TWO_PASS) return KDA_ERR_BAD_VALUE;
+  if (policy != KDA_CHUNK_WS_AUTO && policy != KDA_CHUNK_WS_TWO_PASS &&
+      policy != KDA_CHUNK_WS_MIN)
+    return KDA_ERR_BAD_VALUE;
   if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
     return KDA_ERR_BAD_SHAPE;
   *bytes = 0;
   if (io_dtype != KDA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_OK;
   // packed sequences: batch 1, seq_len = T_total; otherwise n_seqs = batch
-  const int64_t T = batch == 1 && n_seqs != 1 ? int64_t(seq_len) : int64_t(batch) * seq_len;
-  const int64_t N = batch == 1 && n_seqs != 1 ? n_seqs : batch;
-  if (policy == KDA_CHUNK_WS_AUTO && two_pass_wanted(N, num_heads, d_v) == false) return KDA_OK;
-  *bytes = two_pass_workspace_bytes(T, N, num_heads, d_k);
+  const bool packed = cu_seqlens_host || (batch == 1 && n_seqs != 1);
+  const int64_t T = packed ? int64_t(seq_len) : int64_t(batch) * seq_len;
+  const int64_t N = packed ? n_seqs : batch;
+  const size_t full = two_pass_workspace_bytes(T, N, num_heads, d_k);
+  // the largest single sequence (a group needs at least that); without the offsets of packed
+  // sequences, the whole token count
+  const int64_t longest = packed ? (cu_seqlens_host ? max_seq_len(cu_seqlens_host, int(N), 0) : T)
+                                 : int64_t(seq_len);
+  const size_t one = two_pass_workspace_bytes(longest, 1, num_heads, d_k);
+  if (policy == KDA_CHUNK_WS_TWO_PASS) {
+    *bytes = full;
+  } else if (policy == KDA_CHUNK_WS_MIN) {
+    *bytes = one < full ? one : full;
+  } else if (two_pass_wanted(N, num_heads, d_v)) {
+    *bytes = full;
+  } else {
+    // enough (sequence, head, tile) units to fill the device: groups of sequences through a
+    // workspace of at most kGroupedWorkspace bytes (at least the longest sequence's need)
+    size_t cap = kGroupedWorkspace > one ? kGroupedWorkspace : one;
+    *bytes = cap < full ? cap : full;
+  }
   return KDA_OK;
 }
 
@@ -311,11 +333,16 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   const bool two_pass = workspace != nullptr && io_dtype == KDA_BF16;
   size_t need = 0;
   if (two_pass) {
+    // the whole batch at once, or groups of whole sequences; a group needs at least the
+    // longest sequence's slots
     need = two_pass_workspace_bytes(T, N, num_heads, d_k);
+    const size_t need_min =
+        two_pass_workspace_bytes(max_seq_len(cu_seqlens_host, N, seq_len), 1, num_heads, d_k);
     if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
-    if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
-    const int rc = check_workspace_aliasing(workspace, need, q, k, v, g, beta, h0, o, ht, T, N,
-                                            num_heads, d_k, d_v, io_dtype, out_dtype);
+    if (workspace_bytes < (need_min < need ? need_min : need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    const int rc = check_workspace_aliasing(workspace, workspace_bytes < need ? workspace_bytes : need,
+                                            q, k, v, g, beta, h0, o, ht, T, N, num_heads, d_k, d_v,
+                                            io_dtype, out_dtype);
     if (rc != KDA_OK) return rc;
   }
   if (N == 0) return KDA_OK;
@@ -345,11 +372,31 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
     p.mode = kda::kModeWalk;
     p.ws_ops = static_cast<char*>(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int rc = launch_status(
-        kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s));
-    if (rc != KDA_OK) return rc;
-    p.walk_tpw = walk_tiles_per_wg(p.n_units, p.n_vt);
-    return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s));
+    // consecutive groups of whole sequences whose slots fit the workspace (one group when it
+    // holds the whole batch); sequences are independent, so nothing passes between groups
+    auto first_tok = [&](int n) -> int64_t {
+      return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
+    };
+    for (int n0 = 0; n0 < N;) {
+      int n1 = n0 + 1;
+      while (n1 < N && two_pass_workspace_bytes(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0,
+                                                num_heads, d_k) <= workspace_bytes)
+        ++n1;
+      kda::ChunkParams gp = p;
+      gp.seq0 = n0;
+      gp.slot_tok0 = int(first_tok(n0));
+      gp.n_seqs = n1 - n0;
+      gp.n_units = (n1 - n0) * num_heads;
+      const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
+      int rc = launch_status(
+          kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s));
+      if (rc != KDA_OK) return rc;
+      gp.walk_tpw = walk_tiles_per_wg(gp.n_units, gp.n_vt);
+      rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s));
+      if (rc != KDA_OK) return rc;
+      n0 = n1;
+    }
+    return KDA_OK;
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int DV = p.dv;
   const int h = unit % H;
   const int sj = unit / H;              // global segment index n * n_seg + j
-  const int n = sj / p.n_seg;
+  const int n = p.seq0 + sj / p.n_seg;
   const int j = sj % p.n_seg;
   const int mode = p.mode;
 
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     eos = bos + p.seq_len;
   }
   // operand slot of the sequence's first chunk (prep pass)
-  const long long seq_slot0 = (long long)(bos >> 6) + n;
+  const long long seq_slot0 = (long long)((bos - p.slot_tok0) >> 6) + (n - p.seq0);
   const int seq_bos = bos;
   if (p.n_seg > 1) {
     // chunk-aligned contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg)

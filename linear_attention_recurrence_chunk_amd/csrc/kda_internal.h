@@ -47,6 +47,12 @@ struct ChunkParams {
   // to [floor(bos_n / ckpt_every) + j, H, dk, dv] of ckpt.
   float* ckpt;
   int ckpt_every;
+  // a group of whole sequences (two-launch prefill with a workspace smaller than the whole
+  // batch needs): unit sequence index n runs sequence seq0 + n, and operand slots count from
+  // token slot_tok0 (the group's first token): chunk c of sequence m (first token bos_m) uses
+  // slot ((bos_m - slot_tok0) / 64) + (m - seq0) + c. Both 0 otherwise.
+  int seq0;
+  int slot_tok0;
   float scale;
   float g_min;
 };
@@ -77,7 +83,8 @@ hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
 hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream);
 
 // Operand slots: chunk c of sequence n (bos_n its first token) uses slot (bos_n / 64) + n + c,
-// so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them.
+// so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them (for a
+// group of sequences: its tokens and its sequence count).
 inline long long op_slot_count(long long total_tokens, long long n_seqs) {
   return total_tokens / 64 + n_seqs + 1;
 }

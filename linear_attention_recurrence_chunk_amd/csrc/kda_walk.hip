@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   const int DV = p.dv;
   const int h = unit % H;
   const int sj = unit / H;              // global segment index n * n_seg + j
-  const int n = sj / p.n_seg;
+  const int n = p.seq0 + sj / p.n_seg;
   const int j = sj % p.n_seg;
   const int mode = p.mode;
 
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   }
   // operand slot of the sequence's first chunk, then the segment's chunk range (chunk-aligned
   // contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg))
-  long long slot0 = (long long)(bos >> 6) + n;
+  long long slot0 = (long long)((bos - p.slot_tok0) >> 6) + (n - p.seq0);
   if (p.n_seg > 1) {
     const long long nc = (eos - bos + kChunk - 1) / kChunk;
     const int c_lo = int((j * nc) / p.n_seg);

@@ -115,9 +115,10 @@ def test_chunk_cu_seqlens_checks():
                  n_seqs=2) == ALIGN
 
 
-def chunk_ws_size(batch=1, seq_len=8192, n_seqs=1, H=96, dk=128, dv=128, io=BF16, policy=1):
+def chunk_ws_size(batch=1, seq_len=8192, n_seqs=1, H=96, dk=128, dv=128, io=BF16, policy=1,
+                  cu=None):
     out = ctypes.c_size_t(123)
-    st = kda.library().kda_chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io,
+    st = kda.library().kda_chunk_fwd_workspace_size(batch, seq_len, n_seqs, cu, H, dk, dv, io,
                                                     policy, ctypes.byref(out))
     return st, out.value
 
@@ -136,10 +137,16 @@ def test_chunk_workspace_size():
     assert chunk_ws_size(io=F32, dk=64, dv=64) == (OK, 0)
     assert chunk_ws_size(io=F32, dk=64, dv=64, policy=0) == (OK, 0)
     assert chunk_ws_size(dk=96, dv=96) == (OK, 0)
-    assert chunk_ws_size(policy=2)[0] == VALUE
+    assert chunk_ws_size(policy=3)[0] == VALUE
+    # the least the two-launch path accepts: the longest sequence's slots
+    arr, cu = host_cu([0, 100, 1100, 1300])
+    assert chunk_ws_size(seq_len=1300, n_seqs=3, H=3, policy=2, cu=cu) == (
+        OK, (1000 // 64 + 1 + 1) * 3 * slot128)
+    assert chunk_ws_size(batch=4, seq_len=300, n_seqs=4, H=2, policy=2) == (
+        OK, (300 // 64 + 1 + 1) * 2 * slot128)
     assert chunk_ws_size(io=5)[0] == DTYPE
     assert chunk_ws_size(H=0)[0] == SHAPE
-    assert kda.library().kda_chunk_fwd_workspace_size(1, 64, 1, 2, 128, 128, BF16, 1,
+    assert kda.library().kda_chunk_fwd_workspace_size(1, 64, 1, None, 2, 128, 128, BF16, 1,
                                                       None) == NULL
 
 
@@ -148,7 +155,7 @@ def test_chunk_workspace_checks():
     _, need = chunk_ws_size(seq_len=256, H=2)
     ws = ctypes.c_void_p(BASE + 20 * 64 * GiB)
     assert chunk(override=dict(ws=ctypes.c_void_p(ws.value + 8), ws_bytes=need)) == ALIGN
-    assert chunk(override=dict(ws=ws, ws_bytes=need - 16)) == WS
+    assert chunk(override=dict(ws=ws, ws_bytes=need - 16)) == WS     # one sequence: all of it
     assert chunk(override=dict(ws=P[2], ws_bytes=need)) == ALIAS          # overlaps v
     assert chunk(override=dict(ws=ctypes.c_void_p(P[5].value - 1024), ws_bytes=need)) == ALIAS
     # an fp32 call ignores the workspace, as documented

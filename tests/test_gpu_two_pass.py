@@ -91,7 +91,8 @@ def test_workspace_contents_do_not_matter():
     workspace full of NaN bytes gives the same result as a zeroed one."""
     inp = wl.prefill_inputs(T=777, H=2, dk=128, dv=128, dtype="bf16", seed=12, h0_std=0.02)
     d = to_dev(inp)
-    need = kda.chunk_fwd_workspace_size(1, 777, 1, 2, 128, 128, policy=kda.KDA_CHUNK_WS_TWO_PASS)
+    need = kda.chunk_fwd_workspace_size(1, 777, 1, 2, 128, 128,
+                                        policy=kda.KDA_CHUNK_WS_TWO_PASS)
     outs = []
     for fill in (0, 0xFF):
         ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
@@ -102,17 +103,53 @@ def test_workspace_contents_do_not_matter():
 
 
 def test_automatic_path_choice():
-    """The automatic policy takes two launches when the one-launch workgroups would not fill
-    the device (8192 tokens x 96 heads: 192 workgroups) and one launch when they do (64
-    sequences x 96 heads: 12288)."""
+    """The automatic policy takes the whole batch in two launches when the one-launch
+    workgroups would not fill the device (8192 tokens x 96 heads: 192 workgroups), and groups
+    of sequences through an 8 GiB workspace when they would (64 sequences x 96 heads)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     print(f"compute units {cus}", flush=True)
     n_small = kda.chunk_fwd_workspace_size(1, 8192, 1, 96, 128, 128)
-    n_large = kda.chunk_fwd_workspace_size(1, 540000, 64, 96, 128, 128)
-    assert n_large == 0
     if 96 * 2 <= cus:
         assert n_small == kda.chunk_fwd_workspace_size(
             1, 8192, 1, 96, 128, 128, policy=kda.KDA_CHUNK_WS_TWO_PASS) > 0
+    cu = torch.tensor([0] + [8192 * (i + 1) for i in range(64)], dtype=torch.int32)
+    n_large = kda.chunk_fwd_workspace_size(1, 8192 * 64, 64, 96, 128, 128, cu_seqlens_host=cu)
+    assert n_large == 8 << 30
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_grouped_sequences_bit_identical(dk):
+    """A workspace smaller than the batch needs runs groups of whole sequences (here the
+    least it accepts: the longest sequence's slots, so most groups hold one or two
+    sequences): same bits as the one-launch kernel, checkpoints included."""
+    lengths = [300, 0, 640, 129, 1024, 64, 1, 500]
+    print(f"case grouped sequences dk={dk} lengths={lengths}", flush=True)
+    inp = wl.prefill_inputs(H=3, dk=dk, dv=dk, dtype="bf16", seed=57 + dk, h0_std=0.02,
+                            lengths=lengths)
+    d = to_dev(inp)
+    cu = d["cu_seqlens"]
+    T = sum(lengths)
+    need_min = kda.chunk_fwd_workspace_size(1, T, len(lengths), 3, dk, dk,
+                                            policy=kda.KDA_CHUNK_WS_MIN,
+                                            cu_seqlens_host=inp["cu_seqlens"])
+    need_all = kda.chunk_fwd_workspace_size(1, T, len(lengths), 3, dk, dk,
+                                            policy=kda.KDA_CHUNK_WS_TWO_PASS)
+    assert need_min < need_all
+    res = []
+    for ws in (None, torch.empty(need_min, dtype=torch.uint8, device="cuda")):
+        ck = torch.full((T // 128, 3, dk, dk), float("nan"), device="cuda")
+        res.append(kda.chunk_fwd(*_args(d), h0=d["h0"], cu_seqlens=cu, out_dtype=torch.float32,
+                                 workspace=ws, ckpt_every=128, ckpt=ck))
+        torch.cuda.synchronize()
+    (o1, h1, c1), (o2, h2, c2) = res
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.equal(torch.isnan(c1), torch.isnan(c2))
+    written = ~torch.isnan(c1)
+    assert torch.equal(c1[written], c2[written])
+    with pytest.raises(kda.KDAError) as ei:
+        kda.chunk_fwd(*_args(d), h0=d["h0"], cu_seqlens=cu,
+                      workspace=torch.empty(need_min - 16, dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == -6
 
 
 def test_two_tiles_per_workgroup_bit_identical():
