@@ -5,10 +5,11 @@ One step = one kda_chunk_fwd over the 8192-token, 96-head, d = 128 prefill (bf16
 fp32 g, beta and state; entering state h0 ~ N(0, 0.02^2); bf16 output plus fp32 final
 state), inputs resident in HBM before the timed region: that is the line's ``value``. The
 call takes the path the library recommends for the shape (two launches here, with a
-workspace allocated before the timed region); the one-launch path is timed beside it. Two
+workspace allocated before the timed region); the one-launch path is timed beside it. Three
 more legs ride on the same line: ``decode`` (kda_decode_replay on the 256-request, 96-head
-speculative verify: window of 7 drafts plus the bonus token, HBM GB/s and latency) and
-``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill).
+speculative verify: window of 7 drafts plus the bonus token, HBM GB/s and latency),
+``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill) and
+``varlen`` (kda_chunk_fwd on the 64-sequence packed batch with per-sequence h0).
 Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs ...]
@@ -193,6 +194,42 @@ def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
     return out
 
 
+def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
+    """kda_chunk_fwd on the 64-sequence packed batch (lengths uniform in [512, 16384], per
+    sequence h0, final states written), on the library's automatic path."""
+    cfg = wl.CONFIGS["varlen_64"]
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    lengths = wl.varlen_lengths(cfg["n_seqs"], cfg["len_lo"], cfg["len_hi"], cfg["seed"])
+    inp = wl.prefill_inputs(H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], lengths=lengths, device=dev)
+    q, k, v, g, beta, h0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "h0"))
+    cu = inp["cu_seqlens"].to(dev)
+    T, N = sum(lengths), len(lengths)
+    o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    ht = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    ws_bytes = kda.chunk_fwd_workspace_size(1, T, N, H, dk, dv,
+                                            cu_seqlens_host=inp["cu_seqlens"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def launch():
+        kda.chunk_fwd(q, k, v, g, beta, h0=h0, cu_seqlens=cu, o=o, ht=ht, workspace=ws,
+                      stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup)
+    avg = sum(ms) / len(ms)
+    nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2, n_seqs=N)
+    del inp, q, k, v, g, beta, h0, o, ht, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"varlen_64: {N} packed sequences, {T} tokens (lengths uniform in "
+                        f"[512, 16384]), H={H}, d_k=d_v={dk}, bf16 q/k/v and output, fp32 "
+                        "g/beta/state, h0 per sequence, final states written",
+            "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "algorithmic_bytes_per_call": nbytes, "workspace_bytes": ws_bytes,
+            "kernels": ("prep pass (chunk kernel) + walk per group of sequences" if ws_bytes
+                        else "chunk kernel (one launch)")}
+
+
 def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
     cfg = wl.CONFIGS["ultralong_256k"]
     T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
@@ -228,9 +265,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,segment",
+    ap.add_argument("--legs", default="prefill,decode,segment,varlen",
                     help="comma-separated legs to run besides the prefill line "
-                         "(decode, segment); the prefill leg always runs")
+                         "(decode, segment, varlen); the prefill leg always runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -342,7 +379,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
     legs = set(args.legs.split(","))
-    if "decode" in legs or "segment" in legs:
+    if legs & {"decode", "segment", "varlen"}:
         del inp, q, k, v, g, beta, h0, o, ht, ws
         torch.cuda.empty_cache()
     if "decode" in legs:
@@ -351,6 +388,9 @@ def main():
     if "segment" in legs:
         line["segment_cp"] = bench_segment(kda, wl, torch, dev, stream,
                                            max(3, args.steps // 4), min(args.warmup, 2))
+    if "varlen" in legs:
+        line["varlen"] = bench_varlen(kda, wl, torch, dev, stream, max(3, args.steps // 4),
+                                      min(args.warmup, 1))
     print(json.dumps(line), flush=True)
 
 
