@@ -148,6 +148,43 @@ int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
                                  int d_v, int io_dtype, int policy, size_t* bytes);
 
 /*
+ * kda_chunk_fwd_raw: the prefill from raw projections, with the short convolution, the input
+ * norms and the gate activations fused into the prep pass of the two-launch form (the same
+ * token stage as kda_decode_replay: "Noyaux d'inférence", section "1. Le décodage KDA", fused
+ * short convolution, input normalisation and gating; here on the prefill side, so the
+ * convolved and normalised q, k and the activated gates never travel through HBM).
+ *
+ *   q_raw, k_raw, g_raw  [T_total, H, d_k] bf16 projections before the convolution / gate
+ *   v_raw                [T_total, H, d_v] bf16
+ *   beta_raw             [T_total, H] bf16
+ *   conv_w               [H, 2 d_k + d_v, conv_width] fp32, channel order q, k, v; tap
+ *                        conv_width - 1 multiplies the current token
+ *   conv_tail_in         [N, H, 2 d_k + d_v, conv_width - 1] fp32 raw inputs before each
+ *                        sequence, oldest first (a restored prefix), or NULL for zeros
+ *   conv_tail_out        same shape, or NULL: each sequence's last conv_width - 1 raw inputs
+ *                        (older ones from conv_tail_in when it is shorter); must not overlap
+ *                        conv_tail_in
+ * Per token, as in kda_decode_replay: depthwise causal convolution of q, k, v over the raw
+ * inputs, SiLU when act == 1, q and k scaled by 1 / sqrt(sum x^2 + eps_l2),
+ * beta = sigmoid(beta_raw), g = max(-softplus(g_raw), g_min); then the recurrence of
+ * kda_chunk_fwd (h0, ht, o, scale, packed sequences as there). The convolved values are
+ * stored once, in fp32, for the serial walk. Supported: d_k = d_v in {64, 128}, conv_width in
+ * 1..4. `workspace` (16-byte aligned, at least kda_chunk_fwd_raw_workspace_size bytes) holds
+ * the convolved values and the operand slots of the whole batch.
+ */
+int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
+                      const void* g_raw, const void* beta_raw, const float* conv_w,
+                      const float* conv_tail_in, float* conv_tail_out, const float* h0,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int batch,
+                      int seq_len, int n_seqs, int num_heads, int d_k, int d_v, int conv_width,
+                      int act, float eps_l2, float scale, float g_min, void* o, float* ht,
+                      int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kda_chunk_fwd_raw needs (batch / seq_len / n_seqs as in kda_chunk_fwd). */
+int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                     int d_v, size_t* bytes);
+
+/*
  * Bytes of device workspace kda_segment_cp_fwd needs for the given sizes (batch / seq_len /
  * n_seqs as in kda_chunk_fwd; n_segments = 0 asks for the automatic choice). For KDA_BF16
  * inputs with d_k = d_v in {64, 128} the size includes the operand slots of the two-launch

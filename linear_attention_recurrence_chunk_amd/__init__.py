@@ -14,6 +14,7 @@ import ctypes
 import os
 
 __all__ = ["KDAError", "library", "library_path", "chunk_fwd", "chunk_fwd_workspace_size",
+           "chunk_fwd_raw",
            "segment_cp_fwd",
            "segment_cp_workspace_size", "decode_replay", "status_string", "version"]
 
@@ -60,6 +61,12 @@ def library():
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, P, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_workspace_size.restype = I
+    lib.kda_chunk_fwd_raw.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                      F, F, F, P, P, I, P, ctypes.c_size_t, P]
+    lib.kda_chunk_fwd_raw.restype = I
+    lib.kda_chunk_fwd_raw_workspace_size.argtypes = [I, I, I, I, I, I,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_fwd_raw_workspace_size.restype = I
     lib.kda_segment_cp_workspace_size.argtypes = [I, I, I, I, I, I, I, I,
                                                   ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_segment_cp_workspace_size.restype = I
@@ -137,8 +144,10 @@ def _out_dtype(q, out_dtype):
     raise ValueError(f"unsupported out_dtype {out_dtype}")
 
 
-def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype):
+def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype,
+                  gate_dtype=None):
     torch = _torch()
+    gate_dtype = torch.float32 if gate_dtype is None else gate_dtype
     if q.dim() == 4:                 # [B, T, H, d]
         batch, seq_len, H, dk = q.shape
     elif q.dim() == 3:               # [T, H, d]
@@ -150,8 +159,8 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, o
     io = q.dtype
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, io, dev)
-    _check(g, "g", torch.float32, dev)
-    _check(beta, "beta", torch.float32, dev)
+    _check(g, "g", gate_dtype, dev)
+    _check(beta, "beta", gate_dtype, dev)
     _check(h0, "h0", torch.float32, dev)
     cu_dev = cu_host = None
     if cu_seqlens is not None:
@@ -235,6 +244,45 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     if ckpt_every:
         return a["o"], a["ht"], ckpt
     return a["o"], a["ht"]
+
+
+def chunk_fwd_raw(q, k, v, g, beta, conv_w, conv_tail=None, h0=None, cu_seqlens=None,
+                  scale=1.0, g_min=-5.0, eps_l2=1e-6, act=1, o=None, ht=None,
+                  output_final_state=True, out_dtype=None, workspace=None,
+                  conv_tail_out=None, stream=None):
+    """kda_chunk_fwd_raw: the prefill from raw bf16 projections q, k, g [.., H, d_k], v
+    [.., H, d_v], beta [.., H] with the short convolution (taps conv_w [H, 2 d_k + d_v, W]),
+    SiLU (act), L2 input norms and gate activations fused into the prep pass. conv_tail: the
+    entering raw tails [N, H, 2 d_k + d_v, W - 1] fp32 or None. Returns (o, ht, tail_out)."""
+    torch = _torch()
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state,
+                      out_dtype if out_dtype is not None else torch.bfloat16,
+                      gate_dtype=torch.bfloat16)
+    T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
+    dev = q.device
+    _check(conv_w, "conv_w", torch.float32, dev)
+    _check(conv_tail, "conv_tail", torch.float32, dev)
+    W = conv_w.shape[-1]
+    if conv_tail_out is None and W > 1:
+        conv_tail_out = torch.empty(a["n_seqs"], a["H"], 2 * a["dk"] + a["dv"], W - 1,
+                                    dtype=torch.float32, device=dev)
+    _check(conv_tail_out, "conv_tail_out", torch.float32, dev)
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        st = library().kda_chunk_fwd_raw_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"],
+                                                        a["dk"], a["dv"], ctypes.byref(need))
+        if st != 0:
+            raise KDAError(st, "kda_chunk_fwd_raw_workspace_size")
+        workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=dev)
+    st = library().kda_chunk_fwd_raw(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(conv_tail),
+        _ptr(conv_tail_out) if W > 1 else None, _ptr(h0), _ptr(a["cu_dev"]),
+        _cu_host_ptr(a["cu_host"]), a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
+        int(W), int(act), float(eps_l2), float(scale), float(g_min), _ptr(a["o"]),
+        _ptr(a["ht"]), a["out"], _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_raw")
+    return a["o"], a["ht"], conv_tail_out
 
 
 def segment_cp_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF16,

@@ -43,7 +43,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* g
                      const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                      int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
                      float scale, float g_min, const void* o, const float* ht, int* out_N,
-                     int64_t* out_T) {
+                     int64_t* out_T, size_t gate_bytes = 4) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL_ARG;
   if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (out_dtype != io_dtype && out_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
@@ -84,8 +84,8 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* g
   const Range rq = range_of(q, size_t(T) * num_heads * d_k * es);
   const Range rk = range_of(k, size_t(T) * num_heads * d_k * es);
   const Range rv = range_of(v, size_t(T) * num_heads * d_v * es);
-  const Range rg = range_of(g, size_t(T) * num_heads * d_k * 4);
-  const Range rb = range_of(beta, size_t(T) * num_heads * 4);
+  const Range rg = range_of(g, size_t(T) * num_heads * d_k * gate_bytes);
+  const Range rb = range_of(beta, size_t(T) * num_heads * gate_bytes);
   const Range rh0 = range_of(h0, h0 ? size_t(N) * num_heads * d_k * d_v * 4 : 0);
   const Range ro = range_of(o, size_t(T) * num_heads * d_v * dsize(out_dtype));
   const Range rht = range_of(ht, ht ? size_t(N) * num_heads * d_k * d_v * 4 : 0);
@@ -400,6 +400,113 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
+}
+
+size_t raw_vconv_bytes(int64_t T, int H, int dv) {
+  return (size_t(T) * H * dv * 4 + 255) / 256 * 256;   // fp32 convolved values
+}
+
+int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                     int d_v, size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_ARG;
+  if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+    return KDA_ERR_BAD_SHAPE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  const bool packed = batch == 1 && n_seqs != 1;
+  const int64_t T = packed ? int64_t(seq_len) : int64_t(batch) * seq_len;
+  const int64_t N = packed ? n_seqs : batch;
+  *bytes = raw_vconv_bytes(T, num_heads, d_v) + two_pass_workspace_bytes(T, N, num_heads, d_k);
+  return KDA_OK;
+}
+
+int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
+                      const void* g_raw, const void* beta_raw, const float* conv_w,
+                      const float* conv_tail_in, float* conv_tail_out, const float* h0,
+                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int batch,
+                      int seq_len, int n_seqs, int num_heads, int d_k, int d_v, int conv_width,
+                      int act, float eps_l2, float scale, float g_min, void* o, float* ht,
+                      int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!conv_w || !workspace) return KDA_ERR_NULL_ARG;
+  if (conv_width < 1 || conv_width > 4) return KDA_ERR_BAD_SHAPE;
+  if (act != 0 && act != 1) return KDA_ERR_BAD_VALUE;
+  if (!(eps_l2 > 0.f) || !isfinite(eps_l2)) return KDA_ERR_BAD_VALUE;
+  if (d_k != d_v) return KDA_ERR_UNSUPPORTED;
+  // the same shape, sequence and aliasing checks as kda_chunk_fwd with bf16 inputs (g and
+  // beta bf16 too)
+  int N = 0;
+  int64_t T = 0;
+  const int st = validate_prefill(q_raw, k_raw, v_raw, static_cast<const float*>(g_raw),
+                                  static_cast<const float*>(beta_raw), h0, cu_seqlens,
+                                  cu_seqlens_host, batch, seq_len, n_seqs, num_heads, d_k, d_v,
+                                  KDA_BF16, out_dtype, scale, g_min, o, ht, &N, &T, 2);
+  if (st != KDA_OK) return st;
+  const void* ptrs[] = {conv_w, conv_tail_in, conv_tail_out};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+  const size_t vbytes = raw_vconv_bytes(T, num_heads, d_v);
+  const size_t need = vbytes + two_pass_workspace_bytes(T, N, num_heads, d_k);
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t C3 = size_t(2 * d_k + d_v);
+  const size_t tail_bytes = size_t(N) * num_heads * C3 * size_t(conv_width - 1) * 4;
+  {
+    const Range rws = range_of(workspace, need);
+    const Range rout = range_of(conv_tail_out, conv_tail_out ? tail_bytes : 0);
+    const Range rin = range_of(conv_tail_in, conv_tail_in ? tail_bytes : 0);
+    const Range all[] = {
+        range_of(q_raw, size_t(T) * num_heads * d_k * 2), range_of(k_raw, size_t(T) * num_heads * d_k * 2),
+        range_of(v_raw, size_t(T) * num_heads * d_v * 2), range_of(g_raw, size_t(T) * num_heads * d_k * 2),
+        range_of(beta_raw, size_t(T) * num_heads * 2),
+        range_of(h0, h0 ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
+        range_of(o, size_t(T) * num_heads * d_v * dsize(out_dtype)),
+        range_of(ht, ht ? size_t(N) * num_heads * d_k * d_v * 4 : 0),
+        range_of(conv_w, size_t(num_heads) * C3 * conv_width * 4)};
+    for (Range x : all) {
+      if (overlaps(rws, x)) return KDA_ERR_ALIASING;
+      if (overlaps(rout, x)) return KDA_ERR_ALIASING;
+    }
+    // the leaving tail is written while other workgroups still read the entering one
+    if (overlaps(rout, rin) || overlaps(rout, rws) || overlaps(rin, rws)) return KDA_ERR_ALIASING;
+  }
+  if (N == 0) return KDA_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  kda::ChunkParams p{};
+  p.q = q_raw;
+  p.k = k_raw;
+  p.v = v_raw;
+  p.g = static_cast<const float*>(g_raw);         // bf16 data; the raw prep reads it as such
+  p.beta = static_cast<const float*>(beta_raw);
+  p.h0 = h0;
+  p.cu_seqlens = cu_seqlens;
+  p.o = o;
+  p.ht = ht;
+  p.seq_len = cu_seqlens ? 0 : seq_len;
+  p.n_seqs = N;
+  p.H = num_heads;
+  p.dv = d_v;
+  p.n_vt = d_v / 64;
+  p.n_seg = 1;
+  p.n_units = N * num_heads;
+  p.scale = scale;
+  p.g_min = g_min;
+  p.ckpt_every = 64;
+  p.v_conv = static_cast<float*>(workspace);
+  p.ws_ops = static_cast<char*>(workspace) + vbytes;
+  p.conv_w = conv_w;
+  p.conv_tail_in = conv_tail_in;
+  p.conv_tail_out = conv_tail_out;
+  p.conv_width = conv_width;
+  p.act = act;
+  p.eps_l2 = eps_l2;
+  p.decay_floor = expf(g_min);
+  p.mode = kda::kModeWalk;
+  int rc = launch_status(
+      kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s, true));
+  if (rc != KDA_OK) return rc;
+  // the walk reads the convolved values
+  p.v = p.v_conv;
+  p.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
+  return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s, true));
 }
 
 int kda_segment_cp_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

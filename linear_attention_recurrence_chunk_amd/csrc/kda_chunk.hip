@@ -327,7 +327,8 @@ __device__ __forceinline__ void prep_store(char* slot, const typename Pol::ER* s
 // kPrep true: pass 1 of the two-pass prefill. One workgroup per (sequence, group of chunks,
 // head) runs the prologue of each chunk and stores the serial step's operands to the chunk's
 // slot instead of running the step (no state, values or outputs).
-template <class Pol, typename Tio, typename Tout, int DK, bool kOut, bool kPrep = false>
+template <class Pol, typename Tio, typename Tout, int DK, bool kOut, bool kPrep = false,
+          bool kRaw = false>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   using L = ChunkLayout<Pol, DK>;
   using E = typename Pol::E;
@@ -440,11 +441,57 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
   }
 
-  RawChunk<Tio, DK> raw;
+  RawChunk<Tio, DK, kRaw> raw;
+
+  // raw projections: the convolution taps of this thread's q and k channels (prologue
+  // mapping) and of its value channels (value-convolution mapping), right-aligned in a window
+  // of four (tap 3 multiplies the current token, tap 3 - i the token i before it; taps
+  // beyond the width are zero), and the leaving tail
+  float wq[4][4], wk[4][4], wv[4][4];
+  if constexpr (kRaw) {
+    constexpr int C3 = 3 * DK;   // raw mode: d_v = d_k
+    const int W = p.conv_width;
+    const int cq0 = 4 * (lane % PM::kLPT);
+    const int cv0 = 4 * (tid % (DK / 4));
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int mw = m - (4 - W);   // the tap of the width-W window
+        const bool on = mw >= 0;
+        wq[c][m] = on ? p.conv_w[(size_t(h) * C3 + cq0 + c) * W + mw] : 0.f;
+        wk[c][m] = on ? p.conv_w[(size_t(h) * C3 + DK + cq0 + c) * W + mw] : 0.f;
+        wv[c][m] = on ? p.conv_w[(size_t(h) * C3 + 2 * DK + cv0 + c) * W + mw] : 0.f;
+      }
+    // the sequence's leaving tail: its last W - 1 raw inputs (older ones from the entering
+    // tail when it is shorter), written by the workgroup of the group holding its last chunk
+    const int seq_eos = p.cu_seqlens ? p.cu_seqlens[n + 1] : seq_bos + p.seq_len;
+    const int len = seq_eos - seq_bos;
+    const bool last_group = (len == 0 && j == 0) || (bos < eos && eos == seq_eos);
+    if (p.conv_tail_out && W > 1 && last_group) {
+      const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
+      for (int idx = tid; idx < C3 * (W - 1); idx += 256) {
+        const int ch = idx / (W - 1), m = idx % (W - 1);
+        const int pos = seq_eos - (W - 1) + m;
+        float val = 0.f;
+        if (pos >= seq_bos) {
+          const __bf16* src = ch < DK ? reinterpret_cast<const __bf16*>(p.q)
+                                      : ch < 2 * DK ? reinterpret_cast<const __bf16*>(p.k)
+                                                    : reinterpret_cast<const __bf16*>(p.v);
+          const int cc = ch < DK ? ch : ch < 2 * DK ? ch - DK : ch - 2 * DK;
+          const int ld = DK;
+          val = (float)src[(size_t(pos) * H + h) * ld + cc];
+        } else if (p.conv_tail_in) {
+          val = p.conv_tail_in[tb + size_t(ch) * (W - 1) + m + len];
+        }
+        p.conv_tail_out[tb + size_t(ch) * (W - 1) + m] = val;
+      }
+    }
+  }
 
   if (bos < eos)
-    load_chunk_any<kPrep ? kLoadAll & ~kLoadV : (kOut ? kLoadAll : kLoadAll & ~kLoadQ), Tio, DK>(
-        raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
+    load_chunk_any<kPrep ? kLoadAll & ~kLoadV : (kOut ? kLoadAll : kLoadAll & ~kLoadQ), Tio, DK, 0,
+                   8, kRaw>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
 
   const int lane0 = lane, q4_0 = q4, ln0 = ln;
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
@@ -460,7 +507,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     const bool more = cstart + kChunk < eos;
     const int nstart = cstart + kChunk, nLc = min(kChunk, eos - nstart);
 #define KDA_PREFETCH(parts, lo, hi) \
-  if (more) load_chunk_any<parts, Tio, DK, lo, hi>(raw, p, nstart, nLc, w, lane, h, vcol0)
+  if (more) load_chunk_any<parts, Tio, DK, lo, hi, kRaw>(raw, p, nstart, nLc, w, lane, h, vcol0)
 
     // ================= prologue 1: decay factors and operand tiles ======================
     // rho = e^{lambda} (decay from the sub-block start to token r, inclusive) <= 1;
@@ -475,6 +522,123 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     // floor a single max (the product needs no NaN quieting) and feeds v_exp_f32 directly
     const float gmin2 = p.g_min * kLog2e;
     // rows past the end of a ragged last chunk count as zero keys and queries with no decay
+    // raw projections: causal depthwise convolution (history from the rows before this
+    // thread's first token, or the entering tail before the sequence), optional SiLU, and
+    // the L2 norm of each token's q and k over its d_k channels (a sum across the kLPT lanes
+    // holding the row)
+    float qin[TPT][4], kin[TPT][4];
+    if constexpr (kRaw) {
+      const int W = p.conv_width;
+      constexpr int C3 = 3 * DK;   // raw mode: d_v = d_k
+      float hq[3][4], hk[3][4];   // raw q, k of tokens rb0 - 1 - i
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int tok = cstart + rb0 - 1 - i;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) hq[i][c] = hk[i][c] = 0.f;
+        if (i + 1 < W) {
+          if (tok >= seq_bos) {
+            const size_t off = (size_t(tok) * H + h) * DK + c0;
+            const bf16x4 a = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.q) + off);
+            const bf16x4 b = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.k) + off);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              hq[i][c] = (float)a[c];
+              hk[i][c] = (float)b[c];
+            }
+          } else if (p.conv_tail_in) {
+            const int m = (W - 1) - (seq_bos - tok);   // tail slot of that token, oldest first
+            const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              hq[i][c] = p.conv_tail_in[tb + size_t(c0 + c) * (W - 1) + m];
+              hk[i][c] = p.conv_tail_in[tb + size_t(DK + c0 + c) * (W - 1) + m];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // window tap m multiplies token t - 3 + m (history rows before the thread's first)
+          float yq = 0.f, yk = 0.f;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int d = t - 3 + m;   // token offset inside this thread's rows
+            if (d < -3) continue;
+            const float xq = d >= 0 ? to_f32(raw.q[d < 0 ? 0 : d][c]) : hq[d < 0 ? -d - 1 : 0][c];
+            const float xk = d >= 0 ? to_f32(raw.k[d < 0 ? 0 : d][c]) : hk[d < 0 ? -d - 1 : 0][c];
+            yq = fmaf(wq[c][m], xq, yq);
+            yk = fmaf(wk[c][m], xk, yk);
+          }
+          if (p.act) {
+            yq = yq / (1.f + __expf(-yq));
+            yk = yk / (1.f + __expf(-yk));
+          }
+          qin[t][c] = yq;
+          kin[t][c] = yk;
+          ssq = fmaf(yq, yq, ssq);
+          ssk = fmaf(yk, yk, ssk);
+        }
+        ssq = sum_xor8(sum_mirror8(sum_xor2(sum_xor1(ssq))));
+        ssk = sum_xor8(sum_mirror8(sum_xor2(sum_xor1(ssk))));
+        if constexpr (PM::kLPT == 32) {
+          ssq = sum_xor16(ssq);
+          ssk = sum_xor16(ssk);
+        }
+        const float rq = 1.f / sqrtf(ssq + p.eps_l2), rk = 1.f / sqrtf(ssk + p.eps_l2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          qin[t][c] *= rq;
+          kin[t][c] *= rk;
+        }
+      }
+      // the chunk's convolved values for the walk (fp32: after the activation they reach
+      // ~15 x their RMS, and one bf16 rounding of them costs several % of the outputs' RMS):
+      // thread = 4 value channels x kTPV tokens
+      {
+        constexpr int kQuads = DK / 4, kTPV = 64 / (256 / kQuads);
+        const int cv0 = 4 * (tid % kQuads), tv0 = kTPV * (tid / kQuads);
+        const __bf16* vraw = reinterpret_cast<const __bf16*>(p.v);
+        float xv[kTPV + 3][4];
+#pragma unroll
+        for (int i = 0; i < kTPV + 3; ++i) {
+          const int tok = cstart + tv0 - 3 + i;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) xv[i][c] = 0.f;
+          if (i < 3 && i < 3 - (W - 1)) continue;          // history beyond the taps
+          if (tok >= cstart + Lc) continue;
+          if (tok >= seq_bos) {
+            const bf16x4 a = *reinterpret_cast<const bf16x4*>(vraw + (size_t(tok) * H + h) * DK + cv0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xv[i][c] = (float)a[c];
+          } else if (p.conv_tail_in) {
+            const int m = (W - 1) - (seq_bos - tok);
+            const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              xv[i][c] = p.conv_tail_in[tb + size_t(2 * DK + cv0 + c) * (W - 1) + m];
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < kTPV; ++t) {
+          const int tok = cstart + tv0 + t;
+          if (tok >= cstart + Lc) continue;
+          float y[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc = fmaf(wv[c][m], xv[t + m][c], acc);
+            y[c] = p.act ? acc / (1.f + __expf(-acc)) : acc;
+          }
+          *reinterpret_cast<f32x4*>(p.v_conv + (size_t(tok) * H + h) * DK + cv0) =
+              f32x4{y[0], y[1], y[2], y[3]};
+        }
+      }
+    }
     auto raw_in = [&](auto full) {
       constexpr bool kFull = decltype(full)::value;
 #pragma unroll
@@ -482,12 +646,20 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         const bool valid = kFull || rb0 + t < Lc;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float gt = valid ? fmaxf(raw.g[t][c] * kLog2e, gmin2) : 0.f;
-          ex[t][c] = __builtin_amdgcn_exp2f(gt);
+          if constexpr (kRaw) {
+            // decay e^{max(-softplus(x), g_min)} = max(sigmoid(-x), e^{g_min})
+            const float x = (float)raw.g[t][c];
+            ex[t][c] = valid ? fmaxf(1.f / (1.f + __expf(x)), p.decay_floor) : 1.f;
+            kv[t][c] = valid ? kin[t][c] : 0.f;
+            qv[t][c] = valid ? qin[t][c] : 0.f;
+          } else {
+            const float gt = valid ? fmaxf(raw.g[t][c] * kLog2e, gmin2) : 0.f;
+            ex[t][c] = __builtin_amdgcn_exp2f(gt);
+            kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
+            qv[t][c] = (kOut && valid) ? to_f32(raw.q[t][c]) : 0.f;
+          }
           lp[c] *= ex[t][c];
           rho[t][c] = lp[c];
-          kv[t][c] = valid ? to_f32(raw.k[t][c]) : 0.f;
-          qv[t][c] = (kOut && valid) ? to_f32(raw.q[t][c]) : 0.f;
         }
       }
     };
@@ -514,7 +686,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int t = 0; t < TPT; ++t) rho[t][c] *= pre;
     }
-    const float beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
+    float beta_r;
+    if constexpr (kRaw)
+      beta_r = (16 * w + lane < Lc) ? 1.f / (1.f + __expf(-(float)raw.beta)) : 0.f;
+    else
+      beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
     // 1 / rho from one reciprocal per channel: 1/rho_t = (1/rho_last) x the decays after t
     float rinv_next[4];
 #pragma unroll
@@ -886,7 +1062,7 @@ static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool raw) {
   if (!base.ws_ops || !base.q || !base.k || !base.g || !base.beta || base.H < 1 ||
       base.n_seqs < 1 || prep_groups < 1 || (!base.cu_seqlens && base.seq_len < 0))
     return hipErrorInvalidValue;
@@ -904,8 +1080,17 @@ hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
   prep.ws_sin = nullptr;
   prep.ckpt = nullptr;
   const dim3 grid((prep.n_units + 7) / 8 * 8);
-  if (dk == 128)
+  if (raw && (!base.conv_w || !base.v || !base.v_conv || base.conv_width < 1 ||
+              base.conv_width > 4 || base.dv != dk))
+    return hipErrorInvalidValue;
+  if (dk == 128 && raw)
+    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true, true>), grid,
+                       dim3(256), 0, stream, prep);
+  else if (dk == 128)
     hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true>), grid,
+                       dim3(256), 0, stream, prep);
+  else if (dk == 64 && raw)
+    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 64, true, true, true>), grid,
                        dim3(256), 0, stream, prep);
   else if (dk == 64)
     hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 64, true, true>), grid,

@@ -51,13 +51,15 @@ struct ProMap {
 // Raw inputs of one chunk held by one thread: g, k, q of its prologue elements; for each of
 // the four 16-token row blocks rb, four value columns 16 w + 4 (lane % 16 / 4) .. + 3 of token
 // 16 rb + 4 (lane / 16) + lane % 4 (a quad transpose turns them into MFMA accumulator layout);
-// and (lanes < 16) the beta of token 16 w + lane.
-template <typename Tio, int DK>
+// and (lanes < 16) the beta of token 16 w + lane. With kRawG the gates arrive as raw bf16
+// projections (log-decay and beta before their activations) instead of fp32 values.
+template <typename Tio, int DK, bool kRawG = false>
 struct RawChunk {
   static constexpr int kTPT = ProMap<DK>::kTPT;
-  f32x4 g[kTPT];
+  using Tg = std::conditional_t<kRawG, __bf16, float>;
+  typename Quad<Tg>::type g[kTPT];
   typename Quad<Tio>::type k[kTPT], q[kTPT], v[4];
-  float beta;
+  Tg beta;
 };
 
 // Loads of one chunk. Token offsets are wave-uniform (scalar address arithmetic) and each lane
@@ -80,11 +82,13 @@ __device__ __forceinline__ const T* lane_ptr(const void* base, size_t uniform_el
 // its token count), V (values) or B (beta).
 enum : int { kLoadG = 1, kLoadK = 2, kLoadQ = 4, kLoadV = 8, kLoadB = 16, kLoadAll = 31 };
 
-template <bool kFull, int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8>
-__device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkParams& p, int cstart,
-                                           int Lc, int w, int lane, int h, int vcol0) {
+template <bool kFull, int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8, bool kRawG = false>
+__device__ __forceinline__ void load_chunk(RawChunk<Tio, DK, kRawG>& x, const ChunkParams& p,
+                                           int cstart, int Lc, int w, int lane, int h, int vcol0) {
   using M = ProMap<DK>;
   using Q4 = typename Quad<Tio>::type;
+  using Tg = typename RawChunk<Tio, DK, kRawG>::Tg;
+  using G4 = typename Quad<Tg>::type;
   const int H = p.H;
   const int grp = lane / M::kLPT;
   const int c0 = 4 * (lane % M::kLPT);
@@ -97,7 +101,7 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
   for (int t = kLo * M::kTPT / 8; t < kHi * M::kTPT / 8; ++t) {
     const bool ok = 16 * w + grp * M::kTPT + t < Lc;
     const size_t u = u0 + size_t(t) * row;
-    if constexpr ((kParts & kLoadG) != 0) x.g[t] = *lane_ptr<kFull, float, f32x4>(p.g, u, lk, ok, fk);
+    if constexpr ((kParts & kLoadG) != 0) x.g[t] = *lane_ptr<kFull, Tg, G4>(p.g, u, lk, ok, fk);
     if constexpr ((kParts & kLoadK) != 0) x.k[t] = *lane_ptr<kFull, Tio, Q4>(p.k, u, lk, ok, fk);
     if constexpr ((kParts & kLoadQ) != 0) x.q[t] = *lane_ptr<kFull, Tio, Q4>(p.q, u, lk, ok, fk);
   }
@@ -123,16 +127,18 @@ __device__ __forceinline__ void load_chunk(RawChunk<Tio, DK>& x, const ChunkPara
     const bool ok = 16 * w + bl < Lc;
     const uint32_t lb = uint32_t((16 * w + bl) * H + h);
     const size_t fb = size_t(cstart) * H + h;
-    x.beta = *lane_ptr<kFull, float, float>(p.beta, size_t(cstart) * H, lb, ok, fb);
+    x.beta = *lane_ptr<kFull, Tg, Tg>(p.beta, size_t(cstart) * H, lb, ok, fb);
   }
 }
 
-template <int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8>
-__device__ __forceinline__ void load_chunk_any(RawChunk<Tio, DK>& x, const ChunkParams& p,
+template <int kParts, typename Tio, int DK, int kLo = 0, int kHi = 8, bool kRawG = false>
+__device__ __forceinline__ void load_chunk_any(RawChunk<Tio, DK, kRawG>& x, const ChunkParams& p,
                                                int cstart, int Lc, int w, int lane, int h,
                                                int vcol0) {
-  if (Lc == kChunk) load_chunk<true, kParts, Tio, DK, kLo, kHi>(x, p, cstart, Lc, w, lane, h, vcol0);
-  else load_chunk<false, kParts, Tio, DK, kLo, kHi>(x, p, cstart, Lc, w, lane, h, vcol0);
+  if (Lc == kChunk)
+    load_chunk<true, kParts, Tio, DK, kLo, kHi, kRawG>(x, p, cstart, Lc, w, lane, h, vcol0);
+  else
+    load_chunk<false, kParts, Tio, DK, kLo, kHi, kRawG>(x, p, cstart, Lc, w, lane, h, vcol0);
 }
 
 // One chunk-head's serial-step operands, written by the prep pass of the two-pass prefill and

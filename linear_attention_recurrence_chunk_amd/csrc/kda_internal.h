@@ -53,6 +53,18 @@ struct ChunkParams {
   // slot ((bos_m - slot_tok0) / 64) + (m - seq0) + c. Both 0 otherwise.
   int seq0;
   int slot_tok0;
+  // prep mode with raw projections (q, k, v, g, beta before the short convolution, the L2
+  // norms and the gate activations, all bf16): taps [H, 2 dk + dv, conv_width] (q, k, v
+  // channels), entering convolution tails [N, H, 2 dk + dv, conv_width - 1] (null: zeros),
+  // leaving tails (same shape), and the convolved values [T, H, dv] fp32 the walk reads
+  const float* conv_w;
+  const float* conv_tail_in;
+  float* conv_tail_out;
+  float* v_conv;
+  int conv_width;
+  int act;
+  float eps_l2;
+  float decay_floor;        // e^{g_min}
   float scale;
   float g_min;
 };
@@ -79,8 +91,9 @@ hipError_t launch_chunk_fwd(const ChunkParams& p, int io_dtype, int out_dtype, i
 // state tile) in mode kModeWalk (whole sequences: o and ht), kModeTransition (segment
 // summaries [P | Q] into ws_pq) or kModeReplay (o from the entering states in ws_sin).
 hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
-                             hipStream_t stream);
-hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream);
+                             hipStream_t stream, bool raw = false);
+hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream,
+                             bool v_f32 = false);
 
 // Operand slots: chunk c of sequence n (bos_n its first token) uses slot (bos_n / 64) + n + c,
 // so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them (for a

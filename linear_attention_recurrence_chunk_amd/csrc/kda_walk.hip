@@ -362,24 +362,32 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   }
 }
 
-template <typename Tout, int DK, int kTPW>
+// Tv: the values' type (bf16 inputs, or the fp32 convolved values of the raw prefill)
+template <typename Tv, typename Tout, int DK, int kTPW>
 static hipError_t launch_walk_tpw(const ChunkParams& p, hipStream_t stream) {
   const dim3 grid((p.n_units + 7) / 8 * 8 * (p.n_vt / kTPW));
   const dim3 block(256 * kTPW);
   if (p.mode == kModeTransition)
-    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, false, kTPW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, false, kTPW>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_walk_kernel<__bf16, Tout, DK, true, kTPW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, true, kTPW>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename Tout, int DK>
-static hipError_t launch_walk(const ChunkParams& p, hipStream_t stream) {
-  if (p.walk_tpw == 2) return launch_walk_tpw<Tout, DK, 2>(p, stream);
-  return launch_walk_tpw<Tout, DK, 1>(p, stream);
+static hipError_t launch_walk(const ChunkParams& p, hipStream_t stream, bool v_f32) {
+  if (v_f32) {
+    // (the raw prefill: forward walks only)
+    if (p.mode == kModeTransition) return hipErrorInvalidValue;
+    if (p.walk_tpw == 2) return launch_walk_tpw<float, Tout, DK, 2>(p, stream);
+    return launch_walk_tpw<float, Tout, DK, 1>(p, stream);
+  }
+  if (p.walk_tpw == 2) return launch_walk_tpw<__bf16, Tout, DK, 2>(p, stream);
+  return launch_walk_tpw<__bf16, Tout, DK, 1>(p, stream);
 }
 
-hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream) {
+hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream,
+                             bool v_f32) {
   if (!p.ws_ops || !p.v || p.H < 1 || p.n_seqs < 1 || p.n_seg < 1 || p.dv != dk ||
       (long long)p.n_units != (long long)p.n_seqs * p.n_seg * p.H ||
       (!p.cu_seqlens && p.seq_len < 0))
@@ -398,10 +406,10 @@ hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStr
     default:
       return hipErrorInvalidValue;
   }
-  if (dk == 128) return out_dtype == 1 ? launch_walk<__bf16, 128>(p, stream)
-                                       : launch_walk<float, 128>(p, stream);
-  if (dk == 64) return out_dtype == 1 ? launch_walk<__bf16, 64>(p, stream)
-                                      : launch_walk<float, 64>(p, stream);
+  if (dk == 128) return out_dtype == 1 ? launch_walk<__bf16, 128>(p, stream, v_f32)
+                                       : launch_walk<float, 128>(p, stream, v_f32);
+  if (dk == 64) return out_dtype == 1 ? launch_walk<__bf16, 64>(p, stream, v_f32)
+                                      : launch_walk<float, 64>(p, stream, v_f32);
   return hipErrorInvalidValue;
 }
 

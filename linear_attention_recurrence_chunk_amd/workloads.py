@@ -19,7 +19,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["CONFIGS", "prefill_inputs", "varlen_lengths", "decode_inputs", "DecodeWorkload"]
+__all__ = ["CONFIGS", "prefill_inputs", "raw_prefill_inputs", "varlen_lengths", "decode_inputs",
+           "DecodeWorkload"]
 
 
 # name -> parameters. "kind" tells which entry point the configuration exercises.
@@ -149,3 +150,29 @@ def decode_inputs(R=256, H=96, dk=128, dv=128, conv_width=4, n_new=8, window=8, 
     return DecodeWorkload(R=R, H=H, dk=dk, dv=dv, conv_width=conv_width, n_new=n_new,
                           window=window, n_acc=n_acc.to(torch.int32), prev=prev, new=new,
                           conv_w=conv_w, norm_w=norm_w, state=state, conv_tail=tail)
+
+
+def raw_prefill_inputs(T=None, H=2, dk=128, dv=128, conv_width=4, seed=0, h0_std=0.0,
+                       lengths=None, with_tail=True, device="cpu"):
+    """Raw projections for the prefill with the fused token stage, drawn like the decode's:
+    q, k, v, g, beta ~ N(0, 1) in bf16; conv taps 0.5 N(0, 1); entering conv tails N(0, 1)
+    (or none); h0 ~ N(0, h0_std^2) per sequence. Returns a dict with 'cu_seqlens' (CPU)."""
+    if lengths is None:
+        lengths = [int(T)]
+    lengths = [int(x) for x in lengths]
+    total = sum(lengths)
+    gen = _gen(seed, device)
+    f32 = dict(dtype=torch.float32, device=device, generator=gen)
+    bf = lambda *shape: torch.randn(*shape, **f32).to(torch.bfloat16)
+    C = 2 * dk + dv
+    out = dict(q=bf(total, H, dk), k=bf(total, H, dk), v=bf(total, H, dv), g=bf(total, H, dk),
+               beta=bf(total, H))
+    out["conv_w"] = 0.5 * torch.randn(H, C, conv_width, **f32)
+    out["conv_tail"] = (torch.randn(len(lengths), H, C, conv_width - 1, **f32)
+                        if with_tail and conv_width > 1 else None)
+    out["h0"] = (h0_std * torch.randn(len(lengths), H, dk, dv, **f32) if h0_std > 0 else None)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    out["cu_seqlens"] = cu
+    out["lengths"] = lengths
+    return out

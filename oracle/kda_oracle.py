@@ -332,3 +332,54 @@ def decode_replay(state, conv_tail, n_acc, prev, new, conv_w, norm_w, scale=1.0,
                     out_state[r, h] = S
                     out_tail[r, h] = tail
     return {"o": o, "state": out_state, "state_acc": out_acc, "conv_tail": out_tail}
+
+
+# ---------------------------------------------------------------------------------------------
+# Prefill from raw projections: the decode's token stage (short convolution, SiLU, L2 input
+# norms, gate activations; "Noyaux d'inférence", section "1. Le décodage KDA") applied to every
+# token of a sequence in order, then the recurrence.
+# ---------------------------------------------------------------------------------------------
+def prefill_input_stage(q_raw, k_raw, v_raw, g_raw, beta_raw, conv_w, conv_tail=None,
+                        cu_seqlens=None, act=1, eps_l2=1e-6, g_min=-5.0):
+    """Token stage of every token, sequence by sequence and in token order.
+
+    q_raw, k_raw, g_raw: [T, H, d_k]; v_raw: [T, H, d_v]; beta_raw: [T, H]; conv_w:
+    [H, 2 d_k + d_v, W]; conv_tail: [N, H, 2 d_k + d_v, W-1] raw inputs before each sequence
+    (zeros if None). Returns (q, k, v, g, beta, conv_tail_out) with the tail after each
+    sequence's last token."""
+    q_raw, k_raw, v_raw = _f64(q_raw), _f64(k_raw), _f64(v_raw)
+    g_raw, beta_raw, conv_w = _f64(g_raw), _f64(beta_raw), _f64(conv_w)
+    T, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    W = conv_w.shape[-1]
+    bounds = _seq_bounds(T, cu_seqlens)
+    q, k, v = np.zeros((T, H, dk)), np.zeros((T, H, dk)), np.zeros((T, H, dv))
+    tail_out = np.zeros((len(bounds), H, 2 * dk + dv, W - 1))
+    for n, (bos, eos) in enumerate(bounds):
+        for h in range(H):
+            tail = (np.zeros((2 * dk + dv, W - 1)) if conv_tail is None
+                    else _f64(conv_tail)[n, h].copy())
+            for t in range(bos, eos):
+                raw = np.concatenate([q_raw[t, h], k_raw[t, h], v_raw[t, h]])
+                y, tail = causal_conv_window(tail, raw, conv_w[h])
+                if act:
+                    y = silu(y)
+                qq, kk = y[:dk], y[dk:2 * dk]
+                q[t, h] = qq / np.sqrt(np.sum(qq * qq) + eps_l2)
+                k[t, h] = kk / np.sqrt(np.sum(kk * kk) + eps_l2)
+                v[t, h] = y[2 * dk:]
+            tail_out[n, h] = tail
+    beta = sigmoid(beta_raw)
+    g = np.maximum(-softplus(g_raw), g_min)
+    return q, k, v, g, beta, tail_out
+
+
+def prefill_raw_fwd(q_raw, k_raw, v_raw, g_raw, beta_raw, conv_w, conv_tail=None, h0=None,
+                    cu_seqlens=None, scale=1.0, g_min=-5.0, eps_l2=1e-6, act=1):
+    """The raw prefill: the token stage above, then the recurrence. Returns (o, ht,
+    conv_tail_out)."""
+    q, k, v, g, beta, tail = prefill_input_stage(q_raw, k_raw, v_raw, g_raw, beta_raw, conv_w,
+                                                 conv_tail, cu_seqlens, act, eps_l2, g_min)
+    o, ht = recurrence_fwd(q, k, v, g, beta, h0=h0, cu_seqlens=cu_seqlens, scale=scale,
+                           g_min=g_min)
+    return o, ht, tail

@@ -435,3 +435,50 @@ def test_decode_output_norm_unit_rms():
                            wl["conv_w"], np.ones(dv), eps_rms=0.0)
     rms = np.sqrt(np.mean(out["o"] ** 2, axis=-1))
     np.testing.assert_allclose(rms, 1.0, rtol=1e-12)
+
+
+def test_raw_prefill_matches_decode_token_steps():
+    """The raw prefill's token stage is the decode's: running decode_token (no output) over
+    the same tokens from the same state and tail gives the same final state and tail."""
+    rng = np.random.default_rng(91)
+    T, H, dk, dv, W = 9, 2, 8, 8, 4
+    q, k, g = (rng.standard_normal((T, H, dk)) for _ in range(3))
+    v = rng.standard_normal((T, H, dv))
+    beta = rng.standard_normal((T, H))
+    conv_w = 0.5 * rng.standard_normal((H, 2 * dk + dv, W))
+    tail = rng.standard_normal((1, H, 2 * dk + dv, W - 1))
+    h0 = 0.1 * rng.standard_normal((1, H, dk, dv))
+    for act in (0, 1):
+        _, ht, tail_out = ko.prefill_raw_fwd(q, k, v, g, beta, conv_w, conv_tail=tail, h0=h0,
+                                             act=act)
+        for h in range(H):
+            S, tl = h0[0, h].copy(), tail[0, h].copy()
+            for t in range(T):
+                x = dict(q=q[t, h], k=k[t, h], v=v[t, h], g=g[t, h], beta=beta[t, h])
+                S, tl, _ = ko.decode_token(S, tl, x, conv_w[h], np.ones(dv), 1.0, -5.0, 1e-6,
+                                           1e-6, act, output=False)
+            np.testing.assert_allclose(ht[0, h], S, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(tail_out[0, h], tl, rtol=0, atol=0)
+
+
+def test_raw_prefill_tail_of_short_sequences():
+    """A sequence shorter than the tail keeps the older entering-tail entries, shifted; an
+    empty sequence hands the entering tail through unchanged."""
+    rng = np.random.default_rng(92)
+    H, dk, dv, W = 1, 4, 4, 4
+    lengths = [2, 0, 5]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    raw = [rng.standard_normal((T, H, dk)) for _ in range(3)]
+    v = rng.standard_normal((T, H, dv))
+    beta = rng.standard_normal((T, H))
+    tail = rng.standard_normal((3, H, 2 * dk + dv, W - 1))
+    conv_w = rng.standard_normal((H, 2 * dk + dv, W))
+    *_, tail_out = ko.prefill_input_stage(raw[0], raw[1], v, raw[2], beta, conv_w, tail,
+                                          cu_seqlens=cu)
+    # sequence 0 (two tokens): [old tail slot 2, token 0, token 1]
+    np.testing.assert_array_equal(tail_out[0, 0, :dk, 0], tail[0, 0, :dk, 2])
+    np.testing.assert_array_equal(tail_out[0, 0, :dk, 1], raw[0][0, 0])
+    np.testing.assert_array_equal(tail_out[0, 0, 2 * dk:, 2], v[1, 0])
+    np.testing.assert_array_equal(tail_out[1], tail[1])
+    np.testing.assert_array_equal(tail_out[2, 0, dk:2 * dk, :], raw[1][4:7, 0].T)
