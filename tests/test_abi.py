@@ -258,3 +258,33 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(kda, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="libkda.so not found"):
         kda.library()
+
+
+def raw_call(W=4, act=1, eps=1e-6, dk=128, dv=128, conv_w=True, tail_in=None, tail_out=None,
+             ws=True, ws_bytes=None, T=256, H=2):
+    P = [ctypes.c_void_p(BASE + (60 + i) * 64 * GiB) for i in range(12)]
+    need = ctypes.c_size_t(0)
+    kda.library().kda_chunk_fwd_raw_workspace_size(1, T, 1, H, dk, dk, ctypes.byref(need))
+    return kda.library().kda_chunk_fwd_raw(
+        P[0], P[1], P[2], P[3], P[4], P[5] if conv_w else None, tail_in, tail_out, None, None,
+        None, 1, T, 1, H, dk, dv, W, act, eps, 1.0, -5.0, P[6], None, BF16,
+        P[7] if ws else None, need.value if ws_bytes is None else ws_bytes, None)
+
+
+def test_raw_prefill_checks():
+    out = ctypes.c_size_t(0)
+    assert kda.library().kda_chunk_fwd_raw_workspace_size(1, 256, 1, 2, 128, 128,
+                                                          ctypes.byref(out)) == OK
+    # fp32 convolved values plus the operand slots
+    assert out.value == 256 * 2 * 128 * 4 + (256 // 64 + 2) * 2 * 74752
+    assert raw_call(conv_w=False) == NULL
+    assert raw_call(ws=False) == NULL
+    assert raw_call(W=5) == SHAPE
+    assert raw_call(W=0) == SHAPE
+    assert raw_call(act=2) == VALUE
+    assert raw_call(eps=0.0) == VALUE
+    assert raw_call(dv=64) == UNSUP
+    assert raw_call(ws_bytes=16) == WS
+    same = ctypes.c_void_p(BASE + 80 * 64 * GiB)
+    assert raw_call(tail_in=same, tail_out=same) == ALIAS          # tails must not overlap
+    assert raw_call(tail_out=ctypes.c_void_p(BASE + 60 * 64 * GiB)) == ALIAS   # on top of q
