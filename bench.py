@@ -5,11 +5,12 @@ One step = one kda_chunk_fwd over the 8192-token, 96-head, d = 128 prefill (bf16
 fp32 g, beta and state; entering state h0 ~ N(0, 0.02^2); bf16 output plus fp32 final
 state), inputs resident in HBM before the timed region: that is the line's ``value``. The
 call takes the path the library recommends for the shape (two launches here, with a
-workspace allocated before the timed region); the one-launch path is timed beside it. Three
+workspace allocated before the timed region); the one-launch path is timed beside it. Four
 more legs ride on the same line: ``decode`` (kda_decode_replay on the 256-request, 96-head
 speculative verify: window of 7 drafts plus the bonus token, HBM GB/s and latency),
-``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill) and
-``varlen`` (kda_chunk_fwd on the 64-sequence packed batch with per-sequence h0).
+``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill),
+``varlen`` (kda_chunk_fwd on the 64-sequence packed batch with per-sequence h0) and
+``raw_prefill`` (kda_chunk_fwd_raw: the prefill shape from raw projections).
 Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs ...]
@@ -230,6 +231,50 @@ def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
                         else "chunk kernel (one launch)")}
 
 
+def bench_raw(kda, wl, torch, dev, stream, steps, warmup):
+    """kda_chunk_fwd_raw on the prefill shape (8192 tokens x 96 heads, d = 128) from raw bf16
+    projections: short convolution (width 4), SiLU, L2 input norms and gates fused into the
+    prep pass, entering conv tails and h0 given."""
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    inp = wl.raw_prefill_inputs(T=T, H=H, dk=dk, dv=dv, conv_width=4, seed=cfg["seed"],
+                                h0_std=cfg["h0_std"], device=dev)
+    o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    ht = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    tail_out = torch.empty_like(inp["conv_tail"])
+    need = ctypes_size(kda, T, H, dk, dv)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def launch():
+        kda.chunk_fwd_raw(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                          conv_tail=inp["conv_tail"], h0=inp["h0"], o=o, ht=ht, workspace=ws,
+                          conv_tail_out=tail_out, stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup)
+    avg = sum(ms) / len(ms)
+    # raw bf16 q, k, v, g (4 d) and beta in, o out, conv taps and tails, h0 and final state
+    nbytes = (T * H * (2 * 4 * dk + 2 + 2 * dv) + 2 * H * dk * dv * 4
+              + 2 * H * (2 * dk + dv) * 3 * 4 + H * (2 * dk + dv) * 4 * 4)
+    del inp, o, ht, ws, tail_out
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill_8k from raw projections: T={T}, H={H}, d_k=d_v={dk}, bf16 raw "
+                        "q/k/v/g/beta, conv width 4 with entering tails, SiLU, h0, bf16 output",
+            "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "algorithmic_bytes_per_call": nbytes, "workspace_bytes": need,
+            "kernels": "prep pass with the fused token stage (chunk kernel) + walk"}
+
+
+def ctypes_size(kda, T, H, dk, dv):
+    """Workspace bytes of kda_chunk_fwd_raw for one sequence."""
+    import ctypes
+    out = ctypes.c_size_t(0)
+    st = kda.library().kda_chunk_fwd_raw_workspace_size(1, T, 1, H, dk, dv, ctypes.byref(out))
+    if st != 0:
+        raise RuntimeError(f"kda_chunk_fwd_raw_workspace_size: status {st}")
+    return int(out.value)
+
+
 def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
     cfg = wl.CONFIGS["ultralong_256k"]
     T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
@@ -265,9 +310,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,segment,varlen",
+    ap.add_argument("--legs", default="prefill,decode,segment,varlen,raw",
                     help="comma-separated legs to run besides the prefill line "
-                         "(decode, segment, varlen); the prefill leg always runs")
+                         "(decode, segment, varlen, raw); the prefill leg always runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -379,7 +424,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
     legs = set(args.legs.split(","))
-    if legs & {"decode", "segment", "varlen"}:
+    if legs & {"decode", "segment", "varlen", "raw"}:
         del inp, q, k, v, g, beta, h0, o, ht, ws
         torch.cuda.empty_cache()
     if "decode" in legs:
@@ -388,6 +433,8 @@ def main():
     if "segment" in legs:
         line["segment_cp"] = bench_segment(kda, wl, torch, dev, stream,
                                            max(3, args.steps // 4), min(args.warmup, 2))
+    if "raw" in legs:
+        line["raw_prefill"] = bench_raw(kda, wl, torch, dev, stream, args.steps, args.warmup)
     if "varlen" in legs:
         line["varlen"] = bench_varlen(kda, wl, torch, dev, stream, max(3, args.steps // 4),
                                       min(args.warmup, 1))

@@ -289,6 +289,13 @@ __device__ __forceinline__ void store4_split(typename Pol::E* hi, typename Pol::
   }
 }
 
+// Activations of the raw token stage, with the hardware reciprocal and exponential (each
+// within an ulp or two of fp32; the stage's outputs then pass through bf16 and fp16 operands)
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+__device__ __forceinline__ float silu_fast(float x) { return x * sigmoid_fast(x); }
+
 // Prep pass: copy one chunk's serial-step operands from their LDS tiles to its slot, in
 // fragment order (wave w writes fragments w, w + 4, ...; one 16-byte store per lane each).
 template <class Pol, class L, int DK>
@@ -493,6 +500,39 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     load_chunk_any<kPrep ? kLoadAll & ~kLoadV : (kOut ? kLoadAll : kLoadAll & ~kLoadQ), Tio, DK, 0,
                    8, kRaw>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
 
+  // raw mode: a chunk's convolution history (the q, k rows before each thread's first
+  // token) and its raw value rows (value mapping: 4 channels x kTPV tokens per thread, plus
+  // the three rows before), loaded one chunk ahead like the other inputs. Rows before the
+  // sequence come from the entering tail when they are used.
+  constexpr int kQuadsV = DK / 4, kTPV = 64 / (256 / kQuadsV);
+  bf16x4 pre_hq[3], pre_hk[3], pre_v[kTPV + 3];
+  auto raw_prefetch = [&](int cs, int L, int lane_) {
+    const int W = p.conv_width;
+    const int rb0_ = 16 * w + (lane_ / PM::kLPT) * TPT;
+    const int c0_ = 4 * (lane_ % PM::kLPT);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int tok = cs + rb0_ - 1 - i;
+      pre_hq[i] = pre_hk[i] = bf16x4{};
+      if (i + 1 < W && tok >= seq_bos) {
+        const size_t off = (size_t(tok) * H + h) * DK + c0_;
+        pre_hq[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.q) + off);
+        pre_hk[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.k) + off);
+      }
+    }
+    const int cv0 = 4 * (tid % kQuadsV), tv0 = kTPV * (tid / kQuadsV);
+#pragma unroll
+    for (int i = 0; i < kTPV + 3; ++i) {
+      const int tok = cs + tv0 - 3 + i;
+      pre_v[i] = bf16x4{};
+      if (i >= 3 - (W - 1) && tok < cs + L && tok >= seq_bos)
+        pre_v[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.v) +
+                                                    (size_t(tok) * H + h) * DK + cv0);
+    }
+  };
+  if constexpr (kRaw)
+    if (bos < eos) raw_prefetch(bos, min(kChunk, eos - bos), lane);
+
   const int lane0 = lane, q4_0 = q4, ln0 = ln;
   for (int cstart = bos; cstart < eos; cstart += kChunk) {
     const int Lc = min(kChunk, eos - cstart);
@@ -535,18 +575,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       for (int i = 0; i < 3; ++i) {
         const int tok = cstart + rb0 - 1 - i;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) hq[i][c] = hk[i][c] = 0.f;
+        for (int c = 0; c < 4; ++c) {
+          hq[i][c] = (float)pre_hq[i][c];   // zero where not loaded
+          hk[i][c] = (float)pre_hk[i][c];
+        }
         if (i + 1 < W) {
-          if (tok >= seq_bos) {
-            const size_t off = (size_t(tok) * H + h) * DK + c0;
-            const bf16x4 a = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.q) + off);
-            const bf16x4 b = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.k) + off);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              hq[i][c] = (float)a[c];
-              hk[i][c] = (float)b[c];
-            }
-          } else if (p.conv_tail_in) {
+          if (tok < seq_bos && p.conv_tail_in) {
             const int m = (W - 1) - (seq_bos - tok);   // tail slot of that token, oldest first
             const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
 #pragma unroll
@@ -574,8 +608,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
             yk = fmaf(wk[c][m], xk, yk);
           }
           if (p.act) {
-            yq = yq / (1.f + __expf(-yq));
-            yk = yk / (1.f + __expf(-yk));
+            yq = silu_fast(yq);
+            yk = silu_fast(yk);
           }
           qin[t][c] = yq;
           kin[t][c] = yk;
@@ -588,7 +622,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           ssq = sum_xor16(ssq);
           ssk = sum_xor16(ssk);
         }
-        const float rq = 1.f / sqrtf(ssq + p.eps_l2), rk = 1.f / sqrtf(ssk + p.eps_l2);
+        const float rq = __builtin_amdgcn_rsqf(ssq + p.eps_l2);
+        const float rk = __builtin_amdgcn_rsqf(ssk + p.eps_l2);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           qin[t][c] *= rq;
@@ -599,22 +634,16 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       // ~15 x their RMS, and one bf16 rounding of them costs several % of the outputs' RMS):
       // thread = 4 value channels x kTPV tokens
       {
-        constexpr int kQuads = DK / 4, kTPV = 64 / (256 / kQuads);
-        const int cv0 = 4 * (tid % kQuads), tv0 = kTPV * (tid / kQuads);
-        const __bf16* vraw = reinterpret_cast<const __bf16*>(p.v);
+        const int cv0 = 4 * (tid % kQuadsV), tv0 = kTPV * (tid / kQuadsV);
         float xv[kTPV + 3][4];
 #pragma unroll
         for (int i = 0; i < kTPV + 3; ++i) {
           const int tok = cstart + tv0 - 3 + i;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) xv[i][c] = 0.f;
+          for (int c = 0; c < 4; ++c) xv[i][c] = (float)pre_v[i][c];   // zero where not loaded
           if (i < 3 && i < 3 - (W - 1)) continue;          // history beyond the taps
           if (tok >= cstart + Lc) continue;
-          if (tok >= seq_bos) {
-            const bf16x4 a = *reinterpret_cast<const bf16x4*>(vraw + (size_t(tok) * H + h) * DK + cv0);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) xv[i][c] = (float)a[c];
-          } else if (p.conv_tail_in) {
+          if (tok < seq_bos && p.conv_tail_in) {
             const int m = (W - 1) - (seq_bos - tok);
             const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
 #pragma unroll
@@ -632,12 +661,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
             float acc = 0.f;
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc = fmaf(wv[c][m], xv[t + m][c], acc);
-            y[c] = p.act ? acc / (1.f + __expf(-acc)) : acc;
+            y[c] = p.act ? silu_fast(acc) : acc;
           }
           *reinterpret_cast<f32x4*>(p.v_conv + (size_t(tok) * H + h) * DK + cv0) =
               f32x4{y[0], y[1], y[2], y[3]};
         }
       }
+      // the next chunk's history and value rows: a whole chunk to land
+      if (more) raw_prefetch(nstart, nLc, lane);
     }
     auto raw_in = [&](auto full) {
       constexpr bool kFull = decltype(full)::value;
@@ -649,7 +680,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           if constexpr (kRaw) {
             // decay e^{max(-softplus(x), g_min)} = max(sigmoid(-x), e^{g_min})
             const float x = (float)raw.g[t][c];
-            ex[t][c] = valid ? fmaxf(1.f / (1.f + __expf(x)), p.decay_floor) : 1.f;
+            ex[t][c] = valid ? fmaxf(sigmoid_fast(-x), p.decay_floor) : 1.f;
             kv[t][c] = valid ? kin[t][c] : 0.f;
             qv[t][c] = valid ? qin[t][c] : 0.f;
           } else {
@@ -688,7 +719,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
     float beta_r;
     if constexpr (kRaw)
-      beta_r = (16 * w + lane < Lc) ? 1.f / (1.f + __expf(-(float)raw.beta)) : 0.f;
+      beta_r = (16 * w + lane < Lc) ? sigmoid_fast((float)raw.beta) : 0.f;
     else
       beta_r = (16 * w + lane < Lc) ? raw.beta : 0.f;
     // 1 / rho from one reciprocal per channel: 1/rho_t = (1/rho_last) x the decays after t
