@@ -33,6 +33,8 @@ PINS = [
     ("decode single token", pins.test_decode_single_token_is_one_recurrence_step, ()),
     ("decode stream lossless", pins.test_decode_speculative_stream_is_lossless, ()),
     ("decode output norm", pins.test_decode_output_norm_unit_rms, ()),
+    ("raw prefill = decode token steps", pins.test_raw_prefill_matches_decode_token_steps, ()),
+    ("raw prefill tails", pins.test_raw_prefill_tail_of_short_sequences, ()),
 ]
 
 
@@ -208,6 +210,42 @@ def _decode_token(variant):
     return f
 
 
+def _prefill_stage(variant):
+    """The raw prefill's token stage with one planted mistake."""
+    def f(q_raw, k_raw, v_raw, g_raw, beta_raw, conv_w, conv_tail=None, cu_seqlens=None, act=1,
+          eps_l2=1e-6, g_min=-5.0):
+        q_raw, k_raw, v_raw = (np.asarray(x, np.float64) for x in (q_raw, k_raw, v_raw))
+        conv_w = np.asarray(conv_w, np.float64)
+        T, H, dk = q_raw.shape
+        dv = v_raw.shape[-1]
+        W = conv_w.shape[-1]
+        bounds = ko._seq_bounds(T, cu_seqlens)
+        q, k, v = np.zeros((T, H, dk)), np.zeros((T, H, dk)), np.zeros((T, H, dv))
+        tail_out = np.zeros((len(bounds), H, 2 * dk + dv, W - 1))
+        for n, (bos, eos) in enumerate(bounds):
+            for h in range(H):
+                start = (np.zeros((2 * dk + dv, W - 1)) if conv_tail is None
+                         or variant == "entering tail ignored"
+                         else np.asarray(conv_tail, np.float64)[n, h].copy())
+                tail = start.copy()
+                for t in range(bos, eos):
+                    raw = np.concatenate([q_raw[t, h], k_raw[t, h], v_raw[t, h]])
+                    y, new_tail = ko.causal_conv_window(tail, raw, conv_w[h])
+                    if variant != "tail not carried":
+                        tail = new_tail
+                    if act:
+                        y = ko.silu(y)
+                    qq, kk = y[:dk], y[dk:2 * dk]
+                    q[t, h] = qq / np.sqrt(np.sum(qq * qq) + eps_l2)
+                    k[t, h] = kk if variant == "key norm missing" else kk / np.sqrt(np.sum(kk * kk) + eps_l2)
+                    v[t, h] = v_raw[t, h] if variant == "value conv skipped" else y[2 * dk:]
+                tail_out[n, h] = start if variant == "leaving tail not written" else tail
+        beta = ko.sigmoid(beta_raw)
+        g = np.maximum(-ko.softplus(g_raw), g_min)
+        return q, k, v, g, beta, tail_out
+    return f
+
+
 OTHER_MUTANTS = {
     "token map: decay after the correction": ("token_transition", _token_transition("decay after the correction")),
     "token map: correction sign": ("token_transition", _token_transition("correction sign")),
@@ -225,6 +263,11 @@ OTHER_MUTANTS = {
     "decode: decay gate wrong": ("decode_token", _decode_token("decay gate sign")),
     "decode: output gate missing": ("decode_token", _decode_token("output gate missing")),
     "decode: norm weight missing": ("decode_token", _decode_token("norm weight missing")),
+    "raw prefill: key norm missing": ("prefill_input_stage", _prefill_stage("key norm missing")),
+    "raw prefill: tail not carried": ("prefill_input_stage", _prefill_stage("tail not carried")),
+    "raw prefill: entering tail ignored": ("prefill_input_stage", _prefill_stage("entering tail ignored")),
+    "raw prefill: value conv skipped": ("prefill_input_stage", _prefill_stage("value conv skipped")),
+    "raw prefill: leaving tail not written": ("prefill_input_stage", _prefill_stage("leaving tail not written")),
 }
 
 
