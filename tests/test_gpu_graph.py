@@ -1,0 +1,68 @@
+"""The library's launches inside HIP graphs (torch.cuda.CUDAGraph is a HIP graph on ROCm):
+the calls allocate nothing, clear nothing with memsets and synchronise nothing, so they can
+be captured; every replay, with eager work and synchronisation between replays, must give
+the eager result bit for bit."""
+import pytest
+import torch
+
+import linear_attention_recurrence_chunk_amd as kda
+from linear_attention_recurrence_chunk_amd import workloads as wl
+from kda_testutil import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_two_launch_prefill_in_a_graph():
+    print("case graph: two-launch prefill T=700 H=4 d=128", flush=True)
+    d = to_dev(wl.prefill_inputs(T=700, H=4, dk=128, dv=128, dtype="bf16", seed=101,
+                                 h0_std=0.02))
+    args = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    need = kda.chunk_fwd_workspace_size(1, 700, 1, 4, 128, 128,
+                                        policy=kda.KDA_CHUNK_WS_TWO_PASS)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty(700, 4, 128, dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty(1, 4, 128, 128, dtype=torch.float32, device="cuda")
+    o_ref, ht_ref = kda.chunk_fwd(*args, h0=d["h0"], workspace=ws)
+    o_ref, ht_ref = o_ref.clone(), ht_ref.clone()
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.chunk_fwd(*args, h0=d["h0"], o=o, ht=ht, workspace=ws,
+                      stream=torch.cuda.current_stream())
+    for i in range(4):
+        o.zero_()
+        ht.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref), f"replay {i}"
+
+
+def test_decode_verify_in_a_graph():
+    """The page-shaped tiny verify (1 request, 12 heads, 4 new tokens): the graph restores the
+    committed state and tail with device copies, then runs the fused verify."""
+    print("case graph: decode verify R=1 H=12 n_new=4", flush=True)
+    w = wl.decode_inputs(R=1, H=12, dk=128, dv=128, n_new=4, window=4, seed=102,
+                         device="cuda")
+    state, tail = w.state.clone(), w.conv_tail.clone()
+    acc = torch.empty_like(state)
+    o = torch.empty(1, 4, 12, 128, dtype=torch.bfloat16, device="cuda")
+    o_ref, acc_ref = kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w)
+    o_ref, acc_ref, s_ref, t_ref = o_ref.clone(), acc_ref.clone(), state.clone(), tail.clone()
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        state.copy_(w.state)
+        tail.copy_(w.conv_tail)
+        kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
+                          state_acc=acc, o=o, stream=torch.cuda.current_stream())
+    for i in range(4):
+        o.zero_()
+        acc.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(acc, acc_ref), f"replay {i}"
+        assert torch.equal(state, s_ref) and torch.equal(tail, t_ref), f"replay {i}"
