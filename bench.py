@@ -5,9 +5,11 @@ One step = one kda_chunk_fwd over the 8192-token, 96-head, d = 128 prefill (bf16
 fp32 g, beta and state; entering state h0 ~ N(0, 0.02^2); bf16 output plus fp32 final
 state), inputs resident in HBM before the timed region: that is the line's ``value``. The
 call takes the path the library recommends for the shape (two launches here, with a
-workspace allocated before the timed region); the one-launch path is timed beside it. Four
+workspace allocated before the timed region); the one-launch path is timed beside it. Six
 more legs ride on the same line: ``decode`` (kda_decode_replay on the 256-request, 96-head
 speculative verify: window of 7 drafts plus the bonus token, HBM GB/s and latency),
+``verify_tiny`` (the same call for 1 request x 12 heads x 4 new tokens, replayed from a HIP
+graph), ``decode_sweep`` (the 256 x 96 verify's latency for 1, 2, 4 and 8 new tokens),
 ``segment_cp`` (kda_segment_cp_fwd on the 262144-token, 12-head ultra-long prefill),
 ``varlen`` (kda_chunk_fwd on the 64-sequence packed batch with per-sequence h0) and
 ``raw_prefill`` (kda_chunk_fwd_raw: the prefill shape from raw projections).
@@ -195,6 +197,73 @@ def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
     return out
 
 
+def bench_verify_tiny(kda, wl, torch, dev, stream, steps, warmup, per_graph=50):
+    """The fused verify at one tensor-parallel rank's share of a single request: 1 request,
+    12 heads, d = 128, 4 new tokens (3 drafts + 1 bonus), launched back to back from a
+    captured HIP graph so that host launch cost is off the critical path; also the eager
+    per-launch duration."""
+    R, H, D, W, n_new = 1, 12, 128, 4, 4
+    w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=W, n_new=n_new, window=n_new, seed=5,
+                         device=dev)
+    state, tail = w.state.clone(), w.conv_tail.clone()
+    acc = torch.empty_like(state)
+    o = torch.empty(R, n_new, H, D, dtype=torch.bfloat16, device=dev)
+
+    def launch(s):
+        kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
+                          state_acc=acc, o=o, stream=s)
+
+    eager = timed_launches(lambda: launch(stream), stream, steps, warmup)
+    # the state is updated in place, so back-to-back launches do the same work on evolving
+    # values (the delta rule keeps them bounded)
+    launch(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(per_graph):
+            launch(torch.cuda.current_stream())
+    replay = timed_launches(graph.replay, stream, steps, warmup)
+    per_call_us = [1e3 * x / per_graph for x in replay]
+    n_acc_total = int(w.n_acc.sum().item())
+    nbytes = decode_bytes(R, H, D, W, n_new, n_acc_total, 2)
+    avg_us = sum(per_call_us) / len(per_call_us)
+    return {"workload": f"verify_tiny: {R} request x {H} heads, d_k=d_v={D}, {n_new} new tokens, "
+                        f"{n_acc_total} accepted drafts replayed, conv width {W}",
+            "graph_latency_us": avg_us, "graph_min_latency_us": min(per_call_us),
+            "launches_per_graph": per_graph,
+            "eager_latency_us": 1e3 * sum(eager) / len(eager),
+            "achieved_gbs": nbytes / (avg_us * 1e-6) / 1e9,
+            "algorithmic_bytes_per_launch": nbytes}
+
+
+def bench_decode_sweep(kda, wl, torch, dev, stream, steps, warmup, n_news=(1, 2, 4, 8)):
+    """Verify latency of the 256-request, 96-head workload as the new-token window grows."""
+    cfg = wl.CONFIGS["decode_verify"]
+    R, H, D, W = cfg["R"], cfg["H"], cfg["dk"], cfg["conv_width"]
+    out = {}
+    for n_new in n_news:
+        w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=W, n_new=n_new, window=cfg["window"],
+                             seed=cfg["seed"], device=dev)
+        state, tail = w.state.clone(), w.conv_tail.clone()
+        acc = torch.empty_like(state)
+        o = torch.empty(R, n_new, H, D, dtype=torch.bfloat16, device=dev)
+
+        def restore():
+            state.copy_(w.state)
+            tail.copy_(w.conv_tail)
+
+        def launch():
+            kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
+                              state_acc=acc, o=o, stream=stream)
+
+        ms = timed_launches(launch, stream, steps, warmup, before=restore)
+        out[str(n_new)] = sum(ms) / len(ms)
+        del w, state, tail, acc, o
+    return {"workload": f"decode_verify with n_new in {list(n_news)} (window 8, accepted drafts "
+                        "uniform in 0..7)", "latency_ms_by_n_new": out}
+
+
 def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
     """kda_chunk_fwd on the 64-sequence packed batch (lengths uniform in [512, 16384], per
     sequence h0, final states written), on the library's automatic path."""
@@ -310,9 +379,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,segment,varlen,raw",
-                    help="comma-separated legs to run besides the prefill line "
-                         "(decode, segment, varlen, raw); the prefill leg always runs")
+    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen,raw",
+                    help="comma-separated legs to run besides the prefill line (decode, "
+                         "verify_tiny, decode_sweep, segment, varlen, raw); the prefill leg "
+                         "always runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -424,12 +494,18 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
     legs = set(args.legs.split(","))
-    if legs & {"decode", "segment", "varlen", "raw"}:
+    if legs & {"decode", "verify_tiny", "decode_sweep", "segment", "varlen", "raw"}:
         del inp, q, k, v, g, beta, h0, o, ht, ws
         torch.cuda.empty_cache()
     if "decode" in legs:
         line["decode"] = bench_decode(kda, wl, torch, dev, stream, args.steps, args.warmup,
                                       not args.no_cpu_baseline)
+    if "verify_tiny" in legs:
+        line["verify_tiny"] = bench_verify_tiny(kda, wl, torch, dev, stream, args.steps,
+                                                args.warmup)
+    if "decode_sweep" in legs:
+        line["decode_sweep"] = bench_decode_sweep(kda, wl, torch, dev, stream,
+                                                  max(3, args.steps // 4), min(args.warmup, 2))
     if "segment" in legs:
         line["segment_cp"] = bench_segment(kda, wl, torch, dev, stream,
                                            max(3, args.steps // 4), min(args.warmup, 2))

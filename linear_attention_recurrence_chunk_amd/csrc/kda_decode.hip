@@ -318,24 +318,35 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
       const bool output = t >= n_acc;
       const float qk = s_nrm[i][2];
       const float beta = s_beta[i];
+      // the lane's rows of the token's read-out factors (a k^, a q^), every read issued
+      // before the first is used so that their LDS latencies overlap
+      f32x4 ak[RPL / 4], aq[RPL / 4];
+#pragma unroll
+      for (int m = 0; m < RPL / 4; ++m) {
+        ak[m] = *reinterpret_cast<const f32x4*>(&s_k[i][row0 + 4 * m]);
+        aq[m] = *reinterpret_cast<const f32x4*>(&s_q[i][row0 + 4 * m]);
+      }
       float ks[CPL], qs[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         ks[j] = 0.f;
         qs[j] = 0.f;
       }
-      // row factors four at a time (16-byte reads; few registers in flight)
 #pragma unroll
-      for (int i4 = 0; i4 < RPL; i4 += 4) {
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(&s_k[i][row0 + i4]);
-        const f32x4 aq = *reinterpret_cast<const f32x4*>(&s_q[i][row0 + i4]);
+      for (int m = 0; m < RPL / 4; ++m)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int j = 0; j < CPL; ++j) {
-            ks[j] = fmaf(ak[u], S[i4 + u][j], ks[j]);
-            qs[j] = fmaf(aq[u], S[i4 + u][j], qs[j]);
+            ks[j] = fmaf(ak[m][u], S[4 * m + u][j], ks[j]);
+            qs[j] = fmaf(aq[m][u], S[4 * m + u][j], qs[j]);
           }
+      // the update's factors (a, beta k^), read while the column sums are reduced
+      f32x4 fa[RPL / 4], fb[RPL / 4];
+#pragma unroll
+      for (int m = 0; m < RPL / 4; ++m) {
+        fa[m] = *reinterpret_cast<const f32x4*>(&s_a[i][row0 + 4 * m]);
+        fb[m] = *reinterpret_cast<const f32x4*>(&s_bk[i][row0 + 4 * m]);
       }
       // sum over the 8 row groups (lanes cg, cg + 8, ..., cg + 56), fixed butterfly order
 #pragma unroll
@@ -347,14 +358,12 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) e[j] = s_v[i][col0 + j] - ks[j];
 #pragma unroll
-      for (int i4 = 0; i4 < RPL; i4 += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&s_a[i][row0 + i4]);
-        const f32x4 bk = *reinterpret_cast<const f32x4*>(&s_bk[i][row0 + i4]);
+      for (int m = 0; m < RPL / 4; ++m)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) S[i4 + u][j] = fmaf(bk[u], e[j], a[u] * S[i4 + u][j]);
-      }
+          for (int j = 0; j < CPL; ++j)
+            S[4 * m + u][j] = fmaf(fb[m][u], e[j], fa[m][u] * S[4 * m + u][j]);
       if (output) {
         float osq = 0.f;
 #pragma unroll
