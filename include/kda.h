@@ -169,8 +169,11 @@ int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
  * beta = sigmoid(beta_raw), g = max(-softplus(g_raw), g_min); then the recurrence of
  * kda_chunk_fwd (h0, ht, o, scale, packed sequences as there). The convolved values are
  * stored once, in fp32, for the serial walk. Supported: d_k = d_v in {64, 128}, conv_width in
- * 1..4. `workspace` (16-byte aligned, at least kda_chunk_fwd_raw_workspace_size bytes) holds
- * the convolved values and the operand slots of the whole batch.
+ * 1..4. `workspace` (16-byte aligned) holds the convolved values and the operand slots: with
+ * kda_chunk_fwd_raw_workspace_size(...) bytes those of the whole batch; with less, down to
+ * that size for the longest sequence alone, consecutive groups of whole sequences run one
+ * after the other, each group a prep pass and a walk (sequences are independent, so the
+ * result is the same bits). Below that, KDA_ERR_WORKSPACE_TOO_SMALL.
  */
 int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
                       const void* g_raw, const void* beta_raw, const float* conv_w,

@@ -246,6 +246,18 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     return a["o"], a["ht"]
 
 
+def chunk_fwd_raw_workspace_size(batch, seq_len, n_seqs, H, dk, dv):
+    """kda_chunk_fwd_raw_workspace_size: bytes for the whole batch at once. A smaller workspace,
+    down to this size for the longest sequence alone (batch = n_seqs = 1), runs groups of
+    whole sequences."""
+    need = ctypes.c_size_t(0)
+    st = library().kda_chunk_fwd_raw_workspace_size(int(batch), int(seq_len), int(n_seqs),
+                                                    int(H), int(dk), int(dv), ctypes.byref(need))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_raw_workspace_size")
+    return need.value
+
+
 def chunk_fwd_raw(q, k, v, g, beta, conv_w, conv_tail=None, h0=None, cu_seqlens=None,
                   scale=1.0, g_min=-5.0, eps_l2=1e-6, act=1, o=None, ht=None,
                   output_final_state=True, out_dtype=None, workspace=None,

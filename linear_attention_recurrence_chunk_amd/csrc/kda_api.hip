@@ -444,9 +444,17 @@ int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
-  const size_t vbytes = raw_vconv_bytes(T, num_heads, d_v);
-  const size_t need = vbytes + two_pass_workspace_bytes(T, N, num_heads, d_k);
-  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // the whole batch at once, or groups of whole sequences: a group needs the convolved values
+  // and operand slots of its own tokens, at least those of the longest sequence
+  auto raw_bytes = [&](int64_t tokens, int64_t seqs) {
+    return raw_vconv_bytes(tokens, num_heads, d_v) +
+           two_pass_workspace_bytes(tokens, seqs, num_heads, d_k);
+  };
+  const size_t need_all = raw_bytes(T, N);
+  const size_t need_min = raw_bytes(max_seq_len(cu_seqlens_host, N, seq_len), 1);
+  if (workspace_bytes < (need_min < need_all ? need_min : need_all))
+    return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t need = workspace_bytes < need_all ? workspace_bytes : need_all;
   const size_t C3 = size_t(2 * d_k + d_v);
   const size_t tail_bytes = size_t(N) * num_heads * C3 * size_t(conv_width - 1) * 4;
   {
@@ -490,8 +498,6 @@ int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
   p.scale = scale;
   p.g_min = g_min;
   p.ckpt_every = 64;
-  p.v_conv = static_cast<float*>(workspace);
-  p.ws_ops = static_cast<char*>(workspace) + vbytes;
   p.conv_w = conv_w;
   p.conv_tail_in = conv_tail_in;
   p.conv_tail_out = conv_tail_out;
@@ -500,13 +506,39 @@ int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
   p.eps_l2 = eps_l2;
   p.decay_floor = expf(g_min);
   p.mode = kda::kModeWalk;
-  int rc = launch_status(
-      kda::launch_chunk_prep(p, prep_groups(cu_seqlens_host, N, seq_len), d_k, s, true));
-  if (rc != KDA_OK) return rc;
-  // the walk reads the convolved values
-  p.v = p.v_conv;
-  p.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
-  return launch_status(kda::launch_chunk_walk(p, out_dtype, d_k, s, true));
+  auto first_tok = [&](int n) -> int64_t {
+    return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
+  };
+  for (int n0 = 0; n0 < N;) {
+    int n1 = n0 + 1;
+    while (n1 < N && raw_bytes(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0) <= workspace_bytes)
+      ++n1;
+    const int64_t tok0 = first_tok(n0);
+    const int64_t tokens = first_tok(n1) - tok0;
+    kda::ChunkParams gp = p;
+    gp.seq0 = n0;
+    gp.slot_tok0 = int(tok0);
+    gp.n_seqs = n1 - n0;
+    gp.n_units = (n1 - n0) * num_heads;
+    // the kernels index the convolved values by global token: the group's region is handed
+    // over as a base shifted back by its first token (64-bit address arithmetic, so every
+    // address they form lies inside the region)
+    const uintptr_t vbase = reinterpret_cast<uintptr_t>(workspace) -
+                            uintptr_t(tok0) * uintptr_t(num_heads) * uintptr_t(d_v) * 4u;
+    gp.v_conv = reinterpret_cast<float*>(vbase);
+    gp.ws_ops = static_cast<char*>(workspace) + raw_vconv_bytes(tokens, num_heads, d_v);
+    const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
+    int rc = launch_status(
+        kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s, true));
+    if (rc != KDA_OK) return rc;
+    // the walk reads the convolved values
+    gp.v = gp.v_conv;
+    gp.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
+    rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s, true));
+    if (rc != KDA_OK) return rc;
+    n0 = n1;
+  }
+  return KDA_OK;
 }
 
 int kda_segment_cp_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

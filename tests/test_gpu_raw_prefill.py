@@ -93,3 +93,34 @@ def test_raw_prefill_without_entering_tail():
     for e in (_errs(np64(o), o_ref), _errs(np64(ht), ht_ref)):
         assert e[0] <= TOL_RAW_MAX and e[1] <= TOL_RAW_RMS
     assert np.array_equal(np64(tail), tail_ref)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_raw_grouped_sequences_bit_identical(dk):
+    """A workspace smaller than the whole batch needs (here the least it accepts: the longest
+    sequence's convolved values and slots) runs groups of whole sequences: the same bits as
+    the whole batch at once, outputs, final states and leaving tails included."""
+    lengths = [300, 0, 640, 129, 1024, 64, 1, 500]
+    print(f"case raw grouped sequences dk={dk} lengths={lengths}", flush=True)
+    inp = wl.raw_prefill_inputs(lengths=lengths, H=3, dk=dk, dv=dk, conv_width=4, seed=61 + dk,
+                                h0_std=0.02)
+    d = to_dev(inp)
+    need_min = kda.chunk_fwd_raw_workspace_size(1, max(lengths), 1, 3, dk, dk)
+    need_all = kda.chunk_fwd_raw_workspace_size(1, sum(lengths), len(lengths), 3, dk, dk)
+    assert need_min < need_all
+    res = []
+    for nbytes in (need_all, need_min):
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        res.append(kda.chunk_fwd_raw(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"],
+                                     conv_tail=d["conv_tail"], h0=d["h0"],
+                                     cu_seqlens=d["cu_seqlens"], out_dtype=torch.float32,
+                                     workspace=ws))
+        torch.cuda.synchronize()
+    for a, b, name in zip(res[0], res[1], ("o", "ht", "tail_out")):
+        assert torch.equal(a, b), name
+    with pytest.raises(kda.KDAError) as ei:
+        kda.chunk_fwd_raw(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"],
+                          conv_tail=d["conv_tail"], h0=d["h0"], cu_seqlens=d["cu_seqlens"],
+                          workspace=torch.empty(need_min - 16, dtype=torch.uint8,
+                                                device="cuda"))
+    assert ei.value.status == -6
