@@ -145,7 +145,7 @@ def _out_dtype(q, out_dtype):
 
 
 def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype,
-                  gate_dtype=None):
+                  gate_dtype=None, cu_seqlens_host=None):
     torch = _torch()
     gate_dtype = torch.float32 if gate_dtype is None else gate_dtype
     if q.dim() == 4:                 # [B, T, H, d]
@@ -166,7 +166,15 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, o
     if cu_seqlens is not None:
         if batch != 1:
             raise ValueError("cu_seqlens needs batch 1")
-        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        if cu_seqlens_host is not None:
+            # both copies given: nothing is copied here, so the call can be graph-captured
+            if cu_seqlens_host.device.type != "cpu" or cu_seqlens_host.dtype != torch.int32:
+                raise ValueError("cu_seqlens_host must be a CPU int32 tensor")
+            cu_host = cu_seqlens_host.contiguous()
+            if cu_host.numel() != cu_seqlens.numel():
+                raise ValueError("cu_seqlens_host must match cu_seqlens")
+        else:
+            cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
         cu_dev = cu_seqlens.to(dev, torch.int32).contiguous()
         n_seqs = cu_host.numel() - 1
     else:
@@ -206,7 +214,7 @@ def chunk_fwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF1
 
 def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0, o=None,
               ht=None, output_final_state=True, out_dtype=None, workspace="auto", ckpt_every=0,
-              ckpt=None, stream=None):
+              ckpt=None, stream=None, cu_seqlens_host=None):
     """kda_chunk_fwd. q, k: [B, T, H, d_k] or packed [T, H, d_k]; v: [.., d_v];
     g: same shape as k (fp32); beta: [.., H] (fp32); h0: [N, H, d_k, d_v] fp32 or None;
     cu_seqlens: [N + 1] int32 (any device) for packed varlen input; out_dtype: None (same as
@@ -216,8 +224,10 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     tensor (two launches, grouped when it is smaller than the whole batch needs). ckpt_every > 0 (a multiple of 64) also returns
     the states after every ckpt_every tokens of each sequence, [T // ckpt_every, H, d_k, d_v]
     fp32 (slot floor(bos_n / ckpt_every) + j for sequence n): (o, ht, ckpt). Returns (o, ht)
-    otherwise."""
-    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
+    otherwise. cu_seqlens_host: the same offsets as a CPU int32 tensor, when the caller has
+    them (with cu_seqlens already int32 on the device, nothing is copied: graph capture)."""
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype,
+                      cu_seqlens_host=cu_seqlens_host)
     T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
     if isinstance(workspace, str):
         policies = {"auto": KDA_CHUNK_WS_AUTO, "two_pass": KDA_CHUNK_WS_TWO_PASS,
@@ -261,7 +271,7 @@ def chunk_fwd_raw_workspace_size(batch, seq_len, n_seqs, H, dk, dv):
 def chunk_fwd_raw(q, k, v, g, beta, conv_w, conv_tail=None, h0=None, cu_seqlens=None,
                   scale=1.0, g_min=-5.0, eps_l2=1e-6, act=1, o=None, ht=None,
                   output_final_state=True, out_dtype=None, workspace=None,
-                  conv_tail_out=None, stream=None):
+                  conv_tail_out=None, stream=None, cu_seqlens_host=None):
     """kda_chunk_fwd_raw: the prefill from raw bf16 projections q, k, g [.., H, d_k], v
     [.., H, d_v], beta [.., H] with the short convolution (taps conv_w [H, 2 d_k + d_v, W]),
     SiLU (act), L2 input norms and gate activations fused into the prep pass. conv_tail: the
@@ -269,7 +279,7 @@ def chunk_fwd_raw(q, k, v, g, beta, conv_w, conv_tail=None, h0=None, cu_seqlens=
     torch = _torch()
     a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state,
                       out_dtype if out_dtype is not None else torch.bfloat16,
-                      gate_dtype=torch.bfloat16)
+                      gate_dtype=torch.bfloat16, cu_seqlens_host=cu_seqlens_host)
     T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
     dev = q.device
     _check(conv_w, "conv_w", torch.float32, dev)
@@ -311,11 +321,13 @@ def segment_cp_workspace_size(batch, seq_len, n_seqs, H, dk, dv, io_dtype=KDA_BF
 
 def segment_cp_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
                    n_segments=0, workspace=None, o=None, ht=None, output_final_state=True,
-                   out_dtype=None, stream=None):
-    """kda_segment_cp_fwd (same tensors as chunk_fwd). ``workspace`` is a uint8 device
-    tensor of at least segment_cp_workspace_size(...) bytes; allocated here if None."""
+                   out_dtype=None, stream=None, cu_seqlens_host=None):
+    """kda_segment_cp_fwd (same tensors as chunk_fwd, cu_seqlens_host included). ``workspace``
+    is a uint8 device tensor of at least segment_cp_workspace_size(...) bytes; allocated here
+    if None."""
     torch = _torch()
-    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype)
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, output_final_state, out_dtype,
+                      cu_seqlens_host=cu_seqlens_host)
     T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
     need = segment_cp_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
                                      a["io"], n_segments)

@@ -66,3 +66,61 @@ def test_decode_verify_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(acc, acc_ref), f"replay {i}"
         assert torch.equal(state, s_ref) and torch.equal(tail, t_ref), f"replay {i}"
+
+
+def _replays_match(graph, outs, refs, n=4):
+    for i in range(n):
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs, refs):
+            assert torch.equal(x, y), f"replay {i}"
+
+
+def test_segment_path_in_a_graph():
+    """Prep pass, transition walk, ordered scan and replay walk (4 launches) in one graph."""
+    print("case graph: segment path T=2048 H=2 n_segments=4", flush=True)
+    d = to_dev(wl.prefill_inputs(T=2048, H=2, dk=128, dv=128, dtype="bf16", seed=103,
+                                 h0_std=0.02))
+    args = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    need = kda.segment_cp_workspace_size(1, 2048, 1, 2, 128, 128, kda.KDA_BF16, 4)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty(2048, 2, 128, dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty(1, 2, 128, 128, dtype=torch.float32, device="cuda")
+    o_ref, ht_ref = kda.segment_cp_fwd(*args, h0=d["h0"], n_segments=4, workspace=ws)
+    o_ref, ht_ref = o_ref.clone(), ht_ref.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        kda.segment_cp_fwd(*args, h0=d["h0"], n_segments=4, workspace=ws, o=o, ht=ht,
+                           stream=torch.cuda.current_stream())
+    _replays_match(graph, (o, ht), (o_ref, ht_ref))
+
+
+def test_raw_prefill_in_a_graph():
+    """The raw-projection prefill (token stage in the prep pass, then the walk) in a graph:
+    outputs, final states and leaving conv tails of every replay equal the eager call's."""
+    lengths = [200, 70, 333]
+    print(f"case graph: raw prefill lengths={lengths} H=2", flush=True)
+    d = to_dev(wl.raw_prefill_inputs(lengths=lengths, H=2, dk=128, dv=128, conv_width=4,
+                                     seed=104, h0_std=0.02))
+    raw = [d[n] for n in ("q", "k", "v", "g", "beta", "conv_w")]
+    T = sum(lengths)
+    ws = torch.empty(kda.chunk_fwd_raw_workspace_size(1, T, len(lengths), 2, 128, 128),
+                     dtype=torch.uint8, device="cuda")
+    cu_host = d["cu_seqlens"].cpu().to(torch.int32)
+    cu_dev = cu_host.cuda()
+    o_ref, ht_ref, tail_ref = kda.chunk_fwd_raw(*raw, conv_tail=d["conv_tail"], h0=d["h0"],
+                                                cu_seqlens=cu_dev, cu_seqlens_host=cu_host,
+                                                workspace=ws)
+    o_ref, ht_ref, tail_ref = o_ref.clone(), ht_ref.clone(), tail_ref.clone()
+    o, ht, tail = torch.empty_like(o_ref), torch.empty_like(ht_ref), torch.empty_like(tail_ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        kda.chunk_fwd_raw(*raw, conv_tail=d["conv_tail"], h0=d["h0"], cu_seqlens=cu_dev,
+                          cu_seqlens_host=cu_host, workspace=ws, o=o, ht=ht,
+                          conv_tail_out=tail, stream=torch.cuda.current_stream())
+    _replays_match(graph, (o, ht, tail), (o_ref, ht_ref, tail_ref))
