@@ -307,9 +307,11 @@ __device__ __forceinline__ void prep_store(char* slot, const typename Pol::ER* s
                                            int w, int lane, int ln, int q4) {
   using OS = OpSlot<DK>;
   constexpr int NS = OS::NS;
+  // streaming stores: the slot is read back by the walk, a launch later (from HBM, not L2)
   auto put = [&](int f, auto frag) {
     static_assert(sizeof(frag) == 16, "one 16-byte fragment per lane");
-    *reinterpret_cast<decltype(frag)*>(slot + size_t(f) * 1024 + lane * 16) = frag;
+    __builtin_nontemporal_store(
+        frag, reinterpret_cast<decltype(frag)*>(slot + size_t(f) * 1024 + lane * 16));
   };
   for (int f = w; f < 4 * NS; f += 4) {
     put(OS::fKg + f, Pol::load_r(sKg, L::LDP, 16 * (f / NS) + ln, f % NS, q4));
@@ -325,8 +327,9 @@ __device__ __forceinline__ void prep_store(char* slot, const typename Pol::ER* s
   for (int f = w; f < 2 * OS::NTD; f += 4)
     put(OS::fKh + f, Pol::load_r(sKhT, L::LDT, 16 * (f / 2) + ln, f % 2, q4));
   if (w == 0 && lane < DK / 4)
-    *reinterpret_cast<f32x4*>(slot + size_t(OS::kDecay) * 1024 + lane * 16) =
-        *reinterpret_cast<const f32x4*>(sDecay + 4 * lane);
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(sDecay + 4 * lane),
+                                reinterpret_cast<f32x4*>(slot + size_t(OS::kDecay) * 1024 +
+                                                         lane * 16));
 }
 
 // kOut false: the transition pass of the segment-parallel path, which keeps only the state
