@@ -1,4 +1,5 @@
 // C ABI of libkda: argument validation (host only, no HIP call) and kernel dispatch.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -176,6 +177,18 @@ int prep_groups(const int32_t* cu_seqlens_host, int N, int seq_len) {
   const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
   const int64_t groups = (max_chunks + kPrepChunks - 1) / kPrepChunks;
   return groups < 1 ? 1 : int(groups);
+}
+
+// The walk takes a group's sequences longest first (ties in sequence order): with more
+// workgroups than compute units, a long sequence dispatched last would finish alone.
+void set_walk_order(kda::ChunkParams& gp, const int32_t* cu_seqlens_host, int n0, int n1) {
+  gp.n_order = 0;
+  const int m = n1 - n0;
+  if (!cu_seqlens_host || m < 2 || m > kda::kMaxOrder) return;
+  for (int i = 0; i < m; ++i) gp.order[i] = uint16_t(i);
+  auto len = [&](uint16_t i) { return cu_seqlens_host[n0 + i + 1] - cu_seqlens_host[n0 + i]; };
+  std::stable_sort(gp.order, gp.order + m, [&](uint16_t a, uint16_t b) { return len(a) > len(b); });
+  gp.n_order = m;
 }
 
 // Automatic segment count of the two-launch segment path (at most kAutoSegments): the count
@@ -392,6 +405,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
           kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s));
       if (rc != KDA_OK) return rc;
       gp.walk_tpw = walk_tiles_per_wg(gp.n_units, gp.n_vt);
+      set_walk_order(gp, cu_seqlens_host, n0, n1);
       rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s));
       if (rc != KDA_OK) return rc;
       n0 = n1;
@@ -534,6 +548,7 @@ int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
     // the walk reads the convolved values
     gp.v = gp.v_conv;
     gp.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
+    set_walk_order(gp, cu_seqlens_host, n0, n1);
     rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s, true));
     if (rc != KDA_OK) return rc;
     n0 = n1;

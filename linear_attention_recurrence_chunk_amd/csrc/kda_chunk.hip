@@ -517,7 +517,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     for (int i = 0; i < 3; ++i) {
       const int tok = cs + rb0_ - 1 - i;
       pre_hq[i] = pre_hk[i] = bf16x4{};
-      if (i + 1 < W && tok >= seq_bos) {
+      // rows of the sequence only: in a ragged last chunk, threads whose rows lie past its end
+      // would otherwise read past the inputs (their outputs are discarded)
+      if (i + 1 < W && tok >= seq_bos && tok < cs + L) {
         const size_t off = (size_t(tok) * H + h) * DK + c0_;
         pre_hq[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.q) + off);
         pre_hk[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.k) + off);

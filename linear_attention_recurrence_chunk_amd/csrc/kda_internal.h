@@ -17,6 +17,8 @@ enum ChunkMode : int {
   kModeWalk = 4,        // two-pass prefill, pass 2: the serial chunk walk from ws_ops
 };
 
+constexpr int kMaxOrder = 256;   // sequences a walk can reorder (launch-parameter bytes)
+
 // One launch of the chunk kernel. A "unit" is one (sequence, segment, head) triple (one
 // segment per sequence in forward mode); every unit is processed by n_vt workgroups, one per
 // 64-column tile of its state (d_v columns, or d_k + d_v columns [P | Q] in transition mode).
@@ -53,6 +55,11 @@ struct ChunkParams {
   // slot ((bos_m - slot_tok0) / 64) + (m - seq0) + c. Both 0 otherwise.
   int seq0;
   int slot_tok0;
+  // walk: the order in which its workgroups take the group's sequences, longest first, so that
+  // the long ones do not start last (n_order > 0: unit sequence u runs sequence
+  // seq0 + order[u]; groups of more than kMaxOrder sequences keep their own order)
+  int n_order;
+  uint16_t order[kMaxOrder];
   // prep mode with raw projections (q, k, v, g, beta before the short convolution, the L2
   // norms and the gate activations, all bf16): taps [H, 2 dk + dv, conv_width] (q, k, v
   // channels), entering convolution tails [N, H, 2 dk + dv, conv_width - 1] (null: zeros),

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   const int DV = p.dv;
   const int h = unit % H;
   const int sj = unit / H;              // global segment index n * n_seg + j
-  const int n = p.seq0 + sj / p.n_seg;
+  const int n = p.seq0 + (p.n_order > 0 ? int(p.order[sj / p.n_seg]) : sj / p.n_seg);
   const int j = sj % p.n_seg;
   const int mode = p.mode;
 
