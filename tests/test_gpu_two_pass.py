@@ -181,3 +181,16 @@ def test_segment_walks_two_tiles_per_workgroup_bit_identical():
         torch.cuda.synchronize()
     (o1, h1), (o2, h2) = res
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_many_sequences_keep_their_order_bit_identical():
+    """Walks take a group's sequences longest first when the group has at most 256 (the other
+    tests here); a group of 300 keeps sequence order. Both give the one-launch kernel's bits."""
+    g = torch.Generator().manual_seed(58)
+    lengths = torch.randint(0, 90, (300,), generator=g).tolist()
+    print(f"case 300 short sequences, {sum(lengths)} tokens", flush=True)
+    inp = wl.prefill_inputs(H=2, dk=64, dv=64, dtype="bf16", seed=58, h0_std=0.02,
+                            lengths=lengths)
+    (o1, h1), (o2, h2) = _both(inp, varlen=True)
+    assert torch.equal(o1, o2)
+    assert torch.equal(h1, h2)
