@@ -105,7 +105,9 @@ typedef enum kda_dtype {
  * kda_chunk_fwd_workspace_size(..., KDA_CHUNK_WS_TWO_PASS, ...) bytes takes the whole batch
  * in one prep and one walk; a smaller one (at least the KDA_CHUNK_WS_MIN size: the longest
  * sequence's slots) takes consecutive groups of whole sequences that fit, two launches per
- * group, with the same results. The workspace must be 16-byte aligned and overlap no other
+ * group, with the same results. Each walk starts a group's longest sequences first (up to
+ * 256 sequences per group; scheduling only, the results do not depend on it). The workspace
+ * must be 16-byte aligned and overlap no other
  * argument; its contents on entry are ignored and on return are undefined. KDA_F32 ignores
  * the workspace.
  *
