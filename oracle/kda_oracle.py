@@ -49,6 +49,7 @@ import numpy as np
 
 __all__ = [
     "recurrence_fwd",
+    "recurrence_bwd",
     "token_transition",
     "brute_force_fwd",
     "chunk_log_decay",
@@ -105,6 +106,59 @@ def recurrence_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=
             o[t] = scale * np.einsum("hkv,hk->hv", S, q[t])     # read-out after the update
         ht[n] = S
     return o, ht
+
+
+def recurrence_bwd(q, k, v, g, beta, do, dht=None, h0=None, cu_seqlens=None, scale=1.0,
+                   g_min=-5.0):
+    """Gradients of recurrence_fwd by reverse-mode differentiation of the same per-token
+    update (the pages give no backward: this is the chain rule applied to the forward
+    definition above, one step at a time, in reverse token order).
+
+    For a loss L with dL/do = ``do`` [T, H, d_v] and dL/dht = ``dht`` [N, H, d_k, d_v] (None:
+    zeros), returns a dict of dq, dk, dg [T, H, d_k], dv [T, H, d_v], dbeta [T, H] and dh0
+    [N, H, d_k, d_v], all fp64. Per token, with a = exp(max(g_t, g_min)):
+        S' = diag(a) S_prev;  u = v_t - S'^T k_t;  S = S' + beta_t k_t u^T;  o_t = scale S^T q_t
+    and, going backwards with D = dL/dS (starting from dht):
+        D += scale q_t do_t^T;               dq_t = scale S do_t
+        dbeta_t = k_t^T D u;                 du = beta_t D^T k_t;    dv_t = du
+        D' = D - k_t du^T;                   dk_t = beta_t D u - S' du
+        dg_t = a * rowsum(S_prev * D') where g_t > g_min, else 0 (the floor is flat)
+        D = diag(a) D'                       (dL/dS_prev; dh0 is D at the sequence start)
+    """
+    q, k, v, g, beta, do = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta), _f64(do)
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    bounds = _seq_bounds(T, cu_seqlens)
+    grads = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+             "dg": np.zeros((T, H, dk)), "dbeta": np.zeros((T, H)),
+             "dh0": np.zeros((len(bounds), H, dk, dv))}
+    for n, (bos, eos) in enumerate(bounds):
+        # forward again, keeping what the reverse steps read
+        S = np.zeros((H, dk, dv)) if h0 is None else _f64(h0)[n].copy()
+        saved = []
+        for t in range(bos, eos):
+            a = np.exp(np.maximum(g[t], g_min))
+            S_prev = S
+            Sp = a[:, :, None] * S_prev
+            u = v[t] - np.einsum("hkv,hk->hv", Sp, k[t])
+            S = Sp + beta[t][:, None, None] * k[t][:, :, None] * u[:, None, :]
+            saved.append((a, S_prev, Sp, u, S))
+        D = np.zeros((H, dk, dv)) if dht is None else _f64(dht)[n].copy()
+        for t in range(eos - 1, bos - 1, -1):
+            a, S_prev, Sp, u, S = saved[t - bos]
+            D = D + scale * q[t][:, :, None] * do[t][:, None, :]
+            grads["dq"][t] = scale * np.einsum("hkv,hv->hk", S, do[t])
+            Du = np.einsum("hkv,hv->hk", D, u)                   # D u
+            grads["dbeta"][t] = np.einsum("hk,hk->h", k[t], Du)
+            du = beta[t][:, None] * np.einsum("hkv,hk->hv", D, k[t])
+            grads["dv"][t] = du
+            Dp = D - k[t][:, :, None] * du[:, None, :]
+            grads["dk"][t] = beta[t][:, None] * Du - np.einsum("hkv,hv->hk", Sp, du)
+            live = g[t] > g_min
+            grads["dg"][t] = np.where(live, a * np.einsum("hkv,hkv->hk", S_prev, Dp), 0.0)
+            D = a[:, :, None] * Dp
+        grads["dh0"][n] = D
+    return grads
 
 
 def token_transition(k_t, g_t, beta_t, g_min=-5.0):

@@ -278,3 +278,81 @@ def test_other_mutant_is_caught(name, monkeypatch):
     failed = failing_pins()
     print(f"{name}: caught by {failed}")
     assert failed, f"no pin catches the mutant '{name}'"
+
+
+# ------------------------------------------------------------------ mutants of the backward
+import test_oracle_backward as bwd_pins  # noqa: E402
+
+BACKWARD_PINS = [
+    ("backward: central differences", bwd_pins.test_gradients_match_central_differences),
+    ("backward: beta = 0 closed forms", bwd_pins.test_beta_zero_closed_forms),
+    ("backward: floored decay", bwd_pins.test_floored_decay_gets_no_gradient),
+]
+
+
+def _backward(variant):
+    """recurrence_bwd with one planted mistake."""
+    def f(q, k, v, g, beta, do, dht=None, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0):
+        q, k, v, g, beta, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta, do))
+        T, H, dk = k.shape
+        dv = v.shape[-1]
+        cu = [0, T] if cu_seqlens is None else [int(c) for c in cu_seqlens]
+        out = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+               "dg": np.zeros((T, H, dk)), "dbeta": np.zeros((T, H)),
+               "dh0": np.zeros((len(cu) - 1, H, dk, dv))}
+        for n in range(len(cu) - 1):
+            bos, eos = cu[n], cu[n + 1]
+            S = np.zeros((H, dk, dv)) if h0 is None else np.asarray(h0, np.float64)[n].copy()
+            saved = []
+            for t in range(bos, eos):
+                a = np.exp(np.maximum(g[t], g_min))
+                Sp = a[:, :, None] * S
+                u = v[t] - np.einsum("hkv,hk->hv", Sp, k[t])
+                S_new = Sp + beta[t][:, None, None] * k[t][:, :, None] * u[:, None, :]
+                saved.append((a, S, Sp, u, S_new))
+                S = S_new
+            D = np.zeros((H, dk, dv)) if dht is None else np.asarray(dht, np.float64)[n].copy()
+            for t in range(eos - 1, bos - 1, -1):
+                a, S_prev, Sp, u, S_t = saved[t - bos]
+                if variant != "read-out term dropped":
+                    D = D + scale * q[t][:, :, None] * do[t][:, None, :]
+                S_read = Sp if variant == "dq from the state before the update" else S_t
+                out["dq"][t] = scale * np.einsum("hkv,hv->hk", S_read, do[t])
+                Du = np.einsum("hkv,hv->hk", D, u)
+                out["dbeta"][t] = np.einsum("hk,hk->h", k[t], Du)
+                du = beta[t][:, None] * np.einsum("hkv,hk->hv", D, k[t])
+                out["dv"][t] = du
+                Dp = D - k[t][:, :, None] * du[:, None, :]
+                sgn = 1.0 if variant == "dk error-path sign" else -1.0
+                out["dk"][t] = beta[t][:, None] * Du + sgn * np.einsum("hkv,hv->hk", Sp, du)
+                live = np.ones_like(g[t], bool) if variant == "floor mask missing" else g[t] > g_min
+                out["dg"][t] = np.where(live, a * np.einsum("hkv,hkv->hk", S_prev, Dp), 0.0)
+                D = Dp if variant == "decay not carried back" else a[:, :, None] * Dp
+            out["dh0"][n] = D
+        return out
+    return f
+
+
+BACKWARD_MUTANTS = ["read-out term dropped", "dq from the state before the update",
+                    "dk error-path sign", "floor mask missing", "decay not carried back"]
+
+
+def test_backward_reimplementation_is_faithful(monkeypatch):
+    """The unmutated reimplementation passes every backward pin (so a caught mutant is caught
+    for its planted mistake)."""
+    monkeypatch.setattr(ko, "recurrence_bwd", _backward("none"))
+    for _, fn in BACKWARD_PINS:
+        fn()
+
+
+@pytest.mark.parametrize("variant", BACKWARD_MUTANTS)
+def test_backward_mutant_is_caught(variant, monkeypatch):
+    monkeypatch.setattr(ko, "recurrence_bwd", _backward(variant))
+    failed = []
+    for name, fn in BACKWARD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except AssertionError:
+            failed.append(name)
+    assert failed, f"no backward pin caught the mutant '{variant}'"
