@@ -58,6 +58,13 @@ def algorithmic_flops(T, H, dk, dv):
     return T * H * (6 * dk * dv + CHUNK * (3 * dk + 2 * dv))
 
 
+def hbm_roofline(nbytes, ms, traffic=None):
+    """The roofline object of a leg bound by HBM: algorithmic bytes over the measured time."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": traffic}
+
+
 def source_digest(paths=KERNEL_SRC):
     """sha256 of the kernel source file, or of the concatenated files of a tuple."""
     h = hashlib.sha256()
@@ -295,6 +302,7 @@ def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
                         "g/beta/state, h0 per sequence, final states written",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "roofline": hbm_roofline(nbytes, avg),
             "algorithmic_bytes_per_call": nbytes, "workspace_bytes": ws_bytes,
             "kernels": ("prep pass (chunk kernel) + walk per group of sequences" if ws_bytes
                         else "chunk kernel (one launch)")}
@@ -330,6 +338,7 @@ def bench_raw(kda, wl, torch, dev, stream, steps, warmup):
                         "q/k/v/g/beta, conv width 4 with entering tails, SiLU, h0, bf16 output",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "roofline": hbm_roofline(nbytes, avg),
             "algorithmic_bytes_per_call": nbytes, "workspace_bytes": need,
             "kernels": "prep pass with the fused token stage (chunk kernel) + walk"}
 
@@ -369,6 +378,7 @@ def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
                         "output, fp32 g/beta/state, automatic segment count",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+            "roofline": hbm_roofline(nbytes, avg),
             "algorithmic_bytes_per_call": nbytes,
             "kernels": "prep pass (chunk kernel), transition walk, ordered scan, replay walk"}
 

@@ -62,3 +62,9 @@ def test_committed_counters_match_the_current_kernels():
     bench line's traffic fields are not null."""
     assert bench.counter_traffic() is not None
     assert bench.counter_traffic(bench.DECODE_COUNTERS, bench.DECODE_SRC) is not None
+
+
+def test_hbm_roofline_object():
+    r = bench.hbm_roofline(8e9, 2.0)
+    assert r == {"bound": "hbm", "achieved": 4000.0, "peak": 8000.0, "unit": "GB/s",
+                 "frac": 0.5, "traffic": None}
