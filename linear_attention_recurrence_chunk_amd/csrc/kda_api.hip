@@ -191,6 +191,37 @@ void set_walk_order(kda::ChunkParams& gp, const int32_t* cu_seqlens_host, int n0
   gp.n_order = m;
 }
 
+// Consecutive groups of whole sequences, each as long as need(tokens, sequences) fits the
+// budget (at least one sequence per group); run(n0, n1, first token, tokens) is called for
+// each in order and the first error is returned. Sequences are independent, so nothing
+// passes between groups.
+template <class Need, class Run>
+int for_each_group(int N, const int32_t* cu_seqlens_host, int seq_len, size_t budget, Need need,
+                   Run run) {
+  auto first_tok = [&](int n) -> int64_t {
+    return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
+  };
+  for (int n0 = 0; n0 < N;) {
+    int n1 = n0 + 1;
+    while (n1 < N && need(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0) <= budget) ++n1;
+    const int rc = run(n0, n1, first_tok(n0), first_tok(n1) - first_tok(n0));
+    if (rc != KDA_OK) return rc;
+    n0 = n1;
+  }
+  return KDA_OK;
+}
+
+// The launch parameters of one group: its sequences n0 .. n1 - 1, operand slots counted from
+// its first token
+kda::ChunkParams group_params(const kda::ChunkParams& p, int n0, int n1, int64_t tok0) {
+  kda::ChunkParams gp = p;
+  gp.seq0 = n0;
+  gp.slot_tok0 = int(tok0);
+  gp.n_seqs = n1 - n0;
+  gp.n_units = (n1 - n0) * p.H;
+  return gp;
+}
+
 // Automatic segment count of the two-launch segment path (at most kAutoSegments): the count
 // minimising a cost in units of one walk chunk step with one state tile per workgroup
 // (~3.7 us on MI355X). The prep pass is the same for every count. A walk runs in rounds of
@@ -386,31 +417,22 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
     p.ws_ops = static_cast<char*>(workspace);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // consecutive groups of whole sequences whose slots fit the workspace (one group when it
-    // holds the whole batch); sequences are independent, so nothing passes between groups
-    auto first_tok = [&](int n) -> int64_t {
-      return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
-    };
-    for (int n0 = 0; n0 < N;) {
-      int n1 = n0 + 1;
-      while (n1 < N && two_pass_workspace_bytes(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0,
-                                                num_heads, d_k) <= workspace_bytes)
-        ++n1;
-      kda::ChunkParams gp = p;
-      gp.seq0 = n0;
-      gp.slot_tok0 = int(first_tok(n0));
-      gp.n_seqs = n1 - n0;
-      gp.n_units = (n1 - n0) * num_heads;
-      const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
-      int rc = launch_status(
-          kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s));
-      if (rc != KDA_OK) return rc;
-      gp.walk_tpw = walk_tiles_per_wg(gp.n_units, gp.n_vt);
-      set_walk_order(gp, cu_seqlens_host, n0, n1);
-      rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s));
-      if (rc != KDA_OK) return rc;
-      n0 = n1;
-    }
-    return KDA_OK;
+    // holds the whole batch)
+    return for_each_group(
+        N, cu_seqlens_host, seq_len, workspace_bytes,
+        [&](int64_t tokens, int64_t seqs) {
+          return two_pass_workspace_bytes(tokens, seqs, num_heads, d_k);
+        },
+        [&](int n0, int n1, int64_t tok0, int64_t) {
+          kda::ChunkParams gp = group_params(p, n0, n1, tok0);
+          const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
+          int rc = launch_status(
+              kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s));
+          if (rc != KDA_OK) return rc;
+          gp.walk_tpw = walk_tiles_per_wg(gp.n_units, gp.n_vt);
+          set_walk_order(gp, cu_seqlens_host, n0, n1);
+          return launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s));
+        });
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
@@ -520,40 +542,27 @@ int kda_chunk_fwd_raw(const void* q_raw, const void* k_raw, const void* v_raw,
   p.eps_l2 = eps_l2;
   p.decay_floor = expf(g_min);
   p.mode = kda::kModeWalk;
-  auto first_tok = [&](int n) -> int64_t {
-    return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
-  };
-  for (int n0 = 0; n0 < N;) {
-    int n1 = n0 + 1;
-    while (n1 < N && raw_bytes(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0) <= workspace_bytes)
-      ++n1;
-    const int64_t tok0 = first_tok(n0);
-    const int64_t tokens = first_tok(n1) - tok0;
-    kda::ChunkParams gp = p;
-    gp.seq0 = n0;
-    gp.slot_tok0 = int(tok0);
-    gp.n_seqs = n1 - n0;
-    gp.n_units = (n1 - n0) * num_heads;
-    // the kernels index the convolved values by global token: the group's region is handed
-    // over as a base shifted back by its first token (64-bit address arithmetic, so every
-    // address they form lies inside the region)
-    const uintptr_t vbase = reinterpret_cast<uintptr_t>(workspace) -
-                            uintptr_t(tok0) * uintptr_t(num_heads) * uintptr_t(d_v) * 4u;
-    gp.v_conv = reinterpret_cast<float*>(vbase);
-    gp.ws_ops = static_cast<char*>(workspace) + raw_vconv_bytes(tokens, num_heads, d_v);
-    const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
-    int rc = launch_status(
-        kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s, true));
-    if (rc != KDA_OK) return rc;
-    // the walk reads the convolved values
-    gp.v = gp.v_conv;
-    gp.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
-    set_walk_order(gp, cu_seqlens_host, n0, n1);
-    rc = launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s, true));
-    if (rc != KDA_OK) return rc;
-    n0 = n1;
-  }
-  return KDA_OK;
+  return for_each_group(
+      N, cu_seqlens_host, seq_len, workspace_bytes, raw_bytes,
+      [&](int n0, int n1, int64_t tok0, int64_t tokens) {
+        kda::ChunkParams gp = group_params(p, n0, n1, tok0);
+        // the kernels index the convolved values by global token: the group's region is
+        // handed over as a base shifted back by its first token (64-bit address arithmetic,
+        // so every address they form lies inside the region)
+        const uintptr_t vbase = reinterpret_cast<uintptr_t>(workspace) -
+                                uintptr_t(tok0) * uintptr_t(num_heads) * uintptr_t(d_v) * 4u;
+        gp.v_conv = reinterpret_cast<float*>(vbase);
+        gp.ws_ops = static_cast<char*>(workspace) + raw_vconv_bytes(tokens, num_heads, d_v);
+        const int32_t* cu_g = cu_seqlens_host ? cu_seqlens_host + n0 : nullptr;
+        int rc = launch_status(
+            kda::launch_chunk_prep(gp, prep_groups(cu_g, n1 - n0, seq_len), d_k, s, true));
+        if (rc != KDA_OK) return rc;
+        // the walk reads the convolved values
+        gp.v = gp.v_conv;
+        gp.walk_tpw = 1;   // (the fp32-value walk has no register room for two waves per SIMD)
+        set_walk_order(gp, cu_seqlens_host, n0, n1);
+        return launch_status(kda::launch_chunk_walk(gp, out_dtype, d_k, s, true));
+      });
 }
 
 int kda_segment_cp_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
