@@ -42,6 +42,12 @@ KERNEL_SRC = (os.path.join(CSRC, "kda_chunk.hip"), os.path.join(CSRC, "kda_walk.
 COUNTERS = os.path.join(ROOT, "profiles", "chunk_two_pass_prefill_8k_counters.txt")
 DECODE_SRC = os.path.join(CSRC, "kda_decode.hip")
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_replay_verify_counters.txt")
+# the other legs' counter summaries and the sources that shape their traffic
+RAW_COUNTERS = os.path.join(ROOT, "profiles", "raw_prefill_8k_counters.txt")
+SEGMENT_SRC = KERNEL_SRC + (os.path.join(CSRC, "kda_segment.hip"),)
+SEGMENT_COUNTERS = os.path.join(ROOT, "profiles", "segment_cp_ultralong_256k_counters.txt")
+VARLEN_SRC = KERNEL_SRC + (os.path.join(CSRC, "kda_api.hip"),)
+VARLEN_COUNTERS = os.path.join(ROOT, "profiles", "varlen_64_counters.txt")
 
 
 def algorithmic_bytes(T, H, dk, dv, io_bytes, out_bytes, n_seqs=1):
@@ -302,7 +308,7 @@ def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
                         "g/beta/state, h0 per sequence, final states written",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
-            "roofline": hbm_roofline(nbytes, avg),
+            "roofline": hbm_roofline(nbytes, avg, counter_traffic(VARLEN_COUNTERS, VARLEN_SRC)),
             "algorithmic_bytes_per_call": nbytes, "workspace_bytes": ws_bytes,
             "kernels": ("prep pass (chunk kernel) + walk per group of sequences" if ws_bytes
                         else "chunk kernel (one launch)")}
@@ -338,7 +344,7 @@ def bench_raw(kda, wl, torch, dev, stream, steps, warmup):
                         "q/k/v/g/beta, conv width 4 with entering tails, SiLU, h0, bf16 output",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
-            "roofline": hbm_roofline(nbytes, avg),
+            "roofline": hbm_roofline(nbytes, avg, counter_traffic(RAW_COUNTERS)),
             "algorithmic_bytes_per_call": nbytes, "workspace_bytes": need,
             "kernels": "prep pass with the fused token stage (chunk kernel) + walk"}
 
@@ -378,7 +384,7 @@ def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
                         "output, fp32 g/beta/state, automatic segment count",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
-            "roofline": hbm_roofline(nbytes, avg),
+            "roofline": hbm_roofline(nbytes, avg, counter_traffic(SEGMENT_COUNTERS, SEGMENT_SRC)),
             "algorithmic_bytes_per_call": nbytes,
             "kernels": "prep pass (chunk kernel), transition walk, ordered scan, replay walk"}
 

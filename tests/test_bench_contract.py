@@ -62,6 +62,9 @@ def test_committed_counters_match_the_current_kernels():
     bench line's traffic fields are not null."""
     assert bench.counter_traffic() is not None
     assert bench.counter_traffic(bench.DECODE_COUNTERS, bench.DECODE_SRC) is not None
+    assert bench.counter_traffic(bench.RAW_COUNTERS) is not None
+    assert bench.counter_traffic(bench.SEGMENT_COUNTERS, bench.SEGMENT_SRC) is not None
+    assert bench.counter_traffic(bench.VARLEN_COUNTERS, bench.VARLEN_SRC) is not None
 
 
 def test_hbm_roofline_object():
