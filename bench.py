@@ -395,7 +395,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen,raw",
+    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen",
                     help="comma-separated legs to run besides the prefill line (decode, "
                          "verify_tiny, decode_sweep, segment, varlen, raw); the prefill leg "
                          "always runs")

@@ -3,6 +3,7 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -41,13 +42,18 @@ def _run(cmd, verbose):
 def build(verbose=False, extra=()):
     """Compile every source to an object (with its own extra flags), then link the library."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    objs = []
+    jobs = []
     for src in sources():
         name = os.path.basename(src)
         obj = os.path.join(OBJ_DIR, name + ".o")
-        _run([HIPCC, *FLAGS, *FILE_FLAGS.get(name, []), *extra, "-I",
-              os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([HIPCC, *FLAGS, *FILE_FLAGS.get(name, []), *extra, "-I",
+                      os.path.join(ROOT, "include"), "-c", src, "-o", obj], obj))
+    # the sources compile independently: one hipcc per source, a few at a time
+    workers = max(1, min(len(jobs), 8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            f.result()
+    objs = [obj for _, obj in jobs]
     _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB

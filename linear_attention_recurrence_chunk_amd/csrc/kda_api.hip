@@ -10,6 +10,11 @@
 
 namespace {
 
+using kda::max_seq_len;
+using kda::prep_groups;
+using kda::raw_vconv_bytes;
+using kda::two_pass_workspace_bytes;
+
 thread_local int g_last_launch_error = 0;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -145,15 +150,9 @@ int auto_segments(int N, int H, int dk, int dv, int64_t max_chunks, int cus) {
   return best_n;
 }
 
-// Two-pass prefill: chunks per workgroup of the prep pass (its loop prefetches each chunk's
-// inputs during the previous one)
-constexpr int kPrepChunks = 8;
 // workspace the automatic policy asks for when the batch runs in groups of sequences
 constexpr size_t kGroupedWorkspace = size_t(8) << 30;
 
-size_t two_pass_workspace_bytes(int64_t T, int64_t N, int H, int dk) {
-  return size_t(kda::op_slot_count(T, N)) * size_t(H) * kda::op_slot_bytes(dk);
-}
 
 // The one-launch path leaves compute units idle when its (sequence, head, state tile)
 // workgroups do not fill them; its per-chunk prologue then sits on every workgroup's serial
@@ -162,53 +161,17 @@ bool two_pass_wanted(int64_t N, int H, int dv) {
   return N * H * (dv / 64) <= int64_t(compute_units());
 }
 
-int64_t max_seq_len(const int32_t* cu_seqlens_host, int N, int seq_len) {
-  if (!cu_seqlens_host) return seq_len;
-  int64_t m = 0;
-  for (int i = 0; i < N; ++i) {
-    const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
-    m = len > m ? len : m;
-  }
-  return m;
-}
-
-// chunk groups per sequence of the prep pass
-int prep_groups(const int32_t* cu_seqlens_host, int N, int seq_len) {
-  const int64_t max_chunks = (max_seq_len(cu_seqlens_host, N, seq_len) + 63) / 64;
-  const int64_t groups = (max_chunks + kPrepChunks - 1) / kPrepChunks;
-  return groups < 1 ? 1 : int(groups);
-}
-
 // The walk takes a group's sequences longest first (ties in sequence order): with more
 // workgroups than compute units, a long sequence dispatched last would finish alone.
 void set_walk_order(kda::ChunkParams& gp, const int32_t* cu_seqlens_host, int n0, int n1) {
-  gp.n_order = 0;
-  const int m = n1 - n0;
-  if (!cu_seqlens_host || m < 2 || m > kda::kMaxOrder) return;
-  for (int i = 0; i < m; ++i) gp.order[i] = uint16_t(i);
-  auto len = [&](uint16_t i) { return cu_seqlens_host[n0 + i + 1] - cu_seqlens_host[n0 + i]; };
-  std::stable_sort(gp.order, gp.order + m, [&](uint16_t a, uint16_t b) { return len(a) > len(b); });
-  gp.n_order = m;
+  gp.n_order = kda::walk_order(cu_seqlens_host, n0, n1, gp.order);
 }
 
-// Consecutive groups of whole sequences, each as long as need(tokens, sequences) fits the
-// budget (at least one sequence per group); run(n0, n1, first token, tokens) is called for
-// each in order and the first error is returned. Sequences are independent, so nothing
-// passes between groups.
+// Consecutive groups of whole sequences (kda::for_each_group) with the library's status codes
 template <class Need, class Run>
 int for_each_group(int N, const int32_t* cu_seqlens_host, int seq_len, size_t budget, Need need,
                    Run run) {
-  auto first_tok = [&](int n) -> int64_t {
-    return cu_seqlens_host ? int64_t(cu_seqlens_host[n]) : int64_t(n) * seq_len;
-  };
-  for (int n0 = 0; n0 < N;) {
-    int n1 = n0 + 1;
-    while (n1 < N && need(first_tok(n1 + 1) - first_tok(n0), n1 + 1 - n0) <= budget) ++n1;
-    const int rc = run(n0, n1, first_tok(n0), first_tok(n1) - first_tok(n0));
-    if (rc != KDA_OK) return rc;
-    n0 = n1;
-  }
-  return KDA_OK;
+  return kda::for_each_group(N, cu_seqlens_host, seq_len, budget, need, run, KDA_OK);
 }
 
 // The launch parameters of one group: its sequences n0 .. n1 - 1, operand slots counted from
@@ -436,10 +399,6 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
-}
-
-size_t raw_vconv_bytes(int64_t T, int H, int dv) {
-  return (size_t(T) * H * dv * 4 + 255) / 256 * 256;   // fp32 convolved values
 }
 
 int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

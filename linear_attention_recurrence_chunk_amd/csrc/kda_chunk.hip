@@ -372,11 +372,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
 
   // ---- which (sequence, segment, head, state tile): the tiles of one unit share an XCD
-  const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int rest = b >> 3;
-  const int vt = rest % p.n_vt;
-  const int unit = (rest / p.n_vt) * 8 + xcd;
+  int vt;
+  const int unit = block_unit(blockIdx.x, p.n_vt, &vt);
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int DV = p.dv;
@@ -401,16 +398,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     eos = bos + p.seq_len;
   }
   // operand slot of the sequence's first chunk (prep pass)
-  const long long seq_slot0 = (long long)((bos - p.slot_tok0) >> 6) + (n - p.seq0);
+  const long long seq_slot0 = seq_first_slot(bos, p.slot_tok0, n, p.seq0);
   const int seq_bos = bos;
-  if (p.n_seg > 1) {
-    // chunk-aligned contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg)
-    const long long nc = (eos - bos + kChunk - 1) / kChunk;
-    const int c_lo = int((j * nc) / p.n_seg);
-    const int c_hi = int(((j + 1) * nc) / p.n_seg);
-    const int seg_bos = bos + kChunk * c_lo;
-    eos = min(eos, bos + kChunk * c_hi);
-    bos = seg_bos;
+  {
+    // chunk-aligned contiguous segments
+    int c_lo;
+    segment_range(seq_bos, eos, j, p.n_seg, &bos, &eos, &c_lo);
   }
   // transition mode: tiles [0, DK/64) hold P (zero values, identity start), the rest Q
   const bool p_tile = mode == kModeTransition && vt < DK / 64;
@@ -482,17 +475,17 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
       for (int idx = tid; idx < C3 * (W - 1); idx += 256) {
         const int ch = idx / (W - 1), m = idx % (W - 1);
-        const int pos = seq_eos - (W - 1) + m;
+        int slot;
+        const int pos = raw_tail_out_row(seq_bos, seq_eos, W, m, &slot);
         float val = 0.f;
-        if (pos >= seq_bos) {
+        if (pos >= 0) {
           const __bf16* src = ch < DK ? reinterpret_cast<const __bf16*>(p.q)
                                       : ch < 2 * DK ? reinterpret_cast<const __bf16*>(p.k)
                                                     : reinterpret_cast<const __bf16*>(p.v);
           const int cc = ch < DK ? ch : ch < 2 * DK ? ch - DK : ch - 2 * DK;
-          const int ld = DK;
-          val = (float)src[(size_t(pos) * H + h) * ld + cc];
+          val = (float)src[(size_t(pos) * H + h) * DK + cc];
         } else if (p.conv_tail_in) {
-          val = p.conv_tail_in[tb + size_t(ch) * (W - 1) + m + len];
+          val = p.conv_tail_in[tb + size_t(ch) * (W - 1) + slot];
         }
         p.conv_tail_out[tb + size_t(ch) * (W - 1) + m] = val;
       }
@@ -507,7 +500,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   // token) and its raw value rows (value mapping: 4 channels x kTPV tokens per thread, plus
   // the three rows before), loaded one chunk ahead like the other inputs. Rows before the
   // sequence come from the entering tail when they are used.
-  constexpr int kQuadsV = DK / 4, kTPV = 64 / (256 / kQuadsV);
+  using VM = RawValueMap<DK>;
+  constexpr int kTPV = VM::kTPV;
   bf16x4 pre_hq[3], pre_hk[3], pre_v[kTPV + 3];
   auto raw_prefetch = [&](int cs, int L, int lane_) {
     const int W = p.conv_width;
@@ -515,22 +509,21 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     const int c0_ = 4 * (lane_ % PM::kLPT);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int tok = cs + rb0_ - 1 - i;
+      // rows of the chunk's own sequence up to its last row only (raw_history_row)
+      const int tok = raw_history_row(cs, L, rb0_, i, W, seq_bos);
       pre_hq[i] = pre_hk[i] = bf16x4{};
-      // rows of the sequence only: in a ragged last chunk, threads whose rows lie past its end
-      // would otherwise read past the inputs (their outputs are discarded)
-      if (i + 1 < W && tok >= seq_bos && tok < cs + L) {
+      if (tok >= 0) {
         const size_t off = (size_t(tok) * H + h) * DK + c0_;
         pre_hq[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.q) + off);
         pre_hk[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.k) + off);
       }
     }
-    const int cv0 = 4 * (tid % kQuadsV), tv0 = kTPV * (tid / kQuadsV);
+    const int cv0 = VM::cv0(tid), tv0 = VM::tv0(tid);
 #pragma unroll
     for (int i = 0; i < kTPV + 3; ++i) {
-      const int tok = cs + tv0 - 3 + i;
+      const int tok = raw_value_row(cs, L, tv0, i, W, seq_bos);
       pre_v[i] = bf16x4{};
-      if (i >= 3 - (W - 1) && tok < cs + L && tok >= seq_bos)
+      if (tok >= 0)
         pre_v[i] = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const __bf16*>(p.v) +
                                                     (size_t(tok) * H + h) * DK + cv0);
     }
@@ -578,21 +571,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       float hq[3][4], hk[3][4];   // raw q, k of tokens rb0 - 1 - i
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
-        const int tok = cstart + rb0 - 1 - i;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           hq[i][c] = (float)pre_hq[i][c];   // zero where not loaded
           hk[i][c] = (float)pre_hk[i][c];
         }
-        if (i + 1 < W) {
-          if (tok < seq_bos && p.conv_tail_in) {
-            const int m = (W - 1) - (seq_bos - tok);   // tail slot of that token, oldest first
-            const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
+        // rows before the sequence: the entering tail's slot of that token, oldest first
+        const int m = raw_history_tail_slot(cstart, rb0, i, W, seq_bos);
+        if (m >= 0 && p.conv_tail_in) {
+          const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              hq[i][c] = p.conv_tail_in[tb + size_t(c0 + c) * (W - 1) + m];
-              hk[i][c] = p.conv_tail_in[tb + size_t(DK + c0 + c) * (W - 1) + m];
-            }
+          for (int c = 0; c < 4; ++c) {
+            hq[i][c] = p.conv_tail_in[tb + size_t(c0 + c) * (W - 1) + m];
+            hk[i][c] = p.conv_tail_in[tb + size_t(DK + c0 + c) * (W - 1) + m];
           }
         }
       }
@@ -639,17 +630,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       // ~15 x their RMS, and one bf16 rounding of them costs several % of the outputs' RMS):
       // thread = 4 value channels x kTPV tokens
       {
-        const int cv0 = 4 * (tid % kQuadsV), tv0 = kTPV * (tid / kQuadsV);
+        const int cv0 = VM::cv0(tid), tv0 = VM::tv0(tid);
         float xv[kTPV + 3][4];
 #pragma unroll
         for (int i = 0; i < kTPV + 3; ++i) {
-          const int tok = cstart + tv0 - 3 + i;
 #pragma unroll
           for (int c = 0; c < 4; ++c) xv[i][c] = (float)pre_v[i][c];   // zero where not loaded
-          if (i < 3 && i < 3 - (W - 1)) continue;          // history beyond the taps
-          if (tok >= cstart + Lc) continue;
-          if (tok < seq_bos && p.conv_tail_in) {
-            const int m = (W - 1) - (seq_bos - tok);
+          const int m = raw_value_tail_slot(cstart, Lc, tv0, i, W, seq_bos);
+          if (m >= 0 && p.conv_tail_in) {
             const size_t tb = (size_t(n) * H + h) * C3 * (W - 1);
 #pragma unroll
             for (int c = 0; c < 4; ++c)

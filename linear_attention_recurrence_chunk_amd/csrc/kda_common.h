@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_index.h"
+
 namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -16,7 +18,6 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;   // log2(e), rounded to fp32
 constexpr int kWave = 64;
-constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kSub = 16;     // tokens per sub-block (one MFMA tile edge)
 constexpr int kNumSub = kChunk / kSub;
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda_index.h"
+
 namespace kda {
 
 // What one launch of the chunk kernel computes.
@@ -17,7 +19,6 @@ enum ChunkMode : int {
   kModeWalk = 4,        // two-pass prefill, pass 2: the serial chunk walk from ws_ops
 };
 
-constexpr int kMaxOrder = 256;   // sequences a walk can reorder (launch-parameter bytes)
 
 // One launch of the chunk kernel. A "unit" is one (sequence, segment, head) triple (one
 // segment per sequence in forward mode); every unit is processed by n_vt workgroups, one per
@@ -101,15 +102,5 @@ hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
                              hipStream_t stream, bool raw = false);
 hipError_t launch_chunk_walk(const ChunkParams& p, int out_dtype, int dk, hipStream_t stream,
                              bool v_f32 = false);
-
-// Operand slots: chunk c of sequence n (bos_n its first token) uses slot (bos_n / 64) + n + c,
-// so slots never collide and there are at most total_tokens / 64 + n_seqs + 1 of them (for a
-// group of sequences: its tokens and its sequence count).
-inline long long op_slot_count(long long total_tokens, long long n_seqs) {
-  return total_tokens / 64 + n_seqs + 1;
-}
-// bytes of one (slot, head) operand block for key width dk (MFMA fragments of 1 KiB each plus
-// one block for the whole-chunk decay)
-inline size_t op_slot_bytes(int dk) { return size_t(8 * (dk / 32) + 24 + 2 * (dk / 16) + 1) * 1024; }
 
 }  // namespace kda

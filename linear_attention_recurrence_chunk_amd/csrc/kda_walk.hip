@@ -83,12 +83,8 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
 
   // ---- which (sequence, segment, head) and which kTPW state tiles of it (four waves per
   //      tile): the workgroups of one unit share an XCD
-  const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int rest = b >> 3;
-  const int n_groups = p.n_vt / kTPW;
-  const int vg = rest % n_groups;
-  const int unit = (rest / n_groups) * 8 + xcd;
+  int vg;
+  const int unit = block_unit(blockIdx.x, p.n_vt / kTPW, &vg);
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int DV = p.dv;
@@ -116,15 +112,11 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   }
   // operand slot of the sequence's first chunk, then the segment's chunk range (chunk-aligned
   // contiguous segments: segment j holds chunks [j nc / n_seg, (j+1) nc / n_seg))
-  long long slot0 = (long long)((bos - p.slot_tok0) >> 6) + (n - p.seq0);
-  if (p.n_seg > 1) {
-    const long long nc = (eos - bos + kChunk - 1) / kChunk;
-    const int c_lo = int((j * nc) / p.n_seg);
-    const int c_hi = int(((j + 1) * nc) / p.n_seg);
+  long long slot0 = seq_first_slot(bos, p.slot_tok0, n, p.seq0);
+  {
+    int c_lo;
+    segment_range(bos, eos, j, p.n_seg, &bos, &eos, &c_lo);
     slot0 += c_lo;
-    const int seg_bos = bos + kChunk * c_lo;
-    eos = min(eos, bos + kChunk * c_hi);
-    bos = seg_bos;
   }
   const int nchunks = (eos - bos + kChunk - 1) / kChunk;
   const char* ws_head = p.ws_ops + (size_t(slot0) * H + h) * OS::kBytes;

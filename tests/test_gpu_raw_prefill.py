@@ -9,7 +9,11 @@ from linear_attention_recurrence_chunk_amd import workloads as wl
 from oracle import kda_oracle as ko
 from kda_testutil import np64, to_dev
 
-pytestmark = pytest.mark.gpu
+# The raw-projection prefill read q and k rows past the end of a ragged last chunk and faulted
+# the GPU twice; its GPU tests stay off until the CPU address check of its kernels passes
+# (tests/test_raw_addressing.py) on the fixed code.
+pytestmark = [pytest.mark.gpu, pytest.mark.skip(
+    reason="raw-projection prefill off the GPU until its CPU address check passes")]
 
 
 # The raw path's outputs are heavier-tailed than the workloads' (max |o| reaches 25-33 x RMS
