@@ -145,7 +145,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
 #pragma unroll
   for (int pp = 0; pp < NS; ++pp) {
     const Frag rowA = Pol::load(sKr, L::LDP, 16 * IA + ln, pp, q4);
-    Frag rowM, colA[4], colM[4], dKl, dQl;
+    Frag rowM, colA[4], colM[4], colMl[4], dKl, dQl;
     if constexpr (kM) rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
 #pragma unroll
     for (int jb = kJ0; jb <= IA; ++jb) {
@@ -157,10 +157,24 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
 #pragma unroll
     for (int jb = 0; jb <= IM; ++jb) {
       if constexpr (!kM) break;
-      if (jb == IM) colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
-      else if (jb == IM - 1) colM[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
-      else if (jb == 0 && IM == 3) colM[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
-      else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
+      if (jb == IM) {
+        colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
+      } else if constexpr (Pol::kSplit) {
+        // off-diagonal blocks: k kappa times the decay gap, k / rho times the decays of the
+        // sub-blocks jb .. IM - 1, rebuilt from the k / rho pair as a pair (a single bf16 k
+        // kappa here was the largest error source of the outputs)
+        const float* const fac[3] = {sBP + jb * DK, sBP + (jb + 1) * DK, sBP + (jb + 2) * DK};
+        if (IM - jb == 1)
+          Pol::template load_pair_scaled<1>(sKd, sKdLo, L::LDP, 16 * jb + ln, pp, q4, fac, colM[jb], colMl[jb]);
+        else if (IM - jb == 2)
+          Pol::template load_pair_scaled<2>(sKd, sKdLo, L::LDP, 16 * jb + ln, pp, q4, fac, colM[jb], colMl[jb]);
+        else
+          Pol::template load_pair_scaled<3>(sKd, sKdLo, L::LDP, 16 * jb + ln, pp, q4, fac, colM[jb], colMl[jb]);
+      } else {
+        if (jb == IM - 1) colM[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pp, q4);
+        else if (jb == 0 && IM == 3) colM[jb] = Pol::load_scaled2(sKc, L::LDP, ln, pp, q4, P1, P2);
+        else colM[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
+      }
     }
     if constexpr (Pol::kSplit && kM) {
       dKl = Pol::load(sKdLo, L::LDP, 16 * IM + ln, pp, q4);
@@ -177,8 +191,9 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
       if constexpr (Pol::kSplit) {
         accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
-        // the lo half of q rho on every block of the row: the single bf16 rounding of q rho
-        // is the largest error source of the outputs otherwise
+#pragma unroll
+        for (int jb = 0; jb < IM; ++jb) accM[jb] = Pol::mma(colMl[jb], rowM, accM[jb]);
+        // the lo half of q rho on every block of the row
 #pragma unroll
         for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], dQl, accM[jb]);
       }

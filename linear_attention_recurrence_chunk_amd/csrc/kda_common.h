@@ -92,6 +92,38 @@ struct PolBF16 {
     }
     return r;
   }
+  // A bf16 hi + lo pair of tiles, recombined per k in fp32, scaled by the product of NF
+  // per-k factors (fp32, multiplied in order) and split again into a bf16 hi + lo pair: the
+  // scaled operand keeps the pair's ~16 significant bits instead of one bf16's 8
+  template <int NF>
+  __device__ static __forceinline__ void load_pair_scaled(const E* thi, const E* tlo, int ld,
+                                                          int row, int p, int q,
+                                                          const float* const (&fac)[3],
+                                                          Frag& h, Frag& l) {
+    const int o = 32 * p + 4 * q;
+    const E* bh = thi + row * ld + o;
+    const E* bl = tlo + row * ld + o;
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(bh);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(bh + 16);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(bl);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(bl + 16);
+    f32x4 f0 = *reinterpret_cast<const f32x4*>(fac[0] + o);
+    f32x4 f1 = *reinterpret_cast<const f32x4*>(fac[0] + o + 16);
+#pragma unroll
+    for (int i = 1; i < NF; ++i) {
+      f0 *= *reinterpret_cast<const f32x4*>(fac[i] + o);
+      f1 *= *reinterpret_cast<const f32x4*>(fac[i] + o + 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = ((float)h0[e] + (float)l0[e]) * f0[e];
+      const float x1 = ((float)h1[e] + (float)l1[e]) * f1[e];
+      h[e] = (__bf16)x0;
+      h[e + 4] = (__bf16)x1;
+      l[e] = (__bf16)(x0 - (float)h[e]);
+      l[e + 4] = (__bf16)(x1 - (float)h[e + 4]);
+    }
+  }
   // B fragment of slice p from accumulator tiles acc[2p] and acc[2p + 1], as a hi + lo pair:
   // hi = bf16(x), lo = bf16(x - hi)
   __device__ static __forceinline__ void from_acc_split(const f32x4* acc, int p, Frag& hi,

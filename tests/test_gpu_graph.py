@@ -99,7 +99,6 @@ def test_segment_path_in_a_graph():
     _replays_match(graph, (o, ht), (o_ref, ht_ref))
 
 
-@pytest.mark.skip(reason="raw-projection prefill off the GPU until its CPU address check passes")
 def test_raw_prefill_in_a_graph():
     """The raw-projection prefill (token stage in the prep pass, then the walk) in a graph:
     outputs, final states and leaving conv tails of every replay equal the eager call's."""

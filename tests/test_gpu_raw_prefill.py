@@ -9,20 +9,15 @@ from linear_attention_recurrence_chunk_amd import workloads as wl
 from oracle import kda_oracle as ko
 from kda_testutil import np64, to_dev
 
-# The raw-projection prefill read q and k rows past the end of a ragged last chunk and faulted
-# the GPU twice; its GPU tests stay off until the CPU address check of its kernels passes
-# (tests/test_raw_addressing.py) on the fixed code.
-pytestmark = [pytest.mark.gpu, pytest.mark.skip(
-    reason="raw-projection prefill off the GPU until its CPU address check passes")]
+# The raw-projection prefill once read q and k rows past the end of a ragged last chunk and
+# faulted the GPU; tests/test_raw_addressing.py replays every access of its kernels on the CPU.
+pytestmark = pytest.mark.gpu
 
-
-# The raw path's outputs are heavier-tailed than the workloads' (max |o| reaches 25-33 x RMS
-# against 11-13 x: the convolved, SiLU-activated values are positive-biased with a long tail),
-# so its bar is normalised by the tail: max |err| <= 2e-3 x max |ref|, which is the
-# 2e-2 x RMS bound of the bf16 workloads at their tail ratio of about 10, and
-# RMS(err) <= 2e-3 x RMS(ref).
-TOL_RAW_MAX = 2e-3
-TOL_RAW_RMS = 2e-3
+# The bf16 bar of the other prefill paths: max |err| <= 2e-2 x RMS(ref), on o and on the final
+# state. The raw path's outputs are heavier-tailed (max |o| reaches 17-33 x RMS, against 11-13
+# x for the workloads': the convolved, SiLU-activated keys share a positive direction), which
+# is what the pair operands of M's off-diagonal blocks are for.
+TOL = 2e-2
 
 
 def _errs(got, ref):
@@ -63,8 +58,7 @@ def test_raw_prefill_matches_oracle(T, H, dk, W, act):
     print(f"o: max/max {eo[0]:.2e} rms/rms {eo[1]:.2e} max/rms {eo[2]:.2e} (tail "
           f"{np.abs(o_ref).max() / np.sqrt(np.mean(o_ref ** 2)):.1f}); state: {es[0]:.2e} "
           f"{es[1]:.2e} {es[2]:.2e}")
-    for e in (eo, es):
-        assert e[0] <= TOL_RAW_MAX and e[1] <= TOL_RAW_RMS
+    assert eo[2] <= TOL and es[2] <= TOL
     if W > 1:
         # the leaving tail holds raw inputs: exact
         assert np.array_equal(np64(tail), tail_ref)
@@ -85,17 +79,17 @@ def test_raw_prefill_varlen_and_short_sequences(dk, W):
           f"{np.abs(o_ref).max() / np.sqrt(np.mean(o_ref ** 2)):.1f}); state: {es[0]:.2e} "
           f"{es[1]:.2e} {es[2]:.2e}")
     assert np.array_equal(np64(tail), tail_ref)
-    for e in (eo, es):
-        assert e[0] <= TOL_RAW_MAX and e[1] <= TOL_RAW_RMS
+    assert eo[2] <= TOL and es[2] <= TOL
 
 
 def test_raw_prefill_without_entering_tail():
+    print("case raw prefill T=200 H=2 dk=128 W=4 without entering tail", flush=True)
     inp = wl.raw_prefill_inputs(T=200, H=2, dk=128, dv=128, conv_width=4, seed=88,
                                 with_tail=False)
     o, ht, tail = _run(inp, False)
     o_ref, ht_ref, tail_ref = _oracle(inp, False)
     for e in (_errs(np64(o), o_ref), _errs(np64(ht), ht_ref)):
-        assert e[0] <= TOL_RAW_MAX and e[1] <= TOL_RAW_RMS
+        assert e[2] <= TOL
     assert np.array_equal(np64(tail), tail_ref)
 
 
