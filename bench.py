@@ -42,6 +42,7 @@ KERNEL_SRC = (os.path.join(CSRC, "kda_chunk.hip"), os.path.join(CSRC, "kda_walk.
 COUNTERS = os.path.join(ROOT, "profiles", "chunk_two_pass_prefill_8k_counters.txt")
 DECODE_SRC = os.path.join(CSRC, "kda_decode.hip")
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_replay_verify_counters.txt")
+DECODE_TRACE = os.path.join(ROOT, "profiles", "decode_replay_verify_trace.txt")
 # the other legs' counter summaries and the sources that shape their traffic
 RAW_COUNTERS = os.path.join(ROOT, "profiles", "raw_prefill_8k_counters.txt")
 SEGMENT_SRC = KERNEL_SRC + (os.path.join(CSRC, "kda_segment.hip"),)
@@ -78,6 +79,25 @@ def source_digest(paths=KERNEL_SRC):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def trace_avg_ms(summary, source):
+    """A kernel's average duration (ms) from a committed rocprofv3 trace summary (its
+    ``avg_ns:`` line), or None when the kernel source changed since the trace was taken."""
+    if not os.path.exists(summary):
+        return None
+    vals = {}
+    with open(summary) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256") != source_digest(source):
+        return None
+    try:
+        return float(vals["avg_ns"]) * 1e-6
+    except (KeyError, ValueError):
+        return None
 
 
 def counter_traffic(counters=COUNTERS, source=KERNEL_SRC):
@@ -126,9 +146,26 @@ def cpu_baseline(inp, scale):
                       f"{dt:.2f} s on {threads} threads, {cpu_model})"}
 
 
-def timed_launches(fn, stream, steps, warmup, before=None):
+FLUSH_BYTES = 512 << 20   # written between timed launches: more than the 256 MB MALL
+
+
+def make_flush(torch, dev):
+    """A 512 MiB device buffer and a function that overwrites it (a fill kernel on the current
+    stream), so that no timed launch finds its inputs left in L2 or the MALL by the previous
+    work (a different byte every call)."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    count = [0]
+
+    def flush():
+        count[0] += 1
+        buf.fill_(count[0] & 255)
+    return flush
+
+
+def timed_launches(fn, stream, steps, warmup, before=None, flush=None):
     """Per-launch durations (ms) from HIP events recorded on the launch stream; ``before``
-    runs untimed ahead of every launch (e.g. restoring state updated in place)."""
+    runs untimed ahead of every launch (e.g. restoring state updated in place), then
+    ``flush`` (a cache-flushing write), both outside the events."""
     import torch
     for _ in range(warmup):
         if before:
@@ -140,6 +177,8 @@ def timed_launches(fn, stream, steps, warmup, before=None):
     for i in range(steps):
         if before:
             before()
+        if flush:
+            flush()
         starts[i].record(stream)
         fn()
         ends[i].record(stream)
@@ -176,11 +215,13 @@ def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
         kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
                           state_acc=acc, o=o, stream=stream)
 
-    ms = timed_launches(launch, stream, steps, warmup, before=restore)
+    # the state restore writes 1.6 GB just before each launch: a 512 MiB flush after it
+    ms = timed_launches(launch, stream, steps, warmup, before=restore, flush=make_flush(torch, dev))
     avg = sum(ms) / len(ms)
     n_acc_total = int(w.n_acc.sum().item())
     nbytes = decode_bytes(R, H, D, W, n_new, n_acc_total, 2)
     gbs = nbytes / (avg * 1e-3) / 1e9
+    traced = trace_avg_ms(DECODE_TRACE, DECODE_SRC)
     out = {"workload": f"decode_verify: {R} requests x {H} heads, d_k=d_v={D}, fp32 state, "
                        f"window of {cfg['window'] - 1} drafts + 1 bonus, accepted drafts "
                        f"uniform in 0..{cfg['window'] - 1} (mean {n_acc_total / R:.2f}), "
@@ -190,7 +231,14 @@ def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS,
                         "traffic": counter_traffic(DECODE_COUNTERS, DECODE_SRC)},
-           "algorithmic_bytes_per_launch": nbytes, "kernel": "decode_replay_kernel"}
+           "algorithmic_bytes_per_launch": nbytes, "kernel": "decode_replay_kernel",
+           "cache_flush_bytes": FLUSH_BYTES,
+           "rocprof_avg_ms": traced,
+           "rocprof_frac": None if traced is None else nbytes / (traced * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "note": "latency_ms: HIP events around each launch, after the state restore and a "
+                   "512 MiB cache-flushing write; rocprof_avg_ms: the kernel's average duration "
+                   "in the committed rocprofv3 trace of the same bench command (null once the "
+                   "kernel source changed since)"}
     if cpu_baseline:
         import numpy as np
         from oracle import kda_oracle as ko
@@ -255,6 +303,7 @@ def bench_decode_sweep(kda, wl, torch, dev, stream, steps, warmup, n_news=(1, 2,
     cfg = wl.CONFIGS["decode_verify"]
     R, H, D, W = cfg["R"], cfg["H"], cfg["dk"], cfg["conv_width"]
     out = {}
+    flush = make_flush(torch, dev)
     for n_new in n_news:
         w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=W, n_new=n_new, window=cfg["window"],
                              seed=cfg["seed"], device=dev)
@@ -270,7 +319,7 @@ def bench_decode_sweep(kda, wl, torch, dev, stream, steps, warmup, n_news=(1, 2,
             kda.decode_replay(state, tail, w.n_acc, w.prev, w.new, w.conv_w, w.norm_w,
                               state_acc=acc, o=o, stream=stream)
 
-        ms = timed_launches(launch, stream, steps, warmup, before=restore)
+        ms = timed_launches(launch, stream, steps, warmup, before=restore, flush=flush)
         out[str(n_new)] = sum(ms) / len(ms)
         del w, state, tail, acc, o
     return {"workload": f"decode_verify with n_new in {list(n_news)} (window 8, accepted drafts "
@@ -298,7 +347,7 @@ def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
         kda.chunk_fwd(q, k, v, g, beta, h0=h0, cu_seqlens=cu, o=o, ht=ht, workspace=ws,
                       stream=stream)
 
-    ms = timed_launches(launch, stream, steps, warmup)
+    ms = timed_launches(launch, stream, steps, warmup, flush=make_flush(torch, dev))
     avg = sum(ms) / len(ms)
     nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2, n_seqs=N)
     del inp, q, k, v, g, beta, h0, o, ht, ws
@@ -359,7 +408,9 @@ def ctypes_size(kda, T, H, dk, dv):
     return int(out.value)
 
 
-def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
+def bench_segment(kda, wl, torch, dev, stream, steps, warmup, counts=(0, 64, 256)):
+    """kda_segment_cp_fwd on the ultralong workload: the library's automatic segment count
+    (the leg's figure) and the two ends of the workload's 64..256 range."""
     cfg = wl.CONFIGS["ultralong_256k"]
     T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
     inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
@@ -367,22 +418,28 @@ def bench_segment(kda, wl, torch, dev, stream, steps, warmup):
     q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
     o = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
     ht = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
-    n_seg = 0   # the library's automatic choice
-    ws = torch.empty(kda.segment_cp_workspace_size(1, T, 1, H, dk, dv, kda.KDA_BF16, n_seg),
-                     dtype=torch.uint8, device=dev)
+    flush = make_flush(torch, dev)
+    by_count = {}
+    for n_seg in counts:
+        ws = torch.empty(kda.segment_cp_workspace_size(1, T, 1, H, dk, dv, kda.KDA_BF16, n_seg),
+                         dtype=torch.uint8, device=dev)
 
-    def launch():
-        kda.segment_cp_fwd(q, k, v, g, beta, o=o, ht=ht, n_segments=n_seg, workspace=ws,
-                           stream=stream)
+        def launch():
+            kda.segment_cp_fwd(q, k, v, g, beta, o=o, ht=ht, n_segments=n_seg, workspace=ws,
+                               stream=stream)
 
-    ms = timed_launches(launch, stream, steps, warmup)
-    avg = sum(ms) / len(ms)
+        ms = timed_launches(launch, stream, steps, warmup, flush=flush)
+        by_count["auto" if n_seg == 0 else str(n_seg)] = sum(ms) / len(ms)
+        del ws
+        torch.cuda.empty_cache()
+    avg = by_count["auto"]
     nbytes = algorithmic_bytes(T, H, dk, dv, 2, 2)
-    del inp, q, k, v, g, beta, o, ws
+    del inp, q, k, v, g, beta, o
     torch.cuda.empty_cache()
     return {"workload": f"ultralong_256k: B=1, T={T}, H={H}, d_k=d_v={dk}, bf16 q/k/v and "
                         "output, fp32 g/beta/state, automatic segment count",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "ms_per_call_by_segments": by_count,
             "achieved_gbs": nbytes / (avg * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
             "roofline": hbm_roofline(nbytes, avg, counter_traffic(SEGMENT_COUNTERS, SEGMENT_SRC)),
             "algorithmic_bytes_per_call": nbytes,
