@@ -51,7 +51,9 @@ typedef enum kda_status {
   KDA_ERR_UNSUPPORTED = -7,         /* valid but not implemented (d_k, d_v, dtype combination) */
   KDA_ERR_LAUNCH_FAILED = -8,       /* the HIP runtime rejected a launch */
   KDA_ERR_ALIASING = -9,            /* an output overlaps an input it must not overlap */
-  KDA_ERR_BAD_VALUE = -10           /* a scalar is out of range (g_min, eps, scale not finite) */
+  KDA_ERR_BAD_VALUE = -10,          /* a scalar is out of range (g_min, eps, scale not finite) */
+  KDA_ERR_SCRATCH_TOO_SMALL = -11   /* kda_chunk_fwd_noalloc: the longest sequence's operand
+                                       slots exceed KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -148,6 +150,35 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
 int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
                                  const int32_t* cu_seqlens_host, int num_heads, int d_k,
                                  int d_v, int io_dtype, int policy, size_t* bytes);
+
+/*
+ * kda_chunk_fwd_noalloc: kda_chunk_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Arguments,
+ * validation and results are those of kda_chunk_fwd without the workspace; the caller still
+ * passes every input and output. With KDA_BF16 the call takes the two-launch path, its operand
+ * slots in a static device array of KDA_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds
+ * on every GPU it runs on until the process ends: the whole batch in one prep and one walk when
+ * its slots fit, else consecutive groups of whole sequences, with the same bits as
+ * kda_chunk_fwd. A sequence of T tokens needs floor(T / 64) + 2 slots of 74,752 B per head at
+ * d_k = 128 (50,176 B at 64), so it may have up to (floor(KDA_NOALLOC_SCRATCH_BYTES /
+ * (74,752 x num_heads)) - 1) x 64 - 1 tokens: 2,303 at 96 heads, 19,071 at 12; a longer one
+ * returns KDA_ERR_SCRATCH_TOO_SMALL before anything runs. KDA_F32 runs the one-launch path and
+ * uses no scratch.
+ *
+ * The call allocates and frees nothing (no hipMalloc, hipFree or allocating library routine).
+ * The first call on a device, with that device current, looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it; call with the stream's device current. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (concurrent streams, or
+ * threads without ordering) race on it and must be serialised by the caller. Its contents are
+ * overwritten by each call before they are read.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* h0, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                          int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
+                          float scale, float g_min, void* o, float* ht, int ckpt_every,
+                          float* ckpt_states, void* stream);
 
 /*
  * kda_chunk_fwd_raw: the prefill from raw projections, with the short convolution, the input

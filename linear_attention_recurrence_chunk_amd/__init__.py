@@ -58,6 +58,9 @@ def library():
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, P, P, I,
                                   P, P, ctypes.c_size_t, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F,
+                                          P, P, I, P, P]
+    lib.kda_chunk_fwd_noalloc.restype = I
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, P, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_workspace_size.restype = I
@@ -253,6 +256,41 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
         raise KDAError(st, "kda_chunk_fwd")
     if ckpt_every:
         return a["o"], a["ht"], ckpt
+    return a["o"], a["ht"]
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, o, ht=None, h0=None, cu_seqlens=None,
+                      cu_seqlens_host=None, scale=1.0, g_min=-5.0, ckpt_every=0, ckpt=None,
+                      stream=None):
+    """kda_chunk_fwd_noalloc: kda_chunk_fwd with the two-launch path's operand slots in the
+    library's static per-GPU scratch, for callers that cannot allocate. Nothing is allocated or
+    copied here either: o (and ht, ckpt when wanted) must be given, and packed sequences need
+    cu_seqlens as a contiguous int32 device tensor plus cu_seqlens_host as a CPU int32
+    tensor. Returns (o, ht)."""
+    torch = _torch()
+    if o is None:
+        raise ValueError("chunk_fwd_noalloc allocates nothing: pass o")
+    if cu_seqlens is not None and (cu_seqlens_host is None or cu_seqlens.dtype != torch.int32
+                                   or cu_seqlens.device != q.device
+                                   or not cu_seqlens.is_contiguous()):
+        raise ValueError("chunk_fwd_noalloc needs cu_seqlens as a contiguous int32 tensor on "
+                         "q's device and cu_seqlens_host as a CPU int32 tensor")
+    if ckpt_every and ckpt is None:
+        raise ValueError("chunk_fwd_noalloc allocates nothing: pass ckpt")
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, o, ht, False, None,
+                      cu_seqlens_host=cu_seqlens_host)
+    T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
+    _check(ckpt, "ckpt", torch.float32, q.device)
+    st = library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
+        _cu_host_ptr(a["cu_host"]), a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
+        a["io"], a["out"], float(scale), float(g_min), _ptr(a["o"]), _ptr(a["ht"]),
+        int(ckpt_every), _ptr(ckpt) if ckpt_every else None, _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return a["o"], a["ht"]
 
 

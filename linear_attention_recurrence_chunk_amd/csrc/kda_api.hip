@@ -1,5 +1,6 @@
 // C ABI of libkda: argument validation (host only, no HIP call) and kernel dispatch.
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -7,6 +8,11 @@
 #include "../../include/kda.h"
 #include "kda_decode.h"
 #include "kda_internal.h"
+
+// Operand slots of kda_chunk_fwd_noalloc, held by the library on every GPU it runs on for the
+// life of the process. Host code never passes this name to a kernel or a copy: it is a host
+// stand-in for the symbol, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -245,6 +251,33 @@ int check_workspace_aliasing(const void* ws, size_t need, const void* q, const v
   return KDA_OK;
 }
 
+// The device address of this GPU's scratch (the current device's), looked up on the first
+// call on each device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_launch_error = err != hipSuccess ? int(err) : int(hipErrorInvalidDevice);
+    return KDA_ERR_LAUNCH_FAILED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr) {
+      g_last_launch_error = err != hipSuccess ? int(err) : int(hipErrorInvalidSymbol);
+      return KDA_ERR_LAUNCH_FAILED;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +299,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_LAUNCH_FAILED: return "kernel launch failed";
     case KDA_ERR_ALIASING: return "an output overlaps an input";
     case KDA_ERR_BAD_VALUE: return "a scalar argument is out of range";
+    case KDA_ERR_SCRATCH_TOO_SMALL:
+      return "a sequence's operand slots exceed the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }
@@ -399,6 +434,36 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   }
   return launch_status(
       kda::launch_chunk_fwd(p, io_dtype, out_dtype, d_k, static_cast<hipStream_t>(stream)));
+}
+
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* h0, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                          int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
+                          float scale, float g_min, void* o, float* ht, int ckpt_every,
+                          float* ckpt_states, void* stream) {
+  // kda_chunk_fwd's own validation, with no workspace (host only, launches nothing)
+  int N = 0;
+  int64_t T = 0;
+  const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
+                                  seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
+                                  g_min, o, ht, &N, &T);
+  if (st != KDA_OK) return st;
+  if (io_dtype != KDA_BF16)   // one launch, no scratch
+    return kda_chunk_fwd(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len,
+                         n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale, g_min, o, ht,
+                         ckpt_every, ckpt_states, nullptr, 0, stream);
+  // a group holds at least one whole sequence: the longest one's slots must fit
+  const int64_t longest = max_seq_len(cu_seqlens_host, N, seq_len);
+  if (two_pass_workspace_bytes(longest, 1, num_heads, d_k) > KDA_NOALLOC_SCRATCH_BYTES)
+    return KDA_ERR_SCRATCH_TOO_SMALL;
+  if (N == 0) return KDA_OK;
+  void* ws = nullptr;
+  const int rc = device_scratch(&ws);
+  if (rc != KDA_OK) return rc;
+  return kda_chunk_fwd(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs,
+                       num_heads, d_k, d_v, io_dtype, out_dtype, scale, g_min, o, ht, ckpt_every,
+                       ckpt_states, ws, KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

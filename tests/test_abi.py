@@ -288,3 +288,32 @@ def test_raw_prefill_checks():
     same = ctypes.c_void_p(BASE + 80 * 64 * GiB)
     assert raw_call(tail_in=same, tail_out=same) == ALIAS          # tails must not overlap
     assert raw_call(tail_out=ctypes.c_void_p(BASE + 60 * 64 * GiB)) == ALIAS   # on top of q
+
+
+# ----------------------------------------------------------------- no-allocation prefill
+def noalloc(seq_len=256, H=2, dk=128, io=BF16, cu=None, cu_host=None, n_seqs=1, o=True):
+    P = ptrs()
+    return kda.library().kda_chunk_fwd_noalloc(
+        P[0], P[1], P[2], P[3], P[4], None, cu, cu_host, 1, seq_len, n_seqs, H, dk, dk, io, io,
+        1.0, -5.0, P[5] if o else None, None, 0, None, None)
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold():
+    """kda_chunk_fwd_noalloc validates like kda_chunk_fwd, then rejects a sequence whose
+    operand slots exceed the 256 MiB static scratch, all before any HIP call: a sequence of T
+    tokens takes floor(T / 64) + 2 slots of 74752 B per head (d = 128), so at 96 heads it holds
+    (floor(2^28 / (74752 x 96)) - 1) x 64 - 1 = 2303 tokens at most."""
+    too_small = -11
+    assert kda.status_string(too_small) != "unknown status"
+    slots = (256 << 20) // (74752 * 96)
+    limit = (slots - 1) * 64 - 1
+    assert limit == 2303 and (limit // 64 + 2) * 74752 * 96 <= 256 << 20
+    assert ((limit + 1) // 64 + 2) * 74752 * 96 > 256 << 20
+    assert noalloc(seq_len=limit + 1, H=96) == too_small
+    # packed sequences: the longest one counts, not the total
+    arr, cu_host = host_cu([0, 2000, 2000 + limit + 1])
+    assert noalloc(seq_len=2000 + limit + 1, H=96, n_seqs=2, cu=ctypes.c_void_p(BASE + 8 * GiB),
+                   cu_host=cu_host) == too_small
+    # ordinary validation comes first
+    assert noalloc(o=False) == NULL
+    assert noalloc(dk=96) == UNSUP
