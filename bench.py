@@ -408,6 +408,44 @@ def ctypes_size(kda, T, H, dk, dv):
     return int(out.value)
 
 
+def backward_bytes(T, H, dk, dv, io_bytes, n_seqs=1):
+    """Bytes the backward must move: q, k, v, do (io dtype), g and beta read; dq, dk, dg, dv
+    and dbeta written in fp32; h0 and dht read and dh0 written per sequence and head."""
+    per_tok = (2 * dk + 2 * dv) * io_bytes + 4 * dk + 4 + 4 * (3 * dk + dv) + 4
+    return T * H * per_tok + 3 * n_seqs * H * dk * dv * 4
+
+
+def bench_backward(kda, wl, torch, dev, stream, steps, warmup):
+    """kda_chunk_bwd on the prefill shape (8192 tokens x 96 heads, d = 128, bf16 inputs, h0,
+    random do and dht)."""
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device=dev)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    do = torch.randn(T, H, dv, device=dev, generator=gen).to(torch.bfloat16)
+    dht = torch.randn(1, H, dk, dv, device=dev, generator=gen)
+    ws = torch.empty(kda.chunk_bwd_workspace_size(1, T, 1, H, dk, dv), dtype=torch.uint8,
+                     device=dev)
+
+    def launch():
+        kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], do, dht=dht,
+                      h0=inp["h0"], workspace=ws, stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup, flush=make_flush(torch, dev))
+    avg = sum(ms) / len(ms)
+    nbytes = backward_bytes(T, H, dk, dv, 2)
+    del inp, do, dht, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"backward of prefill_8k: T={T}, H={H}, d_k=d_v={dk}, bf16 q/k/v/do, "
+                        "fp32 g/beta/h0/dht, fp32 gradients",
+            "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "roofline": hbm_roofline(nbytes, avg),
+            "algorithmic_bytes_per_call": nbytes,
+            "kernels": "chunk_bwd_tile_kernel (per-token fp32 reverse walk per 16-column tile) "
+                       "+ chunk_bwd_reduce_kernel"}
+
+
 def bench_segment(kda, wl, torch, dev, stream, steps, warmup, counts=(0, 64, 256)):
     """kda_segment_cp_fwd on the ultralong workload: the library's automatic segment count
     (the leg's figure) and the two ends of the workload's 64..256 range."""
@@ -452,9 +490,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen",
+    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen,backward",
                     help="comma-separated legs to run besides the prefill line (decode, "
-                         "verify_tiny, decode_sweep, segment, varlen, raw); the prefill leg "
+                         "verify_tiny, decode_sweep, segment, varlen, raw, backward); the "
+                         "prefill leg "
                          "always runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
@@ -567,7 +606,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
     legs = set(args.legs.split(","))
-    if legs & {"decode", "verify_tiny", "decode_sweep", "segment", "varlen", "raw"}:
+    if legs & {"decode", "verify_tiny", "decode_sweep", "segment", "varlen", "raw", "backward"}:
         del inp, q, k, v, g, beta, h0, o, ht, ws
         torch.cuda.empty_cache()
     if "decode" in legs:
@@ -584,6 +623,9 @@ def main():
                                            max(3, args.steps // 4), min(args.warmup, 2))
     if "raw" in legs:
         line["raw_prefill"] = bench_raw(kda, wl, torch, dev, stream, args.steps, args.warmup)
+    if "backward" in legs:
+        line["backward"] = bench_backward(kda, wl, torch, dev, stream, max(3, args.steps // 4),
+                                          min(args.warmup, 1))
     if "varlen" in legs:
         line["varlen"] = bench_varlen(kda, wl, torch, dev, stream, max(3, args.steps // 4),
                                       min(args.warmup, 1))

@@ -181,6 +181,54 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
                           float* ckpt_states, void* stream);
 
 /*
+ * kda_chunk_bwd: gradients of kda_chunk_fwd's outputs (training; "Noyaux KDA et FlashKDA",
+ * section "FlashKDA : le noyau par blocs": the kernel serves training as well as prefill). The
+ * pages give no backward; this is reverse-mode differentiation of the per-token update above,
+ * token by token in reverse order, in fp32:
+ *
+ *   D = dL/dS, from dht at the end of each sequence;  per token t, backwards:
+ *   D += scale q_t do_t^T;  dq_t = scale S_t do_t;  de = beta_t D^T k_t;  dv_t = de;
+ *   dk_t = beta_t D e_t - S'_t de;  dbeta_t = k_t^T D e_t;  D' = D - k_t de^T;
+ *   dg_t = a_t * rowsum(S_{t-1} * D') where g_t > g_min, else 0 (the floor is flat);
+ *   D = diag(a_t) D';  dh0 = D at the sequence start
+ *
+ * (e_t = v_t - S'_t^T k_t, S'_t = diag(a_t) S_{t-1}). The forward states are recomputed from
+ * checkpoints every 16 tokens that the call writes to its workspace.
+ *
+ *   q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs, num_heads,
+ *   d_k, d_v, io_dtype, scale, g_min: as for kda_chunk_fwd (the forward's inputs)
+ *   d_o      [T_total, H, d_v]   io_dtype   dL/do
+ *   dht      [N, H, d_k, d_v]    fp32       dL/d(final state), or NULL for zeros
+ *   dq, dk   [T_total, H, d_k]   fp32 outputs
+ *   dv       [T_total, H, d_v]   fp32
+ *   dg       [T_total, H, d_k]   fp32 (with respect to the raw g, before the floor)
+ *   dbeta    [T_total, H]        fp32
+ *   dh0      [N, H, d_k, d_v]    fp32, or NULL to skip it
+ *   workspace  at least kda_chunk_bwd_workspace_size bytes, 16-byte aligned, overlapping no
+ *              argument; its contents on entry are ignored, on return undefined.
+ *
+ * Supported: io_dtype KDA_BF16 or KDA_F32 with d_k = d_v in {64, 128}. Outputs must not overlap
+ * any input or each other. Results are deterministic (partial sums over value-column tiles are
+ * added in a fixed order). Two launches: the per-tile reverse walk, then the sum over tiles.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                  int num_heads, int d_k, int d_v, int io_dtype, float scale, float g_min,
+                  const void* d_o, const float* dht, float* dq, float* dk, float* dv, float* dg,
+                  float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Workspace bytes of kda_chunk_bwd: (T_total / 16 + N + 1) x H x d_k x d_v x 4 for the state
+ * checkpoints, plus 3 x (d_v / 16) x T_total x H x d_k x 4 and 4 x (d_v / 16) x T_total x H x 4
+ * for the partial sums (each part rounded up to 256 bytes). Same batch / seq_len / n_seqs
+ * conventions as kda_chunk_fwd_workspace_size.
+ */
+int kda_chunk_bwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                 int d_v, size_t* bytes);
+
+/*
  * kda_chunk_fwd_raw: the prefill from raw projections, with the short convolution, the input
  * norms and the gate activations fused into the prep pass of the two-launch form (the same
  * token stage as kda_decode_replay: "Noyaux d'inférence", section "1. Le décodage KDA", fused

@@ -61,6 +61,11 @@ def library():
     lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F,
                                           P, P, I, P, P]
     lib.kda_chunk_fwd_noalloc.restype = I
+    lib.kda_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, F, P, P, P, P,
+                                  P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_chunk_bwd.restype = I
+    lib.kda_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_chunk_bwd_workspace_size.restype = I
     lib.kda_chunk_fwd_workspace_size.argtypes = [I, I, I, P, I, I, I, I, I,
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_chunk_fwd_workspace_size.restype = I
@@ -257,6 +262,47 @@ def chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
     if ckpt_every:
         return a["o"], a["ht"], ckpt
     return a["o"], a["ht"]
+
+
+def chunk_bwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv):
+    out = ctypes.c_size_t(0)
+    st = library().kda_chunk_bwd_workspace_size(batch, seq_len, n_seqs, H, dk, dv,
+                                                ctypes.byref(out))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd_workspace_size")
+    return out.value
+
+
+def chunk_bwd(q, k, v, g, beta, do, dht=None, h0=None, cu_seqlens=None, scale=1.0, g_min=-5.0,
+              workspace=None, stream=None, cu_seqlens_host=None, want_dh0=True):
+    """kda_chunk_bwd: gradients of chunk_fwd's outputs. do: [.., H, d_v] like o (same dtype as
+    q); dht: [N, H, d_k, d_v] fp32 or None. Returns a dict of fp32 tensors dq, dk, dv, dg,
+    dbeta and dh0 (None when want_dh0 is False)."""
+    torch = _torch()
+    a = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, do, None, False, None,
+                      cu_seqlens_host=cu_seqlens_host)
+    if do.dtype != q.dtype:
+        raise ValueError("do must have q's dtype")
+    _check(dht, "dht", torch.float32, q.device)
+    T_arg = a["seq_len"] if a["cu_dev"] is None else int(a["cu_host"][-1])
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grads = {"dq": torch.empty(*q.shape, **f32), "dk": torch.empty(*k.shape, **f32),
+             "dv": torch.empty(*v.shape, **f32), "dg": torch.empty(*g.shape, **f32),
+             "dbeta": torch.empty(*beta.shape, **f32),
+             "dh0": (torch.empty(a["n_seqs"], a["H"], a["dk"], a["dv"], **f32)
+                     if want_dh0 else None)}
+    if workspace is None:
+        need = chunk_bwd_workspace_size(a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"])
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = library().kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(a["cu_dev"]),
+        _cu_host_ptr(a["cu_host"]), a["batch"], T_arg, a["n_seqs"], a["H"], a["dk"], a["dv"],
+        a["io"], float(scale), float(g_min), _ptr(do), _ptr(dht), _ptr(grads["dq"]),
+        _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]),
+        _ptr(grads["dh0"]), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd")
+    return grads
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20   # KDA_NOALLOC_SCRATCH_BYTES

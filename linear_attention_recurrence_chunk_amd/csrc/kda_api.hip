@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/kda.h"
+#include "kda_bwd.h"
 #include "kda_decode.h"
 #include "kda_internal.h"
 
@@ -464,6 +465,98 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
   return kda_chunk_fwd(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs,
                        num_heads, d_k, d_v, io_dtype, out_dtype, scale, g_min, o, ht, ckpt_every,
                        ckpt_states, ws, KDA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+int kda_chunk_bwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
+                                 int d_v, size_t* bytes) {
+  if (!bytes) return KDA_ERR_NULL_ARG;
+  if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
+    return KDA_ERR_BAD_SHAPE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  const bool packed = batch == 1 && n_seqs != 1;
+  const int64_t T = packed ? int64_t(seq_len) : int64_t(batch) * seq_len;
+  const int64_t N = packed ? n_seqs : batch;
+  *bytes = kda::bwd_workspace_bytes(T, N, num_heads, d_k, d_v);
+  return KDA_OK;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, const float* h0, const int32_t* cu_seqlens,
+                  const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
+                  int num_heads, int d_k, int d_v, int io_dtype, float scale, float g_min,
+                  const void* d_o, const float* dht, float* dq, float* dk, float* dv, float* dg,
+                  float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!d_o || !dq || !dk || !dv || !dg || !dbeta || !workspace) return KDA_ERR_NULL_ARG;
+  if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+  // the forward's checks (shapes, sequences, values), with d_o standing in for its output;
+  // fp32 inputs are validated as bf16 ones of the same widths (the backward takes both)
+  int N = 0;
+  int64_t T = 0;
+  const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
+                                  seq_len, n_seqs, num_heads, d_k, d_v, KDA_BF16, KDA_BF16, scale,
+                                  g_min, d_o, nullptr, &N, &T, 4);
+  if (st != KDA_OK) return st;
+  const size_t es = dsize(io_dtype);
+  const void* ptrs[] = {d_o, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const size_t need = kda::bwd_workspace_bytes(T, N, num_heads, d_k, d_v);
+  if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  {
+    const size_t st_bytes = size_t(N) * num_heads * d_k * d_v * 4;
+    const Range in[] = {
+        range_of(q, size_t(T) * num_heads * d_k * es), range_of(k, size_t(T) * num_heads * d_k * es),
+        range_of(v, size_t(T) * num_heads * d_v * es), range_of(g, size_t(T) * num_heads * d_k * 4),
+        range_of(beta, size_t(T) * num_heads * 4), range_of(h0, h0 ? st_bytes : 0),
+        range_of(d_o, size_t(T) * num_heads * d_v * es), range_of(dht, dht ? st_bytes : 0)};
+    const Range out[] = {
+        range_of(dq, size_t(T) * num_heads * d_k * 4), range_of(dk, size_t(T) * num_heads * d_k * 4),
+        range_of(dv, size_t(T) * num_heads * d_v * 4), range_of(dg, size_t(T) * num_heads * d_k * 4),
+        range_of(dbeta, size_t(T) * num_heads * 4), range_of(dh0, dh0 ? st_bytes : 0),
+        range_of(workspace, need)};
+    const int n_out = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < n_out; ++i) {
+      for (Range x : in)
+        if (overlaps(out[i], x)) return KDA_ERR_ALIASING;
+      for (int j = i + 1; j < n_out; ++j)
+        if (overlaps(out[i], out[j])) return KDA_ERR_ALIASING;
+    }
+  }
+  if (N == 0) return KDA_OK;
+  kda::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.h0 = h0;
+  p.d_o = d_o;
+  p.dht = dht;
+  p.cu_seqlens = cu_seqlens;
+  p.seq_len = cu_seqlens ? 0 : seq_len;
+  p.n_seqs = N;
+  p.H = num_heads;
+  p.n_ct = d_v / 16;
+  p.n_units = N * num_heads;
+  p.T = T;
+  p.scale = scale;
+  p.g_min = g_min;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dg = dg;
+  p.dbeta = dbeta;
+  p.dh0 = dh0;
+  char* ws = static_cast<char*>(workspace);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t ckpt_bytes = size_t(kda::bwd_ckpt_slots(T, N)) * num_heads * d_k * d_v * 4;
+  const size_t part_bytes = size_t(3) * p.n_ct * T * num_heads * d_k * 4;
+  p.ckpt = reinterpret_cast<float*>(ws);
+  p.part = reinterpret_cast<float*>(ws + up(ckpt_bytes));
+  p.part_beta = reinterpret_cast<float*>(ws + up(ckpt_bytes) + up(part_bytes));
+  return launch_status(kda::launch_chunk_bwd(p, io_dtype, d_k, static_cast<hipStream_t>(stream)));
 }
 
 int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

@@ -317,3 +317,37 @@ def test_noalloc_rejects_what_its_scratch_cannot_hold():
     # ordinary validation comes first
     assert noalloc(o=False) == NULL
     assert noalloc(dk=96) == UNSUP
+
+
+# ----------------------------------------------------------------------------- backward
+def bwd(io=BF16, dk=128, H=2, seq_len=256, ws_bytes=None, override=None):
+    P = ptrs(16)
+    a = dict(q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4], do=P[5], dq=P[6], dk=P[7], dv=P[8],
+             dg=P[9], dbeta=P[10], dh0=None, ws=P[11])
+    if override:
+        a.update(override)
+    need = ctypes.c_size_t(1 << 30)
+    kda.library().kda_chunk_bwd_workspace_size(1, seq_len, 1, H, dk, dk, ctypes.byref(need))
+    return kda.library().kda_chunk_bwd(
+        a["q"], a["k"], a["v"], a["g"], a["beta"], None, None, None, 1, seq_len, 1, H, dk, dk,
+        io, 1.0, -5.0, a["do"], None, a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"], a["dh0"],
+        a["ws"], need.value if ws_bytes is None else ws_bytes, None)
+
+
+def test_backward_validation():
+    for name in ("do", "dq", "dk", "dv", "dg", "dbeta", "ws"):
+        assert bwd(override={name: None}) == NULL
+    assert bwd(io=5) == DTYPE
+    assert bwd(dk=96) == UNSUP
+    assert bwd(ws_bytes=1024) == WS
+    assert bwd(override={"dq": ctypes.c_void_p(BASE + 0 * 64 * GiB)}) == ALIAS   # dq on q
+    assert bwd(override={"dk": ctypes.c_void_p(BASE + 6 * 64 * GiB)}) == ALIAS   # dk on dq
+    assert bwd(override={"dg": ctypes.c_void_p(BASE + 9 * 64 * GiB + 4)}) == ALIGN
+    need = ctypes.c_size_t(0)
+    assert kda.library().kda_chunk_bwd_workspace_size(1, 1024, 1, 4, 128, 128,
+                                                       ctypes.byref(need)) == OK
+    # checkpoints every 16 tokens, three partial sums per column tile, dbeta per wave and tile
+    ckpt = (1024 // 16 + 2) * 4 * 128 * 128 * 4
+    part = 3 * 8 * 1024 * 4 * 128 * 4
+    part_b = 4 * 8 * 1024 * 4 * 4
+    assert need.value == ckpt + part + part_b
