@@ -795,6 +795,7 @@ int kda_segment_cp_fwd(const void* q, const void* k, const void* v, const float*
   sp.n_seg = ns;
   sp.H = num_heads;
   sp.dv = d_v;
+  sp.f32 = io_dtype == KDA_F32;
   rc = launch_status(kda::launch_segment_scan(sp, d_k, s));
   if (rc != KDA_OK) return rc;
   // (3) all segments replay their tokens in parallel

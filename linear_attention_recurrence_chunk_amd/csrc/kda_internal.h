@@ -86,6 +86,7 @@ struct ScanParams {
   const int32_t* cu_seqlens;  // device [N + 1] or null (fixed length seq_len)
   int seq_len;
   int N, n_seg, H, dv;
+  int f32;                  // 1: fp32 products (fp32 io), 0: split bf16 (bf16 io)
 };
 
 hipError_t launch_segment_scan(const ScanParams& p, int dk, hipStream_t stream);

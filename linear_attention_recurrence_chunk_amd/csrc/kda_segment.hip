@@ -10,23 +10,30 @@
 // stored side by side as [P | Q]). The scan walks the segments of one sequence in order:
 //   S_in(0) = h0,  S_in(j + 1) = P_j S_in(j) + Q_j,  final state = S_in(n_seg).
 // Value columns stay independent, so one workgroup (4 waves x 16 columns) owns a 64-column
-// slice of one (sequence, head) and keeps it in MFMA accumulators. P_j is staged through LDS
-// as a hi + lo pair of bf16 values and multiplied with three bf16 MFMAs per product
-// (hi*hi + lo*hi + hi*lo, ~16 mantissa bits); S_in(j) is split the same way in registers.
+// slice of one (sequence, head) and keeps it in MFMA accumulators. For bf16 inputs P_j is
+// staged through LDS as a hi + lo pair of bf16 values and multiplied with three bf16 MFMAs per
+// product (hi*hi + lo*hi + hi*lo, ~16 mantissa bits), S_in(j) split the same way in
+// registers. For fp32 inputs (held to 1e-4 x RMS) P_j stays fp32 in LDS and the products run
+// on fp32 MFMA (v_mfma_f32_16x16x4_f32), with S_in(j) as its own operand.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <int DK>
+template <int DK, bool kF32>
 __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
   using Pol = PolBF16;
   using Frag = PolBF16::Frag;
   constexpr int LDP = DK + 8;
+  constexpr int LDF = DK + 1;   // fp32 rows: 16 consecutive rows fall in distinct banks
   constexpr int NS = DK / 32;
   constexpr int NTD = DK / 16;
-  __shared__ __attribute__((aligned(16))) __bf16 sPh[DK * LDP];
-  __shared__ __attribute__((aligned(16))) __bf16 sPl[DK * LDP];
+  // bf16: P as (hi, lo) pairs; fp32: P itself in the same bytes
+  constexpr size_t kPBytes = kF32 ? size_t(DK) * LDF * 4 : size_t(2) * DK * LDP * 2;
+  __shared__ __attribute__((aligned(16))) char smem[kPBytes];
+  __bf16* sPh = reinterpret_cast<__bf16*>(smem);
+  __bf16* sPl = sPh + DK * LDP;
+  float* sPf = reinterpret_cast<float*>(smem);
 
   const int n_vt = p.dv / 64;
   const int vt = blockIdx.x % n_vt;
@@ -88,38 +95,63 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
       continue;
     }
 
-    // P_j into LDS as (hi, lo) bf16, row = key channel
+    // P_j into LDS, row = key channel: (hi, lo) bf16, or fp32
 #pragma unroll
     for (int i = 0; i < kPPT; ++i) {
       const int idx = (tid + 256 * i) * 4;
       const int r = idx / DK, c = idx % DK;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = (__bf16)pr[i][e];
-        sPh[r * LDP + c + e] = hi;
-        sPl[r * LDP + c + e] = (__bf16)(pr[i][e] - (float)hi);
+        if constexpr (kF32) {
+          sPf[r * LDF + c + e] = pr[i][e];
+        } else {
+          const __bf16 hi = (__bf16)pr[i][e];
+          sPh[r * LDP + c + e] = hi;
+          sPl[r * LDP + c + e] = (__bf16)(pr[i][e] - (float)hi);
+        }
       }
     }
     __syncthreads();
 
     // S <- P_j S + Q_j
-    Frag Sh[NS], Sl[NS];
+    if constexpr (kF32) {
+      // k-slice s of the fp32 MFMA takes key rows 16 (s / 4) + 4 q4 + s % 4: the B operand
+      // is then this lane's own accumulator register S[s / 4][s % 4]
+      f32x4 Sold[NTD];
 #pragma unroll
-    for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
-    const float* q = p.pq + seg * DK * ldpq + DK;
+      for (int t = 0; t < NTD; ++t) Sold[t] = S[t];
+      const float* q = p.pq + seg * DK * ldpq + DK;
 #pragma unroll
-    for (int t = 0; t < NTD; ++t)
+      for (int t = 0; t < NTD; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
-    if (j + 1 < p.n_seg) fetch(j + 1);
-#pragma unroll
-    for (int pp = 0; pp < NS; ++pp) {
+        for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
+      if (j + 1 < p.n_seg) fetch(j + 1);
 #pragma unroll
       for (int t = 0; t < NTD; ++t) {
-        const Frag ah = Pol::load(sPh, LDP, 16 * t + ln, pp, q4);
-        S[t] = Pol::mma(ah, Sh[pp], S[t]);
-        S[t] = Pol::mma(Pol::load(sPl, LDP, 16 * t + ln, pp, q4), Sh[pp], S[t]);
-        S[t] = Pol::mma(ah, Sl[pp], S[t]);
+        const float* prow = sPf + (16 * t + ln) * LDF + 4 * q4;
+#pragma unroll
+        for (int s2 = 0; s2 < DK / 4; ++s2)
+          S[t] = mma_f32(prow[16 * (s2 >> 2) + (s2 & 3)], Sold[s2 >> 2][s2 & 3], S[t]);
+      }
+    } else {
+      Frag Sh[NS], Sl[NS];
+#pragma unroll
+      for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
+      const float* q = p.pq + seg * DK * ldpq + DK;
+#pragma unroll
+      for (int t = 0; t < NTD; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
+      if (j + 1 < p.n_seg) fetch(j + 1);
+#pragma unroll
+      for (int pp = 0; pp < NS; ++pp) {
+#pragma unroll
+        for (int t = 0; t < NTD; ++t) {
+          const Frag ah = Pol::load(sPh, LDP, 16 * t + ln, pp, q4);
+          S[t] = Pol::mma(ah, Sh[pp], S[t]);
+          S[t] = Pol::mma(Pol::load(sPl, LDP, 16 * t + ln, pp, q4), Sh[pp], S[t]);
+          S[t] = Pol::mma(ah, Sl[pp], S[t]);
+        }
       }
     }
     __syncthreads();
@@ -137,10 +169,14 @@ hipError_t launch_segment_scan(const ScanParams& p, int dk, hipStream_t stream) 
   if (p.N < 1 || p.H < 1 || p.n_seg < 1 || p.dv < 64 || p.dv % 64 || !p.pq || !p.sin)
     return hipErrorInvalidValue;
   const dim3 grid(p.N * p.H * (p.dv / 64));
-  if (dk == 128)
-    hipLaunchKernelGGL((segment_scan_kernel<128>), grid, dim3(256), 0, stream, p);
+  if (dk == 128 && p.f32)
+    hipLaunchKernelGGL((segment_scan_kernel<128, true>), grid, dim3(256), 0, stream, p);
+  else if (dk == 128)
+    hipLaunchKernelGGL((segment_scan_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  else if (dk == 64 && p.f32)
+    hipLaunchKernelGGL((segment_scan_kernel<64, true>), grid, dim3(256), 0, stream, p);
   else if (dk == 64)
-    hipLaunchKernelGGL((segment_scan_kernel<64>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((segment_scan_kernel<64, false>), grid, dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

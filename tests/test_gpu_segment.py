@@ -74,6 +74,21 @@ def test_segments_f32():
     assert e_o <= TOL_F32 and e_s <= TOL_F32
 
 
+@pytest.mark.parametrize("n_seg", [64, 256])
+def test_segments_f32_many_segments(n_seg):
+    """fp32 inputs across the workload's 64..256 segment range (16384 tokens, so that 256
+    segments still hold one chunk each): the ordered scan's products run in fp32, so the
+    composition of 256 summaries stays within the fp32 bar of 1e-4 x RMS."""
+    T = 16384
+    print(f"case segment f32 T={T} H=2 d=64 n_seg={n_seg}", flush=True)
+    inp = wl.prefill_inputs(T=T, H=2, dk=64, dv=64, dtype="f32", seed=60 + n_seg, h0_std=0.02)
+    o, ht = _seg(inp, n_seg, scale=0.9)
+    o_ref, ht_ref = _oracle(inp, varlen=False, scale=0.9)
+    e_o, e_s = rel_max_err(np64(o), o_ref), rel_max_err(np64(ht), ht_ref)
+    print(f"f32 n_seg={n_seg}: err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
+
+
 def test_workspace_too_small_is_rejected():
     inp = to_dev(wl.prefill_inputs(T=256, H=2, dk=128, dv=128, dtype="bf16", seed=1))
     # below the segment summaries themselves (the size the query gives for fp32 inputs)
