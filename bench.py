@@ -150,15 +150,15 @@ FLUSH_BYTES = 512 << 20   # written between timed launches: more than the 256 MB
 
 
 def make_flush(torch, dev):
-    """A 512 MiB device buffer and a function that overwrites it (a fill kernel on the current
+    """A 512 MiB device buffer and a function that reads all of it (a sum on the current
     stream), so that no timed launch finds its inputs left in L2 or the MALL by the previous
-    work (a different byte every call)."""
-    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    count = [0]
+    work. A read, not a write: the caches are left holding clean lines, so the timed launch
+    does not pay for writing back the flush's own data (or the state restore's, which the
+    read evicts first)."""
+    buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def flush():
-        count[0] += 1
-        buf.fill_(count[0] & 255)
+        buf.sum()
     return flush
 
 
@@ -236,7 +236,7 @@ def bench_decode(kda, wl, torch, dev, stream, steps, warmup, cpu_baseline):
            "rocprof_avg_ms": traced,
            "rocprof_frac": None if traced is None else nbytes / (traced * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "note": "latency_ms: HIP events around each launch, after the state restore and a "
-                   "512 MiB cache-flushing write; rocprof_avg_ms: the kernel's average duration "
+                   "512 MiB cache-flushing read; rocprof_avg_ms: the kernel's average duration "
                    "in the committed rocprofv3 trace of the same bench command (null once the "
                    "kernel source changed since)"}
     if cpu_baseline:

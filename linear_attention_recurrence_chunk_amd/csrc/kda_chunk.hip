@@ -132,11 +132,16 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
   constexpr int IM = 3 - IA;
   constexpr bool kTake30 = !kM && IA == 0;   // this wave also computes A block (3, 0)
   constexpr int kJ0 = (!kM && IA == 3) ? 1 : 0;   // first column block of the row
+  // M block (3, 0) moves from wave 0 to wave 3 (bf16 inputs, where M's off-diagonal column
+  // operands are rebuilt pairs): the waves then run 10, 11, 9 and 10 MFMAs per k-slice and
+  // 2, 2, 1 and 1 rebuilt blocks, instead of 13, 11, 9, 7 and 3, 2, 1, 0
+  constexpr bool kM30 = kM && Pol::kSplit && IA == 3;
+  constexpr int kMJ0 = (kM && Pol::kSplit && IM == 3) ? 1 : 0;   // first M column block
   // gap between sub-blocks i and j (i - j >= 2): the whole-sub-block decays strictly between
   // them, (2, 0) -> P_1, (3, 1) -> P_2, (3, 0) -> P_1 P_2 (sBP row b holds P_b per channel)
   const float* P1 = sBP + DK;
   const float* P2 = sBP + 2 * DK;
-  f32x4 accA[4], accM[4], acc30 = zero4();
+  f32x4 accA[4], accM[4], acc30 = zero4(), accM30 = zero4();
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
     accA[jb] = zero4();
@@ -145,8 +150,14 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
 #pragma unroll
   for (int pp = 0; pp < NS; ++pp) {
     const Frag rowA = Pol::load(sKr, L::LDP, 16 * IA + ln, pp, q4);
-    Frag rowM, colA[4], colM[4], colMl[4], dKl, dQl;
+    Frag rowM, colA[4], colM[4], colMl[4], dKl, dQl, rowM3, dQl3, colM30, colM30l;
     if constexpr (kM) rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pp, q4);
+    if constexpr (kM30) {
+      const float* const fac[3] = {sBP, sBP + DK, sBP + 2 * DK};
+      rowM3 = Pol::load(sQr, L::LDP, 48 + ln, pp, q4);
+      dQl3 = Pol::load(sQrLo, L::LDP, 48 + ln, pp, q4);
+      Pol::template load_pair_scaled<3>(sKd, sKdLo, L::LDP, ln, pp, q4, fac, colM30, colM30l);
+    }
 #pragma unroll
     for (int jb = kJ0; jb <= IA; ++jb) {
       if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
@@ -155,7 +166,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
       else colA[jb] = Pol::load_scaled(sKc, L::LDP, 16 * jb + ln, pp, q4, jb == 0 ? P1 : P2);
     }
 #pragma unroll
-    for (int jb = 0; jb <= IM; ++jb) {
+    for (int jb = kMJ0; jb <= IM; ++jb) {
       if constexpr (!kM) break;
       if (jb == IM) {
         colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pp, q4);
@@ -188,14 +199,17 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     }
     if constexpr (kM) {
 #pragma unroll
-      for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
+      for (int jb = kMJ0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
+      if constexpr (kM30) accM30 = Pol::mma(colM30, rowM3, accM30);
       if constexpr (Pol::kSplit) {
         accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
 #pragma unroll
-        for (int jb = 0; jb < IM; ++jb) accM[jb] = Pol::mma(colMl[jb], rowM, accM[jb]);
+        for (int jb = kMJ0; jb < IM; ++jb) accM[jb] = Pol::mma(colMl[jb], rowM, accM[jb]);
+        if constexpr (kM30) accM30 = Pol::mma(colM30l, rowM3, accM30);
         // the lo half of q rho on every block of the row
 #pragma unroll
-        for (int jb = 0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], dQl, accM[jb]);
+        for (int jb = kMJ0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], dQl, accM[jb]);
+        if constexpr (kM30) accM30 = Pol::mma(colM30, dQl3, accM30);
       }
     }
   }
@@ -217,13 +231,18 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     *reinterpret_cast<f32x4*>(sA + (48 + ln) * L::LDA + 4 * q4) = b3 * acc30;
   }
 #pragma unroll
-  for (int jb = 0; jb <= IM; ++jb) {
+  for (int jb = kMJ0; jb <= IM; ++jb) {
     if constexpr (!kM) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = 16 * jb + 4 * q4 + e;
       store_split_r<Pol>(sM, sMLo, rm * L::LDT + s, (jb == IM && s > rm) ? 0.f : accM[jb][e]);
     }
+  }
+  if constexpr (kM30) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      store_split_r<Pol>(sM, sMLo, (48 + ln) * L::LDT + 4 * q4 + e, accM30[e]);
   }
   // Diagonal block IA of T = (I + A)^{-1} in fp32, by right-looking substitution: the quad of
   // lanes 4 jc .. 4 jc + 3 solves column jc, lane part pp holding rows pp, pp + 4, pp + 8,

@@ -332,15 +332,25 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
         ks[j] = 0.f;
         qs[j] = 0.f;
       }
+      // (replayed drafts produce no output: their read-out sums are skipped)
+      if (output) {
 #pragma unroll
-      for (int m = 0; m < RPL / 4; ++m)
+        for (int m = 0; m < RPL / 4; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            ks[j] = fmaf(ak[m][u], S[4 * m + u][j], ks[j]);
-            qs[j] = fmaf(aq[m][u], S[4 * m + u][j], qs[j]);
-          }
+            for (int j = 0; j < CPL; ++j) {
+              ks[j] = fmaf(ak[m][u], S[4 * m + u][j], ks[j]);
+              qs[j] = fmaf(aq[m][u], S[4 * m + u][j], qs[j]);
+            }
+      } else {
+#pragma unroll
+        for (int m = 0; m < RPL / 4; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) ks[j] = fmaf(ak[m][u], S[4 * m + u][j], ks[j]);
+      }
       // the update's factors (a, beta k^), read while the column sums are reduced
       f32x4 fa[RPL / 4], fb[RPL / 4];
 #pragma unroll
@@ -350,9 +360,10 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
       }
       // sum over the 8 row groups (lanes cg, cg + 8, ..., cg + 56), fixed butterfly order
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        ks[j] = sum_xor32(sum_xor16(sum_xor8(ks[j])));
-        qs[j] = sum_xor32(sum_xor16(sum_xor8(qs[j])));
+      for (int j = 0; j < CPL; ++j) ks[j] = sum_xor32(sum_xor16(sum_xor8(ks[j])));
+      if (output) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) qs[j] = sum_xor32(sum_xor16(sum_xor8(qs[j])));
       }
       float e[CPL];
 #pragma unroll
