@@ -97,6 +97,21 @@ struct ChunkLayout {
   static_assert(kBytes <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
+// t * b split into a hi + lo pair: hi rounds the fp32 product, lo is the exact remainder
+// rounded (one explicit fma), so the bits never depend on whether the compiler fuses the
+// product into the subtraction
+template <class Pol>
+__device__ __forceinline__ void store_split_prod(typename Pol::E* hi, typename Pol::E* lo,
+                                                 int idx, float t, float b) {
+  using E = typename Pol::E;
+  const E h = from_f32<E>(t * b);
+  hi[idx] = h;
+  if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(fmaf(t, b, -to_f32(h)));
+}
+__device__ __forceinline__ void split_prod_bf16(float t, float b, __bf16& h, __bf16& l) {
+  h = (__bf16)(t * b);
+  l = (__bf16)fmaf(t, b, -(float)h);
+}
 // one element as an fp16 hi + lo pair (fp32 for fp32 inputs)
 template <class Pol>
 __device__ __forceinline__ void store_split_r(typename Pol::ER* hi, typename Pol::ER* lo, int idx,
@@ -105,15 +120,6 @@ __device__ __forceinline__ void store_split_r(typename Pol::ER* hi, typename Pol
   const R h = R(x);
   hi[idx] = h;
   if constexpr (Pol::kSplit) lo[idx] = R(x - float(h));
-}
-
-template <class Pol>
-__device__ __forceinline__ void store_split(typename Pol::E* hi, typename Pol::E* lo, int idx,
-                                            float x) {
-  using E = typename Pol::E;
-  const E h = from_f32<E>(x);
-  hi[idx] = h;
-  if constexpr (Pol::kSplit) lo[idx] = from_f32<E>(x - to_f32(h));
 }
 
 // Row-block IA of A and (kM) row-block 3 - IA of M for one wave. Column operands: k / rho on
@@ -283,7 +289,7 @@ __device__ __forceinline__ void am_rows(const typename Pol::E* sKr, const typena
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * IA + pp + 4 * i;
       sA[r * L::LDA + 16 * IA + jc] = x[i];
-      store_split<Pol>(sT, sTLo, r * L::LDT + 16 * IA + jc, x[i] * bj);
+      store_split_prod<Pol>(sT, sTLo, r * L::LDT + 16 * IA + jc, x[i], bj);
     }
   }
 }
@@ -895,7 +901,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
-        store_split<Pol>(sT, sTLo, (16 * bi + 4 * q4 + e) * L::LDT + 16 * bj + ln, -Y[e] * bcol);
+        store_split_prod<Pol>(sT, sTLo, (16 * bi + 4 * q4 + e) * L::LDT + 16 * bj + ln, -Y[e],
+                              bcol);
       }
     };
     if (w & 1) {
@@ -1108,6 +1115,531 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Pass 1 of the two-launch prefill for bf16 inputs: each chunk's prologue, stored to its operand
+// slot. The arithmetic is chunk_fwd_kernel's prologue operation for operation, per key channel
+// and per product accumulator, so the slot holds the same bits as the operands that kernel
+// computes for its serial step. What differs is where the data lives:
+//  * channels go in passes of 64: in pass h a thread takes channels 64 h + CPT l .. + CPT - 1
+//    (l = lane % (d_k / 4), CPT = 2 at d_k = 128, 4 at 64) of the same tokens as there, so
+//    each channel's decay products see the same operations in the same order; the prologue
+//    tiles hold 64 channels and A and M accumulate over the passes;
+//  * the serial step's operands go from registers straight to the slot: Q e^Gamma, K e^Gamma
+//    and (K e^{Gamma_L - Gamma})^T per pass, M from its accumulators, T diag(beta) from the
+//    fp32 inverse once complete; no LDS holds them.
+// LDS: six 64-channel tiles, the fp32 A / T matrix and small vectors, 72 KB: two workgroups
+// per compute unit, so one workgroup's loads and stores run under the other's products.
+template <int DK>
+struct PrepLayout {
+  static constexpr int PW = 64;              // channels per pass
+  static constexpr int LDP = PW + 4;         // tile row stride: 2 dwords modulo 32 banks
+  static constexpr int LDA = 64 + 4;         // fp32 A / T working matrix
+  static constexpr size_t tP = size_t(64) * LDP * 2;
+  static constexpr size_t oQr = 0;
+  static constexpr size_t oQrLo = oQr + tP;
+  static constexpr size_t oKd = oQrLo + tP;
+  static constexpr size_t oKdLo = oKd + tP;
+  static constexpr size_t oKr = oKdLo + tP;
+  static constexpr size_t oKc = oKr + tP;
+  static constexpr size_t oA = oKc + tP;
+  static constexpr size_t oBeta = oA + size_t(64) * LDA * 4;   // two chunks' betas
+  static constexpr size_t oBP = oBeta + 2 * 64 * 4;             // [4][DK] sub-block decays
+  static constexpr size_t oDecay = oBP + 4 * DK * 4;            // [DK] whole-chunk decay
+  static constexpr size_t kBytes = oDecay + DK * 4;
+  static_assert(2 * kBytes <= 160 * 1024, "two workgroups per compute unit");
+};
+
+// Products of one channel pass for wave IA: row block IA of A and row block IM = 3 - IA of M
+// (M block (3, 0) on wave 3, as in am_rows), over the pass's two k-slices (global slices
+// 2 h and 2 h + 1), into accumulators kept across the passes. Same loads and MFMAs, in the same
+// order per accumulator, as am_rows in forward mode.
+template <int DK, int IA>
+__device__ __forceinline__ void prep_am_pass(const __bf16* sKr, const __bf16* sKd,
+                                             const __bf16* sKdLo, const __bf16* sKc,
+                                             const __bf16* sQr, const __bf16* sQrLo,
+                                             const float* sBP, int hp, f32x4 (&accA)[4],
+                                             f32x4 (&accM)[4], f32x4& accM30, int ln, int q4) {
+  using Pol = PolBF16;
+  using Frag = Pol::Frag;
+  using L = PrepLayout<DK>;
+  constexpr int IM = 3 - IA;
+  constexpr bool kM30 = IA == 3;
+  constexpr int kMJ0 = IM == 3 ? 1 : 0;
+  const float* P1 = sBP + DK;
+  const float* P2 = sBP + 2 * DK;
+  // (one slice at a time: the fragments of both slices at once do not fit the registers of
+  // two waves per SIMD)
+#pragma unroll 1
+  for (int pl = 0; pl < 2; ++pl) {
+    const int pp = 2 * hp + pl;   // global k-slice (factor columns); pl indexes the tiles
+    const Frag rowA = Pol::load(sKr, L::LDP, 16 * IA + ln, pl, q4);
+    Frag rowM, colA[4], colM[4], colMl[4], dKl, dQl, rowM3, dQl3, colM30, colM30l;
+    rowM = Pol::load(sQr, L::LDP, 16 * IM + ln, pl, q4);
+    if constexpr (kM30) {
+      const float* const fac[3] = {sBP, sBP + DK, sBP + 2 * DK};
+      rowM3 = Pol::load(sQr, L::LDP, 48 + ln, pl, q4);
+      dQl3 = Pol::load(sQrLo, L::LDP, 48 + ln, pl, q4);
+      Pol::template load_pair_scaled_at<3>(sKd, sKdLo, L::LDP, ln, pl, pp, q4, fac, colM30, colM30l);
+    }
+#pragma unroll
+    for (int jb = 0; jb <= IA; ++jb) {
+      if (jb == IA) colA[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pl, q4);
+      else if (jb == IA - 1) colA[jb] = Pol::load(sKc, L::LDP, 16 * jb + ln, pl, q4);
+      else if (jb == 0 && IA == 3) colA[jb] = Pol::load_scaled2_at(sKc, L::LDP, ln, pl, pp, q4, P1, P2);
+      else colA[jb] = Pol::load_scaled_at(sKc, L::LDP, 16 * jb + ln, pl, pp, q4, jb == 0 ? P1 : P2);
+    }
+#pragma unroll
+    for (int jb = kMJ0; jb <= IM; ++jb) {
+      if (jb == IM) {
+        colM[jb] = Pol::load(sKd, L::LDP, 16 * jb + ln, pl, q4);
+      } else {
+        const float* const fac[3] = {sBP + jb * DK, sBP + (jb + 1) * DK, sBP + (jb + 2) * DK};
+        if (IM - jb == 1)
+          Pol::template load_pair_scaled_at<1>(sKd, sKdLo, L::LDP, 16 * jb + ln, pl, pp, q4, fac, colM[jb], colMl[jb]);
+        else if (IM - jb == 2)
+          Pol::template load_pair_scaled_at<2>(sKd, sKdLo, L::LDP, 16 * jb + ln, pl, pp, q4, fac, colM[jb], colMl[jb]);
+        else
+          Pol::template load_pair_scaled_at<3>(sKd, sKdLo, L::LDP, 16 * jb + ln, pl, pp, q4, fac, colM[jb], colMl[jb]);
+      }
+    }
+    dKl = Pol::load(sKdLo, L::LDP, 16 * IM + ln, pl, q4);
+    dQl = Pol::load(sQrLo, L::LDP, 16 * IM + ln, pl, q4);
+#pragma unroll
+    for (int jb = 0; jb <= IA; ++jb) accA[jb] = Pol::mma(colA[jb], rowA, accA[jb]);
+#pragma unroll
+    for (int jb = kMJ0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], rowM, accM[jb]);
+    if constexpr (kM30) accM30 = Pol::mma(colM30, rowM3, accM30);
+    accM[IM] = Pol::mma(dKl, rowM, accM[IM]);
+#pragma unroll
+    for (int jb = kMJ0; jb < IM; ++jb) accM[jb] = Pol::mma(colMl[jb], rowM, accM[jb]);
+    if constexpr (kM30) accM30 = Pol::mma(colM30l, rowM3, accM30);
+#pragma unroll
+    for (int jb = kMJ0; jb <= IM; ++jb) accM[jb] = Pol::mma(colM[jb], dQl, accM[jb]);
+    if constexpr (kM30) accM30 = Pol::mma(colM30, dQl3, accM30);
+  }
+}
+
+// After the passes: A's row block into the fp32 matrix, M's blocks straight to the slot (fp16
+// hi and lo fragments; zeros for the strictly upper block sharing a fragment with the
+// diagonal one), and the diagonal block of T = (I + A)^{-1} by the same fp32 substitution as
+// am_rows (T diag(beta) is formed later, from the fp32 matrix).
+template <int DK, int IA>
+__device__ __forceinline__ void prep_am_finish(const f32x4 (&accA)[4], const f32x4 (&accM)[4],
+                                               const f32x4& accM30, const float* sBeta,
+                                               float* sA, char* slot, int ln, int q4) {
+  using L = PrepLayout<DK>;
+  using OS = OpSlot<DK>;
+  constexpr int IM = 3 - IA;
+  constexpr bool kM30 = IA == 3;
+  constexpr int kMJ0 = IM == 3 ? 1 : 0;
+  const int lane = 16 * q4 + ln;
+  const int ra = 16 * IA + ln, rm = 16 * IM + ln;
+  const float br = sBeta[ra];
+#pragma unroll
+  for (int jb = 0; jb <= IA; ++jb) {
+    f32x4 outv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 16 * jb + 4 * q4 + e;
+      outv[e] = (jb == IA && s >= ra) ? 0.f : br * accA[jb][e];
+    }
+    *reinterpret_cast<f32x4*>(sA + ra * L::LDA + 16 * jb + 4 * q4) = outv;
+  }
+  // M block (row block i, column block jb): register e is column 16 jb + 4 q4 + e of row
+  // 16 i + ln, i.e. half jb % 2 of this lane's 16 bytes in fragment (i, jb / 2)
+  auto put_m = [&](int i, int jb, f32x4 x) {
+    f16x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 h = (_Float16)x[e];
+      hi[e] = h;
+      lo[e] = (_Float16)(x[e] - float(h));
+    }
+    const int f = OS::tri(i, jb / 2);
+    char* dst = slot + lane * 16 + (jb & 1) * 8;
+    *reinterpret_cast<f16x4*>(dst + size_t(OS::fM + f) * 1024) = hi;
+    *reinterpret_cast<f16x4*>(dst + size_t(OS::fMLo + f) * 1024) = lo;
+  };
+#pragma unroll
+  for (int jb = kMJ0; jb <= IM; ++jb) {
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = 16 * jb + 4 * q4 + e;
+      x[e] = (jb == IM && s > rm) ? 0.f : accM[jb][e];
+    }
+    put_m(IM, jb, x);
+  }
+  if constexpr (IM % 2 == 0) put_m(IM, IM + 1, zero4());   // strictly upper, same fragment
+  if constexpr (kM30) put_m(3, 0, accM30);
+  // diagonal block IA of T, as in am_rows
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  {
+    const int jc = lane >> 2, pp = lane & 3;
+    const float* Ab = sA + 16 * IA * L::LDA + 16 * IA;
+    f32x4 arow[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        arow[i][m] = *reinterpret_cast<const f32x4*>(Ab + (pp + 4 * i) * L::LDA + 4 * m);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (pp + 4 * i == jc) ? 1.f : 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 15; ++s2) {
+      float xs;
+      switch (s2 & 3) {
+        case 0: xs = quad_bcast<0>(x[s2 >> 2]); break;
+        case 1: xs = quad_bcast<1>(x[s2 >> 2]); break;
+        case 2: xs = quad_bcast<2>(x[s2 >> 2]); break;
+        default: xs = quad_bcast<3>(x[s2 >> 2]); break;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = fmaf(-arow[i][s2 >> 2][s2 & 3], xs, x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sA[(16 * IA + pp + 4 * i) * L::LDA + 16 * IA + jc] = x[i];
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
+  using Pol = PolBF16;
+  using L = PrepLayout<DK>;
+  using OS = OpSlot<DK>;
+  using PM = ProMap<DK>;
+  constexpr int TPT = PM::kTPT;          // tokens per thread
+  constexpr int NPASS = DK / 64;         // channel passes
+  constexpr int CPT = 4 / NPASS;         // channels per thread and pass
+  constexpr int NS = DK / 32;
+  using GV = float __attribute__((ext_vector_type(CPT)));
+  using BV = __bf16 __attribute__((ext_vector_type(CPT)));
+  using HV = _Float16 __attribute__((ext_vector_type(CPT)));
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  __bf16* sQr = reinterpret_cast<__bf16*>(smem + L::oQr);
+  __bf16* sQrLo = reinterpret_cast<__bf16*>(smem + L::oQrLo);
+  __bf16* sKd = reinterpret_cast<__bf16*>(smem + L::oKd);
+  __bf16* sKdLo = reinterpret_cast<__bf16*>(smem + L::oKdLo);
+  __bf16* sKr = reinterpret_cast<__bf16*>(smem + L::oKr);
+  __bf16* sKc = reinterpret_cast<__bf16*>(smem + L::oKc);
+  float* sA = reinterpret_cast<float*>(smem + L::oA);
+  float* sBetaAll = reinterpret_cast<float*>(smem + L::oBeta);
+  float* sBP = reinterpret_cast<float*>(smem + L::oBP);
+  float* sDecay = reinterpret_cast<float*>(smem + L::oDecay);
+
+  int sub;
+  const int unit = block_unit(blockIdx.x, 1, &sub);
+  if (unit >= p.n_units) return;
+  const int H = p.H;
+  const int h = unit % H;
+  const int sj = unit / H;
+  const int n = p.seq0 + sj / p.n_seg;
+  const int j = sj % p.n_seg;
+  int bos, eos;
+  if (p.cu_seqlens) {
+    bos = p.cu_seqlens[n];
+    eos = p.cu_seqlens[n + 1];
+  } else {
+    bos = n * p.seq_len;
+    eos = bos + p.seq_len;
+  }
+  const long long seq_slot0 = seq_first_slot(bos, p.slot_tok0, n, p.seq0);
+  const int seq_bos = bos;
+  {
+    int c_lo;
+    segment_range(seq_bos, eos, j, p.n_seg, &bos, &eos, &c_lo);
+  }
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int q4 = lane >> 4;
+  const int ln = lane & 15;
+  const int grp = lane / PM::kLPT;
+  const int li = lane % PM::kLPT;
+  const int rb0 = 16 * w + grp * TPT;          // first token row of this thread
+  const float gmin2 = p.g_min * kLog2e;
+  const __bf16* gq = reinterpret_cast<const __bf16*>(p.q);
+  const __bf16* gk = reinterpret_cast<const __bf16*>(p.k);
+
+  int cnum = 0;
+  for (int cstart = bos; cstart < eos; cstart += kChunk, ++cnum) {
+    const int Lc = min(kChunk, eos - cstart);
+    float* sBeta = sBetaAll + 64 * (cnum & 1);
+    char* slot = p.ws_ops + (size_t(seq_slot0 + (cstart - seq_bos) / kChunk) * H + h) * OS::kBytes;
+    float beta_r;
+    {
+      const int bl = lane & 15;
+      const int r = 16 * w + bl;
+      beta_r = p.beta[size_t(r < Lc ? cstart + r : cstart) * H + h];
+      beta_r = r < Lc ? beta_r : 0.f;
+    }
+    if (lane < 16) sBeta[16 * w + lane] = beta_r;
+
+    f32x4 accA[4], accM[4], accM30 = zero4();
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      accA[jb] = zero4();
+      accM[jb] = zero4();
+    }
+#pragma unroll
+    for (int hp = 0; hp < NPASS; ++hp) {
+      const int c0 = 64 * hp + CPT * li;   // first channel of the thread in this pass
+      const int tc0 = CPT * li;            // its column in the 64-channel tiles
+      // ---- this pass's inputs (rows past a ragged chunk's end read its first row; their
+      //      values are masked below)
+      GV gin[TPT];
+      BV kin[TPT], qin[TPT];
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const int r = rb0 + t;
+        const size_t row = (size_t(r < Lc ? cstart + r : cstart) * H + h) * DK + c0;
+        gin[t] = *reinterpret_cast<const GV*>(p.g + row);
+        kin[t] = *reinterpret_cast<const BV*>(gk + row);
+        qin[t] = *reinterpret_cast<const BV*>(gq + row);
+      }
+      // ---- decay factors, as in chunk_fwd_kernel's prologue, per channel
+      float rho[TPT][CPT], qv[TPT][CPT], kv[TPT][CPT], ex[TPT][CPT];
+      float lp[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) lp[c] = 1.f;
+#pragma unroll
+      for (int t = 0; t < TPT; ++t) {
+        const bool valid = rb0 + t < Lc;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const float gt = valid ? fmaxf(gin[t][c] * kLog2e, gmin2) : 0.f;
+          ex[t][c] = __builtin_amdgcn_exp2f(gt);
+          kv[t][c] = valid ? (float)kin[t][c] : 0.f;
+          qv[t][c] = valid ? (float)qin[t][c] : 0.f;
+          lp[c] *= ex[t][c];
+          rho[t][c] = lp[c];
+        }
+      }
+      float bp[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        float pre;
+        if constexpr (PM::kNG == 2) {
+          const float o = __shfl_xor(lp[c], 32);
+          pre = grp ? o : 1.f;
+          bp[c] = lp[c] * o;
+        } else {
+          static_assert(PM::kNG == 4, "token groups per sub-block");
+          const float a = __shfl_xor(lp[c], 16);
+          const float pair = lp[c] * a;
+          const float b2 = __shfl_xor(pair, 32);
+          pre = ((grp & 2) ? b2 : 1.f) * ((grp & 1) ? a : 1.f);
+          bp[c] = pair * b2;
+        }
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) rho[t][c] *= pre;
+      }
+      float rinv_next[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) rinv_next[c] = __builtin_amdgcn_rcpf(rho[TPT - 1][c]);
+#pragma unroll
+      for (int t = TPT - 1; t >= 0; --t) {
+        BV qh, ql, dh, dl, kr, kc;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const float rh = rho[t][c];
+          const float rinv = rinv_next[c];
+          if (t > 0) rinv_next[c] = rinv * ex[t][c];
+          const float k0 = kv[t][c];
+          const float xq = qv[t][c] * rh;
+          const float xkd = k0 * rinv;
+          const float xkr = k0 * rh;
+          const float xkc = xkd * bp[c];
+          qv[t][c] = xq;
+          kv[t][c] = xkr;
+          rho[t][c] = xkc;
+          qh[c] = (__bf16)xq;
+          ql[c] = (__bf16)(xq - (float)qh[c]);
+          dh[c] = (__bf16)xkd;
+          dl[c] = (__bf16)(xkd - (float)dh[c]);
+          kr[c] = (__bf16)xkr;
+          kc[c] = (__bf16)xkc;
+        }
+        const int idx = (rb0 + t) * L::LDP + tc0;
+        *reinterpret_cast<BV*>(sQr + idx) = qh;
+        *reinterpret_cast<BV*>(sQrLo + idx) = ql;
+        *reinterpret_cast<BV*>(sKd + idx) = dh;
+        *reinterpret_cast<BV*>(sKdLo + idx) = dl;
+        *reinterpret_cast<BV*>(sKr + idx) = kr;
+        *reinterpret_cast<BV*>(sKc + idx) = kc;
+      }
+      if (grp == 0) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) sBP[w * DK + c0 + c] = bp[c];
+      }
+      __syncthreads();
+      // ---- this pass's recurrence operands, straight to the slot: Q e^Gamma and K e^Gamma
+      //      (token rows, fragment (w, channel / 32)) and (K e^{Gamma_L - Gamma})^T (channel
+      //      rows, fragment (channel / 16, token / 32)), fp16
+      {
+        float fs[CPT], fe[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          float pb[4];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) pb[bb] = sBP[bb * DK + c0 + c];
+          fs[c] = 1.f;
+          fe[c] = 1.f;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            if (bb < w) fs[c] *= pb[bb];
+            if (bb > w) fe[c] *= pb[bb];
+          }
+          if (w == 0 && grp == 0) sDecay[c0 + c] = pb[0] * pb[1] * pb[2] * pb[3];
+        }
+        // channel c0 of token row r: lane 16 ((c0 % 16) / 4) + r % 16 of fragment
+        // (r / 16, c0 / 32), bytes from 8 ((c0 % 32) / 16) + 2 (c0 % 4)
+        const size_t fbase = size_t(w * NS + c0 / 32) * 1024 + size_t((c0 % 16) / 4) * 256 +
+                             ((c0 % 32) / 16) * 8 + (c0 % 4) * 2;
+#pragma unroll
+        for (int t = 0; t < TPT; ++t) {
+          HV xq, xk;
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) {
+            xq[c] = (_Float16)(qv[t][c] * fs[c]);
+            xk[c] = (_Float16)(kv[t][c] * fs[c]);
+          }
+          const size_t o = fbase + size_t((rb0 + t) % 16) * 16;
+          *reinterpret_cast<HV*>(slot + size_t(OS::fQg) * 1024 + o) = xq;
+          *reinterpret_cast<HV*>(slot + size_t(OS::fKg) * 1024 + o) = xk;
+        }
+        // channel row c0 + c, tokens rb0 + t4 .. + 3: lane 16 ((token % 16) / 4) + channel % 16
+        // of fragment (channel / 16, token / 32), bytes from 8 ((token % 32) / 16)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int ch = c0 + c;
+#pragma unroll
+          for (int t4 = 0; t4 < TPT; t4 += 4) {
+            const int r = rb0 + t4;
+            f16x4 col;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) col[e] = (_Float16)(rho[t4 + e][c] * fe[c]);
+            const size_t o = size_t(OS::fKh + 2 * (ch / 16) + r / 32) * 1024 +
+                             size_t(16 * ((r % 16) / 4) + ch % 16) * 16 + ((r % 32) / 16) * 8;
+            *reinterpret_cast<f16x4*>(slot + o) = col;
+          }
+        }
+      }
+      // ---- A and M products over this pass's two k-slices
+      switch (w) {
+        case 0: prep_am_pass<DK, 0>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
+        case 1: prep_am_pass<DK, 1>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
+        case 2: prep_am_pass<DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
+        default: prep_am_pass<DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
+      }
+      __syncthreads();   // the tiles are rewritten by the next pass (or the next chunk)
+    }
+    // ---- A's row blocks, M to the slot, diagonal blocks of T
+    switch (w) {
+      case 0: prep_am_finish<DK, 0>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
+      case 1: prep_am_finish<DK, 1>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
+      case 2: prep_am_finish<DK, 2>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
+      default: prep_am_finish<DK, 3>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
+    }
+    __syncthreads();
+    // ---- off-diagonal blocks of T, as in chunk_fwd_kernel (level 1 on waves 1 and 3, then
+    //      one level-2 block per wave); T_ij (i > j) in the free upper position (j, i)
+    auto tblk = [&](int bi, int bj) -> float* {
+      return bi == bj ? sA + 16 * bi * L::LDA + 16 * bi : sA + 16 * bj * L::LDA + 16 * bi;
+    };
+    auto ablk = [&](int bi, int bj) -> const float* { return sA + 16 * bi * L::LDA + 16 * bj; };
+    auto mm_acc2 = [&](f32x4& Xa, const float* A1, const float* T1, f32x4& Xb, const float* A2,
+                       const float* T2) {
+#pragma unroll
+      for (int kk2 = 0; kk2 < 4; ++kk2) {
+        Xa = mma_f32(A1[ln * L::LDA + 4 * kk2 + q4], T1[(4 * kk2 + q4) * L::LDA + ln], Xa);
+        Xb = mma_f32(A2[ln * L::LDA + 4 * kk2 + q4], T2[(4 * kk2 + q4) * L::LDA + ln], Xb);
+      }
+    };
+    auto mm_acc_split = [&](f32x4& Xa, f32x4& Xb, const float* Ab, const float* Tb) {
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        Xa = mma_f32(Ab[ln * L::LDA + 4 * kk2 + q4], Tb[(4 * kk2 + q4) * L::LDA + ln], Xa);
+        Xb = mma_f32(Ab[ln * L::LDA + 4 * kk2 + 8 + q4], Tb[(4 * kk2 + 8 + q4) * L::LDA + ln], Xb);
+      }
+    };
+    auto mm_reg2 = [&](f32x4& Ya, const float* T1, f32x4 X1, f32x4& Yb, const float* T2, f32x4 X2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Ya = mma_f32(T1[ln * L::LDA + 4 * q4 + e], X1[e], Ya);
+        Yb = mma_f32(T2[ln * L::LDA + 4 * q4 + e], X2[e], Yb);
+      }
+    };
+    auto mm_reg_split = [&](f32x4& Ya, f32x4& Yb, const float* Tb, f32x4 X) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Ya = mma_f32(Tb[ln * L::LDA + 4 * q4 + e], X[e], Ya);
+        Yb = mma_f32(Tb[ln * L::LDA + 4 * q4 + e + 2], X[e + 2], Yb);
+      }
+    };
+    auto put = [&](int bi, int bj, f32x4 Y) {
+      float* To = tblk(bi, bj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) To[(4 * q4 + e) * L::LDA + ln] = -Y[e];
+    };
+    if (w & 1) {
+      const int lo = w - 1;
+      f32x4 Xa = zero4(), Xb = zero4(), Ya = zero4(), Yb = zero4();
+      mm_acc_split(Xa, Xb, ablk(lo + 1, lo), tblk(lo, lo));
+      mm_reg_split(Ya, Yb, tblk(lo + 1, lo + 1), Xa + Xb);
+      put(lo + 1, lo, Ya + Yb);
+    }
+    __syncthreads();
+    {
+      const int bj = w & 1;
+      const bool row3 = w >= 2;
+      f32x4 X2a = zero4(), X2b = zero4(), X3a = zero4(), X3b = zero4();
+      if (bj == 0) {
+        mm_acc2(X2a, ablk(2, 0), tblk(0, 0), X2b, ablk(2, 1), tblk(1, 0));
+        if (row3) mm_acc2(X3a, ablk(3, 0), tblk(0, 0), X3b, ablk(3, 1), tblk(1, 0));
+      } else {
+        mm_acc_split(X2a, X2b, ablk(2, 1), tblk(1, 1));
+        if (row3) mm_acc_split(X3a, X3b, ablk(3, 1), tblk(1, 1));
+      }
+      f32x4 Ya = zero4(), Yb = zero4();
+      if (!row3) mm_reg_split(Ya, Yb, tblk(2, 2), X2a + X2b);
+      else mm_reg2(Ya, tblk(3, 2), X2a + X2b, Yb, tblk(3, 3), X3a + X3b);
+      put(row3 ? 3 : 2, bj, Ya + Yb);
+    }
+    __syncthreads();
+    // ---- T diag(beta) (bf16 hi and lo) of the 6 lower fragments, from the fp32 matrix: lane
+    //      (q4, ln) holds row 16 rb + ln, columns 32 pp + 16 hh + 4 q4 + e; and the decay
+    for (int i = w; i < 6; i += 4) {
+      const int rb = i < 2 ? i : (i < 4 ? 2 : 3), pp = i < 2 ? 0 : (i & 1);
+      const int r = 16 * rb + ln;
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int c = 32 * pp + 16 * (e8 >> 2) + 4 * q4 + (e8 & 3);
+        const int cb = c >> 4;
+        float t;
+        if (cb > rb) t = 0.f;
+        else if (cb == rb) t = sA[r * L::LDA + c];
+        else t = sA[(16 * cb + ln) * L::LDA + 16 * rb + (c & 15)];
+        __bf16 h, l;
+        split_prod_bf16(t, sBeta[c], h, l);   // as store_split_prod
+        hi[e8] = h;
+        lo[e8] = l;
+      }
+      __builtin_nontemporal_store(hi, reinterpret_cast<bf16x8*>(slot + size_t(OS::fT + i) * 1024 + lane * 16));
+      __builtin_nontemporal_store(lo, reinterpret_cast<bf16x8*>(slot + size_t(OS::fTLo + i) * 1024 + lane * 16));
+    }
+    if (w == 0 && lane < DK / 4)
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(sDecay + 4 * lane),
+                                  reinterpret_cast<f32x4*>(slot + size_t(OS::kDecay) * 1024 + lane * 16));
+  }
+}
+
 template <class Pol, typename Tio, typename Tout, int DK>
 static hipError_t launch_one(const ChunkParams& p, hipStream_t stream) {
   const int groups = (p.n_units + 7) / 8;
@@ -1145,14 +1677,12 @@ hipError_t launch_chunk_prep(const ChunkParams& base, int prep_groups, int dk,
     hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true, true>), grid,
                        dim3(256), 0, stream, prep);
   else if (dk == 128)
-    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 128, true, true>), grid,
-                       dim3(256), 0, stream, prep);
+    hipLaunchKernelGGL((chunk_prep_kernel<128>), grid, dim3(256), 0, stream, prep);
   else if (dk == 64 && raw)
     hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 64, true, true, true>), grid,
                        dim3(256), 0, stream, prep);
   else if (dk == 64)
-    hipLaunchKernelGGL((chunk_fwd_kernel<PolBF16, __bf16, float, 64, true, true>), grid,
-                       dim3(256), 0, stream, prep);
+    hipLaunchKernelGGL((chunk_prep_kernel<64>), grid, dim3(256), 0, stream, prep);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

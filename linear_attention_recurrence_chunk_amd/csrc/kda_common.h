@@ -58,8 +58,14 @@ struct PolBF16 {
   // fragment scaled per k by fac[k] (fp32), rounded once to bf16
   __device__ static __forceinline__ Frag load_scaled(const E* tile, int ld, int row, int p,
                                                      int q, const float* fac) {
+    return load_scaled_at(tile, ld, row, p, p, q, fac);
+  }
+  // the same with the tile's slice p and the factors' slice pf given apart (tiles that hold
+  // only part of the channels)
+  __device__ static __forceinline__ Frag load_scaled_at(const E* tile, int ld, int row, int p,
+                                                        int pf, int q, const float* fac) {
     const E* base = tile + row * ld + 32 * p + 4 * q;
-    const float* fb = fac + 32 * p + 4 * q;
+    const float* fb = fac + 32 * pf + 4 * q;
     bf16x4 lo = *reinterpret_cast<const bf16x4*>(base);
     bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16);
     f32x4 flo = *reinterpret_cast<const f32x4*>(fb);
@@ -76,8 +82,13 @@ struct PolBF16 {
   __device__ static __forceinline__ Frag load_scaled2(const E* tile, int ld, int row, int p,
                                                       int q, const float* fac1,
                                                       const float* fac2) {
+    return load_scaled2_at(tile, ld, row, p, p, q, fac1, fac2);
+  }
+  __device__ static __forceinline__ Frag load_scaled2_at(const E* tile, int ld, int row, int p,
+                                                         int pf, int q, const float* fac1,
+                                                         const float* fac2) {
     const E* base = tile + row * ld + 32 * p + 4 * q;
-    const int o = 32 * p + 4 * q;
+    const int o = 32 * pf + 4 * q;
     bf16x4 lo = *reinterpret_cast<const bf16x4*>(base);
     bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16);
     f32x4 alo = *reinterpret_cast<const f32x4*>(fac1 + o);
@@ -100,9 +111,17 @@ struct PolBF16 {
                                                           int row, int p, int q,
                                                           const float* const (&fac)[3],
                                                           Frag& h, Frag& l) {
-    const int o = 32 * p + 4 * q;
-    const E* bh = thi + row * ld + o;
-    const E* bl = tlo + row * ld + o;
+    load_pair_scaled_at<NF>(thi, tlo, ld, row, p, p, q, fac, h, l);
+  }
+  template <int NF>
+  __device__ static __forceinline__ void load_pair_scaled_at(const E* thi, const E* tlo, int ld,
+                                                             int row, int p, int pf, int q,
+                                                             const float* const (&fac)[3],
+                                                             Frag& h, Frag& l) {
+    const int ot = 32 * p + 4 * q;
+    const int o = 32 * pf + 4 * q;
+    const E* bh = thi + row * ld + ot;
+    const E* bl = tlo + row * ld + ot;
     const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(bh);
     const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(bh + 16);
     const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(bl);
