@@ -891,6 +891,7 @@ int kda_decode_replay(int n_requests, int num_heads, int d_k, int d_v, int conv_
   p.decay_floor = expf(g_min);
   p.eps_l2 = eps_l2;
   p.eps_rms = eps_rms;
+  p.waves = kda::decode_waves(int64_t(n_requests) * num_heads, compute_units());
   return launch_status(kda::launch_decode_replay(p, static_cast<hipStream_t>(stream)));
 }
 

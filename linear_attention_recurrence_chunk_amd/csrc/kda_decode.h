@@ -28,8 +28,14 @@ struct DecodeParams {
   float* conv_tail;         // [R, H, 3D, W - 1]
   void* o;                  // [R, n_new, H, D] bf16 or fp32 (n_new: the most per request)
   int out_f32;
+  int waves;                // waves per workgroup: 4 or 8
   float scale, decay_floor, eps_l2, eps_rms;
 };
+
+// Waves per decode workgroup (one workgroup per request and head): 4 while the workgroups
+// fill the device (three per CU), 8 when at most half the compute units get one, so that a
+// head's per-token work spreads over two waves per SIMD (same results either way).
+inline int decode_waves(long long units, int cus) { return units * 2 <= cus ? 8 : 4; }
 
 hipError_t launch_decode_replay(const DecodeParams& p, hipStream_t stream);
 

@@ -9,11 +9,14 @@
 // writes straight into the destination buffer; section 5: tiles own disjoint value columns
 // and walk the same tokens in order.)
 //
-// Work decomposition: one workgroup (4 waves) per (request, head). The head's fp32 state
-// (d_k x d_v) is read from HBM once, lives in registers for every token (wave w owns value
-// columns [D/4 w, D/4 (w + 1)); lane (row group rg = lane / 8, column group cg = lane % 8)
-// holds rows D/8 rg .. + D/8 - 1 of its D/32 columns), and is written back twice: after the
-// replayed drafts (state_acc) and after the bonus token (state, in place).
+// Work decomposition: one workgroup of NW waves per (request, head): 4 for large batches
+// (three workgroups per CU), 8 when the batch leaves most CUs idle, so that the head's
+// per-token work spreads over two waves per SIMD. The head's fp32 state (d_k x d_v) is read
+// from HBM once, lives in registers for every token (wave w owns value columns
+// [D/NW w, D/NW (w + 1)); lane (row group rg = lane / 8, column group cg = lane % 8) holds
+// rows D/8 rg .. + D/8 - 1 of its D/(8 NW) columns), and is written back twice: after the
+// replayed drafts (state_acc) and after the bonus token (state, in place). A lane's rows and
+// the order of every sum do not depend on NW, so all widths give the same bits.
 //
 // Tokens go in blocks of eight. The whole block's projected inputs are loaded one block
 // ahead; the block's input stage (causal convolution, SiLU, decay and output gates, L2 norms
@@ -38,20 +41,54 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
-template <int D, int W, typename Tout>
-__global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
+// A wave-uniform value held in scalar registers and opaque to the optimiser, so that a
+// per-lane choice between two launch parameters stays a register select instead of becoming
+// a per-lane load from the parameter block (which costs a memory round trip before the
+// address it feeds is known).
+template <typename T>
+__device__ __forceinline__ T in_sgpr(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+// (pointers keep the global address space, so that their loads stay global loads)
+#define KDA_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ const KDA_GLOBAL __bf16* in_sgpr_global(const __bf16* x) {
+  auto g = (const KDA_GLOBAL __bf16*)x;
+  asm volatile("" : "+s"(g));
+  return g;
+}
+
+// Workgroup barrier over LDS only. Global loads and stores stay in flight across it (a full
+// barrier's fence would wait for the state's loads before the input stage's results could be
+// shared, and for the state's stores before the output norm): no thread of a workgroup reads
+// global memory that another thread of it writes (each lane reads and writes only its own
+// state elements, convolution tails and outputs).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, int W, typename Tout, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void decode_replay_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dimension");
   static_assert(W >= 1 && W <= 4, "convolution width");
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(D % (8 * NW) == 0, "at least one value column per lane");
+  constexpr int NT = 64 * NW;         // threads
   constexpr int NB = 8;               // tokens per block
   constexpr int RPL = D / 8;          // rows of S per lane
-  constexpr int CPW = D / 4;          // value columns per wave
+  constexpr int CPW = D / NW;         // value columns per wave
   constexpr int CPL = CPW / 8;        // value columns per lane
   constexpr int C3 = 3 * D;           // convolved channels q, k, v
   constexpr int CPG = D / 32;         // channels per thread in the 32-thread token groups
+  // small batches (latency-bound) fetch the first block's new-window rows before the accepted
+  // count arrives, and keep them when it is 0; large batches (HBM-bound) never spend the loads
+  constexpr bool kSpeculate = NW > 4;
 
   const int rh = blockIdx.x;
-  const int r = rh / p.H;
-  const int h = rh % p.H;
+  const int r = __builtin_amdgcn_readfirstlane(rh / p.H);   // (scalar: uniform loads)
+  const int h = __builtin_amdgcn_readfirstlane(rh % p.H);
   const int H = p.H;
   int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -71,19 +108,13 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 s_raw[NB][kRows][D];
   __shared__ float s_rbeta[NB];
   __shared__ float s_nrm[NB][3];        // 1/|q|, 1/|k|, (q . k) of the normalised vectors
-  __shared__ float s_osq[NB][4];        // per wave: sum of o^2 over its columns
 
   // Loads are issued in the order their data is needed: the request's accepted count, the
   // convolution tails and taps, the first block of inputs, then the state (first read by
   // the recurrence, after the block's input stage).
   int n_acc = p.n_acc[r];
-  n_acc = n_acc < 0 ? 0 : (n_acc > p.prev_slots - 1 ? p.prev_slots - 1 : n_acc);
   int n_new = p.n_new;
-  if (p.n_new_r) {
-    n_new = p.n_new_r[r];
-    n_new = n_new < 1 ? 1 : (n_new > p.n_new ? p.n_new : n_new);
-  }
-  const int n_tok = n_acc + n_new;
+  if (p.n_new_r) n_new = __builtin_amdgcn_readfirstlane(p.n_new_r[r]);
 
   // ---- input-stage role (whole waves): threads [0, D) own q and k channel tid; [D, 2D) own
   // v, g and z channel tid - D. Each keeps the causal-convolution tail of its channels in
@@ -114,78 +145,124 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
 
   // ---- projected inputs of one block: replay slots 1..n_acc of the previous window, then
   // slots 0..n_new-1 of the current one. They are fetched one block ahead in 16-byte pieces
-  // (thread tid takes pieces tid, tid + 256, ...) into registers and written to s_raw once
-  // the block before has been replayed.
+  // (thread tid takes pieces tid, tid + NT, ...) into registers and written to s_raw once
+  // the block before has been replayed. Piece c is part c % kPPR of row kind
+  // f = c / (NB kPPR) of token (c / kPPR) % NB: the kind, and with it the base pointer, is
+  // the same across a wave, and every lane loads (rows past the end read a present row), so
+  // the loads of a block go out back to back with no wait between them.
   constexpr int kPPR = D * 2 / 16;                  // 16-byte pieces per row
-  constexpr int kPieces = NB * kRows * kPPR;        // per block
-  constexpr int kPPT = (kPieces + 255) / 256;       // per thread
+  constexpr int kPPF = NB * kPPR;                   // pieces per row kind
+  constexpr int kPieces = kRows * kPPF;             // per block
+  constexpr int kPPT = (kPieces + NT - 1) / NT;     // per thread
+  static_assert(kPPF % 64 == 0 && kPieces % 64 == 0, "whole waves per row kind");
   bf16x8 praw[kPPT];
-  float pbeta = 0.f;
+  __bf16 pbeta = __bf16(0.f);   // raw bits, converted when staged
+  int n_tok = 0;
+  const int prev_slots = in_sgpr(p.prev_slots), cur_slots = in_sgpr(p.cur_slots);
   auto token_row = [&](int t) -> size_t {
     const bool replay = t < n_acc;
     const int slot = replay ? t + 1 : t - n_acc;
-    const int slots = replay ? p.prev_slots : p.cur_slots;
+    const int slots = replay ? prev_slots : cur_slots;
     return (size_t(r) * slots + slot) * H + h;
+  };
+  using GB = const KDA_GLOBAL __bf16;
+  using GB8 = const KDA_GLOBAL bf16x8;
+  auto row_base = [&](int f, bool replay) -> GB* {
+    switch (f) {
+      case 0: return replay ? in_sgpr_global(p.prev_q) : in_sgpr_global(p.cur_q);
+      case 1: return replay ? in_sgpr_global(p.prev_k) : in_sgpr_global(p.cur_k);
+      case 2: return replay ? in_sgpr_global(p.prev_v) : in_sgpr_global(p.cur_v);
+      case 3: return replay ? in_sgpr_global(p.prev_g) : in_sgpr_global(p.cur_g);
+      default: return in_sgpr_global(p.cur_z);
+    }
   };
   auto fetch_block = [&](int tb) {
 #pragma unroll
     for (int m = 0; m < kPPT; ++m) {
-      const int c = tid + 256 * m;
-      if (c >= kPieces) break;
-      const int i = c / (kRows * kPPR), f = (c / kPPR) % kRows, part = c % kPPR;
+      const int c = tid + NT * m;
+      if (NT * (m + 1) > kPieces && c >= kPieces) break;   // whole waves
+      const int f = __builtin_amdgcn_readfirstlane(c / kPPF);
+      const int i = (c / kPPR) % NB, part = c % kPPR;
       const int t = tb + i;
       const bool replay = t < n_acc;
       // rows past the end, and z of replayed tokens (never used), read a present row
       const bool use = t < n_tok && !(f == 4 && replay);
-      const __bf16* base;
-      switch (f) {
-        case 0: base = replay ? p.prev_q : p.cur_q; break;
-        case 1: base = replay ? p.prev_k : p.cur_k; break;
-        case 2: base = replay ? p.prev_v : p.cur_v; break;
-        case 3: base = replay ? p.prev_g : p.cur_g; break;
-        default: base = p.cur_z; break;
-      }
+      GB* base = use ? row_base(f, replay) : in_sgpr_global(p.cur_q);
       const size_t row = use ? token_row(t) : size_t(0);
-      if (!use) base = p.cur_q;
-      praw[m] = *reinterpret_cast<const bf16x8*>(base + row * D + 8 * part);
+      praw[m] = *reinterpret_cast<GB8*>(base + row * D + 8 * part);
     }
-    if (tid < NB && tb + tid < n_tok) {
-      const int t = tb + tid;
-      pbeta = (float)(t < n_acc ? p.prev_beta : p.cur_beta)[token_row(t)];
+    if (w == 0) {   // lanes below NB carry the block's betas
+      const int t = tb + (lane < NB ? lane : 0);
+      const bool use = lane < NB && t < n_tok;
+      GB* bb = use && t < n_acc ? in_sgpr_global(p.prev_beta) : in_sgpr_global(p.cur_beta);
+      pbeta = bb[use ? token_row(t) : size_t(0)];
     }
   };
   auto stage_block = [&]() {
 #pragma unroll
     for (int m = 0; m < kPPT; ++m) {
-      const int c = tid + 256 * m;
-      if (c >= kPieces) break;
-      const int i = c / (kRows * kPPR), f = (c / kPPR) % kRows, part = c % kPPR;
+      const int c = tid + NT * m;
+      if (NT * (m + 1) > kPieces && c >= kPieces) break;
+      const int f = c / kPPF, i = (c / kPPR) % NB, part = c % kPPR;
       *reinterpret_cast<bf16x8*>(&s_raw[i][f][8 * part]) = praw[m];
     }
-    if (tid < NB) s_rbeta[tid] = pbeta;
+    if (tid < NB) s_rbeta[tid] = (float)pbeta;
   };
-  fetch_block(0);
-
+  // the first block of the new window alone (token t = slot t), in bounds whatever the
+  // accepted count: slots below n_new exist for every request
+  auto fetch_first_new = [&]() {
+#pragma unroll
+    for (int m = 0; m < kPPT; ++m) {
+      const int c = tid + NT * m;
+      if (NT * (m + 1) > kPieces && c >= kPieces) break;
+      const int f = __builtin_amdgcn_readfirstlane(c / kPPF);
+      const int i = (c / kPPR) % NB, part = c % kPPR;
+      const size_t row = i < p.n_new ? (size_t(r) * cur_slots + i) * H + h : size_t(0);
+      praw[m] = *reinterpret_cast<GB8*>(row_base(f, false) + row * D + 8 * part);
+    }
+    if (w == 0) {
+      const int i = lane < NB && lane < p.n_new ? lane : 0;
+      pbeta = p.cur_beta[(size_t(r) * cur_slots + i) * H + h];
+    }
+  };
   // ---- state tile into registers
   const size_t sbase = (size_t(r) * H + h) * D * D;
   float S[RPL][CPL];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const float* src = p.state + sbase + size_t(row0 + i) * D + col0;
-    if constexpr (CPL == 4) {
-      // read once: a streaming (non-temporal) load
-      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+    for (int i = 0; i < RPL; ++i) {
+      const float* src = p.state + sbase + size_t(row0 + i) * D + col0;
+      if constexpr (CPL == 4) {
+        // read once: a streaming (non-temporal) load
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[i][j] = x[j];
-    } else {
+        for (int j = 0; j < 4; ++j) S[i][j] = x[j];
+      } else if constexpr (CPL == 2) {
+        const f32x2 x = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(src));
+        S[i][0] = x[0];
+        S[i][1] = x[1];
+      } else {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) S[i][j] = src[j];
+        for (int j = 0; j < CPL; ++j) S[i][j] = src[j];
+      }
     }
+  };
+  // (small batches: the state's loads go out before the accepted count is waited for)
+  if constexpr (kSpeculate) {
+    fetch_first_new();
+    load_state();
   }
+  n_acc = n_acc < 0 ? 0 : (n_acc > p.prev_slots - 1 ? p.prev_slots - 1 : n_acc);
+  if (p.n_new_r) n_new = n_new < 1 ? 1 : (n_new > p.n_new ? p.n_new : n_new);
+  n_tok = n_acc + n_new;
+  if (!kSpeculate || n_acc > 0) fetch_block(0);
+  if constexpr (!kSpeculate) load_state();
+
+
 
 
   stage_block();
-  __syncthreads();
+  lds_barrier();
 
   for (int tb = 0; tb < n_tok; tb += NB) {
     const int nb = min(NB, n_tok - tb);
@@ -250,7 +327,7 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
       }
     }
     if (tid < nb) s_beta[tid] = sigmoidf_(s_rbeta[tid]);
-    __syncthreads();
+    lds_barrier();
 
     // the next block's inputs load while this block is replayed
     const bool more = tb + NB < n_tok;
@@ -281,13 +358,13 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
         s_nrm[i][2] = sqk * iq * ik;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // per-row factors of the recurrence, once per token and channel
 #pragma unroll
-    for (int m = 0; m < NB * D / 256; ++m) {
-      const int idx = tid + 256 * m;
+    for (int m = 0; m < (NB * D + NT - 1) / NT; ++m) {
+      const int idx = tid + NT * m;
       const int i = idx / D, c = idx % D;
-      if (i < nb) {
+      if (idx < NB * D && i < nb) {
         const float a = s_a[i][c];
         const float kn = s_k[i][c] * s_nrm[i][1];
         s_k[i][c] = a * kn;
@@ -295,7 +372,7 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
         s_bk[i][c] = s_beta[i] * kn;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     if (tb == 0 && n_acc == 0 && p.state_acc) {
       // no accepted drafts: the accepted state is the committed entering state
@@ -305,6 +382,8 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
         if constexpr (CPL == 4) {
           __builtin_nontemporal_store(f32x4{S[ii][0], S[ii][1], S[ii][2], S[ii][3]},
                                       reinterpret_cast<f32x4*>(dst));
+        } else if constexpr (CPL == 2) {
+          __builtin_nontemporal_store(f32x2{S[ii][0], S[ii][1]}, reinterpret_cast<f32x2*>(dst));
         } else {
 #pragma unroll
           for (int j = 0; j < CPL; ++j) dst[j] = S[ii][j];
@@ -375,17 +454,10 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
 #pragma unroll
           for (int j = 0; j < CPL; ++j)
             S[4 * m + u][j] = fmaf(fb[m][u], e[j], fa[m][u] * S[4 * m + u][j]);
-      if (output) {
-        float osq = 0.f;
+      if (output && rg == 0) {
+        // each column is held by 8 lanes; row group 0 writes it
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const float ov = p.scale * fmaf(beta * qk, e[j], qs[j]);
-          if (rg == 0) s_o[i][col0 + j] = ov;
-          osq += ov * ov;
-        }
-        // each column is held by 8 lanes; count it once (row group 0)
-        osq = sum_mirror8(sum_xor2(sum_xor1(osq)));   // over the 8 lanes of row group 0
-        if (lane == 0) s_osq[i][w] = osq;
+        for (int j = 0; j < CPL; ++j) s_o[i][col0 + j] = p.scale * fmaf(beta * qk, e[j], qs[j]);
       }
       float* dst_state = nullptr;
       if (t == n_acc - 1) dst_state = p.state_acc;   // after the accepted drafts
@@ -398,6 +470,8 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
             // written once, read by a later launch: streaming (non-temporal) stores
             __builtin_nontemporal_store(f32x4{S[ii][0], S[ii][1], S[ii][2], S[ii][3]},
                                         reinterpret_cast<f32x4*>(dst));
+          } else if constexpr (CPL == 2) {
+            __builtin_nontemporal_store(f32x2{S[ii][0], S[ii][1]}, reinterpret_cast<f32x2*>(dst));
           } else {
 #pragma unroll
             for (int j = 0; j < CPL; ++j) dst[j] = S[ii][j];
@@ -406,22 +480,31 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
       }
     }
     if (more) stage_block();   // s_raw of this block was last read before the first barrier
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- gated RMS normalisation of the block's outputs ----------------------
-    {
+    // 32 threads per token, CPG consecutive channels each; the sum of squares in a fixed
+    // order (the thread's channels, then the same butterfly as the input norms)
+    if (tid < 32 * NB) {
       const int i = tid >> 5, l = tid & 31;
       const int t = tb + i;
-      if (i < nb && t >= n_acc) {
-        const float tot = s_osq[i][0] + s_osq[i][1] + s_osq[i][2] + s_osq[i][3];
-        const float rinv = 1.f / sqrtf(tot / float(D) + p.eps_rms);
+      const bool live = i < nb && t >= n_acc;
+      const int c0 = CPG * l;
+      float ov[CPG];
+      float osq = 0.f;
+#pragma unroll
+      for (int m = 0; m < CPG; ++m) {
+        ov[m] = live ? s_o[i][c0 + m] : 0.f;
+        osq = fmaf(ov[m], ov[m], osq);
+      }
+      osq = sum_xor16(sum_xor8(sum_mirror8(sum_xor2(sum_xor1(osq)))));
+      if (live) {
+        const float rinv = 1.f / sqrtf(osq / float(D) + p.eps_rms);
         Tout* dst = reinterpret_cast<Tout*>(p.o) + ((size_t(r) * p.n_new + (t - n_acc)) * H + h) * D;
-        // CPG consecutive channels per thread, one vector store
-        const int c0 = CPG * l;
-        float ov[CPG];
+        // one vector store per thread
 #pragma unroll
         for (int m = 0; m < CPG; ++m)
-          ov[m] = s_o[i][c0 + m] * rinv * p.norm_w[c0 + m] * s_z[i][c0 + m];
+          ov[m] = ov[m] * rinv * p.norm_w[c0 + m] * s_z[i][c0 + m];
         if constexpr (CPG == 4 && sizeof(Tout) == 2)
           *reinterpret_cast<bf16x4*>(dst + c0) =
               bf16x4{(__bf16)ov[0], (__bf16)ov[1], (__bf16)ov[2], (__bf16)ov[3]};
@@ -433,19 +516,28 @@ __global__ __launch_bounds__(256, 3) void decode_replay_kernel(DecodeParams p) {
           *reinterpret_cast<f32x2*>(dst + c0) = f32x2{ov[0], ov[1]};
       }
     }
-    if (more) __syncthreads();   // the next block rewrites the shared vectors
+    if (more) lds_barrier();   // the next block rewrites the shared vectors
   }
+}
+
+template <int D, int W, int NW>
+static hipError_t launch_decode_nw(const DecodeParams& p, hipStream_t stream) {
+  if (p.out_f32)
+    hipLaunchKernelGGL((decode_replay_kernel<D, W, float, NW>), dim3(p.R * p.H), dim3(64 * NW),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_replay_kernel<D, W, __bf16, NW>), dim3(p.R * p.H), dim3(64 * NW),
+                       0, stream, p);
+  return hipGetLastError();
 }
 
 template <int D, int W>
 static hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (p.out_f32)
-    hipLaunchKernelGGL((decode_replay_kernel<D, W, float>), dim3(p.R * p.H), dim3(256), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((decode_replay_kernel<D, W, __bf16>), dim3(p.R * p.H), dim3(256), 0,
-                       stream, p);
-  return hipGetLastError();
+  switch (p.waves) {
+    case 4: return launch_decode_nw<D, W, 4>(p, stream);
+    case 8: return launch_decode_nw<D, W, 8>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int D>

@@ -1,5 +1,7 @@
 """Parity of kda_decode_replay (HIP, through the C ABI) with the fp64 CPU oracle, and
 bit-identity of replayed states with one-token-at-a-time launches."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -89,6 +91,30 @@ def test_replay_bit_identical_to_single_token_launches(a):
     assert torch.equal(s_a, state)
     assert torch.equal(tail_a, tail)
     assert torch.equal(o_a[:, 0], o_b[:, 0])
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_small_batch_waves_bit_identical(D):
+    """A launch gives each (request, head) workgroup 8 waves when the pairs would leave most
+    compute units idle, and 4 otherwise. Every lane keeps the same key rows and every sum the
+    same order, so requests run inside a large batch (4 waves) and alone in a small one
+    (8 waves, first block fetched before the accepted count is known) agree bit for bit,
+    with accepted counts 0 and above among them."""
+    R, H = 64, 12
+    print(f"case decode widths D={D}: {R}x{H} against 3x{H}", flush=True)
+    w = wl.decode_inputs(R=R, H=H, dk=D, dv=D, conv_width=4, n_new=4, window=8, seed=77 + D)
+    w.n_acc[0] = 0
+    w.n_acc[5] = 6
+    pick = [0, 5, 63]
+    big = _run_gpu(w)                                   # 768 pairs: 4 waves
+    sel = lambda x: None if x is None else x[pick].clone()
+    sub = dataclasses.replace(w, R=len(pick), n_acc=w.n_acc[pick].clone(),
+                              prev={k: sel(v) for k, v in w.prev.items()},
+                              new={k: sel(v) for k, v in w.new.items()},
+                              state=w.state[pick].clone(), conv_tail=w.conv_tail[pick].clone())
+    small = _run_gpu(sub)                               # 36 pairs: 8 waves
+    for name, x, y in zip(("o", "state", "state_acc", "tail"), big, small):
+        assert torch.equal(x[pick], y), name
 
 
 def test_speculative_stream_matches_oracle():
