@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_tile_kernel(BwdParams p) {
   auto col_reduce = [&](float x) -> float {
     x = sum_xor32(sum_xor16(x));
     if (lane < 16) sRed[par][w][lane] = x;
-    __syncthreads();
+    lds_barrier();
     const float s = ((sRed[par][0][c] + sRed[par][1][c]) + sRed[par][2][c]) + sRed[par][3][c];
     par ^= 1;
     return s;

@@ -784,7 +784,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
     if (grp == 0) *reinterpret_cast<f32x4*>(sBP + w * DK + c0) = f32x4{bp[0], bp[1], bp[2], bp[3]};
     if (lane < 16) sBeta[16 * w + lane] = beta_r;
-    __syncthreads();
+    lds_barrier();
 
     // ---- chunk-level factors from the four sub-block products of each channel (read-only
     //      here; the whole-chunk decay is first read after two more barriers)
@@ -819,7 +819,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       default: am_rows<Pol, L, DK, 3, kOut>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, sBeta, sA, sM, sMLo, sT, sTLo, ln, q4); break;
     }
     KDA_PREFETCH(kLoadG, 0, 4);
-    __syncthreads();
+    lds_barrier();
 
     // ================= prologue 3: recurrence operand tiles; off-diagonal inverse ===========
     {
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
       mm_reg_split(Ya, Yb, tblk(lo + 1, lo + 1), Xa + Xb);
       put(lo + 1, lo, Ya + Yb);
     }
-    __syncthreads();
+    lds_barrier();
     KDA_PREFETCH(kLoadK, 0, 4);
     if constexpr (kOut) KDA_PREFETCH(kLoadQ, 0, 4);
     {
@@ -934,7 +934,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     }
     KDA_PREFETCH(kLoadK, 4, 8);
     if constexpr (kOut) KDA_PREFETCH(kLoadQ, 4, 8);
-    __syncthreads();
+    lds_barrier();
 
 
     if constexpr (kPrep) {
@@ -1095,7 +1095,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     if constexpr (!kPrep)
       if (mode == kModeForward)
         write_checkpoint<DK, NTD>(p, S, seq_bos, cstart + Lc, Lc, h, col0, q4, ln);
-    __syncthreads();
+    lds_barrier();
 #undef KDA_PREFETCH
   }
 
@@ -1477,7 +1477,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) sBP[w * DK + c0 + c] = bp[c];
       }
-      __syncthreads();
+      lds_barrier();
       // ---- this pass's recurrence operands, straight to the slot: Q e^Gamma and K e^Gamma
       //      (token rows, fragment (w, channel / 32)) and (K e^{Gamma_L - Gamma})^T (channel
       //      rows, fragment (channel / 16, token / 32)), fp16
@@ -1537,7 +1537,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
         case 2: prep_am_pass<DK, 2>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
         default: prep_am_pass<DK, 3>(sKr, sKd, sKdLo, sKc, sQr, sQrLo, sBP, hp, accA, accM, accM30, ln, q4); break;
       }
-      __syncthreads();   // the tiles are rewritten by the next pass (or the next chunk)
+      lds_barrier();   // the tiles are rewritten by the next pass (or the next chunk)
     }
     // ---- A's row blocks, M to the slot, diagonal blocks of T
     switch (w) {
@@ -1546,7 +1546,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
       case 2: prep_am_finish<DK, 2>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
       default: prep_am_finish<DK, 3>(accA, accM, accM30, sBeta, sA, slot, ln, q4); break;
     }
-    __syncthreads();
+    lds_barrier();
     // ---- off-diagonal blocks of T, as in chunk_fwd_kernel (level 1 on waves 1 and 3, then
     //      one level-2 block per wave); T_ij (i > j) in the free upper position (j, i)
     auto tblk = [&](int bi, int bj) -> float* {
@@ -1594,7 +1594,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
       mm_reg_split(Ya, Yb, tblk(lo + 1, lo + 1), Xa + Xb);
       put(lo + 1, lo, Ya + Yb);
     }
-    __syncthreads();
+    lds_barrier();
     {
       const int bj = w & 1;
       const bool row3 = w >= 2;
@@ -1611,7 +1611,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
       else mm_reg2(Ya, tblk(3, 2), X2a + X2b, Yb, tblk(3, 3), X3a + X3b);
       put(row3 ? 3 : 2, bj, Ya + Yb);
     }
-    __syncthreads();
+    lds_barrier();
     // ---- T diag(beta) (bf16 hi and lo) of the 6 lower fragments, from the fp32 matrix: lane
     //      (q4, ln) holds row 16 rb + ln, columns 32 pp + 16 hh + 4 q4 + e; and the decay
     for (int i = w; i < 6; i += 4) {

@@ -254,6 +254,17 @@ __device__ __forceinline__ float quad_bcast(float v) {
   return quad_perm<kSrc * 0x55>(v);   // [kSrc, kSrc, kSrc, kSrc]
 }
 
+// Workgroup barrier that orders LDS only: global loads and stores stay in flight across it
+// (a full barrier's fence waits for every outstanding global access, stores included). For
+// kernels whose threads never read global memory that another thread of the workgroup
+// wrote during the launch; data staged by global-to-LDS loads is waited for by each wave
+// (vmcnt) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sums across lanes without LDS traffic (DPP and the gfx950 row-swap instructions). Each
 // returns x + x' where x' is the value of the partner lane named; both partners get the same
 // bits (fp32 addition commutes).

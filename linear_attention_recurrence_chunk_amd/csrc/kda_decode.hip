@@ -58,17 +58,6 @@ __device__ __forceinline__ const KDA_GLOBAL __bf16* in_sgpr_global(const __bf16*
   return g;
 }
 
-// Workgroup barrier over LDS only. Global loads and stores stay in flight across it (a full
-// barrier's fence would wait for the state's loads before the input stage's results could be
-// shared, and for the state's stores before the output norm): no thread of a workgroup reads
-// global memory that another thread of it writes (each lane reads and writes only its own
-// state elements, convolution tails and outputs).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <int D, int W, typename Tout, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void decode_replay_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head dimension");

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // S <- P_j S + Q_j
     if constexpr (kF32) {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (p.ht) {
     float* ht = p.ht + size_t(nh) * DK * DV;

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     values_to_x0(min(kChunk, eos - bos));
   }
-  __syncthreads();
+  lds_barrier();
 
   // outputs of a chunk, transposed (lane: token 16 rb + tq, four consecutive columns)
   const uint32_t lo_el = uint32_t((tq * H + h) * DV + col0 + 4 * (ln >> 2));
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
       values_to_x0(min(kChunk, eos - cstart - kChunk));
     }
     if constexpr (kOut) store_out(O, cstart, Lc);
-    __syncthreads();
+    lds_barrier();
   }
 
   float* s_out = nullptr;
