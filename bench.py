@@ -495,6 +495,9 @@ def main():
                          "verify_tiny, decode_sweep, segment, varlen, raw, backward); the "
                          "prefill leg "
                          "always runs")
+    ap.add_argument("--segment-counts", default="0,64,256",
+                    help="segment counts the segment leg times (0: the library's automatic "
+                         "count, whose figure the leg reports; it must come first)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes --steps times (the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -619,8 +622,11 @@ def main():
         line["decode_sweep"] = bench_decode_sweep(kda, wl, torch, dev, stream,
                                                   max(3, args.steps // 4), min(args.warmup, 2))
     if "segment" in legs:
+        counts = tuple(int(x) for x in args.segment_counts.split(","))
+        if not counts or counts[0] != 0:
+            raise SystemExit("--segment-counts must start with 0 (the automatic count)")
         line["segment_cp"] = bench_segment(kda, wl, torch, dev, stream,
-                                           max(3, args.steps // 4), min(args.warmup, 2))
+                                           max(3, args.steps // 4), min(args.warmup, 2), counts)
     if "raw" in legs:
         line["raw_prefill"] = bench_raw(kda, wl, torch, dev, stream, args.steps, args.warmup)
     if "backward" in legs:
