@@ -98,7 +98,7 @@ __device__ __forceinline__ bool rows_writer(int lane) {
 }
 
 template <typename Tio, int DK>
-__global__ __launch_bounds__(256) void chunk_bwd_tile_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void chunk_bwd_tile_kernel(BwdParams p) {
   constexpr int RPT = DK / 16;   // key rows per thread
   constexpr int DV = DK;
   constexpr int SUB = kBwdSub;
@@ -145,33 +145,50 @@ __global__ __launch_bounds__(256) void chunk_bwd_tile_kernel(BwdParams p) {
     return s;
   };
 
-  // one token's inputs for this thread
-  struct Tok {
-    float a[RPT], k[RPT], beta;
-    bool live[RPT];
+  // one token's inputs for this thread, as loaded: every loop below loads the next token's
+  // while the current one is computed, so a step does not wait for memory
+  struct In {
+    float g[RPT], k[RPT], beta, v;
   };
-  auto load_tok = [&](int t, Tok& x) {
+  auto load_in = [&](int t, In& x) {
     const size_t row = (size_t(t) * H + h) * DK + r0;
-    float gv4[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; i += 4) {
       const f32x4 a4 = *reinterpret_cast<const f32x4*>(p.g + row + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gv4[i + e] = a4[e];
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      x.live[i] = gv4[i] > gmin;
-      x.a[i] = __expf(fmaxf(gv4[i], gmin));
+      for (int e = 0; e < 4; ++e) x.g[i + e] = a4[e];
     }
     load_rows<Tio, RPT>(gk + row, x.k);
     x.beta = p.beta[size_t(t) * H + h];
+    x.v = to_f32(gv[(size_t(t) * H + h) * DV + col]);
   };
-  // S <- S' + beta k e^T for token t; returns e (this thread's column)
-  auto fwd_step = [&](int t, const float (&Sin)[RPT], float (&Sout)[RPT]) -> float {
+  // the reverse step's extra inputs: q rows and the output gradient of the column
+  struct InB {
+    float q[RPT], d_o;
+  };
+  auto load_inb = [&](int t, InB& x) {
+    load_rows<Tio, RPT>(gq + (size_t(t) * H + h) * DK + r0, x.q);
+    x.d_o = to_f32(gdo[(size_t(t) * H + h) * DV + col]);
+  };
+  // one token's decays and keys
+  struct Tok {
+    float a[RPT], k[RPT], beta;
+    bool live[RPT];
+  };
+  auto decode = [&](const In& in, Tok& x) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      x.live[i] = in.g[i] > gmin;
+      x.a[i] = __expf(fmaxf(in.g[i], gmin));
+      x.k[i] = in.k[i];
+    }
+    x.beta = in.beta;
+  };
+  // S <- S' + beta k e^T for one token; returns e (this thread's column)
+  auto fwd_step = [&](const In& in, const float (&Sin)[RPT], float (&Sout)[RPT]) -> float {
     Tok x;
-    load_tok(t, x);
-    const float vc = to_f32(gv[(size_t(t) * H + h) * DV + col]);
+    decode(in, x);
+    const float vc = in.v;
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -193,16 +210,21 @@ __global__ __launch_bounds__(256) void chunk_bwd_tile_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) S[i] = p.h0 ? p.h0[state_off + size_t(r0 + i) * DV + col] : 0.f;
   const int nsub = (len + SUB - 1) / SUB;
+  In cur;
+  if (len > 0) load_in(bos, cur);
   for (int j = 0; j < nsub; ++j) {
     float* cp = ckpt_ptr(j);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) cp[size_t(i) * DV] = S[i];
     const int t0 = bos + SUB * j, t1 = min(eos, t0 + SUB);
     for (int t = t0; t < t1; ++t) {
+      In nxt;
+      if (t + 1 < eos) load_in(t + 1, nxt);
       float Sn[RPT];
-      fwd_step(t, S, Sn);
+      fwd_step(cur, S, Sn);
 #pragma unroll
       for (int i = 0; i < RPT; ++i) S[i] = Sn[i];
+      cur = nxt;
     }
   }
 
@@ -224,19 +246,37 @@ __global__ __launch_bounds__(256) void chunk_bwd_tile_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) Ss[0][i] = cp[size_t(i) * DV];
     }
-    static_for<0, SUB>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      if (i < L) es[i] = fwd_step(t0 + i, Ss[i], Ss[i + 1]);
-    });
+    {
+      In in;
+      load_in(t0, in);
+      static_for<0, SUB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (i < L) {
+          In nxt;
+          if (i + 1 < L) load_in(t0 + i + 1, nxt);
+          es[i] = fwd_step(in, Ss[i], Ss[i + 1]);
+          in = nxt;
+        }
+      });
+    }
+    In inr;
+    InB inb;
+    load_in(t0 + L - 1, inr);
+    load_inb(t0 + L - 1, inb);
     static_for<0, SUB>([&](auto ic) {
       constexpr int i = SUB - 1 - decltype(ic)::value;
       if (i >= L) return;
       const int t = t0 + i;
       Tok x;
-      load_tok(t, x);
+      decode(inr, x);
       float qv[RPT];
-      load_rows<Tio, RPT>(gq + (size_t(t) * H + h) * DK + r0, qv);
-      const float doc = to_f32(gdo[(size_t(t) * H + h) * DV + col]);
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) qv[r] = inb.q[r];
+      const float doc = inb.d_o;
+      if (i > 0) {
+        load_in(t - 1, inr);
+        load_inb(t - 1, inb);
+      }
       const float e = es[i];
       float rq[RPT], rk[RPT], ra[RPT];
       float pde = 0.f, pb = 0.f;
