@@ -55,8 +55,24 @@ def build(verbose=False, extra=()):
             f.result()
     objs = [obj for _, obj in jobs]
     _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", LIB + ".tmp"], verbose)
+    _check_defined(LIB + ".tmp")
     os.replace(LIB + ".tmp", LIB)
     return LIB
+
+
+def _check_defined(lib):
+    """Refuse a library that leaves any of its own symbols undefined: a source whose host
+    pass failed to emit its kernels' launch stubs still compiles to an object (hipcc exits
+    0), and a shared library links with the holes."""
+    res = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{res.stderr}")
+    missing = [l.split()[-1] for l in res.stdout.splitlines()
+               if "kda" in l or "device_stub" in l]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("libkda.so would leave its own symbols undefined: " +
+                           ", ".join(missing[:8]))
 
 
 if __name__ == "__main__":
