@@ -196,7 +196,7 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  *   D = diag(a_t) D';  dh0 = D at the sequence start
  *
  * (e_t = v_t - S'_t^T k_t, S'_t = diag(a_t) S_{t-1}). The forward states are recomputed from
- * checkpoints every 16 tokens that the call writes to its workspace.
+ * checkpoints every 8 tokens that the call writes to its workspace.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs, num_heads,
  *   d_k, d_v, io_dtype, scale, g_min: as for kda_chunk_fwd (the forward's inputs)
@@ -223,7 +223,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   void* stream);
 
 /*
- * Workspace bytes of kda_chunk_bwd: (T_total / 16 + N + 1) x H x d_k x d_v x 4 for the state
+ * Workspace bytes of kda_chunk_bwd: (T_total / 8 + N + 1) x H x d_k x d_v x 4 for the state
  * checkpoints, plus 3 x (d_v / 16) x T_total x H x d_k x 4 and 4 x (d_v / 16) x T_total x H x 4
  * for the partial sums (each part rounded up to 256 bytes). Same batch / seq_len / n_seqs
  * conventions as kda_chunk_fwd_workspace_size.

@@ -34,7 +34,7 @@ struct BwdParams {
 };
 
 // tokens between the backward's state checkpoints (a sub-chunk, recomputed in registers)
-constexpr int kBwdSub = 16;
+constexpr int kBwdSub = 8;
 
 inline long long bwd_ckpt_slots(long long T, long long N) { return T / kBwdSub + N + 1; }
 

@@ -17,9 +17,9 @@
 // head): 4 waves x 64 lanes, lane = (row group, column), each thread DK / 16 consecutive key
 // rows of one column. Everything is fp32 vector arithmetic (no matrix cores: one token at a
 // time). Per workgroup:
-//   1. a forward pass over the sequence stores the state at every 16th token (the workspace's
+//   1. a forward pass over the sequence stores the state at every 8th token (the workspace's
 //      checkpoints; fp32, so the states match the per-token definition to rounding);
-//   2. the sub-chunks of 16 tokens are taken in reverse: the 17 states of one are recomputed
+//   2. the sub-chunks of 8 tokens are taken in reverse: the 9 states of one are recomputed
 //      from its checkpoint into registers, then its tokens are differentiated in reverse.
 // Sums over value columns (dq, dk, dg and dbeta) are partial per tile; a second kernel adds
 // the tiles in a fixed order, so results are deterministic. dv and dh0 are complete per tile.
@@ -98,7 +98,7 @@ __device__ __forceinline__ bool rows_writer(int lane) {
 }
 
 template <typename Tio, int DK>
-__global__ __launch_bounds__(256, 2) void chunk_bwd_tile_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 3) void chunk_bwd_tile_kernel(BwdParams p) {
   constexpr int RPT = DK / 16;   // key rows per thread
   constexpr int DV = DK;
   constexpr int SUB = kBwdSub;
@@ -259,24 +259,21 @@ __global__ __launch_bounds__(256, 2) void chunk_bwd_tile_kernel(BwdParams p) {
         }
       });
     }
-    In inr;
-    InB inb;
-    load_in(t0 + L - 1, inr);
-    load_inb(t0 + L - 1, inb);
     static_for<0, SUB>([&](auto ic) {
       constexpr int i = SUB - 1 - decltype(ic)::value;
       if (i >= L) return;
       const int t = t0 + i;
+      // (loaded at the step: the sub-chunk's states leave no registers for a look-ahead)
+      In inr;
+      InB inb;
+      load_in(t, inr);
+      load_inb(t, inb);
       Tok x;
       decode(inr, x);
       float qv[RPT];
 #pragma unroll
       for (int r = 0; r < RPT; ++r) qv[r] = inb.q[r];
       const float doc = inb.d_o;
-      if (i > 0) {
-        load_in(t - 1, inr);
-        load_inb(t - 1, inb);
-      }
       const float e = es[i];
       float rq[RPT], rk[RPT], ra[RPT];
       float pde = 0.f, pb = 0.f;
@@ -317,26 +314,31 @@ __global__ __launch_bounds__(256, 2) void chunk_bwd_tile_kernel(BwdParams p) {
   }
 }
 
-// dq, dk, dg (sums over the tiles) and dbeta; one thread per (token, head, key row)
+// dq, dk, dg (sums over the tiles, in tile order) and dbeta; one thread per (token, head) and
+// four consecutive key rows, 16-byte loads and stores
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_bwd_reduce_kernel(BwdParams p) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = p.T * p.H * DK;
-  if (idx >= total) return;
+  const long long idx4 = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total4 = p.T * p.H * DK / 4;
+  if (idx4 >= total4) return;
+  const long long idx = 4 * idx4;
   const long long th = idx / DK;   // t * H + h
   const size_t stride = size_t(p.n_ct) * p.T * p.H * DK;
   const size_t tile = size_t(p.T) * p.H * DK;
-  float sq = 0.f, sk = 0.f, sa = 0.f;
+  f32x4 sq = zero4(), sk = zero4(), sa = zero4();
   for (int ct = 0; ct < p.n_ct; ++ct) {
     const size_t o = size_t(ct) * tile + size_t(idx);
-    sq += p.part[o];
-    sk += p.part[stride + o];
-    sa += p.part[2 * stride + o];
+    sq += *reinterpret_cast<const f32x4*>(p.part + o);
+    sk += *reinterpret_cast<const f32x4*>(p.part + stride + o);
+    sa += *reinterpret_cast<const f32x4*>(p.part + 2 * stride + o);
   }
-  const float g = p.g[idx];
-  p.dq[idx] = sq;
-  p.dk[idx] = sk;
-  p.dg[idx] = g > p.g_min ? __expf(g) * sa : 0.f;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(p.g + idx);
+  f32x4 dg;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dg[e] = g[e] > p.g_min ? __expf(g[e]) * sa[e] : 0.f;
+  *reinterpret_cast<f32x4*>(p.dq + idx) = sq;
+  *reinterpret_cast<f32x4*>(p.dk + idx) = sk;
+  *reinterpret_cast<f32x4*>(p.dg + idx) = dg;
   if (idx % DK == 0) {
     float sb = 0.f;
     for (int i = 0; i < 4 * p.n_ct; ++i) sb += p.part_beta[size_t(i) * p.T * p.H + size_t(th)];
@@ -350,9 +352,9 @@ static hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_bwd_tile_kernel<Tio, DK>), grid, dim3(256), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long total = p.T * p.H * DK;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bwd_reduce_kernel<DK>), dim3(unsigned((total + 255) / 256)),
+  const long long total4 = p.T * p.H * DK / 4;
+  if (total4 == 0) return hipSuccess;
+  hipLaunchKernelGGL((chunk_bwd_reduce_kernel<DK>), dim3(unsigned((total4 + 255) / 256)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
