@@ -442,8 +442,9 @@ def bench_backward(kda, wl, torch, dev, stream, steps, warmup):
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
             "roofline": hbm_roofline(nbytes, avg),
             "algorithmic_bytes_per_call": nbytes,
-            "kernels": "chunk_bwd_tile_kernel (per-token fp32 reverse walk per 16-column tile) "
-                       "+ chunk_bwd_reduce_kernel"}
+            "kernels": "cbwd_fwd_kernel (forward walk: chunk-entering states) + cbwd_rev_kernel "
+                       "(reverse walk: leaving-state gradients, dv, dh0) + cbwd_grad_kernel "
+                       "(dq, dk, dbeta, dg per 16-token chunk)"}
 
 
 def bench_segment(kda, wl, torch, dev, stream, steps, warmup, counts=(0, 64, 256)):

@@ -186,17 +186,18 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
 /*
  * kda_chunk_bwd: gradients of kda_chunk_fwd's outputs (training; "Noyaux KDA et FlashKDA",
  * section "FlashKDA : le noyau par blocs": the kernel serves training as well as prefill). The
- * pages give no backward; this is reverse-mode differentiation of the per-token update above,
- * token by token in reverse order, in fp32:
+ * pages give no backward; this is reverse-mode differentiation of the per-token update above.
+ * Token by token, going back from D = dL/dS = dht at each sequence's end:
  *
- *   D = dL/dS, from dht at the end of each sequence;  per token t, backwards:
  *   D += scale q_t do_t^T;  dq_t = scale S_t do_t;  de = beta_t D^T k_t;  dv_t = de;
  *   dk_t = beta_t D e_t - S'_t de;  dbeta_t = k_t^T D e_t;  D' = D - k_t de^T;
  *   dg_t = a_t * rowsum(S_{t-1} * D') where g_t > g_min, else 0 (the floor is flat);
  *   D = diag(a_t) D';  dh0 = D at the sequence start
  *
- * (e_t = v_t - S'_t^T k_t, S'_t = diag(a_t) S_{t-1}). The forward states are recomputed from
- * checkpoints every 8 tokens that the call writes to its workspace.
+ * (e_t = v_t - S'_t^T k_t, S'_t = diag(a_t) S_{t-1}). The library evaluates the same gradients
+ * in chunk form, 16 tokens at a time, in fp32 on the matrix cores: a forward walk stores each
+ * chunk's entering state, a reverse walk each chunk's leaving-state gradient (both in the
+ * workspace), and one workgroup per chunk then forms dq, dk, dbeta and dg from them.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs, num_heads,
  *   d_k, d_v, io_dtype, scale, g_min: as for kda_chunk_fwd (the forward's inputs)
@@ -211,8 +212,9 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  *              argument; its contents on entry are ignored, on return undefined.
  *
  * Supported: io_dtype KDA_BF16 or KDA_F32 with d_k = d_v in {64, 128}. Outputs must not overlap
- * any input or each other. Results are deterministic (partial sums over value-column tiles are
- * added in a fixed order). Two launches: the per-tile reverse walk, then the sum over tiles.
+ * any input or each other. Results are deterministic (every sum is taken in a fixed order, no
+ * atomics). Three launches on the stream: the forward walk, the reverse walk, the per-chunk
+ * gradients.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
@@ -223,10 +225,10 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   void* stream);
 
 /*
- * Workspace bytes of kda_chunk_bwd: (T_total / 8 + N + 1) x H x d_k x d_v x 4 for the state
- * checkpoints, plus 3 x (d_v / 16) x T_total x H x d_k x 4 and 4 x (d_v / 16) x T_total x H x 4
- * for the partial sums (each part rounded up to 256 bytes). Same batch / seq_len / n_seqs
- * conventions as kda_chunk_fwd_workspace_size.
+ * Workspace bytes of kda_chunk_bwd: (T_total / 16 + N + 1) chunk slots x H x (2 d_k d_v + 64 d_v)
+ * x 4 (per 16-token chunk and head: the entering state and the leaving state's gradient, and
+ * four 16 x d_v fp32 row blocks). Same batch / seq_len / n_seqs conventions as
+ * kda_chunk_fwd_workspace_size.
  */
 int kda_chunk_bwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
                                  int d_v, size_t* bytes);

@@ -476,7 +476,7 @@ int kda_chunk_bwd_workspace_size(int batch, int seq_len, int n_seqs, int num_hea
   const bool packed = batch == 1 && n_seqs != 1;
   const int64_t T = packed ? int64_t(seq_len) : int64_t(batch) * seq_len;
   const int64_t N = packed ? n_seqs : batch;
-  *bytes = kda::bwd_workspace_bytes(T, N, num_heads, d_k, d_v);
+  *bytes = kda::cbwd_workspace_bytes(T, N, num_heads, d_k, d_v);
   return KDA_OK;
 }
 
@@ -502,7 +502,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
   const void* ptrs[] = {d_o, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
-  const size_t need = kda::bwd_workspace_bytes(T, N, num_heads, d_k, d_v);
+  const size_t need = kda::cbwd_workspace_bytes(T, N, num_heads, d_k, d_v);
   if (workspace_bytes < need) return KDA_ERR_WORKSPACE_TOO_SMALL;
   {
     const size_t st_bytes = size_t(N) * num_heads * d_k * d_v * 4;
@@ -525,7 +525,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
     }
   }
   if (N == 0) return KDA_OK;
-  kda::BwdParams p{};
+  kda::CBwdParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -541,6 +541,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
   p.n_ct = d_v / 16;
   p.n_units = N * num_heads;
   p.T = T;
+  p.n_slots = kda::cbwd_slots(T, N);
   p.scale = scale;
   p.g_min = g_min;
   p.dq = dq;
@@ -549,14 +550,18 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
   p.dg = dg;
   p.dbeta = dbeta;
   p.dh0 = dh0;
-  char* ws = static_cast<char*>(workspace);
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t ckpt_bytes = size_t(kda::bwd_ckpt_slots(T, N)) * num_heads * d_k * d_v * 4;
-  const size_t part_bytes = size_t(3) * p.n_ct * T * num_heads * d_k * 4;
-  p.ckpt = reinterpret_cast<float*>(ws);
-  p.part = reinterpret_cast<float*>(ws + up(ckpt_bytes));
-  p.part_beta = reinterpret_cast<float*>(ws + up(ckpt_bytes) + up(part_bytes));
-  return launch_status(kda::launch_chunk_bwd(p, io_dtype, d_k, static_cast<hipStream_t>(stream)));
+  // workspace: S0 and dS ([slots, H, d_k, d_v] each), then U, X0, dU, dY ([slots, H, 16, d_v])
+  float* ws = static_cast<float*>(workspace);
+  const size_t sts = size_t(p.n_slots) * num_heads * d_k * d_v;
+  const size_t rows = size_t(p.n_slots) * num_heads * kda::kCBChunk * d_v;
+  p.S0 = ws;
+  p.dS = ws + sts;
+  p.U = ws + 2 * sts;
+  p.X0 = ws + 2 * sts + rows;
+  p.dU = ws + 2 * sts + 2 * rows;
+  p.dY = ws + 2 * sts + 3 * rows;
+  return launch_status(
+      kda::launch_chunk_bwd_mfma(p, io_dtype, d_k, static_cast<hipStream_t>(stream)));
 }
 
 int kda_chunk_fwd_raw_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,

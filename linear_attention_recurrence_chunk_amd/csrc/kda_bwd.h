@@ -6,7 +6,10 @@
 
 namespace kda {
 
-struct BwdParams {
+// 16-token chunks, every product on fp32 matrix cores
+constexpr int kCBChunk = 16;
+
+struct CBwdParams {
   const void* q;            // [T, H, DK] io dtype
   const void* k;
   const void* v;            // [T, H, DV]
@@ -14,40 +17,36 @@ struct BwdParams {
   const float* beta;        // [T, H]
   const float* h0;          // [N, H, DK, DV] or null (zeros)
   const void* d_o;          // [T, H, DV] io dtype: dL/do
-  const float* dht;         // [N, H, DK, DV] or null (zeros): dL/d(final state)
+  const float* dht;         // [N, H, DK, DV] or null (zeros)
   const int32_t* cu_seqlens;  // device [N + 1] or null (fixed length seq_len)
   int seq_len, n_seqs, H, n_ct;   // n_ct: 16-column state tiles per head (DV / 16)
   int n_units;              // n_seqs * H
   long long T;              // tokens in all
+  long long n_slots;        // chunk slots: T / 16 + N + 1
   float scale, g_min;
-  // outputs (fp32)
-  float* dq;                // [T, H, DK]
+  float* dq;                // [T, H, DK] fp32 outputs
   float* dk;
   float* dv;                // [T, H, DV]
   float* dg;                // [T, H, DK]
   float* dbeta;             // [T, H]
   float* dh0;               // [N, H, DK, DV] or null
-  // workspace
-  float* ckpt;              // [T / 16 + N + 1, H, DK, DV] states at every 16th token
-  float* part;              // [3, n_ct, T, H, DK] per-tile sums of dq, dk, da
-  float* part_beta;         // [4 n_ct, T, H] per-wave sums of dbeta
+  // workspace, per chunk slot and head; chunk c of sequence n (first token bos_n) uses slot
+  // floor(bos_n / 16) + n + c
+  float* S0;                // [slots, H, DK, DV] state entering the chunk
+  float* dS;                // [slots, H, DK, DV] dL/d(state leaving the chunk)
+  float* U;                 // [slots, H, 16, DV] T diag(beta) (V - K_Gamma S0)
+  float* X0;                // [slots, H, 16, DV] V - K_Gamma S0
+  float* dU;                // [slots, H, 16, DV]
+  float* dY;                // [slots, H, 16, DV] T^T dU
 };
 
-// tokens between the backward's state checkpoints (a sub-chunk, recomputed in registers)
-constexpr int kBwdSub = 8;
+inline long long cbwd_slots(long long T, long long N) { return T / kCBChunk + N + 1; }
 
-inline long long bwd_ckpt_slots(long long T, long long N) { return T / kBwdSub + N + 1; }
-
-// Workspace bytes of the backward for T tokens in N sequences
-inline size_t bwd_workspace_bytes(long long T, long long N, int H, int dk, int dv) {
-  const long long n_ct = dv / 16;
-  const size_t ckpt = size_t(bwd_ckpt_slots(T, N)) * H * dk * dv * 4;
-  const size_t part = size_t(3) * n_ct * T * H * dk * 4;
-  const size_t part_beta = size_t(4) * n_ct * T * H * 4;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up(ckpt) + up(part) + up(part_beta);
+// Workspace bytes of the chunked backward for T tokens in N sequences
+inline size_t cbwd_workspace_bytes(long long T, long long N, int H, int dk, int dv) {
+  return size_t(cbwd_slots(T, N)) * H * (2 * size_t(dk) * dv + 4 * size_t(kCBChunk) * dv) * 4;
 }
 
-hipError_t launch_chunk_bwd(const BwdParams& p, int io_dtype, int dk, hipStream_t stream);
+hipError_t launch_chunk_bwd_mfma(const CBwdParams& p, int io_dtype, int dk, hipStream_t stream);
 
 }  // namespace kda

@@ -346,8 +346,7 @@ def test_backward_validation():
     need = ctypes.c_size_t(0)
     assert kda.library().kda_chunk_bwd_workspace_size(1, 1024, 1, 4, 128, 128,
                                                        ctypes.byref(need)) == OK
-    # checkpoints every 8 tokens, three partial sums per column tile, dbeta per wave and tile
-    ckpt = (1024 // 8 + 2) * 4 * 128 * 128 * 4
-    part = 3 * 8 * 1024 * 4 * 128 * 4
-    part_b = 4 * 8 * 1024 * 4 * 4
-    assert need.value == ckpt + part + part_b
+    # per 16-token chunk slot (1024 / 16 + 1 sequence + 1) and head: the entering state and
+    # the leaving state's gradient (d_k x d_v each), and four 16 x d_v row blocks
+    slots = 1024 // 16 + 2
+    assert need.value == slots * 4 * (2 * 128 * 128 + 4 * 16 * 128) * 4
