@@ -195,9 +195,10 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  *   D = diag(a_t) D';  dh0 = D at the sequence start
  *
  * (e_t = v_t - S'_t^T k_t, S'_t = diag(a_t) S_{t-1}). The library evaluates the same gradients
- * in chunk form, 16 tokens at a time, in fp32 on the matrix cores: a forward walk stores each
- * chunk's entering state, a reverse walk each chunk's leaving-state gradient (both in the
- * workspace), and one workgroup per chunk then forms dq, dk, dbeta and dg from them.
+ * in chunk form, 16 tokens at a time, in fp32 on the matrix cores: a parallel pass forms each
+ * chunk's operands, a forward walk stores each chunk's entering state, a reverse walk each
+ * chunk's leaving-state gradient (all in the workspace), and one workgroup per chunk then forms
+ * dq, dk, dbeta and dg from them.
  *
  *   q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len, n_seqs, num_heads,
  *   d_k, d_v, io_dtype, scale, g_min: as for kda_chunk_fwd (the forward's inputs)
@@ -213,8 +214,8 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  *
  * Supported: io_dtype KDA_BF16 or KDA_F32 with d_k = d_v in {64, 128}. Outputs must not overlap
  * any input or each other. Results are deterministic (every sum is taken in a fixed order, no
- * atomics). Three launches on the stream: the forward walk, the reverse walk, the per-chunk
- * gradients.
+ * atomics). Four launches on the stream: the operand pass, the forward walk, the reverse walk,
+ * the per-chunk gradients.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, const float* h0, const int32_t* cu_seqlens,
@@ -225,10 +226,11 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                   void* stream);
 
 /*
- * Workspace bytes of kda_chunk_bwd: (T_total / 16 + N + 1) chunk slots x H x (2 d_k d_v + 64 d_v)
- * x 4 (per 16-token chunk and head: the entering state and the leaving state's gradient, and
- * four 16 x d_v fp32 row blocks). Same batch / seq_len / n_seqs conventions as
- * kda_chunk_fwd_workspace_size.
+ * Workspace bytes of kda_chunk_bwd: (T_total / 16 + N + 1) chunk slots x H x (2 d_k d_v +
+ * 64 d_v + 49 d_k + 528) x 4 (per 16-token chunk and head, fp32: the entering state and the
+ * leaving state's gradient, four 16 x d_v row blocks, and the chunk's operand block: three
+ * 16 x d_k decayed tiles, two 16 x 16 matrices, d_k decay factors and 16 betas). Same batch /
+ * seq_len / n_seqs conventions as kda_chunk_fwd_workspace_size.
  */
 int kda_chunk_bwd_workspace_size(int batch, int seq_len, int n_seqs, int num_heads, int d_k,
                                  int d_v, size_t* bytes);

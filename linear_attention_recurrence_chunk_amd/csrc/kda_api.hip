@@ -550,16 +550,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
   p.dg = dg;
   p.dbeta = dbeta;
   p.dh0 = dh0;
-  // workspace: S0 and dS ([slots, H, d_k, d_v] each), then U, X0, dU, dY ([slots, H, 16, d_v])
-  float* ws = static_cast<float*>(workspace);
-  const size_t sts = size_t(p.n_slots) * num_heads * d_k * d_v;
-  const size_t rows = size_t(p.n_slots) * num_heads * kda::kCBChunk * d_v;
-  p.S0 = ws;
-  p.dS = ws + sts;
-  p.U = ws + 2 * sts;
-  p.X0 = ws + 2 * sts + rows;
-  p.dU = ws + 2 * sts + 2 * rows;
-  p.dY = ws + 2 * sts + 3 * rows;
+  kda::cbwd_bind_workspace(p, workspace, d_k, d_v);
   return launch_status(
       kda::launch_chunk_bwd_mfma(p, io_dtype, d_k, static_cast<hipStream_t>(stream)));
 }

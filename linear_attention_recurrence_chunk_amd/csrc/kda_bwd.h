@@ -38,13 +38,35 @@ struct CBwdParams {
   float* X0;                // [slots, H, 16, DV] V - K_Gamma S0
   float* dU;                // [slots, H, 16, DV]
   float* dY;                // [slots, H, 16, DV] T^T dU
+  float* ops;               // [slots, H, cbwd_op_floats(DK)] per-chunk operand blocks
 };
+
+// floats of one (chunk slot, head) operand block: three 16 x dk tiles, two 16 x 16 matrices,
+// dk decay factors and 16 betas
+inline constexpr size_t cbwd_op_floats(int dk) { return 49 * size_t(dk) + 528; }
 
 inline long long cbwd_slots(long long T, long long N) { return T / kCBChunk + N + 1; }
 
 // Workspace bytes of the chunked backward for T tokens in N sequences
 inline size_t cbwd_workspace_bytes(long long T, long long N, int H, int dk, int dv) {
-  return size_t(cbwd_slots(T, N)) * H * (2 * size_t(dk) * dv + 4 * size_t(kCBChunk) * dv) * 4;
+  return size_t(cbwd_slots(T, N)) * H *
+         (2 * size_t(dk) * dv + 4 * size_t(kCBChunk) * dv + cbwd_op_floats(dk)) * 4;
+}
+
+// Points p's workspace arrays into ws (at least cbwd_workspace_bytes(p.T, p.n_seqs, p.H, dk,
+// dv) bytes, 16-byte aligned); p.T, p.n_seqs and p.H must be set.
+inline void cbwd_bind_workspace(CBwdParams& p, void* ws, int dk, int dv) {
+  const size_t slots = size_t(cbwd_slots(p.T, p.n_seqs));
+  const size_t st = slots * p.H * dk * dv;          // one [slots, H, dk, dv] array
+  const size_t rows = slots * p.H * kCBChunk * dv;  // one [slots, H, 16, dv] array
+  float* f = static_cast<float*>(ws);
+  p.S0 = f;
+  p.dS = f + st;
+  p.U = f + 2 * st;
+  p.X0 = f + 2 * st + rows;
+  p.dU = f + 2 * st + 2 * rows;
+  p.dY = f + 2 * st + 3 * rows;
+  p.ops = f + 2 * st + 4 * rows;
 }
 
 hipError_t launch_chunk_bwd_mfma(const CBwdParams& p, int io_dtype, int dk, hipStream_t stream);

@@ -24,13 +24,17 @@
 // inside fp32 (|G| <= 16 x 5.4); the pairwise factors e^(G_t - G_s) are formed as
 // e^(G_t - G_m) e^(G_m - G_s) around the chunk's mid value G_m, so no factor exceeds e^44.
 //
-// Three launches:
+// Four launches:
+//   0. cbwd_prep_kernel: one workgroup per (chunk, head) forms the chunk's operand block: the
+//      decayed tiles K_G, K^, Q_G, T, M, e^(G_C) and beta;
 //   1. cbwd_fwd_kernel: one wave per (sequence, head, 16-column tile) walks the chunks
 //      forward and stores each chunk's entering state S0, X0 and U;
 //   2. cbwd_rev_kernel: the same waves walk back, storing dS (the gradient of the state
 //      leaving each chunk), dU and dY, writing dv, and dh0 at the sequence start;
 //   3. cbwd_grad_kernel: one workgroup per (chunk, head) forms dq, dk, dbeta and dg.
-// Sums over value columns happen inside launch 3 in a fixed order: results are deterministic.
+// The walks stage each chunk's operand block into LDS (global-to-LDS loads) while the previous
+// chunk is computed, so their chains hold the state products only. Sums over value columns
+// happen inside launch 3 in a fixed order: results are deterministic.
 #include "kda_bwd.h"
 #include "kda_common.h"
 
@@ -73,73 +77,67 @@ __device__ __forceinline__ f32x4 ld4(const __bf16* p, size_t i) {
   return r;
 }
 
-// One wave's prologue of a chunk for the walks: the in-chunk decays of its key channels
-// (lane, lane + 64, ...), written to LDS as the operand tiles the chunk's products read.
-// Token-major tiles have rows of LK floats, channel-major ones rows of LT.
-template <typename Tio, int DK, bool kRev>
-struct WalkTiles {
-  static constexpr int CPL = DK / 64;
-  static constexpr int LK = DK + 1;   // (odd strides: the 16 rows a product reads hit 16 banks)
-  static constexpr int LT = kC + 1;
-  float* Kg;     // token-major K e^G (forward), or channel-major (reverse)
-  float* Kh;     // channel-major K e^(G_C - G) (forward), or token-major (reverse)
-  float* QgT;    // channel-major Q e^G (reverse only)
-  float* Kq;     // token-major K e^(G - G_m)
-  float* Kk;     // token-major K e^(G_m - G)
-  float* Qq;     // token-major Q e^(G - G_m) (reverse only)
-  float* eGC;    // e^(G_C) per channel
-  float* beta;   // per token
-
-  __device__ void build(const CBwdParams& p, int cs, int L, int h, int lane) const {
-    const int H = p.H;
-    const Tio* gk = reinterpret_cast<const Tio*>(p.k);
-    const Tio* gq = reinterpret_cast<const Tio*>(p.q);
-    float G[kC][CPL], kv[kC][CPL], qv[kC][CPL];
-    float acc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int t = 0; t < kC; ++t) {
-      const bool valid = t < L;
-      const size_t row = (size_t(valid ? cs + t : cs) * H + h) * DK;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int ch = lane + 64 * i;
-        const float gv = p.g[row + ch];
-        acc[i] += fmaxf(gv, p.g_min) * keep_f(valid);
-        G[t][i] = acc[i];
-        kv[t][i] = ld_keep(gk, row + ch, valid);
-        if constexpr (kRev) qv[t][i] = ld_keep(gq, row + ch, valid);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int ch = lane + 64 * i;
-      const float gc = G[kC - 1][i];
-      const float gm = 0.5f * (G[0][i] + gc);
-      eGC[ch] = __expf(gc);
-#pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        const float eg = __expf(G[t][i]);
-        const float eh = __expf(gc - G[t][i]);
-        const float em = __expf(G[t][i] - gm);
-        const float emi = __expf(gm - G[t][i]);
-        Kq[t * LK + ch] = kv[t][i] * em;
-        Kk[t * LK + ch] = kv[t][i] * emi;
-        if constexpr (!kRev) {
-          Kg[t * LK + ch] = kv[t][i] * eg;
-          Kh[ch * LT + t] = kv[t][i] * eh;
-        } else {
-          Kg[ch * LT + t] = kv[t][i] * eg;
-          Kh[t * LK + ch] = kv[t][i] * eh;
-          QgT[ch * LT + t] = qv[t][i] * eg;
-          Qq[t * LK + ch] = qv[t][i] * em;
-        }
-      }
-    }
-    if (lane < kC) beta[lane] = lane < L ? p.beta[size_t(cs + lane) * H + h] : 0.f;
-  }
+// The operand block of one (chunk slot, head), in floats: the [16][DK] tiles K_G, K^ and Q_G
+// (element (t, c) at t DK + (c ^ swz(t))), T and M ([16][16] row-major), e^(G_C) per key channel
+// and beta per token. The forward walk stages the first kFwd floats, the reverse walk all.
+template <int DK>
+struct OpBlock {
+  static constexpr int kKG = 0;
+  static constexpr int kKH = 16 * DK;
+  static constexpr int kT = 32 * DK;
+  static constexpr int kEGC = kT + 256;
+  static constexpr int kBeta = kEGC + DK;
+  static constexpr int kFwd = kBeta + 16;
+  static constexpr int kQG = kFwd;
+  static constexpr int kM = kQG + 16 * DK;
+  static constexpr int kFloats = kM + 256;
+  static_assert(kFwd % 4 == 0 && kFloats % 4 == 0, "16-byte units");
+  static_assert(kFloats == cbwd_op_floats(DK), "workspace layout");
 };
+// The swizzle of the tiles' rows: with it, both access patterns of the walks (lanes along the
+// tokens with four channel groups, and lanes along the channels with four token groups) read
+// 64 distinct banks.
+__device__ __forceinline__ int swz(int t) { return (t & 3) | ((t >> 2) << 4); }
+
+// Copies the 16 x 16 tile of a chunk (rows cs + t, or cs for t >= L; columns col0 ..
+// col0 + 15 of rows ld elements apart) from global src to LDS dst, row-major (one wave; the LDS
+// address of a global-to-LDS load is its wave-uniform base plus 16 bytes per lane).
+// Asynchronous: the data is there once the wave's vector-memory count has drained.
+template <typename Tio>
+__device__ __forceinline__ void stage_vtile(const Tio* src, size_t ld, int cs, int L, int col0,
+                                            float* dst, int lane) {
+  constexpr int kPer = sizeof(Tio);          // 16-byte units per row
+  constexpr int kEl = 16 / sizeof(Tio);      // elements per unit
+  if (lane < 16 * kPer) {
+    const int t = lane / kPer, part = lane % kPer;
+    const Tio* g = src + size_t(t < L ? cs + t : cs) * ld + col0 + kEl * part;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(g), dst, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The chunk that a chunk slot holds: the sequence n (the last one whose first slot
+// floor(bos_n / 16) + n is at most slot), the chunk's first token and length. False for slots
+// that no chunk uses.
+__device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, int* cs_out,
+                                           int* L_out) {
+  auto first_tok = [&](int i) -> long long {
+    return p.cu_seqlens ? (long long)p.cu_seqlens[i] : (long long)i * p.seq_len;
+  };
+  int lo = 0, hi = p.n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first_tok(mid) / kC + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  const long long bos = first_tok(lo), eos = first_tok(lo + 1);
+  const long long c = slot - (bos / kC + lo);
+  if (c < 0 || bos + kC * c >= eos) return false;
+  *cs_out = int(bos + kC * c);
+  *L_out = int(min((long long)kC, eos - *cs_out));
+  return true;
+}
 
 // 16 x 16 product over the key channels: D[t][s] = sum_c X[t][c] Y[s][c] (token-major tiles)
 template <int DK>
@@ -155,8 +153,10 @@ __device__ __forceinline__ f32x4 gram16(const float* X, const float* Y, int ln, 
 }
 
 // T = (I + A)^-1 for the strictly lower A[t][s] = beta_t B[t][s] (B stored with row stride 17):
-// lane j < 16 solves column j by forward substitution into sT (row stride 20)
-__device__ __forceinline__ void invert16(const float* sB, const float* sBeta, float* sT, int lane) {
+// lane j < 16 solves column j by forward substitution into sT (row stride 20) and, when gT is
+// set, into gT (row stride 16)
+__device__ __forceinline__ void invert16(const float* sB, const float* sBeta, float* sT,
+                                         float* gT, int lane) {
   if (lane < kC) {
     float x[kC];
 #pragma unroll
@@ -167,6 +167,7 @@ __device__ __forceinline__ void invert16(const float* sB, const float* sBeta, fl
       for (int m = 0; m < i; ++m) v = fmaf(-bi * sB[i * 17 + m], x[m], v);
       x[i] = v;
       sT[i * 20 + lane] = v;
+      if (gT) gT[i * 16 + lane] = v;
     }
   }
 }
@@ -180,27 +181,125 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
+// ---- 0. operand blocks: one workgroup (one thread per key channel) per (chunk slot, head)
+template <typename Tio, int DK>
+__global__ __launch_bounds__(DK) void cbwd_prep_kernel(CBwdParams p) {
+  using OB = OpBlock<DK>;
+  constexpr int LK = DK + 1;
+  __shared__ float sKq[kC * LK], sKk[kC * LK], sQq[kC * LK];
+  __shared__ float sB[kC * 17], sT[kC * 20], sBeta[kC];
+  const int H = p.H;
+  const int h = int(blockIdx.x % unsigned(H));
+  const long long slot = blockIdx.x / unsigned(H);
+  int cs, L;
+  if (!slot_chunk(p, slot, &cs, &L)) return;
+  float* ob = p.ops + (size_t(slot) * H + h) * OB::kFloats;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q4 = lane >> 4, ln = lane & 15;
+  const Tio* gq = reinterpret_cast<const Tio*>(p.q);
+  const Tio* gk = reinterpret_cast<const Tio*>(p.k);
+  {
+    float G[kC], kv[kC], qv[kC];
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      const bool valid = t < L;
+      const size_t row = (size_t(valid ? cs + t : cs) * H + h) * DK + tid;
+      acc += fmaxf(p.g[row], p.g_min) * keep_f(valid);
+      G[t] = acc;
+      kv[t] = ld_keep(gk, row, valid);
+      qv[t] = ld_keep(gq, row, valid);
+    }
+    const float gc = G[kC - 1];
+    const float gm = 0.5f * (G[0] + gc);
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      const float eg = __expf(G[t]), eh = __expf(gc - G[t]);
+      const float em = __expf(G[t] - gm), emi = __expf(gm - G[t]);
+      const int sa = t * DK + (tid ^ swz(t));
+      ob[OB::kKG + sa] = kv[t] * eg;
+      ob[OB::kKH + sa] = kv[t] * eh;
+      ob[OB::kQG + sa] = qv[t] * eg;
+      sKq[t * LK + tid] = kv[t] * em;
+      sKk[t * LK + tid] = kv[t] * emi;
+      sQq[t * LK + tid] = qv[t] * em;
+    }
+    ob[OB::kEGC + tid] = __expf(gc);
+  }
+  if (tid < kC) {
+    const float b = tid < L ? p.beta[size_t(cs + tid) * H + h] : 0.f;
+    sBeta[tid] = b;
+    ob[OB::kBeta + tid] = b;
+  }
+  lds_barrier();
+  if (w == 0) {
+    const f32x4 b = gram16<DK>(sKq, sKk, ln, q4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * q4 + r;
+      sB[t * 17 + ln] = ln < t ? b[r] : 0.f;
+    }
+    wave_sync();
+    invert16(sB, sBeta, sT, ob + OB::kT, lane);
+  }
+  if (w == DK / 64 - 1) {
+    const f32x4 m = gram16<DK>(sQq, sKk, ln, q4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * q4 + r;
+      ob[OB::kM + t * 16 + ln] = ln <= t ? m[r] : 0.f;
+    }
+  }
+}
+
+// The walks: a workgroup of four waves per (sequence, head, group of four 16-column tiles);
+// wave w owns tile 4 sub + w. The waves walk the same chunks and share each chunk's operand
+// block in LDS, double-buffered: while a chunk is computed, the next chunk's block (a quarter
+// of it staged by each wave) and each wave's own 16 x 16 input tile are copied in. One barrier
+// per chunk publishes the staged buffer and frees the one just read. (At 8192 x 96, d = 128:
+// 192 workgroups, one per CU and one wave per SIMD; with two waves per workgroup, 384 of them,
+// the backward took 7.6 instead of 6.5 ms.)
+constexpr int kWalkWaves = 4;
+
+// Copies a block of N4 16-byte units from global src to LDS dst, 64 units per instruction;
+// wave w of the walk issues instructions w, w + kWalkWaves, ... (asynchronous, as above)
+template <int N4>
+__device__ __forceinline__ void stage_block_half(const float* src, float* dst, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < N4 / 64; ++i)
+    if (i % kWalkWaves == w)
+      __builtin_amdgcn_global_load_lds(src + 4 * (64 * i + lane), dst + 256 * i, 16, 0, 0);
+  if constexpr (N4 % 64 != 0) {
+    if ((N4 / 64) % kWalkWaves == w && lane < N4 % 64)
+      __builtin_amdgcn_global_load_lds(src + 4 * (64 * (N4 / 64) + lane), dst + 256 * (N4 / 64),
+                                       16, 0, 0);
+  }
+}
+
 // ---- 1. forward walk: S0, X0 and U of every chunk
 template <typename Tio, int DK>
-__global__ __launch_bounds__(64) void cbwd_fwd_kernel(CBwdParams p) {
+__global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
-  using WT = WalkTiles<Tio, DK, false>;
-  constexpr int LK = WT::LK, LT = WT::LT;
-  __shared__ float sKg[kC * LK], sKq[kC * LK], sKk[kC * LK];
-  __shared__ float sKhT[DK * LT];
-  __shared__ float sB[kC * 17], sT[kC * 20], sGC[DK], sBeta[kC];
+  using OB = OpBlock<DK>;
+  // per buffer: the block's first kFwd floats, then each wave's 16 x 16 value tile
+  constexpr int kTile = 64 * int(sizeof(Tio));   // floats of one tile
+  constexpr int kBuf = OB::kFwd + kWalkWaves * kTile;
+  __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
 
-  int ct;
-  const int unit = block_unit(blockIdx.x, p.n_ct, &ct);
+  int sub;
+  const int unit = block_unit(blockIdx.x, p.n_ct / kWalkWaves, &sub);
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int h = unit % H, n = unit / H;
   const int bos = p.cu_seqlens ? p.cu_seqlens[n] : n * p.seq_len;
   const int eos = p.cu_seqlens ? p.cu_seqlens[n + 1] : bos + p.seq_len;
-  const int lane = threadIdx.x, q4 = lane >> 4, ln = lane & 15;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
+  const int ct = kWalkWaves * sub + w;
   const int col = 16 * ct + ln;
-  const Tio* gv = reinterpret_cast<const Tio*>(p.v);
-  const WT tiles{sKg, sKhT, nullptr, sKq, sKk, nullptr, sGC, sBeta};
+  const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
+  const int nch = (eos - bos + kC - 1) / kC;
+  const float* ops0 = p.ops + (size_t(cb_slot(bos, n, 0)) * H + h) * OB::kFloats;
+  const size_t ops_stride = size_t(H) * OB::kFloats;
+  auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(bos, n, c)) * H + h) * DK * DV; };
 
   // the state tile in accumulator layout: block rb, register r = row 16 rb + 4 q4 + r
   f32x4 S[NTD];
@@ -213,49 +312,70 @@ __global__ __launch_bounds__(64) void cbwd_fwd_kernel(CBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[rb][r] = p.h0[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col];
   }
-
-  int c = 0;
-  for (int cs = bos; cs < eos; cs += kC, ++c) {
-    const int L = min(kC, eos - cs);
-    const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
-    tiles.build(p, cs, L, h, lane);
-    wave_sync();
-    {
-      const f32x4 b = gram16<DK>(sKq, sKk, ln, q4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * q4 + r;
-        sB[t * 17 + ln] = ln < t ? b[r] : 0.f;
-      }
-    }
-    wave_sync();
-    invert16(sB, sBeta, sT, lane);
-    wave_sync();
-    // the state entering the chunk
-    float* s0 = p.S0 + blk * DK * DV;
+  if (nch == 0) return;
+  // a chunk's operand block (this wave's half) and value tile into buffer dst
+  auto stage = [&](int c, float* dst) {
+    const int cs = bos + kC * c;
+    stage_block_half<OB::kFwd / 4>(ops0 + c * ops_stride, dst, w, lane);
+    stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct, dst + OB::kFwd + w * kTile,
+                lane);
+  };
+  auto store_state = [&](float* dst) {
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s0[size_t(16 * rb + 4 * q4 + r) * DV + col] = S[rb][r];
+      for (int r = 0; r < 4; ++r) dst[size_t(16 * rb + 4 * q4 + r) * DV + col] = S[rb][r];
+  };
+  stage(0, sb0);
+  wait_vmem();
+  lds_barrier();
+  store_state(s0_of(0));
+
+  for (int c = 0; c < nch; ++c) {
+    const float* cur = (c & 1) ? sb1 : sb0;
+    // the next chunk's block and values (the last chunk's again at the end: nothing is
+    // staged conditionally); the buffer was last read in the previous chunk, before the
+    // barrier that ended it
+    stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
+    const int cs = bos + kC * c, L = min(kC, eos - cs);
+    const int sl = swz(ln);
     // X = K_G S (k order: the state's own register order)
     f32x4 X = zero4();
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) X = mma_f32(sKg[ln * LK + 16 * rb + 4 * q4 + r], S[rb][r], X);
-    // X0 = V - X, Y = diag(beta) X0 (rows past a ragged chunk's end stay zero)
+      for (int r = 0; r < 4; ++r)
+        X = mma_f32(cur[OB::kKG + ln * DK + ((16 * rb + 4 * q4 + r) ^ sl)], S[rb][r], X);
+    // X0 = V - X, Y = diag(beta) X0 (rows past a ragged chunk's end are zero)
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
+    const Tio* vt = reinterpret_cast<const Tio*>(cur + OB::kFwd + w * kTile);
     f32x4 X0, Y;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 4 * q4 + r;
-      const float vv = ld_f32(gv, (size_t(t < L ? cs + t : cs) * H + h) * DV + col);
-      X0[r] = (vv - X[r]) * keep_f(t < L);
-      Y[r] = sBeta[t] * X0[r];
+      X0[r] = (to_f32(vt[(4 * q4 + r) * 16 + ln]) - X[r]) * keep_f(4 * q4 + r < L);
+      Y[r] = bt[r] * X0[r];
     }
     // U = T Y
     f32x4 U = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) U = mma_f32(sT[ln * 20 + 4 * q4 + kk], Y[kk], U);
+    for (int kk = 0; kk < 4; ++kk) U = mma_f32(cur[OB::kT + ln * 16 + 4 * q4 + kk], Y[kk], U);
+    // S = e^(G_C) S + K^^T U
+#pragma unroll
+    for (int rb = 0; rb < NTD; ++rb) {
+      const f32x4 e = *reinterpret_cast<const f32x4*>(cur + OB::kEGC + 16 * rb + 4 * q4);
+      S[rb] *= e;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int t = 4 * q4 + kk;
+        S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
+      }
+    }
+    // this wave's part of the next buffer has landed (and its earlier stores are done); the
+    // barrier publishes both parts. This chunk's stores go out after the wait, so the next
+    // wait finds them done.
+    wait_vmem();
+    lds_barrier();
+    const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
     float* wx = p.X0 + blk * kC * DV;
     float* wu = p.U + blk * kC * DV;
 #pragma unroll
@@ -263,40 +383,34 @@ __global__ __launch_bounds__(64) void cbwd_fwd_kernel(CBwdParams p) {
       wx[size_t(4 * q4 + r) * DV + col] = X0[r];
       wu[size_t(4 * q4 + r) * DV + col] = U[r];
     }
-    // S = e^(G_C) S + K^^T U
-#pragma unroll
-    for (int rb = 0; rb < NTD; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[rb][r] *= sGC[16 * rb + 4 * q4 + r];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        S[rb] = mma_f32(sKhT[(16 * rb + ln) * LT + 4 * q4 + kk], U[kk], S[rb]);
-    }
-    wave_sync();   // the next chunk rewrites the tiles
+    if (c + 1 < nch) store_state(s0_of(c + 1));
   }
 }
 
 // ---- 2. reverse walk: dS, dU, dY of every chunk, dv, and dh0
 template <typename Tio, int DK>
-__global__ __launch_bounds__(64) void cbwd_rev_kernel(CBwdParams p) {
+__global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
-  using WT = WalkTiles<Tio, DK, true>;
-  constexpr int LK = WT::LK, LT = WT::LT;
-  __shared__ float sKh[kC * LK], sKq[kC * LK], sKk[kC * LK], sQq[kC * LK];
-  __shared__ float sKgT[DK * LT], sQgT[DK * LT];
-  __shared__ float sB[kC * 17], sM[kC * 17], sT[kC * 20], sGC[DK], sBeta[kC];
+  using OB = OpBlock<DK>;
+  // per buffer: the operand block, then each wave's 16 x 16 tile of output gradients
+  constexpr int kTile = 64 * int(sizeof(Tio));
+  constexpr int kBuf = OB::kFloats + kWalkWaves * kTile;
+  __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
 
-  int ct;
-  const int unit = block_unit(blockIdx.x, p.n_ct, &ct);
+  int sub;
+  const int unit = block_unit(blockIdx.x, p.n_ct / kWalkWaves, &sub);
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int h = unit % H, n = unit / H;
   const int bos = p.cu_seqlens ? p.cu_seqlens[n] : n * p.seq_len;
   const int eos = p.cu_seqlens ? p.cu_seqlens[n + 1] : bos + p.seq_len;
-  const int lane = threadIdx.x, q4 = lane >> 4, ln = lane & 15;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
+  const int ct = kWalkWaves * sub + w;
   const int col = 16 * ct + ln;
-  const Tio* gdo = reinterpret_cast<const Tio*>(p.d_o);
-  const WT tiles{sKgT, sKh, sQgT, sKq, sKk, sQq, sGC, sBeta};
+  const Tio* gdo = reinterpret_cast<const Tio*>(p.d_o) + size_t(h) * DV;
+  const int nch = (eos - bos + kC - 1) / kC;
+  const float* ops0 = p.ops + (size_t(cb_slot(bos, n, 0)) * H + h) * OB::kFloats;
+  const size_t ops_stride = size_t(H) * OB::kFloats;
 
   f32x4 D[NTD];
   const size_t st_off = (size_t(n) * H + h) * DK * DV;
@@ -308,76 +422,80 @@ __global__ __launch_bounds__(64) void cbwd_rev_kernel(CBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[rb][r] = p.dht[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col];
   }
-
-  const int nch = (eos - bos + kC - 1) / kC;
-  for (int c = nch - 1; c >= 0; --c) {
+  auto stage = [&](int c, float* dst) {
     const int cs = bos + kC * c;
-    const int L = min(kC, eos - cs);
-    const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
-    tiles.build(p, cs, L, h, lane);
-    wave_sync();
-    {
-      const f32x4 b = gram16<DK>(sKq, sKk, ln, q4);
-      const f32x4 m = gram16<DK>(sQq, sKk, ln, q4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * q4 + r;
-        sB[t * 17 + ln] = ln < t ? b[r] : 0.f;
-        sM[t * 17 + ln] = ln <= t ? m[r] : 0.f;
-      }
-    }
-    wave_sync();
-    invert16(sB, sBeta, sT, lane);
-    wave_sync();
-    // the gradient of the state leaving the chunk
-    float* ds = p.dS + blk * DK * DV;
+    stage_block_half<OB::kFloats / 4>(ops0 + c * ops_stride, dst, w, lane);
+    stage_vtile(gdo, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct,
+                dst + OB::kFloats + w * kTile, lane);
+  };
+  auto store_grad = [&](int c) {
+    float* ds = p.dS + (size_t(cb_slot(bos, n, c)) * H + h) * DK * DV;
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ds[size_t(16 * rb + 4 * q4 + r) * DV + col] = D[rb][r];
-    // s dO as the products' right operand: token 4 q4 + kk, this lane's column
-    float sdo[4];
+  };
+  if (nch > 0) {
+    stage(nch - 1, sb0);
+    wait_vmem();
+    lds_barrier();
+    store_grad(nch - 1);
+    for (int i = 0; i < nch; ++i) {
+      const int c = nch - 1 - i;
+      const float* cur = (i & 1) ? sb1 : sb0;
+      stage(max(c - 1, 0), (i & 1) ? sb0 : sb1);
+      const int cs = bos + kC * c, L = min(kC, eos - cs);
+      const int sl = swz(ln);
+      // s dO as the products' right operand: token 4 q4 + kk, this lane's column
+      const Tio* dt = reinterpret_cast<const Tio*>(cur + OB::kFloats + w * kTile);
+      float sdo[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int t = 4 * q4 + kk;
-      sdo[kk] = p.scale * ld_keep(gdo, (size_t(t < L ? cs + t : cs) * H + h) * DV + col, t < L);
-    }
-    // dU = M^T (s dO) + K^ D
-    f32x4 dU = zero4();
+      for (int kk = 0; kk < 4; ++kk)
+        sdo[kk] = (p.scale * keep_f(4 * q4 + kk < L)) * to_f32(dt[(4 * q4 + kk) * 16 + ln]);
+      // dU = M^T (s dO) + K^ D
+      f32x4 dU = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) dU = mma_f32(sM[(4 * q4 + kk) * 17 + ln], sdo[kk], dU);
+      for (int kk = 0; kk < 4; ++kk) dU = mma_f32(cur[OB::kM + (4 * q4 + kk) * 16 + ln], sdo[kk], dU);
 #pragma unroll
-    for (int rb = 0; rb < NTD; ++rb)
+      for (int rb = 0; rb < NTD; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dU = mma_f32(sKh[ln * LK + 16 * rb + 4 * q4 + r], D[rb][r], dU);
-    // dY = T^T dU
-    f32x4 dY = zero4();
+        for (int r = 0; r < 4; ++r)
+          dU = mma_f32(cur[OB::kKH + ln * DK + ((16 * rb + 4 * q4 + r) ^ sl)], D[rb][r], dU);
+      // dY = T^T dU
+      f32x4 dY = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) dY = mma_f32(sT[(4 * q4 + kk) * 20 + ln], dU[kk], dY);
-    float* wdu = p.dU + blk * kC * DV;
-    float* wdy = p.dY + blk * kC * DV;
+      for (int kk = 0; kk < 4; ++kk) dY = mma_f32(cur[OB::kT + (4 * q4 + kk) * 16 + ln], dU[kk], dY);
+      // D = e^(G_C) D + Q_G^T (s dO) - K_G^T diag(beta) dY
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
+      float bdy[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * q4 + r;
-      wdu[size_t(t) * DV + col] = dU[r];
-      wdy[size_t(t) * DV + col] = dY[r];
-      if (t < L) p.dv[(size_t(cs + t) * H + h) * DV + col] = sBeta[t] * dY[r];
-    }
-    // D = e^(G_C) D + Q_G^T (s dO) - K_G^T diag(beta) dY
-    float bdy[4];
+      for (int kk = 0; kk < 4; ++kk) bdy[kk] = -bt[kk] * dY[kk];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) bdy[kk] = -sBeta[4 * q4 + kk] * dY[kk];
+      for (int rb = 0; rb < NTD; ++rb) {
+        const f32x4 e = *reinterpret_cast<const f32x4*>(cur + OB::kEGC + 16 * rb + 4 * q4);
+        D[rb] *= e;
 #pragma unroll
-    for (int rb = 0; rb < NTD; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) D[rb][r] *= sGC[16 * rb + 4 * q4 + r];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        D[rb] = mma_f32(sQgT[(16 * rb + ln) * LT + 4 * q4 + kk], sdo[kk], D[rb]);
-        D[rb] = mma_f32(sKgT[(16 * rb + ln) * LT + 4 * q4 + kk], bdy[kk], D[rb]);
+        for (int kk = 0; kk < 4; ++kk) {
+          const int t = 4 * q4 + kk;
+          const int a = t * DK + ((16 * rb + ln) ^ swz(t));
+          D[rb] = mma_f32(cur[OB::kQG + a], sdo[kk], D[rb]);
+          D[rb] = mma_f32(cur[OB::kKG + a], bdy[kk], D[rb]);
+        }
       }
+      wait_vmem();
+      lds_barrier();
+      const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
+      float* wdu = p.dU + blk * kC * DV;
+      float* wdy = p.dY + blk * kC * DV;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * q4 + r;
+        wdu[size_t(t) * DV + col] = dU[r];
+        wdy[size_t(t) * DV + col] = dY[r];
+        if (t < L) p.dv[(size_t(cs + t) * H + h) * DV + col] = bt[r] * dY[r];
+      }
+      if (c > 0) store_grad(c - 1);
     }
-    wave_sync();
   }
   if (p.dh0) {
 #pragma unroll
@@ -391,7 +509,7 @@ __global__ __launch_bounds__(64) void cbwd_rev_kernel(CBwdParams p) {
 // (chunk slot, head); workgroups of unused slots exit.
 template <typename Tio, int DK>
 __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
-  constexpr int DV = DK, NT = 4 * DK;
+  constexpr int DV = DK;
   constexpr int LK = DK + 1, LV = DV + 4;
   __shared__ float sKq[kC * LK], sKk[kC * LK], sQq[kC * LK];
   __shared__ float sG[kC * LK];   // G, then each token's log-decay gradient
@@ -402,22 +520,8 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
   const int H = p.H;
   const int h = int(blockIdx.x % unsigned(H));
   const long long slot = blockIdx.x / unsigned(H);
-  // the sequence whose slots hold this one: the last n with floor(bos_n / 16) + n <= slot
-  auto first_tok = [&](int i) -> long long {
-    return p.cu_seqlens ? (long long)p.cu_seqlens[i] : (long long)i * p.seq_len;
-  };
-  int lo = 0, hi = p.n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (first_tok(mid) / kC + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  const int n = lo;
-  const long long bos = first_tok(n), eos = first_tok(n + 1);
-  const long long c = slot - (bos / kC + n);
-  if (c < 0 || bos + kC * c >= eos) return;
-  const int cs = int(bos + kC * c);
-  const int L = int(min((long long)kC, eos - cs));
+  int cs, L;
+  if (!slot_chunk(p, slot, &cs, &L)) return;
   const size_t blk = size_t(slot) * H + h;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q4 = lane >> 4, ln = lane & 15;
@@ -516,7 +620,7 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
       sB[t * 17 + ln] = ln < t ? b[r] : 0.f;
     }
     wave_sync();
-    invert16(sB, sBeta, sT, lane);
+    invert16(sB, sBeta, sT, nullptr, lane);
   } else if (w == 3) {
     // first part of dbeta: X0 . dY per token, four lanes a token
     const int t = lane >> 2, part = lane & 3;
@@ -641,20 +745,24 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
 
 template <typename Tio, int DK>
 static hipError_t launch_cbwd(const CBwdParams& p, hipStream_t stream) {
-  const dim3 walk((p.n_units + 7) / 8 * 8 * p.n_ct);
-  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(64), 0, stream, p);
+  const dim3 walk((p.n_units + 7) / 8 * 8 * (p.n_ct / kWalkWaves));
+  const dim3 chunks(unsigned(p.n_slots * p.H));
+  hipLaunchKernelGGL((cbwd_prep_kernel<Tio, DK>), chunks, dim3(DK), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(64 * kWalkWaves), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_grad_kernel<Tio, DK>), dim3(unsigned(p.n_slots * p.H)), dim3(4 * DK),
-                     0, stream, p);
+  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(64 * kWalkWaves), 0, stream, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((cbwd_grad_kernel<Tio, DK>), chunks, dim3(4 * DK), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_bwd_mfma(const CBwdParams& p, int io_dtype, int dk, hipStream_t stream) {
-  if (p.n_ct != dk / 16 || p.n_units != p.n_seqs * p.H || p.H < 1 || p.n_seqs < 1 ||
+  if (p.n_ct != dk / 16 || p.n_ct % kWalkWaves != 0 || p.n_units != p.n_seqs * p.H || p.H < 1 ||
+      p.n_seqs < 1 ||
       p.n_slots != cbwd_slots(p.T, p.n_seqs) || p.n_slots * p.H > 0x7fffffffLL)
     return hipErrorInvalidValue;
   if (dk == 128) return io_dtype == 1 ? launch_cbwd<__bf16, 128>(p, stream)

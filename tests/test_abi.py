@@ -347,6 +347,8 @@ def test_backward_validation():
     assert kda.library().kda_chunk_bwd_workspace_size(1, 1024, 1, 4, 128, 128,
                                                        ctypes.byref(need)) == OK
     # per 16-token chunk slot (1024 / 16 + 1 sequence + 1) and head: the entering state and
-    # the leaving state's gradient (d_k x d_v each), and four 16 x d_v row blocks
+    # the leaving state's gradient (d_k x d_v each), four 16 x d_v row blocks, and the operand
+    # block (three 16 x d_k tiles, two 16 x 16 matrices, d_k decay factors, 16 betas)
     slots = 1024 // 16 + 2
-    assert need.value == slots * 4 * (2 * 128 * 128 + 4 * 16 * 128) * 4
+    op_block = 3 * 16 * 128 + 2 * 256 + 128 + 16
+    assert need.value == slots * 4 * (2 * 128 * 128 + 4 * 16 * 128 + op_block) * 4
