@@ -94,10 +94,11 @@ struct OpBlock {
   static_assert(kFwd % 4 == 0 && kFloats % 4 == 0, "16-byte units");
   static_assert(kFloats == cbwd_op_floats(DK), "workspace layout");
 };
-// The swizzle of the tiles' rows: with it, both access patterns of the walks (lanes along the
-// tokens with four channel groups, and lanes along the channels with four token groups) read
-// 64 distinct banks.
-__device__ __forceinline__ int swz(int t) { return (t & 3) | ((t >> 2) << 4); }
+// The swizzle of the tiles' rows (an XOR on bits 2..5 of the channel): both access patterns of
+// the walks read 64 distinct banks: lanes along the tokens reading four consecutive channels
+// each (one 16-byte read: the XOR keeps aligned groups of four together), and lanes along the
+// channels with four token groups.
+__device__ __forceinline__ int swz(int t) { return 4 * t; }
 
 // Copies the 16 x 16 tile of a chunk (rows cs + t, or cs for t >= L; columns col0 ..
 // col0 + 15 of rows ld elements apart) from global src to LDS dst, row-major (one wave; the LDS
@@ -116,6 +117,18 @@ __device__ __forceinline__ void stage_vtile(const Tio* src, size_t ld, int cs, i
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stores a 16 x 16 tile held in accumulator layout (lane (q4, ln), register r: row 4 q4 + r,
+// column ln) to row-major dst (rows ld floats apart) with one 16-byte store per lane: after a
+// transpose inside each quad of lanes, lane (q4, ln) holds row 4 q4 + (ln & 3), columns
+// 4 (ln >> 2) .. + 3.
+__device__ __forceinline__ void store_tile16(float* dst, size_t ld, f32x4 a, int lane) {
+  float x[4] = {a[0], a[1], a[2], a[3]};
+  quad_transpose(x, lane);
+  const int q4 = (lane >> 4) & 3, ln = lane & 15;
+  *reinterpret_cast<f32x4*>(dst + size_t(4 * q4 + (ln & 3)) * ld + 4 * (ln >> 2)) =
+      f32x4{x[0], x[1], x[2], x[3]};
+}
 
 // The chunk that a chunk slot holds: the sequence n (the last one whose first slot
 // floor(bos_n / 16) + n is at most slot), the chunk's first token and length. False for slots
@@ -342,10 +355,11 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
     // X = K_G S (k order: the state's own register order)
     f32x4 X = zero4();
 #pragma unroll
-    for (int rb = 0; rb < NTD; ++rb)
+    for (int rb = 0; rb < NTD; ++rb) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(cur + OB::kKG + ln * DK + ((16 * rb + 4 * q4) ^ sl));
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        X = mma_f32(cur[OB::kKG + ln * DK + ((16 * rb + 4 * q4 + r) ^ sl)], S[rb][r], X);
+      for (int r = 0; r < 4; ++r) X = mma_f32(a[r], S[rb][r], X);
+    }
     // X0 = V - X, Y = diag(beta) X0 (rows past a ragged chunk's end are zero)
     const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
     const Tio* vt = reinterpret_cast<const Tio*>(cur + OB::kFwd + w * kTile);
@@ -370,9 +384,9 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
         S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
       }
     }
-    // this wave's part of the next buffer has landed (and its earlier stores are done); the
-    // barrier publishes both parts. This chunk's stores go out after the wait, so the next
-    // wait finds them done.
+    // this wave's part of the next buffer has landed (and the previous chunk's stores are
+    // done); the barrier publishes all parts and frees the buffer just read. This chunk's
+    // stores go out after the wait, so the next wait finds them done.
     wait_vmem();
     lds_barrier();
     const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
@@ -431,19 +445,18 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
   auto store_grad = [&](int c) {
     float* ds = p.dS + (size_t(cb_slot(bos, n, c)) * H + h) * DK * DV;
 #pragma unroll
-    for (int rb = 0; rb < NTD; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ds[size_t(16 * rb + 4 * q4 + r) * DV + col] = D[rb][r];
+    for (int rb = 0; rb < NTD; ++rb) store_tile16(ds + size_t(16 * rb) * DV + 16 * ct, DV, D[rb], lane);
   };
   if (nch > 0) {
     stage(nch - 1, sb0);
     wait_vmem();
     lds_barrier();
-    store_grad(nch - 1);
     for (int i = 0; i < nch; ++i) {
       const int c = nch - 1 - i;
       const float* cur = (i & 1) ? sb1 : sb0;
       stage(max(c - 1, 0), (i & 1) ? sb0 : sb1);
+      // the gradient of the state leaving the chunk (its stores overlap the products below)
+      store_grad(c);
       const int cs = bos + kC * c, L = min(kC, eos - cs);
       const int sl = swz(ln);
       // s dO as the products' right operand: token 4 q4 + kk, this lane's column
@@ -457,16 +470,32 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) dU = mma_f32(cur[OB::kM + (4 * q4 + kk) * 16 + ln], sdo[kk], dU);
 #pragma unroll
-      for (int rb = 0; rb < NTD; ++rb)
+      for (int rb = 0; rb < NTD; ++rb) {
+        const f32x4 a =
+            *reinterpret_cast<const f32x4*>(cur + OB::kKH + ln * DK + ((16 * rb + 4 * q4) ^ sl));
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dU = mma_f32(cur[OB::kKH + ln * DK + ((16 * rb + 4 * q4 + r) ^ sl)], D[rb][r], dU);
+        for (int r = 0; r < 4; ++r) dU = mma_f32(a[r], D[rb][r], dU);
+      }
       // dY = T^T dU
       f32x4 dY = zero4();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) dY = mma_f32(cur[OB::kT + (4 * q4 + kk) * 16 + ln], dU[kk], dY);
-      // D = e^(G_C) D + Q_G^T (s dO) - K_G^T diag(beta) dY
       const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
+      {
+        const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
+        store_tile16(p.dU + blk * kC * DV + 16 * ct, DV, dU, lane);
+        store_tile16(p.dY + blk * kC * DV + 16 * ct, DV, dY, lane);
+        // dv = diag(beta) dY, row-major: lane (q4, ln) stores token 4 q4 + (ln & 3), columns
+        // 4 (ln >> 2) .. + 3 of this tile
+        float x[4] = {dY[0], dY[1], dY[2], dY[3]};
+        quad_transpose(x, lane);
+        const int t = 4 * q4 + (ln & 3);
+        const float b = cur[OB::kBeta + t];
+        if (t < L)
+          *reinterpret_cast<f32x4*>(p.dv + (size_t(cs + t) * H + h) * DV + 16 * ct + 4 * (ln >> 2)) =
+              f32x4{b * x[0], b * x[1], b * x[2], b * x[3]};
+      }
+      // D = e^(G_C) D + Q_G^T (s dO) - K_G^T diag(beta) dY
       float bdy[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bdy[kk] = -bt[kk] * dY[kk];
@@ -484,17 +513,6 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
       }
       wait_vmem();
       lds_barrier();
-      const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
-      float* wdu = p.dU + blk * kC * DV;
-      float* wdy = p.dY + blk * kC * DV;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * q4 + r;
-        wdu[size_t(t) * DV + col] = dU[r];
-        wdy[size_t(t) * DV + col] = dY[r];
-        if (t < L) p.dv[(size_t(cs + t) * H + h) * DV + col] = bt[r] * dY[r];
-      }
-      if (c > 0) store_grad(c - 1);
     }
   }
   if (p.dh0) {
