@@ -363,6 +363,35 @@ def bench_varlen(kda, wl, torch, dev, stream, steps, warmup):
                         else "chunk kernel (one launch)")}
 
 
+def bench_prefill_f32(kda, wl, torch, dev, stream, steps, warmup):
+    """kda_chunk_fwd on the prefill shape (8192 tokens x 96 heads, d = 128) with fp32 inputs
+    and output: the 16-token chunk form on fp32 matrix cores (operand pass + walk)."""
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype="f32", seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device=dev)
+    q, k, v, g, beta, h0 = (inp[n] for n in ("q", "k", "v", "g", "beta", "h0"))
+    o = torch.empty_like(v)
+    ht = torch.empty_like(h0)
+    ws_bytes = kda.chunk_fwd_workspace_size(1, T, 1, H, dk, dv, io_dtype=kda.KDA_F32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def launch():
+        kda.chunk_fwd(q, k, v, g, beta, h0=h0, o=o, ht=ht, workspace=ws, stream=stream)
+
+    ms = timed_launches(launch, stream, steps, warmup, flush=make_flush(torch, dev))
+    avg = sum(ms) / len(ms)
+    nbytes = algorithmic_bytes(T, H, dk, dv, 4, 4)
+    del inp, q, k, v, g, beta, h0, o, ht, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill_8k in fp32: T={T}, H={H}, d_k=d_v={dk}, fp32 q/k/v, output, "
+                        "g/beta/state, with h0 and final state",
+            "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
+            "roofline": hbm_roofline(nbytes, avg), "algorithmic_bytes_per_call": nbytes,
+            "workspace_bytes": ws_bytes,
+            "kernels": "cbwd_prep_kernel (per-chunk operand blocks) + c16_prefill_kernel (walk)"}
+
+
 def bench_raw(kda, wl, torch, dev, stream, steps, warmup):
     """kda_chunk_fwd_raw on the prefill shape (8192 tokens x 96 heads, d = 128) from raw bf16
     projections: short convolution (width 4), SiLU, L2 input norms and gates fused into the
@@ -491,9 +520,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="prefill,decode,verify_tiny,decode_sweep,segment,varlen,backward",
+    ap.add_argument("--legs",
+                    default="prefill,decode,verify_tiny,decode_sweep,segment,varlen,backward,prefill_f32",
                     help="comma-separated legs to run besides the prefill line (decode, "
-                         "verify_tiny, decode_sweep, segment, varlen, raw, backward); the "
+                         "verify_tiny, decode_sweep, segment, varlen, raw, backward, "
+                         "prefill_f32); the "
                          "prefill leg "
                          "always runs")
     ap.add_argument("--segment-counts", default="0,64,256",
@@ -610,7 +641,8 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, scale)
     legs = set(args.legs.split(","))
-    if legs & {"decode", "verify_tiny", "decode_sweep", "segment", "varlen", "raw", "backward"}:
+    if legs & {"decode", "verify_tiny", "decode_sweep", "segment", "varlen", "raw", "backward",
+               "prefill_f32"}:
         del inp, q, k, v, g, beta, h0, o, ht, ws
         torch.cuda.empty_cache()
     if "decode" in legs:
@@ -633,6 +665,9 @@ def main():
     if "backward" in legs:
         line["backward"] = bench_backward(kda, wl, torch, dev, stream, max(3, args.steps // 4),
                                           min(args.warmup, 1))
+    if "prefill_f32" in legs:
+        line["prefill_f32"] = bench_prefill_f32(kda, wl, torch, dev, stream, args.steps,
+                                                args.warmup)
     if "varlen" in legs:
         line["varlen"] = bench_varlen(kda, wl, torch, dev, stream, max(3, args.steps // 4),
                                       min(args.warmup, 1))

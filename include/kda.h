@@ -83,7 +83,8 @@ typedef enum kda_dtype {
  * same N + 1 int32 offsets) are given, N = n_seqs and T_total = seq_len = cu_seqlens_host[N].
  * Chunks restart at every sequence start; a sequence of length 0 copies h0 to ht.
  *
- * Supported: io_dtype KDA_BF16 with d_k = d_v in {64, 128}; KDA_F32 with d_k = d_v = 64.
+ * Supported: io_dtype KDA_BF16 with d_k = d_v in {64, 128}; KDA_F32 with d_k = d_v in
+ * {64, 128} (fp32 output).
  * g_min must lie in [-5.4, 0] (the in-chunk exponent range stays finite in fp32);
  * g values above 0 are accepted but are not decays. o must not overlap any input; ht may
  * alias h0 (in-place state update).
@@ -113,8 +114,14 @@ typedef enum kda_dtype {
  * group, with the same results. Each walk starts a group's longest sequences first (up to
  * 256 sequences per group; scheduling only, the results do not depend on it). The workspace
  * must be 16-byte aligned and overlap no other
- * argument; its contents on entry are ignored and on return are undefined. KDA_F32 ignores
- * the workspace.
+ * argument; its contents on entry are ignored and on return are undefined. KDA_F32 at
+ * d_k = 64 ignores the workspace (one launch). KDA_F32 at d_k = 128 always takes two launches
+ * through a workspace, in the 16-token chunk form with every product in fp32 on the matrix
+ * cores (the form kda_chunk_bwd uses): (1) per 16-token chunk and head, the decayed tiles
+ * K e^G, K e^(G_C - G), Q e^G, the inverse T, the matrix M, e^(G_C) and beta (26.6 KiB at
+ * d_k = 128); (2) the walk per (sequence, head, four 16-column state tiles), o = scale (Q e^G S0
+ * + M U) per chunk. Without a workspace it returns KDA_ERR_WORKSPACE_TOO_SMALL; the same
+ * grouping of whole sequences applies.
  *
  * State checkpoints (prefix-cache resume points; the prefill hands states on to later
  * requests, "Inférence : cache KV, décodage, quantification", prefill/decode disaggregation):
@@ -143,7 +150,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
  * cu_seqlens_host conventions as kda_chunk_fwd; cu_seqlens_host may be NULL, then packed
  * sequences are sized as if one of them held every token). Slots: a batch or group of
  * sequences with T tokens and N sequences needs (T / 64 + N + 1) x num_heads slots of
- * 74,752 B (d_k = 128) or 50,176 B (d_k = 64). 0 for KDA_F32 and unsupported widths.
+ * 74,752 B (d_k = 128) or 50,176 B (d_k = 64). KDA_F32 at d_k = 128: (T / 16 + N + 1) x
+ * num_heads operand blocks of 27,200 B (the policies as for KDA_BF16, KDA_CHUNK_WS_AUTO
+ * capping the size like a large batch's). 0 for KDA_F32 at d_k = 64 and unsupported widths.
  * KDA_CHUNK_WS_AUTO returns the whole-batch size while the one-launch workgroups
  * (sequences x heads x d_v / 64) do not exceed the current device's compute units (the
  * prologue then sits on every serial chain); beyond that, min(whole batch, max(8 GiB, longest
@@ -165,8 +174,10 @@ int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
  * kda_chunk_fwd. A sequence of T tokens needs floor(T / 64) + 2 slots of 74,752 B per head at
  * d_k = 128 (50,176 B at 64), so it may have up to (floor(KDA_NOALLOC_SCRATCH_BYTES /
  * (74,752 x num_heads)) - 1) x 64 - 1 tokens: 2,303 at 96 heads, 19,071 at 12; a longer one
- * returns KDA_ERR_SCRATCH_TOO_SMALL before anything runs. KDA_F32 runs the one-launch path and
- * uses no scratch.
+ * returns KDA_ERR_SCRATCH_TOO_SMALL before anything runs. KDA_F32 at d_k = 64 runs the
+ * one-launch path and uses no scratch; at d_k = 128 its operand blocks (27,200 B per 16 tokens
+ * and head, floor(T / 16) + 2 per sequence) go in the same array (up to 1,615 tokens per
+ * sequence at 96 heads, 13,135 at 12).
  *
  * The call allocates and frees nothing (no hipMalloc, hipFree or allocating library routine).
  * The first call on a device, with that device current, looks up the array's device address

@@ -56,7 +56,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* g
                      const int32_t* cu_seqlens_host, int batch, int seq_len, int n_seqs,
                      int num_heads, int d_k, int d_v, int io_dtype, int out_dtype,
                      float scale, float g_min, const void* o, const float* ht, int* out_N,
-                     int64_t* out_T, size_t gate_bytes = 4) {
+                     int64_t* out_T, size_t gate_bytes = 4, bool f32_wide = false) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL_ARG;
   if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_BAD_DTYPE;
   if (out_dtype != io_dtype && out_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
@@ -86,7 +86,8 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* g
     return KDA_ERR_BAD_SHAPE;
 
   const bool ok_bf16 = io_dtype == KDA_BF16 && d_k == d_v && (d_k == 64 || d_k == 128);
-  const bool ok_f32 = io_dtype == KDA_F32 && d_k == 64 && d_v == 64;
+  // fp32 inputs: d = 64 everywhere; d = 128 for kda_chunk_fwd (the 16-token chunk form)
+  const bool ok_f32 = io_dtype == KDA_F32 && d_k == d_v && (d_k == 64 || (f32_wide && d_k == 128));
   if (!ok_bf16 && !ok_f32) return KDA_ERR_UNSUPPORTED;
 
   const void* ptrs[] = {q, k, v, g, beta, o, h0, ht};
@@ -317,22 +318,27 @@ int kda_chunk_fwd_workspace_size(int batch, int seq_len, int n_seqs,
   if (batch < 0 || seq_len < 0 || n_seqs < 0 || num_heads <= 0 || d_k <= 0 || d_v <= 0)
     return KDA_ERR_BAD_SHAPE;
   *bytes = 0;
-  if (io_dtype != KDA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_OK;
+  const bool c16 = io_dtype == KDA_F32 && d_k == 128 && d_v == 128;
+  if (!c16 && (io_dtype != KDA_BF16 || d_k != d_v || (d_k != 64 && d_k != 128))) return KDA_OK;
   // packed sequences: batch 1, seq_len = T_total; otherwise n_seqs = batch
   const bool packed = cu_seqlens_host || (batch == 1 && n_seqs != 1);
   const int64_t T = packed ? int64_t(seq_len) : int64_t(batch) * seq_len;
   const int64_t N = packed ? n_seqs : batch;
-  const size_t full = two_pass_workspace_bytes(T, N, num_heads, d_k);
+  auto need = [&](int64_t tokens, int64_t seqs) {
+    return c16 ? kda::c16_prefill_workspace_bytes(tokens, seqs, num_heads, d_k)
+               : two_pass_workspace_bytes(tokens, seqs, num_heads, d_k);
+  };
+  const size_t full = need(T, N);
   // the largest single sequence (a group needs at least that); without the offsets of packed
   // sequences, the whole token count
   const int64_t longest = packed ? (cu_seqlens_host ? max_seq_len(cu_seqlens_host, int(N), 0) : T)
                                  : int64_t(seq_len);
-  const size_t one = two_pass_workspace_bytes(longest, 1, num_heads, d_k);
+  const size_t one = need(longest, 1);
   if (policy == KDA_CHUNK_WS_TWO_PASS) {
     *bytes = full;
   } else if (policy == KDA_CHUNK_WS_MIN) {
     *bytes = one < full ? one : full;
-  } else if (two_pass_wanted(N, num_heads, d_v)) {
+  } else if (!c16 && two_pass_wanted(N, num_heads, d_v)) {
     *bytes = full;
   } else {
     // enough (sequence, head, tile) units to fill the device: groups of sequences through a
@@ -353,7 +359,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
   int64_t T = 0;
   const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
                                   seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
-                                  g_min, o, ht, &N, &T);
+                                  g_min, o, ht, &N, &T, 4, true);
   if (st != KDA_OK) return st;
   if (ckpt_every < 0 || ckpt_every % 64 != 0) return KDA_ERR_BAD_SHAPE;
   if (ckpt_every > 0 && T / ckpt_every == 0) ckpt_every = 0;   // no sequence reaches a slot
@@ -372,6 +378,54 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
         range_of(workspace, workspace ? workspace_bytes : 0)};
     for (Range x : all)
       if (overlaps(rc, x)) return KDA_ERR_ALIASING;
+  }
+  // fp32 at d = 128: the 16-token chunk form, always through a workspace of operand blocks
+  const bool c16 = io_dtype == KDA_F32 && d_k == 128;
+  if (c16) {
+    auto c16_need = [&](int64_t tokens, int64_t seqs) {
+      return kda::c16_prefill_workspace_bytes(tokens, seqs, num_heads, d_k);
+    };
+    const size_t need = c16_need(T, N);
+    const size_t need_min = c16_need(max_seq_len(cu_seqlens_host, N, seq_len), 1);
+    if (!workspace || workspace_bytes < (need_min < need ? need_min : need))
+      return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+    const int rc = check_workspace_aliasing(workspace, workspace_bytes < need ? workspace_bytes : need,
+                                            q, k, v, g, beta, h0, o, ht, T, N, num_heads, d_k, d_v,
+                                            io_dtype, out_dtype);
+    if (rc != KDA_OK) return rc;
+    if (N == 0) return KDA_OK;
+    kda::CBwdParams cp{};
+    cp.q = q;
+    cp.k = k;
+    cp.v = v;
+    cp.g = g;
+    cp.beta = beta;
+    cp.h0 = h0;
+    cp.cu_seqlens = cu_seqlens;
+    cp.seq_len = cu_seqlens ? 0 : seq_len;
+    cp.H = num_heads;
+    cp.n_ct = d_v / 16;
+    cp.scale = scale;
+    cp.g_min = g_min;
+    cp.o = static_cast<float*>(o);
+    cp.ht = ht;
+    cp.ckpt = ckpt_every > 0 ? ckpt_states : nullptr;
+    cp.ckpt_every = ckpt_every > 0 ? ckpt_every : 64;
+    cp.ops = static_cast<float*>(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // consecutive groups of whole sequences whose operand blocks fit the workspace
+    return for_each_group(N, cu_seqlens_host, seq_len, workspace_bytes, c16_need,
+                          [&](int n0, int n1, int64_t tok0, int64_t tokens) {
+                            kda::CBwdParams gp = cp;
+                            gp.seq0 = n0;
+                            gp.slot_tok0 = int(tok0);
+                            gp.n_seqs = n1 - n0;
+                            gp.n_units = (n1 - n0) * num_heads;
+                            gp.T = tokens;
+                            gp.n_slots = kda::cbwd_slots(tokens, n1 - n0);
+                            return launch_status(kda::launch_c16_prefill(gp, d_k, s));
+                          });
   }
   const bool two_pass = workspace != nullptr && io_dtype == KDA_BF16;
   size_t need = 0;
@@ -448,16 +502,18 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
   int64_t T = 0;
   const int st = validate_prefill(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch,
                                   seq_len, n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale,
-                                  g_min, o, ht, &N, &T);
+                                  g_min, o, ht, &N, &T, 4, true);
   if (st != KDA_OK) return st;
-  if (io_dtype != KDA_BF16)   // one launch, no scratch
+  const bool c16 = io_dtype == KDA_F32 && d_k == 128;
+  if (io_dtype != KDA_BF16 && !c16)   // one launch, no scratch
     return kda_chunk_fwd(q, k, v, g, beta, h0, cu_seqlens, cu_seqlens_host, batch, seq_len,
                          n_seqs, num_heads, d_k, d_v, io_dtype, out_dtype, scale, g_min, o, ht,
                          ckpt_every, ckpt_states, nullptr, 0, stream);
   // a group holds at least one whole sequence: the longest one's slots must fit
   const int64_t longest = max_seq_len(cu_seqlens_host, N, seq_len);
-  if (two_pass_workspace_bytes(longest, 1, num_heads, d_k) > KDA_NOALLOC_SCRATCH_BYTES)
-    return KDA_ERR_SCRATCH_TOO_SMALL;
+  const size_t one = c16 ? kda::c16_prefill_workspace_bytes(longest, 1, num_heads, d_k)
+                         : two_pass_workspace_bytes(longest, 1, num_heads, d_k);
+  if (one > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_TOO_SMALL;
   if (N == 0) return KDA_OK;
   void* ws = nullptr;
   const int rc = device_scratch(&ws);

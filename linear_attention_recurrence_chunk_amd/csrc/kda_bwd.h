@@ -1,4 +1,5 @@
-// Launch parameters of the backward of the recurrence (gradients of kda_chunk_fwd's outputs).
+// Launch parameters of the 16-token chunk form of the recurrence on fp32 matrix cores: the
+// backward (gradients of kda_chunk_fwd's outputs) and the fp32 prefill at d = 128.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,6 +22,9 @@ struct CBwdParams {
   const int32_t* cu_seqlens;  // device [N + 1] or null (fixed length seq_len)
   int seq_len, n_seqs, H, n_ct;   // n_ct: 16-column state tiles per head (DV / 16)
   int n_units;              // n_seqs * H
+  // the launch's sequences i = 0 .. n_seqs - 1 are the call's sequences seq0 + i (first token
+  // bos); their chunk slots count from token slot_tok0 (a group of sequences of the prefill)
+  int seq0, slot_tok0;
   long long T;              // tokens in all
   long long n_slots;        // chunk slots: T / 16 + N + 1
   float scale, g_min;
@@ -39,6 +43,11 @@ struct CBwdParams {
   float* dU;                // [slots, H, 16, DV]
   float* dY;                // [slots, H, 16, DV] T^T dU
   float* ops;               // [slots, H, cbwd_op_floats(DK)] per-chunk operand blocks
+  // the prefill's outputs
+  float* o;                 // [T, H, DV]
+  float* ht;                // [N, H, DK, DV] or null
+  float* ckpt;              // [floor(T / ckpt_every), H, DK, DV] or null
+  int ckpt_every;           // a multiple of 64 when ckpt is set
 };
 
 // floats of one (chunk slot, head) operand block: three 16 x dk tiles, two 16 x 16 matrices,
@@ -70,5 +79,14 @@ inline void cbwd_bind_workspace(CBwdParams& p, void* ws, int dk, int dv) {
 }
 
 hipError_t launch_chunk_bwd_mfma(const CBwdParams& p, int io_dtype, int dk, hipStream_t stream);
+
+// Workspace bytes of the fp32 prefill at d = 128 for T tokens in N sequences: the operand blocks
+inline size_t c16_prefill_workspace_bytes(long long T, long long N, int H, int dk) {
+  return size_t(cbwd_slots(T, N)) * H * cbwd_op_floats(dk) * 4;
+}
+
+// The fp32 prefill (o, ht, checkpoints) of the launch's sequences: the operand pass, then the
+// walk. p.ops holds c16_prefill_workspace_bytes of the launch's tokens and sequences.
+hipError_t launch_c16_prefill(const CBwdParams& p, int dk, hipStream_t stream);
 
 }  // namespace kda

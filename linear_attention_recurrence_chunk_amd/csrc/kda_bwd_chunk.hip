@@ -44,9 +44,15 @@ namespace {
 
 constexpr int kC = kCBChunk;
 
-// chunk slot of chunk c of sequence n (whose first token is bos)
-__device__ __forceinline__ long long cb_slot(int bos, int n, int c) {
-  return (long long)(bos / kC) + n + c;
+// chunk slot of chunk c of the launch's sequence i (whose first token is sbos tokens after the
+// launch's slot origin)
+__device__ __forceinline__ long long cb_slot(int sbos, int i, int c) {
+  return (long long)(sbos / kC) + i + c;
+}
+
+// first token of the launch's sequence i (i = n_seqs: the end of the last one)
+__device__ __forceinline__ int seq_first_token(const CBwdParams& p, int i) {
+  return p.cu_seqlens ? p.cu_seqlens[p.seq0 + i] : (p.seq0 + i) * p.seq_len;
 }
 
 template <typename T>
@@ -130,22 +136,20 @@ __device__ __forceinline__ void store_tile16(float* dst, size_t ld, f32x4 a, int
       f32x4{x[0], x[1], x[2], x[3]};
 }
 
-// The chunk that a chunk slot holds: the sequence n (the last one whose first slot
-// floor(bos_n / 16) + n is at most slot), the chunk's first token and length. False for slots
-// that no chunk uses.
+// The chunk that a chunk slot holds: the launch's sequence i (the last one whose first slot
+// floor((bos_i - slot_tok0) / 16) + i is at most slot), the chunk's first token and length.
+// False for slots that no chunk uses.
 __device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, int* cs_out,
                                            int* L_out) {
-  auto first_tok = [&](int i) -> long long {
-    return p.cu_seqlens ? (long long)p.cu_seqlens[i] : (long long)i * p.seq_len;
-  };
+  auto first_tok = [&](int i) -> long long { return seq_first_token(p, i); };
   int lo = 0, hi = p.n_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (first_tok(mid) / kC + mid <= slot) lo = mid;
+    if ((first_tok(mid) - p.slot_tok0) / kC + mid <= slot) lo = mid;
     else hi = mid - 1;
   }
   const long long bos = first_tok(lo), eos = first_tok(lo + 1);
-  const long long c = slot - (bos / kC + lo);
+  const long long c = slot - ((bos - p.slot_tok0) / kC + lo);
   if (c < 0 || bos + kC * c >= eos) return false;
   *cs_out = int(bos + kC * c);
   *L_out = int(min((long long)kC, eos - *cs_out));
@@ -303,20 +307,20 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int h = unit % H, n = unit / H;
-  const int bos = p.cu_seqlens ? p.cu_seqlens[n] : n * p.seq_len;
-  const int eos = p.cu_seqlens ? p.cu_seqlens[n + 1] : bos + p.seq_len;
+  const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
+  const int sbos = bos - p.slot_tok0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
   const int ct = kWalkWaves * sub + w;
   const int col = 16 * ct + ln;
   const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
   const int nch = (eos - bos + kC - 1) / kC;
-  const float* ops0 = p.ops + (size_t(cb_slot(bos, n, 0)) * H + h) * OB::kFloats;
+  const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
   const size_t ops_stride = size_t(H) * OB::kFloats;
-  auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(bos, n, c)) * H + h) * DK * DV; };
+  auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV; };
 
   // the state tile in accumulator layout: block rb, register r = row 16 rb + 4 q4 + r
   f32x4 S[NTD];
-  const size_t st_off = (size_t(n) * H + h) * DK * DV;
+  const size_t st_off = (size_t(p.seq0 + n) * H + h) * DK * DV;
 #pragma unroll
   for (int rb = 0; rb < NTD; ++rb) S[rb] = zero4();
   if (p.h0) {
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
     // stores go out after the wait, so the next wait finds them done.
     wait_vmem();
     lds_barrier();
-    const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
+    const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
     float* wx = p.X0 + blk * kC * DV;
     float* wu = p.U + blk * kC * DV;
 #pragma unroll
@@ -416,18 +420,18 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
   if (unit >= p.n_units) return;
   const int H = p.H;
   const int h = unit % H, n = unit / H;
-  const int bos = p.cu_seqlens ? p.cu_seqlens[n] : n * p.seq_len;
-  const int eos = p.cu_seqlens ? p.cu_seqlens[n + 1] : bos + p.seq_len;
+  const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
+  const int sbos = bos - p.slot_tok0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
   const int ct = kWalkWaves * sub + w;
   const int col = 16 * ct + ln;
   const Tio* gdo = reinterpret_cast<const Tio*>(p.d_o) + size_t(h) * DV;
   const int nch = (eos - bos + kC - 1) / kC;
-  const float* ops0 = p.ops + (size_t(cb_slot(bos, n, 0)) * H + h) * OB::kFloats;
+  const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
   const size_t ops_stride = size_t(H) * OB::kFloats;
 
   f32x4 D[NTD];
-  const size_t st_off = (size_t(n) * H + h) * DK * DV;
+  const size_t st_off = (size_t(p.seq0 + n) * H + h) * DK * DV;
 #pragma unroll
   for (int rb = 0; rb < NTD; ++rb) D[rb] = zero4();
   if (p.dht) {
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
                 dst + OB::kFloats + w * kTile, lane);
   };
   auto store_grad = [&](int c) {
-    float* ds = p.dS + (size_t(cb_slot(bos, n, c)) * H + h) * DK * DV;
+    float* ds = p.dS + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV;
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb) store_tile16(ds + size_t(16 * rb) * DV + 16 * ct, DV, D[rb], lane);
   };
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
       for (int kk = 0; kk < 4; ++kk) dY = mma_f32(cur[OB::kT + (4 * q4 + kk) * 16 + ln], dU[kk], dY);
       const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
       {
-        const size_t blk = size_t(cb_slot(bos, n, c)) * H + h;
+        const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
         store_tile16(p.dU + blk * kC * DV + 16 * ct, DV, dU, lane);
         store_tile16(p.dY + blk * kC * DV + 16 * ct, DV, dY, lane);
         // dv = diag(beta) dY, row-major: lane (q4, ln) stores token 4 q4 + (ln & 3), columns
@@ -521,6 +525,121 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) p.dh0[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col] = D[rb][r];
   }
+}
+
+// ---- the fp32 prefill at d = 128: the forward walk of the same chunk form, producing
+// o = s (Q_G S0 + M U) per chunk, the final state and checkpoints. Workgroups as above (four
+// waves, four 16-column tiles of one (sequence, head)); the whole operand block is staged.
+template <int DK>
+__global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams p) {
+  using Tio = float;
+  constexpr int DV = DK, NTD = DK / 16;
+  using OB = OpBlock<DK>;
+  constexpr int kTile = 64 * int(sizeof(Tio));
+  constexpr int kBuf = OB::kFloats + kWalkWaves * kTile;
+  __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
+
+  int sub;
+  const int unit = block_unit(blockIdx.x, p.n_ct / kWalkWaves, &sub);
+  if (unit >= p.n_units) return;
+  const int H = p.H;
+  const int h = unit % H, n = unit / H;
+  const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
+  const int sbos = bos - p.slot_tok0;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
+  const int ct = kWalkWaves * sub + w;
+  const int col = 16 * ct + ln;
+  const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
+  const int nch = (eos - bos + kC - 1) / kC;
+  const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
+  const size_t ops_stride = size_t(H) * OB::kFloats;
+  const int sl = swz(ln);
+
+  f32x4 S[NTD];
+  const size_t st_off = (size_t(p.seq0 + n) * H + h) * DK * DV;
+#pragma unroll
+  for (int rb = 0; rb < NTD; ++rb) S[rb] = zero4();
+  if (p.h0) {
+#pragma unroll
+    for (int rb = 0; rb < NTD; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[rb][r] = p.h0[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col];
+  }
+  // the state, row-major at dst (this wave's 16 columns)
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int rb = 0; rb < NTD; ++rb) store_tile16(dst + size_t(16 * rb) * DV + 16 * ct, DV, S[rb], lane);
+  };
+  auto stage = [&](int c, float* dst) {
+    const int cs = bos + kC * c;
+    stage_block_half<OB::kFloats / 4>(ops0 + c * ops_stride, dst, w, lane);
+    stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct, dst + OB::kFloats + w * kTile,
+                lane);
+  };
+  // K S with the [16][DK] tile at offset off of buffer b (k order: the state's register order)
+  auto tile_times_state = [&](const float* b, int off) {
+    f32x4 x = zero4();
+#pragma unroll
+    for (int rb = 0; rb < NTD; ++rb) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(b + off + ln * DK + ((16 * rb + 4 * q4) ^ sl));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x = mma_f32(a[r], S[rb][r], x);
+    }
+    return x;
+  };
+  if (nch > 0) {
+    stage(0, sb0);
+    wait_vmem();
+    lds_barrier();
+  }
+  for (int c = 0; c < nch; ++c) {
+    const float* cur = (c & 1) ? sb1 : sb0;
+    stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
+    const int cs = bos + kC * c, L = min(kC, eos - cs);
+    // X = K_G S and the inter-chunk part of the output, Q_G S
+    const f32x4 X = tile_times_state(cur, OB::kKG);
+    f32x4 O = tile_times_state(cur, OB::kQG);
+    // X0 = V - X, Y = diag(beta) X0 (rows past a ragged chunk's end are zero), U = T Y
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
+    const Tio* vt = reinterpret_cast<const Tio*>(cur + OB::kFloats + w * kTile);
+    f32x4 Y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Y[r] = bt[r] * ((vt[(4 * q4 + r) * 16 + ln] - X[r]) * keep_f(4 * q4 + r < L));
+    f32x4 U = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) U = mma_f32(cur[OB::kT + ln * 16 + 4 * q4 + kk], Y[kk], U);
+    // the intra-chunk part, M U
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) O = mma_f32(cur[OB::kM + ln * 16 + 4 * q4 + kk], U[kk], O);
+    // S = e^(G_C) S + K^^T U
+#pragma unroll
+    for (int rb = 0; rb < NTD; ++rb) {
+      S[rb] *= *reinterpret_cast<const f32x4*>(cur + OB::kEGC + 16 * rb + 4 * q4);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int t = 4 * q4 + kk;
+        S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
+      }
+    }
+    wait_vmem();
+    lds_barrier();
+    {
+      // o rows of this chunk: after a quad transpose lane (q4, ln) holds token
+      // 4 q4 + (ln & 3), columns 4 (ln >> 2) .. + 3 of this tile
+      float x[4] = {O[0], O[1], O[2], O[3]};
+      quad_transpose(x, lane);
+      const int t = 4 * q4 + (ln & 3);
+      if (t < L)
+        *reinterpret_cast<f32x4*>(p.o + (size_t(cs + t) * H + h) * DV + 16 * ct + 4 * (ln >> 2)) =
+            f32x4{p.scale * x[0], p.scale * x[1], p.scale * x[2], p.scale * x[3]};
+    }
+    // the state after a multiple of ckpt_every tokens of the sequence
+    const int done = kC * (c + 1);
+    if (p.ckpt && done <= eos - bos && done % p.ckpt_every == 0)
+      store_state(p.ckpt + (size_t(bos / p.ckpt_every + done / p.ckpt_every - 1) * H + h) * DK * DV);
+  }
+  if (p.ht) store_state(p.ht + st_off);
 }
 
 // ---- 3. gradients of one chunk: dq, dk, dbeta and dg. One workgroup (DK / 16 waves) per
@@ -775,6 +894,20 @@ static hipError_t launch_cbwd(const CBwdParams& p, hipStream_t stream) {
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((cbwd_grad_kernel<Tio, DK>), chunks, dim3(4 * DK), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_c16_prefill(const CBwdParams& p, int dk, hipStream_t stream) {
+  if (dk != 128 || p.n_ct != dk / 16 || p.n_ct % kWalkWaves != 0 ||
+      p.n_units != p.n_seqs * p.H || p.H < 1 || p.n_seqs < 1 || !p.ops || !p.o ||
+      (p.ckpt && (p.ckpt_every < 64 || p.ckpt_every % 64 != 0)) || p.n_slots * p.H > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  const dim3 walk((p.n_units + 7) / 8 * 8 * (p.n_ct / kWalkWaves));
+  hipLaunchKernelGGL((cbwd_prep_kernel<float, 128>), dim3(unsigned(p.n_slots * p.H)), dim3(128), 0,
+                     stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((c16_prefill_kernel<128>), walk, dim3(64 * kWalkWaves), 0, stream, p);
   return hipGetLastError();
 }
 

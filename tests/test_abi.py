@@ -84,7 +84,8 @@ def test_chunk_dtype_shape_value_checks():
     assert chunk(n_seqs=2) == SHAPE                             # batch 1 without cu_seqlens
     assert chunk(dk=96, dv=96) == UNSUP
     assert chunk(dk=128, dv=64) == UNSUP
-    assert chunk(io=F32, dk=128, dv=128) == UNSUP
+    assert chunk(io=F32, dk=128, dv=64) == UNSUP
+    assert chunk(io=F32, dk=128, dv=128) == WS                  # fp32 at d = 128 needs a workspace
     assert chunk(g_min=-6.0) == VALUE
     assert chunk(g_min=0.5) == VALUE
     assert chunk(scale=float("nan")) == VALUE
@@ -133,7 +134,16 @@ def test_chunk_workspace_size():
     assert chunk_ws_size(seq_len=1000, n_seqs=5, H=3) == (OK, (1000 // 64 + 5 + 1) * 3 * slot128)
     assert chunk_ws_size(batch=4, seq_len=300, n_seqs=4, H=2, dk=64, dv=64) == (
         OK, (1200 // 64 + 4 + 1) * 2 * slot64)
-    # fp32 and unsupported widths never take the two-launch path
+    # fp32 at d = 128: operand blocks of the 16-token chunk form, (T / 16 + N + 1) x heads x
+    # (three 16 x 128 tiles, two 16 x 16 matrices, 128 decay factors, 16 betas) fp32
+    block = (3 * 16 * 128 + 2 * 256 + 128 + 16) * 4
+    assert chunk_ws_size(io=F32) == (OK, (8192 // 16 + 1 + 1) * 96 * block)
+    arr, cu = host_cu([0, 100, 1100, 1300])
+    assert chunk_ws_size(io=F32, seq_len=1300, n_seqs=3, H=3, policy=2, cu=cu) == (
+        OK, (1000 // 16 + 1 + 1) * 3 * block)
+    assert chunk_ws_size(io=F32, seq_len=1300, n_seqs=3, H=3, policy=0, cu=cu) == (
+        OK, (1300 // 16 + 3 + 1) * 3 * block)
+    # fp32 at d = 64 and unsupported widths never take a two-launch path
     assert chunk_ws_size(io=F32, dk=64, dv=64) == (OK, 0)
     assert chunk_ws_size(io=F32, dk=64, dv=64, policy=0) == (OK, 0)
     assert chunk_ws_size(dk=96, dv=96) == (OK, 0)
@@ -158,8 +168,13 @@ def test_chunk_workspace_checks():
     assert chunk(override=dict(ws=ws, ws_bytes=need - 16)) == WS     # one sequence: all of it
     assert chunk(override=dict(ws=P[2], ws_bytes=need)) == ALIAS          # overlaps v
     assert chunk(override=dict(ws=ctypes.c_void_p(P[5].value - 1024), ws_bytes=need)) == ALIAS
-    # an fp32 call ignores the workspace, as documented
+    # an fp32 call at d = 64 ignores the workspace, as documented
     assert chunk(io=F32, dk=64, dv=64, q=False, override=dict(ws=ws, ws_bytes=0)) == NULL
+    # fp32 at d = 128: the workspace is required, aligned, large enough, and overlaps nothing
+    _, need32 = chunk_ws_size(seq_len=256, H=2, io=F32)
+    assert chunk(io=F32, override=dict(ws=ws, ws_bytes=need32 - 16)) == WS
+    assert chunk(io=F32, override=dict(ws=ctypes.c_void_p(ws.value + 8), ws_bytes=need32)) == ALIGN
+    assert chunk(io=F32, override=dict(ws=P[2], ws_bytes=need32)) == ALIAS
 
 
 def test_chunk_checkpoint_checks():

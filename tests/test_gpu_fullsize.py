@@ -15,7 +15,7 @@ import linear_attention_recurrence_chunk_amd as kda
 from linear_attention_recurrence_chunk_amd import workloads as wl
 from oracle import c_recurrence_fwd
 from oracle import kda_oracle as ko
-from kda_testutil import TOL_BF16, np64, rel_max_err
+from kda_testutil import TOL_BF16, TOL_F32, np64, rel_max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,26 @@ def test_prefill_8k_full():
     e_s = rel_max_err(_host_heads(ht32, heads), ht_ref)
     print(f"all {H} heads: err_o={e_o:.3e} err_state={e_s:.3e}")
     assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+
+def test_prefill_8k_full_f32():
+    """The prefill_8k shape with fp32 inputs (the 16-token chunk form on fp32 matrix cores at
+    d = 128), every head against the oracle at the fp32 bar."""
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    print(f"case prefill_8k fp32 T={T} H={H} d={dk}", flush=True)
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype="f32", seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device="cuda")
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    o32, ht32 = kda.chunk_fwd(*args, h0=inp["h0"])
+    torch.cuda.synchronize()
+    heads = list(range(H))
+    o_ref, ht_ref = c_recurrence_fwd(*[_host_heads(x, heads) for x in args],
+                                     h0=_host_heads(inp["h0"], heads))
+    e_o = rel_max_err(_host_heads(o32, heads), o_ref)
+    e_s = rel_max_err(_host_heads(ht32, heads), ht_ref)
+    print(f"all {H} heads: err_o={e_o:.3e} err_state={e_s:.3e}")
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
 
 
 _ULTRALONG = {}
