@@ -1,5 +1,5 @@
-// Chunked backward of the KDA recurrence on gfx950: 16-token chunks, every product on fp32
-// matrix cores (v_mfma_f32_16x16x4_f32).
+// The KDA recurrence in 16-token chunks on gfx950, every product on fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32): the backward, and the fp32 prefill at d = 128.
 //
 // The pages give the forward only ("Noyaux KDA et FlashKDA", section "FlashKDA : le noyau par
 // blocs": the chunked kernel serves training as well as prefill). This file differentiates the
@@ -24,7 +24,7 @@
 // inside fp32 (|G| <= 16 x 5.4); the pairwise factors e^(G_t - G_s) are formed as
 // e^(G_t - G_m) e^(G_m - G_s) around the chunk's mid value G_m, so no factor exceeds e^44.
 //
-// Four launches:
+// The backward's four launches:
 //   0. cbwd_prep_kernel: one workgroup per (chunk, head) forms the chunk's operand block: the
 //      decayed tiles K_G, K^, Q_G, T, M, e^(G_C) and beta;
 //   1. cbwd_fwd_kernel: one wave per (sequence, head, 16-column tile) walks the chunks
@@ -32,6 +32,8 @@
 //   2. cbwd_rev_kernel: the same waves walk back, storing dS (the gradient of the state
 //      leaving each chunk), dU and dY, writing dv, and dh0 at the sequence start;
 //   3. cbwd_grad_kernel: one workgroup per (chunk, head) forms dq, dk, dbeta and dg.
+// The fp32 prefill: the same operand pass, then c16_prefill_kernel, the forward walk producing
+// o = s (Q_G S0 + M U), the final state and checkpoints.
 // The walks stage each chunk's operand block into LDS (global-to-LDS loads) while the previous
 // chunk is computed, so their chains hold the state products only. Sums over value columns
 // happen inside launch 3 in a fixed order: results are deterministic.
