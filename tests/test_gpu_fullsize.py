@@ -79,6 +79,33 @@ def test_prefill_8k_full_f32():
     assert e_o <= TOL_F32 and e_s <= TOL_F32
 
 
+def test_backward_8k_full_sampled_heads():
+    """kda_chunk_bwd on the backward leg's workload (8192 tokens x 96 heads, d = 128, bf16,
+    the same seeded inputs, output and final-state gradients), every gradient of heads 0 and
+    95 against the oracle's per-token backward (one head at a time: it keeps every token's
+    state)."""
+    cfg = wl.CONFIGS["prefill_8k"]
+    T, H, dk, dv = cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    print(f"case backward 8k full T={T} H={H} d={dk}", flush=True)
+    dev = torch.device("cuda")
+    inp = wl.prefill_inputs(T=T, H=H, dk=dk, dv=dv, dtype=cfg["dtype"], seed=cfg["seed"],
+                            h0_std=cfg["h0_std"], device=dev)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    do = torch.randn(T, H, dv, device=dev, generator=gen).to(torch.bfloat16)
+    dht = torch.randn(1, H, dk, dv, device=dev, generator=gen)
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    got = kda.chunk_bwd(*args, do, dht=dht, h0=inp["h0"])
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        sl = [h]
+        ref = ko.recurrence_bwd(*[_host_heads(x, sl) for x in args], _host_heads(do, sl),
+                                dht=_host_heads(dht, sl), h0=_host_heads(inp["h0"], sl))
+        for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            e = rel_max_err(_host_heads(got[name], sl), ref[name])
+            print(f"head {h} {name}: err {e:.3e}", flush=True)
+            assert e <= TOL_BF16, (h, name)
+
+
 _ULTRALONG = {}
 
 
