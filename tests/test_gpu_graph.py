@@ -124,3 +124,55 @@ def test_raw_prefill_in_a_graph():
                           cu_seqlens_host=cu_host, workspace=ws, o=o, ht=ht,
                           conv_tail_out=tail, stream=torch.cuda.current_stream())
     _replays_match(graph, (o, ht, tail), (o_ref, ht_ref, tail_ref))
+
+
+def test_backward_in_a_graph():
+    """kda_chunk_bwd (four launches) captured: every replay gives the eager gradients."""
+    print("case graph: backward T=300 H=2 d=128 packed", flush=True)
+    lengths = [200, 0, 100]
+    d = to_dev(wl.prefill_inputs(H=2, dk=128, dv=128, dtype="bf16", seed=103, h0_std=0.02,
+                                 lengths=lengths))
+    args = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    gen = torch.Generator(device="cuda").manual_seed(104)
+    do = torch.randn(300, 2, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    dht = torch.randn(3, 2, 128, 128, device="cuda", generator=gen)
+    cu = d["cu_seqlens"]
+    cu_host = cu.to("cpu")
+    ws = torch.empty(kda.chunk_bwd_workspace_size(1, 300, 3, 2, 128, 128), dtype=torch.uint8,
+                     device="cuda")
+    ref = kda.chunk_bwd(*args, do, dht=dht, h0=d["h0"], cu_seqlens=cu, workspace=ws,
+                        cu_seqlens_host=cu_host)
+    ref = {n: x.clone() for n, x in ref.items()}
+    outs = {n: torch.empty_like(x) for n, x in ref.items()}
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        got = kda.chunk_bwd(*args, do, dht=dht, h0=d["h0"], cu_seqlens=cu, workspace=ws,
+                            cu_seqlens_host=cu_host, stream=torch.cuda.current_stream())
+        for n in outs:
+            outs[n].copy_(got[n])
+    names = sorted(ref)
+    _replays_match(graph, [outs[n] for n in names], [ref[n] for n in names])
+
+
+def test_fp32_wide_prefill_in_a_graph():
+    """kda_chunk_fwd with fp32 inputs at d = 128 (operand pass and walk) captured."""
+    print("case graph: fp32 prefill T=300 H=2 d=128", flush=True)
+    d = to_dev(wl.prefill_inputs(T=300, H=2, dk=128, dv=128, dtype="f32", seed=105,
+                                 h0_std=0.02))
+    args = [d[n] for n in ("q", "k", "v", "g", "beta")]
+    ws = torch.empty(kda.chunk_fwd_workspace_size(1, 300, 1, 2, 128, 128,
+                                                  io_dtype=kda.KDA_F32),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(300, 2, 128, dtype=torch.float32, device="cuda")
+    ht = torch.empty(1, 2, 128, 128, dtype=torch.float32, device="cuda")
+    o_ref, ht_ref = kda.chunk_fwd(*args, h0=d["h0"], workspace=ws)
+    o_ref, ht_ref = o_ref.clone(), ht_ref.clone()
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        kda.chunk_fwd(*args, h0=d["h0"], o=o, ht=ht, workspace=ws,
+                      stream=torch.cuda.current_stream())
+    _replays_match(graph, [o, ht], [o_ref, ht_ref])
