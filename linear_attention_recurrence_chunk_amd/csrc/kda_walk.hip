@@ -48,6 +48,14 @@ struct WalkPlan {
   static constexpr __host__ __device__ int count(int s) {
     return (kind(s) == kT || kind(s) == kM) ? (pp(s) == 0 ? 8 : 4) : 4;
   }
+  // the slot blocks the walk reads, in fetch order (without outputs: no Q e^Gamma and no M)
+  static constexpr int kFetched = kOut ? OS::kBlocks : 4 * NS + 12 + (OS::kBlocks - OS::fKh);
+  static constexpr __host__ __device__ int fetched(int j) {
+    return kOut ? j
+         : j < 4 * NS ? OS::fKg + j
+         : j < 4 * NS + 12 ? OS::fT + (j - 4 * NS)
+         : OS::fKh + (j - 4 * NS - 12);
+  }
   // fragment k of stage s
   static constexpr __host__ __device__ int frag(int s, int k) {
     const int kd = kind(s), p = pp(s);
@@ -67,8 +75,13 @@ struct WalkPlan {
 // the chunk kernel's serial step, operation for operation, so the two paths agree bit for bit.
 // Slots stream into two LDS buffers by direct global-to-LDS loads: the next chunk's slot is in
 // flight while the current one is consumed, and the next chunk's values load into registers.
-template <typename Tio, typename Tout, int DK, bool kOut, int kTPW>
-__global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
+// kMem (one state tile per workgroup): a fifth wave issues every slot load. A 1 KiB
+// global-to-LDS load occupies the compute unit's vector-memory queue for tens of cycles, and a
+// wave stalls in order until the queue takes its load; the waves that compute would otherwise
+// spend about a quarter of each chunk step issuing them. The fifth wave shares a SIMD with one
+// of them, so every wave is held to 256 registers and the fragment look-ahead is one stage.
+template <typename Tio, typename Tout, int DK, bool kOut, int kTPW, bool kMem>
+__global__ __launch_bounds__(256 * kTPW + (kMem ? 64 : 0)) void chunk_walk_kernel(ChunkParams p) {
   using Pol = PolBF16;
   using Frag = typename Pol::Frag;
   using FragR = typename Pol::FragR;
@@ -127,6 +140,32 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
   const int col0 = vt * VT + 16 * w;   // first state column owned by this wave
   const int ldS = kOut ? DV : DK + DV;   // row stride of the state this tile writes
   Tout* __restrict__ go = reinterpret_cast<Tout*>(p.o);
+  using Plan = WalkPlan<DK, kOut>;
+
+  if constexpr (kMem) {
+    if (wid == 4 * kTPW) {
+      // the load wave: moves each chunk's slot into LDS a chunk ahead (the waves that compute
+      // issue no slot loads, so they never stall on the memory pipeline's queue for them)
+      auto fetch_all = [&](int ci, char* dst) {
+        const char* src = ws_head + size_t(ci) * slot_stride;
+#pragma unroll
+        for (int jf = 0; jf < Plan::kFetched; ++jf) {
+          const int f = Plan::fetched(jf);
+          __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024 + lane * 16, dst + f * 1024, 16,
+                                           0, 0);
+        }
+      };
+      if (nchunks > 0) fetch_all(0, smem);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      for (int ci = 0; ci < nchunks; ++ci) {
+        if (ci + 1 < nchunks) fetch_all(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+      }
+      return;
+    }
+  }
 
   // ---- entering state in accumulator layout: tile t, register e = row 16t + 4 q4 + e
   f32x4 S[NTD];
@@ -191,7 +230,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
     }
   };
   if (nchunks > 0) {
-    fetch_slot(0, smem);
+    if constexpr (!kMem) fetch_slot(0, smem);
     if (!p_tile)
       load_chunk_any<kLoadV, Tio, DK>(raw, p, bos, min(kChunk, eos - bos), w, lane, h, vcol0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -219,7 +258,6 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
     }
   };
 
-  using Plan = WalkPlan<DK, kOut>;
   using V16 = int __attribute__((ext_vector_type(4)));
   f32x4 O[4];
   for (int ci = 0; ci < nchunks; ++ci) {
@@ -228,7 +266,9 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
     const char* cur = smem + (ci & 1) * OS::kBytes;
     const bool more = ci + 1 < nchunks;
     // the next slot streams in behind this chunk (issued first: it has the whole chunk to land)
-    if (more) fetch_slot(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
+    if constexpr (!kMem) {
+      if (more) fetch_slot(ci + 1, smem + ((ci + 1) & 1) * OS::kBytes);
+    }
 
     // the state as fp16 B fragments (both products with decayed keys and queries), then its
     // decay for the update: S is not read again before S += K^T U
@@ -248,7 +288,7 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
     // from LDS two stages ahead of its MFMAs, into three rotating register buffers.
     // stages of fragment look-ahead: two with one wave per SIMD; one with two waves per SIMD
     // (both waves' registers fit the SIMD's file only then)
-    constexpr int kAhead = kTPW == 1 ? 2 : 1;
+    constexpr int kAhead = kTPW == 1 && !kMem ? 2 : 1;
     V16 fb[kAhead + 1][8];
     auto load_stage = [&](int st, V16* dst) {
 #pragma unroll
@@ -357,12 +397,14 @@ __global__ __launch_bounds__(256 * kTPW) void chunk_walk_kernel(ChunkParams p) {
 // Tv: the values' type (bf16 inputs, or the fp32 convolved values of the raw prefill)
 template <typename Tv, typename Tout, int DK, int kTPW>
 static hipError_t launch_walk_tpw(const ChunkParams& p, hipStream_t stream) {
+  // one state tile per workgroup: four waves that compute and a fifth that loads the slots
+  constexpr bool kMem = kTPW == 1;
   const dim3 grid((p.n_units + 7) / 8 * 8 * (p.n_vt / kTPW));
-  const dim3 block(256 * kTPW);
+  const dim3 block(256 * kTPW + (kMem ? 64 : 0));
   if (p.mode == kModeTransition)
-    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, false, kTPW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, false, kTPW, kMem>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, true, kTPW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chunk_walk_kernel<Tv, Tout, DK, true, kTPW, kMem>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
