@@ -1305,19 +1305,108 @@ __device__ __forceinline__ void prep_am_finish(const f32x4 (&accA)[4], const f32
   }
 }
 
+// A 32-bit word moved from lane l ^ 1 (quad_perm), l ^ 8 (row rotation by eight) or l ^ 4
+// (swizzle) of the wave.
+__device__ __forceinline__ uint32_t word_xor1(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), kQuadXor1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t word_xor8(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t word_xor4(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_ds_swizzle(int(x), 0x101F));   // and 0x1f, xor 4
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
+
+// The prep pass's Q e^Gamma and K e^Gamma of one channel pass (products qv fs, kv fs rounded
+// to fp16 as before, then exchanged, not recomputed) written as whole 16-byte lane rows of
+// their fragments. Thread (grp, li) holds channels c0 .. c0 + CPT - 1 of tokens rb0 .. rb0 +
+// TPT - 1. With CPT = 2 the partner l ^ 1 holds channels c0 ^ 2 and l ^ 8 channels c0 ^ 16;
+// with CPT = 4 the partner l ^ 4 holds channels c0 ^ 16.
+template <int DK, int CPT, int TPT>
+__device__ __forceinline__ void store_qk_rows(const float (&qv)[TPT][CPT],
+                                              const float (&kv)[TPT][CPT], const float (&fs)[CPT],
+                                              char* fq, char* fk, int w, int li, int rb0, int c0,
+                                              int lane) {
+  constexpr int NS = DK / 32;
+  static_assert((CPT == 2 && TPT == 8) || (CPT == 4 && TPT == 4), "prep thread map");
+  // u[m][t][j]: word j (channels 2 j, 2 j + 1 of the thread) of token t, matrix m (q, k)
+  uint32_t u[2][TPT][CPT / 2];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t)
+#pragma unroll
+    for (int j = 0; j < CPT / 2; ++j) {
+      u[0][t][j] = pack_f16x2(qv[t][2 * j] * fs[2 * j], qv[t][2 * j + 1] * fs[2 * j + 1]);
+      u[1][t][j] = pack_f16x2(kv[t][2 * j] * fs[2 * j], kv[t][2 * j + 1] * fs[2 * j + 1]);
+    }
+  // p[m][i]: channels 4 q .. 4 q + 3 (two words) of token tok1(i), four of them
+  uint32_t pw[2][4][2];
+  int tok1_base;
+  if constexpr (CPT == 2) {
+    // lanes l and l ^ 1: the even one keeps tokens 0..3 and takes its partner's words of
+    // them, the odd one keeps tokens 4..7
+    const bool odd = (lane & 1) != 0;
+    tok1_base = odd ? 4 : 0;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = word_xor1(odd ? u[m][i][0] : u[m][4 + i][0]);
+        pw[m][i][0] = odd ? r : u[m][i][0];
+        pw[m][i][1] = odd ? u[m][4 + i][0] : r;
+      }
+  } else {
+    tok1_base = 0;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[m][i][0] = u[m][i][0];
+        pw[m][i][1] = u[m][i][CPT / 2 - 1];
+      }
+  }
+  // lanes holding channel groups 4 q and 16 + 4 q: the lower keeps tokens 0, 1 of its four,
+  // the upper tokens 2, 3; each ends with two 16-byte rows
+  const bool up = CPT == 2 ? (lane & 8) != 0 : (lane & 4) != 0;
+  const int q = CPT == 2 ? (li % 8) / 2 : li % 4;
+  const int slice = c0 / 32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int tt = tok1_base + (up ? 2 : 0) + i;
+    const int r = rb0 + tt;
+    char* dq = fq + size_t(w * NS + slice) * 1024 + size_t(16 * q + r % 16) * 16;
+    char* dk = fk + size_t(w * NS + slice) * 1024 + size_t(16 * q + r % 16) * 16;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t r0, r1;
+      if constexpr (CPT == 2) {
+        r0 = word_xor8(up ? pw[m][i][0] : pw[m][2 + i][0]);
+        r1 = word_xor8(up ? pw[m][i][1] : pw[m][2 + i][1]);
+      } else {
+        r0 = word_xor4(up ? pw[m][i][0] : pw[m][2 + i][0]);
+        r1 = word_xor4(up ? pw[m][i][1] : pw[m][2 + i][1]);
+      }
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 row = up ? u32x4{r0, r1, pw[m][2 + i][0], pw[m][2 + i][1]}
+                           : u32x4{pw[m][i][0], pw[m][i][1], r0, r1};
+      *reinterpret_cast<u32x4*>(m == 0 ? dq : dk) = row;
+    }
+  }
+}
+
 template <int DK>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
-  using Pol = PolBF16;
   using L = PrepLayout<DK>;
   using OS = OpSlot<DK>;
   using PM = ProMap<DK>;
   constexpr int TPT = PM::kTPT;          // tokens per thread
   constexpr int NPASS = DK / 64;         // channel passes
   constexpr int CPT = 4 / NPASS;         // channels per thread and pass
-  constexpr int NS = DK / 32;
   using GV = float __attribute__((ext_vector_type(CPT)));
   using BV = __bf16 __attribute__((ext_vector_type(CPT)));
-  using HV = _Float16 __attribute__((ext_vector_type(CPT)));
 
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   __bf16* sQr = reinterpret_cast<__bf16*>(smem + L::oQr);
@@ -1497,22 +1586,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(ChunkParams p) {
           }
           if (w == 0 && grp == 0) sDecay[c0 + c] = pb[0] * pb[1] * pb[2] * pb[3];
         }
-        // channel c0 of token row r: lane 16 ((c0 % 16) / 4) + r % 16 of fragment
-        // (r / 16, c0 / 32), bytes from 8 ((c0 % 32) / 16) + 2 (c0 % 4)
-        const size_t fbase = size_t(w * NS + c0 / 32) * 1024 + size_t((c0 % 16) / 4) * 256 +
-                             ((c0 % 32) / 16) * 8 + (c0 % 4) * 2;
-#pragma unroll
-        for (int t = 0; t < TPT; ++t) {
-          HV xq, xk;
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) {
-            xq[c] = (_Float16)(qv[t][c] * fs[c]);
-            xk[c] = (_Float16)(kv[t][c] * fs[c]);
-          }
-          const size_t o = fbase + size_t((rb0 + t) % 16) * 16;
-          *reinterpret_cast<HV*>(slot + size_t(OS::fQg) * 1024 + o) = xq;
-          *reinterpret_cast<HV*>(slot + size_t(OS::fKg) * 1024 + o) = xk;
-        }
+        // Channel c0 of token row r sits in lane 16 ((c0 % 16) / 4) + r % 16 of fragment
+        // (r / 16, c0 / 32), bytes from 8 ((c0 % 32) / 16) + 2 (c0 % 4): a lane's 16 bytes are
+        // channels 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3 of one token, held here by two
+        // (d_k = 64) or four (d_k = 128) threads. They swap fp16 words across lanes (DPP, or
+        // a swizzle for the lane distance 4) until each holds whole 16-byte rows of two tokens,
+        // so both operands leave with two 16-byte stores a thread instead of one store per
+        // token (the vector-memory queue takes one instruction per 64 lanes whatever its width).
+        store_qk_rows<DK, CPT, TPT>(qv, kv, fs, slot + size_t(OS::fQg) * 1024,
+                                    slot + size_t(OS::fKg) * 1024, w, li, rb0, c0, lane);
         // channel row c0 + c, tokens rb0 + t4 .. + 3: lane 16 ((token % 16) / 4) + channel % 16
         // of fragment (channel / 16, token / 32), bytes from 8 ((token % 32) / 16)
 #pragma unroll
