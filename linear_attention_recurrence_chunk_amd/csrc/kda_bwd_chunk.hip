@@ -272,11 +272,11 @@ __global__ __launch_bounds__(DK) void cbwd_prep_kernel(CBwdParams p) {
 
 // The walks: a workgroup of four waves per (sequence, head, group of four 16-column tiles);
 // wave w owns tile 4 sub + w. The waves walk the same chunks and share each chunk's operand
-// block in LDS, double-buffered: while a chunk is computed, the next chunk's block (a quarter
-// of it staged by each wave) and each wave's own 16 x 16 input tile are copied in. One barrier
-// per chunk publishes the staged buffer and frees the one just read. (At 8192 x 96, d = 128:
-// 192 workgroups, one per CU and one wave per SIMD; with two waves per workgroup, 384 of them,
-// the backward took 7.6 instead of 6.5 ms.)
+// block in LDS, double-buffered: while a chunk is computed, the next chunk's block and the
+// 16 x 16 input tiles are copied in. One barrier per chunk publishes the staged buffer and
+// frees the one just read. (At 8192 x 96, d = 128: 192 workgroups, one per CU and one
+// computing wave per SIMD; with two waves per workgroup, 384 of them, the backward took 7.6
+// instead of 6.5 ms.)
 constexpr int kWalkWaves = 4;
 
 // Copies a block of N4 16-byte units from global src to LDS dst, 64 units per instruction;
@@ -294,15 +294,69 @@ __device__ __forceinline__ void stage_block_half(const float* src, float* dst, i
   }
 }
 
+// The backward's two walks add two waves to the four that compute: wave kLoader stages each
+// chunk's operand block and input tiles into LDS a chunk ahead, and wave kStorer writes the
+// results the computing waves leave in LDS (double-buffered, one buffer per chunk parity) to
+// global memory. A 16-byte store or a 1 KiB global-to-LDS load holds the compute unit's
+// vector-memory queue for tens of cycles and a wave stalls in order until the queue takes it;
+// in the computing waves these stalls took 35-45% of each chunk step. Each of the two waves
+// waits only for its own accesses (the loader for its loads before each barrier; the
+// storer's stores are never waited for), and all six pass the same barriers.
+constexpr int kLoader = kWalkWaves, kStorer = kWalkWaves + 1;
+constexpr int kWalkThreads = 64 * (kWalkWaves + 2);
+constexpr int kOutLd = 68;   // row stride (floats) of the LDS result tiles: 64 columns + 4
+
+// All N4 16-byte units of a block, issued by one wave.
+template <int N4>
+__device__ __forceinline__ void stage_block_all(const float* src, float* dst, int lane) {
+#pragma unroll
+  for (int w = 0; w < kWalkWaves; ++w) stage_block_half<N4>(src, dst, w, lane);
+}
+
+// A 16 x 16 accumulator tile into a row-major LDS tile of kOutLd-float rows, 16 bytes a lane
+// (the quad transpose of store_tile16).
+__device__ __forceinline__ void put_tile16(float* dst, f32x4 a, int lane) {
+  float x[4] = {a[0], a[1], a[2], a[3]};
+  quad_transpose(x, lane);
+  const int q4 = (lane >> 4) & 3, ln = lane & 15;
+  *reinterpret_cast<f32x4*>(dst + (4 * q4 + (ln & 3)) * kOutLd + 4 * (ln >> 2)) =
+      f32x4{x[0], x[1], x[2], x[3]};
+}
+
+// The storer's copy of `rows` rows of a workgroup's 64 columns from an LDS result tile to
+// row-major global memory (rows ld floats apart): 4 rows per instruction, eight loads from LDS
+// in flight ahead of their stores. Rows at or past `keep` are not written.
+template <int kRows>
+__device__ __forceinline__ void copy_rows(const float* src, float* dst, size_t ld, int keep,
+                                          int lane) {
+  const int rr = lane >> 4, cc = 4 * (lane & 15);
+  constexpr int kGroup = kRows / 4 < 8 ? kRows / 4 : 8;
+#pragma unroll
+  for (int i0 = 0; i0 < kRows / 4; i0 += kGroup) {
+    f32x4 v[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+      v[j] = *reinterpret_cast<const f32x4*>(src + (4 * (i0 + j) + rr) * kOutLd + cc);
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int row = 4 * (i0 + j) + rr;
+      if (row < keep) *reinterpret_cast<f32x4*>(dst + size_t(row) * ld + cc) = v[j];
+    }
+  }
+}
+
 // ---- 1. forward walk: S0, X0 and U of every chunk
 template <typename Tio, int DK>
-__global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p) {
+__global__ __launch_bounds__(kWalkThreads) void cbwd_fwd_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
   using OB = OpBlock<DK>;
-  // per buffer: the block's first kFwd floats, then each wave's 16 x 16 value tile
+  // per buffer: the block's first kFwd floats, then the four 16 x 16 value tiles
   constexpr int kTile = 64 * int(sizeof(Tio));   // floats of one tile
   constexpr int kBuf = OB::kFwd + kWalkWaves * kTile;
+  // results of a chunk: the next chunk's entering state S (DK rows), X0 and U (16 rows each)
+  constexpr int kOS = 0, kOX = DK * kOutLd, kOU = kOX + 16 * kOutLd, kOut = kOU + 16 * kOutLd;
   __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
+  __shared__ __attribute__((aligned(16))) float so[2][kOut];
 
   int sub;
   const int unit = block_unit(blockIdx.x, p.n_ct / kWalkWaves, &sub);
@@ -311,15 +365,56 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
   const int h = unit % H, n = unit / H;
   const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
   const int sbos = bos - p.slot_tok0;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
-  const int ct = kWalkWaves * sub + w;
-  const int col = 16 * ct + ln;
-  const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
   const int nch = (eos - bos + kC - 1) / kC;
+  if (nch == 0) return;
   const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
   const size_t ops_stride = size_t(H) * OB::kFloats;
-  auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV; };
+  const int col0 = 64 * sub;   // the workgroup's first state column
 
+  if (w == kLoader) {
+    const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
+    // a chunk's operand block and the four value tiles (the last chunk's again at the end:
+    // nothing is staged conditionally); the buffer was last read in the chunk before last
+    auto stage = [&](int c, float* dst) {
+      const int cs = bos + kC * c;
+      stage_block_all<OB::kFwd / 4>(ops0 + c * ops_stride, dst, lane);
+#pragma unroll
+      for (int t = 0; t < kWalkWaves; ++t)
+        stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), col0 + 16 * t,
+                    dst + OB::kFwd + t * kTile, lane);
+    };
+    stage(0, sb0);
+    wait_vmem();
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+      stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
+      wait_vmem();
+      lds_barrier();
+    }
+    return;
+  }
+  if (w == kStorer) {
+    // interval c (after barrier c - 1) writes what chunk c - 1 left: S0 of chunk c, X0 and U
+    // of chunk c - 1 (for c = 0 the entering state only)
+    auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV; };
+    lds_barrier();
+    for (int c = 0; c <= nch; ++c) {
+      const float* src = so[(c + 1) & 1];
+      if (c < nch) copy_rows<DK>(src + kOS, s0_of(c) + col0, DV, DK, lane);
+      if (c > 0) {
+        const size_t blk = size_t(cb_slot(sbos, n, c - 1)) * H + h;
+        copy_rows<16>(src + kOX, p.X0 + blk * kC * DV + col0, DV, 16, lane);
+        copy_rows<16>(src + kOU, p.U + blk * kC * DV + col0, DV, 16, lane);
+      }
+      if (c < nch) lds_barrier();
+    }
+    return;
+  }
+
+  const int ct = kWalkWaves * sub + w;
+  const int col = 16 * ct + ln;
   // the state tile in accumulator layout: block rb, register r = row 16 rb + 4 q4 + r
   f32x4 S[NTD];
   const size_t st_off = (size_t(p.seq0 + n) * H + h) * DK * DV;
@@ -331,31 +426,14 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[rb][r] = p.h0[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col];
   }
-  if (nch == 0) return;
-  // a chunk's operand block (this wave's half) and value tile into buffer dst
-  auto stage = [&](int c, float* dst) {
-    const int cs = bos + kC * c;
-    stage_block_half<OB::kFwd / 4>(ops0 + c * ops_stride, dst, w, lane);
-    stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct, dst + OB::kFwd + w * kTile,
-                lane);
-  };
-  auto store_state = [&](float* dst) {
+  // the entering state goes out through buffer 1 (the storer's interval 0 reads it)
 #pragma unroll
-    for (int rb = 0; rb < NTD; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[size_t(16 * rb + 4 * q4 + r) * DV + col] = S[rb][r];
-  };
-  stage(0, sb0);
-  wait_vmem();
+  for (int rb = 0; rb < NTD; ++rb) put_tile16(so[1] + kOS + 16 * rb * kOutLd + 16 * w, S[rb], lane);
   lds_barrier();
-  store_state(s0_of(0));
 
   for (int c = 0; c < nch; ++c) {
     const float* cur = (c & 1) ? sb1 : sb0;
-    // the next chunk's block and values (the last chunk's again at the end: nothing is
-    // staged conditionally); the buffer was last read in the previous chunk, before the
-    // barrier that ended it
-    stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
+    float* out = so[c & 1];
     const int cs = bos + kC * c, L = min(kC, eos - cs);
     const int sl = swz(ln);
     // X = K_G S (k order: the state's own register order)
@@ -379,6 +457,8 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
     f32x4 U = zero4();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) U = mma_f32(cur[OB::kT + ln * 16 + 4 * q4 + kk], Y[kk], U);
+    put_tile16(out + kOX + 16 * w, X0, lane);
+    put_tile16(out + kOU + 16 * w, U, lane);
     // S = e^(G_C) S + K^^T U
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb) {
@@ -390,32 +470,28 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_fwd_kernel(CBwdParams p)
         S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
       }
     }
-    // this wave's part of the next buffer has landed (and the previous chunk's stores are
-    // done); the barrier publishes all parts and frees the buffer just read. This chunk's
-    // stores go out after the wait, so the next wait finds them done.
-    wait_vmem();
-    lds_barrier();
-    const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
-    float* wx = p.X0 + blk * kC * DV;
-    float* wu = p.U + blk * kC * DV;
+    if (c + 1 < nch) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wx[size_t(4 * q4 + r) * DV + col] = X0[r];
-      wu[size_t(4 * q4 + r) * DV + col] = U[r];
+      for (int rb = 0; rb < NTD; ++rb) put_tile16(out + kOS + 16 * rb * kOutLd + 16 * w, S[rb], lane);
     }
-    if (c + 1 < nch) store_state(s0_of(c + 1));
+    // publishes the next staged buffer and this chunk's results; frees the buffer just read
+    lds_barrier();
   }
 }
 
 // ---- 2. reverse walk: dS, dU, dY of every chunk, dv, and dh0
 template <typename Tio, int DK>
-__global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p) {
+__global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
   using OB = OpBlock<DK>;
-  // per buffer: the operand block, then each wave's 16 x 16 tile of output gradients
+  // per buffer: the operand block, then the four 16 x 16 tiles of output gradients
   constexpr int kTile = 64 * int(sizeof(Tio));
   constexpr int kBuf = OB::kFloats + kWalkWaves * kTile;
+  // results of a chunk: dS (the gradient of the state leaving it, DK rows), dU, dY, dv
+  constexpr int kOD = 0, kOdU = DK * kOutLd, kOdY = kOdU + 16 * kOutLd, kOdv = kOdY + 16 * kOutLd,
+                kOut = kOdv + 16 * kOutLd;
   __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
+  __shared__ __attribute__((aligned(16))) float so[2][kOut];
 
   int sub;
   const int unit = block_unit(blockIdx.x, p.n_ct / kWalkWaves, &sub);
@@ -424,14 +500,56 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
   const int h = unit % H, n = unit / H;
   const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
   const int sbos = bos - p.slot_tok0;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
-  const int ct = kWalkWaves * sub + w;
-  const int col = 16 * ct + ln;
-  const Tio* gdo = reinterpret_cast<const Tio*>(p.d_o) + size_t(h) * DV;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
   const int nch = (eos - bos + kC - 1) / kC;
   const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
   const size_t ops_stride = size_t(H) * OB::kFloats;
+  const int col0 = 64 * sub;
 
+  if (w == kLoader) {
+    const Tio* gdo = reinterpret_cast<const Tio*>(p.d_o) + size_t(h) * DV;
+    auto stage = [&](int c, float* dst) {
+      const int cs = bos + kC * c;
+      stage_block_all<OB::kFloats / 4>(ops0 + c * ops_stride, dst, lane);
+#pragma unroll
+      for (int t = 0; t < kWalkWaves; ++t)
+        stage_vtile(gdo, size_t(H) * DV, cs, min(kC, eos - cs), col0 + 16 * t,
+                    dst + OB::kFloats + t * kTile, lane);
+    };
+    if (nch > 0) {
+      stage(nch - 1, sb0);
+      wait_vmem();
+      lds_barrier();
+      for (int i = 0; i < nch; ++i) {
+        stage(max(nch - 2 - i, 0), (i & 1) ? sb0 : sb1);
+        wait_vmem();
+        lds_barrier();
+      }
+    }
+    return;
+  }
+  if (w == kStorer) {
+    // interval i (after barrier i - 1) writes what iteration i - 1 (chunk nch - i) left
+    if (nch > 0) {
+      lds_barrier();
+      for (int i = 1; i <= nch; ++i) {
+        lds_barrier();
+        const float* src = so[(i - 1) & 1];
+        const int c = nch - i, cs = bos + kC * c, L = min(kC, eos - cs);
+        const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
+        copy_rows<DK>(src + kOD, p.dS + blk * DK * DV + col0, DV, DK, lane);
+        copy_rows<16>(src + kOdU, p.dU + blk * kC * DV + col0, DV, 16, lane);
+        copy_rows<16>(src + kOdY, p.dY + blk * kC * DV + col0, DV, 16, lane);
+        copy_rows<16>(src + kOdv, p.dv + (size_t(cs) * H + h) * DV + col0, size_t(H) * DV, L,
+                      lane);
+      }
+    }
+    return;
+  }
+
+  const int ct = kWalkWaves * sub + w;
+  const int col = 16 * ct + ln;
   f32x4 D[NTD];
   const size_t st_off = (size_t(p.seq0 + n) * H + h) * DK * DV;
 #pragma unroll
@@ -442,27 +560,15 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) D[rb][r] = p.dht[st_off + size_t(16 * rb + 4 * q4 + r) * DV + col];
   }
-  auto stage = [&](int c, float* dst) {
-    const int cs = bos + kC * c;
-    stage_block_half<OB::kFloats / 4>(ops0 + c * ops_stride, dst, w, lane);
-    stage_vtile(gdo, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct,
-                dst + OB::kFloats + w * kTile, lane);
-  };
-  auto store_grad = [&](int c) {
-    float* ds = p.dS + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV;
-#pragma unroll
-    for (int rb = 0; rb < NTD; ++rb) store_tile16(ds + size_t(16 * rb) * DV + 16 * ct, DV, D[rb], lane);
-  };
   if (nch > 0) {
-    stage(nch - 1, sb0);
-    wait_vmem();
     lds_barrier();
     for (int i = 0; i < nch; ++i) {
       const int c = nch - 1 - i;
       const float* cur = (i & 1) ? sb1 : sb0;
-      stage(max(c - 1, 0), (i & 1) ? sb0 : sb1);
-      // the gradient of the state leaving the chunk (its stores overlap the products below)
-      store_grad(c);
+      float* out = so[i & 1];
+      // the gradient of the state leaving the chunk
+#pragma unroll
+      for (int rb = 0; rb < NTD; ++rb) put_tile16(out + kOD + 16 * rb * kOutLd + 16 * w, D[rb], lane);
       const int cs = bos + kC * c, L = min(kC, eos - cs);
       const int sl = swz(ln);
       // s dO as the products' right operand: token 4 q4 + kk, this lane's column
@@ -487,20 +593,10 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) dY = mma_f32(cur[OB::kT + (4 * q4 + kk) * 16 + ln], dU[kk], dY);
       const f32x4 bt = *reinterpret_cast<const f32x4*>(cur + OB::kBeta + 4 * q4);
-      {
-        const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
-        store_tile16(p.dU + blk * kC * DV + 16 * ct, DV, dU, lane);
-        store_tile16(p.dY + blk * kC * DV + 16 * ct, DV, dY, lane);
-        // dv = diag(beta) dY, row-major: lane (q4, ln) stores token 4 q4 + (ln & 3), columns
-        // 4 (ln >> 2) .. + 3 of this tile
-        float x[4] = {dY[0], dY[1], dY[2], dY[3]};
-        quad_transpose(x, lane);
-        const int t = 4 * q4 + (ln & 3);
-        const float b = cur[OB::kBeta + t];
-        if (t < L)
-          *reinterpret_cast<f32x4*>(p.dv + (size_t(cs + t) * H + h) * DV + 16 * ct + 4 * (ln >> 2)) =
-              f32x4{b * x[0], b * x[1], b * x[2], b * x[3]};
-      }
+      put_tile16(out + kOdU + 16 * w, dU, lane);
+      put_tile16(out + kOdY + 16 * w, dY, lane);
+      // dv = diag(beta) dY (row-major, like the tiles above; the storer drops rows past L)
+      put_tile16(out + kOdv + 16 * w, bt * dY, lane);
       // D = e^(G_C) D + Q_G^T (s dO) - K_G^T diag(beta) dY
       float bdy[4];
 #pragma unroll
@@ -517,7 +613,6 @@ __global__ __launch_bounds__(64 * kWalkWaves) void cbwd_rev_kernel(CBwdParams p)
           D[rb] = mma_f32(cur[OB::kKG + a], bdy[kk], D[rb]);
         }
       }
-      wait_vmem();
       lds_barrier();
     }
   }
@@ -889,10 +984,10 @@ static hipError_t launch_cbwd(const CBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((cbwd_prep_kernel<Tio, DK>), chunks, dim3(DK), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(64 * kWalkWaves), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(kWalkThreads), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(64 * kWalkWaves), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(kWalkThreads), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((cbwd_grad_kernel<Tio, DK>), chunks, dim3(4 * DK), 0, stream, p);
