@@ -626,9 +626,11 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
 
 // ---- the fp32 prefill at d = 128: the forward walk of the same chunk form, producing
 // o = s (Q_G S0 + M U) per chunk, the final state and checkpoints. Workgroups as above (four
-// waves, four 16-column tiles of one (sequence, head)); the whole operand block is staged.
+// computing waves, four 16-column tiles of one (sequence, head), and the loader wave kLoader
+// staging the whole operand block and the value tiles); the computing waves store o.
+constexpr int kPrefillThreads = 64 * (kWalkWaves + 1);
 template <int DK>
-__global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams p) {
+__global__ __launch_bounds__(kPrefillThreads) void c16_prefill_kernel(CBwdParams p) {
   using Tio = float;
   constexpr int DV = DK, NTD = DK / 16;
   using OB = OpBlock<DK>;
@@ -643,13 +645,39 @@ __global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams
   const int h = unit % H, n = unit / H;
   const int bos = seq_first_token(p, n), eos = seq_first_token(p, n + 1);
   const int sbos = bos - p.slot_tok0;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
-  const int ct = kWalkWaves * sub + w;
-  const int col = 16 * ct + ln;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, ln = lane & 15;
   const Tio* gv = reinterpret_cast<const Tio*>(p.v) + size_t(h) * DV;
   const int nch = (eos - bos + kC - 1) / kC;
   const float* ops0 = p.ops + (size_t(cb_slot(sbos, n, 0)) * H + h) * OB::kFloats;
   const size_t ops_stride = size_t(H) * OB::kFloats;
+
+  if (w == kLoader) {
+    // a chunk's operand block and the four value tiles (the last chunk's again at the end:
+    // nothing is staged conditionally); the buffer was last read in the chunk before last
+    auto stage = [&](int c, float* dst) {
+      const int cs = bos + kC * c;
+      stage_block_all<OB::kFloats / 4>(ops0 + c * ops_stride, dst, lane);
+#pragma unroll
+      for (int t = 0; t < kWalkWaves; ++t)
+        stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), 64 * sub + 16 * t,
+                    dst + OB::kFloats + t * kTile, lane);
+    };
+    if (nch > 0) {
+      stage(0, sb0);
+      wait_vmem();
+      lds_barrier();
+      for (int c = 0; c < nch; ++c) {
+        stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
+        wait_vmem();
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  const int ct = kWalkWaves * sub + w;
+  const int col = 16 * ct + ln;
   const int sl = swz(ln);
 
   f32x4 S[NTD];
@@ -667,12 +695,6 @@ __global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams
 #pragma unroll
     for (int rb = 0; rb < NTD; ++rb) store_tile16(dst + size_t(16 * rb) * DV + 16 * ct, DV, S[rb], lane);
   };
-  auto stage = [&](int c, float* dst) {
-    const int cs = bos + kC * c;
-    stage_block_half<OB::kFloats / 4>(ops0 + c * ops_stride, dst, w, lane);
-    stage_vtile(gv, size_t(H) * DV, cs, min(kC, eos - cs), 16 * ct, dst + OB::kFloats + w * kTile,
-                lane);
-  };
   // K S with the [16][DK] tile at offset off of buffer b (k order: the state's register order)
   auto tile_times_state = [&](const float* b, int off) {
     f32x4 x = zero4();
@@ -684,14 +706,9 @@ __global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams
     }
     return x;
   };
-  if (nch > 0) {
-    stage(0, sb0);
-    wait_vmem();
-    lds_barrier();
-  }
+  if (nch > 0) lds_barrier();
   for (int c = 0; c < nch; ++c) {
     const float* cur = (c & 1) ? sb1 : sb0;
-    stage(min(c + 1, nch - 1), (c & 1) ? sb0 : sb1);
     const int cs = bos + kC * c, L = min(kC, eos - cs);
     // X = K_G S and the inter-chunk part of the output, Q_G S
     const f32x4 X = tile_times_state(cur, OB::kKG);
@@ -719,7 +736,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void c16_prefill_kernel(CBwdParams
         S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
       }
     }
-    wait_vmem();
+    // publishes the next staged buffer, frees the one just read
     lds_barrier();
     {
       // o rows of this chunk: after a quad transpose lane (q4, ln) holds token
@@ -1004,7 +1021,7 @@ hipError_t launch_c16_prefill(const CBwdParams& p, int dk, hipStream_t stream) {
                      stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((c16_prefill_kernel<128>), walk, dim3(64 * kWalkWaves), 0, stream, p);
+  hipLaunchKernelGGL((c16_prefill_kernel<128>), walk, dim3(kPrefillThreads), 0, stream, p);
   return hipGetLastError();
 }
 
