@@ -140,9 +140,9 @@ __device__ __forceinline__ void store_tile16(float* dst, size_t ld, f32x4 a, int
 
 // The chunk that a chunk slot holds: the launch's sequence i (the last one whose first slot
 // floor((bos_i - slot_tok0) / 16) + i is at most slot), the chunk's first token and length.
-// False for slots that no chunk uses.
+// False for slots that no chunk uses. c_out (optional): the chunk's index in its sequence.
 __device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, int* cs_out,
-                                           int* L_out) {
+                                           int* L_out, int* c_out = nullptr) {
   auto first_tok = [&](int i) -> long long { return seq_first_token(p, i); };
   int lo = 0, hi = p.n_seqs - 1;
   while (lo < hi) {
@@ -155,6 +155,7 @@ __device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, 
   if (c < 0 || bos + kC * c >= eos) return false;
   *cs_out = int(bos + kC * c);
   *L_out = int(min((long long)kC, eos - *cs_out));
+  if (c_out) *c_out = int(c);
   return true;
 }
 
@@ -396,13 +397,14 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_fwd_kernel(CBwdParams p) {
     return;
   }
   if (w == kStorer) {
-    // interval c (after barrier c - 1) writes what chunk c - 1 left: S0 of chunk c, X0 and U
-    // of chunk c - 1 (for c = 0 the entering state only)
+    // interval c (after barrier c - 1) writes what chunk c - 1 left: S0 of chunk c when c is
+    // even, X0 and U of chunk c - 1 (for c = 0 the entering state only). The gradient pass
+    // advances an odd chunk's entering state from the even one before it.
     auto s0_of = [&](int c) { return p.S0 + (size_t(cb_slot(sbos, n, c)) * H + h) * DK * DV; };
     lds_barrier();
     for (int c = 0; c <= nch; ++c) {
       const float* src = so[(c + 1) & 1];
-      if (c < nch) copy_rows<DK>(src + kOS, s0_of(c) + col0, DV, DK, lane);
+      if (c < nch && c % 2 == 0) copy_rows<DK>(src + kOS, s0_of(c) + col0, DV, DK, lane);
       if (c > 0) {
         const size_t blk = size_t(cb_slot(sbos, n, c - 1)) * H + h;
         copy_rows<16>(src + kOX, p.X0 + blk * kC * DV + col0, DV, 16, lane);
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_fwd_kernel(CBwdParams p) {
         S[rb] = mma_f32(cur[OB::kKH + t * DK + ((16 * rb + ln) ^ swz(t))], U[kk], S[rb]);
       }
     }
-    if (c + 1 < nch) {
+    if (c + 1 < nch && (c + 1) % 2 == 0) {
 #pragma unroll
       for (int rb = 0; rb < NTD; ++rb) put_tile16(out + kOS + 16 * rb * kOutLd + 16 * w, S[rb], lane);
     }
@@ -765,15 +767,19 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
   __shared__ float sKq[kC * LK], sKk[kC * LK], sQq[kC * LK];
   __shared__ float sG[kC * LK];   // G, then each token's log-decay gradient
   __shared__ __attribute__((aligned(16))) float sdO[kC * LV], sU[kC * LV], sdY[kC * LV];
+  __shared__ __attribute__((aligned(16))) float sUp[kC * LV];   // U of the chunk before (odd chunks)
   __shared__ float sB[kC * 17], sdT[kC * 17], sdM[kC * 17], sW[kC * 17], sT[kC * 20];
   __shared__ float sGm[DK], sGC[DK], sExtra[DK], sBeta[kC], sdb[kC];
 
   const int H = p.H;
   const int h = int(blockIdx.x % unsigned(H));
   const long long slot = blockIdx.x / unsigned(H);
-  int cs, L;
-  if (!slot_chunk(p, slot, &cs, &L)) return;
+  int cs, L, ci;
+  if (!slot_chunk(p, slot, &cs, &L, &ci)) return;
   const size_t blk = size_t(slot) * H + h;
+  // the forward walk keeps the entering states of even chunks; an odd chunk's is advanced
+  // here from the one before it (the same sequence's previous slot)
+  const bool odd = (ci & 1) != 0;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q4 = lane >> 4, ln = lane & 15;
   const Tio* gq = reinterpret_cast<const Tio*>(p.q);
@@ -828,6 +834,16 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     for (int it = 0; it < 4; ++it) {
       const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
       *reinterpret_cast<f32x4*>(dst + t * LV + j) = x[it];
+    }
+    if (odd && tile == 1) {
+      const float* src = p.U + (blk - H) * kC * DV;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) x[it] = ld4(src, 4 * size_t(v + DK * it));
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
+        *reinterpret_cast<f32x4*>(sUp + t * LV + j) = x[it];
+      }
     }
     if (tid - DK < kC) sBeta[tid - DK] = tid - DK < L ? p.beta[size_t(cs + tid - DK) * H + h] : 0.f;
   }
@@ -924,12 +940,33 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
   f32x4 aQ = zero4(), aKg = zero4(), aKh = zero4();
   float rs = 0.f;
   {
-    const float* s0 = p.S0 + blk * DK * DV + size_t(ch) * DV;
+    // S0 of an odd chunk: e^(G_C) S0' + K^'^T U' from the chunk before (' marks its values),
+    // the forward walk's update with the same products in the same order, here transposed:
+    // lane (q4, ln) gets channel ch, value columns j .. j + 3 of column block i
+    using OB = OpBlock<DK>;
+    const float* s0 = p.S0 + (odd ? blk - H : blk) * DK * DV + size_t(ch) * DV;
     const float* ds = p.dS + blk * DK * DV + size_t(ch) * DV;
+    float ech = 1.f, khp[4] = {0.f, 0.f, 0.f, 0.f};
+    if (odd) {
+      const float* ob = p.ops + (blk - H) * OB::kFloats;
+      ech = ob[OB::kEGC + ch];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int t = 4 * q4 + kk;
+        khp[kk] = ob[OB::kKH + t * DK + (ch ^ swz(t))];
+      }
+    }
 #pragma unroll 4
     for (int i = 0; i < DV / 16; ++i) {
       const int j = 16 * i + 4 * q4;
-      const f32x4 bs = ld4(s0, j), bd = ld4(ds, j);
+      f32x4 bs = ld4(s0, j);
+      const f32x4 bd = ld4(ds, j);
+      if (odd) {
+        bs *= ech;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          bs = mma_f32(sUp[(4 * q4 + kk) * LV + 16 * i + ln], khp[kk], bs);
+      }
       const f32x4 ao = *reinterpret_cast<const f32x4*>(sdO + ln * LV + j);
       const f32x4 ay = *reinterpret_cast<const f32x4*>(sdY + ln * LV + j);
       const f32x4 au = *reinterpret_cast<const f32x4*>(sU + ln * LV + j);
