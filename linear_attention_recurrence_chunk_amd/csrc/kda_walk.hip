@@ -186,16 +186,20 @@ __global__ __launch_bounds__(256 * kTPW + (kMem ? 64 : 0)) void chunk_walk_kerne
       for (int e = 0; e < 4; ++e) S[t][e] = (p_tile && 16 * t + 4 * q4 + e == col0 + ln) ? 1.f : 0.f;
   }
 
-  // wave wid moves blocks wid, wid + 4 kTPW, ... of the fragment ranges the walk reads (without outputs:
-  // no Q e^Gamma and no M) of chunk ci's slot into buffer dst
-  // (the global address is a wave-uniform block address plus the lane's 16-byte offset)
+  // waves 0..3 (one per SIMD) move blocks wid, wid + 4, ... of the fragment ranges the walk
+  // reads (without outputs: no Q e^Gamma and no M) of chunk ci's slot into buffer dst; with
+  // two tiles per workgroup the other wave of each SIMD issues none, so it computes while its
+  // partner waits for the memory pipeline to take the loads (the global address is a
+  // wave-uniform block address plus the lane's 16-byte offset)
   auto fetch_range = [&](const char* src, char* dst, int f0, int f1) {
+    if (wid < 4) {
 #pragma unroll
-    for (int i = 0; i < (OS::kBlocks + 4 * kTPW - 1) / (4 * kTPW); ++i) {
-      const int f = f0 + wid + 4 * kTPW * i;
-      if (f < f1)
-        __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024 + lane * 16, dst + f * 1024, 16,
-                                         0, 0);
+      for (int i = 0; i < (OS::kBlocks + 3) / 4; ++i) {
+        const int f = f0 + wid + 4 * i;
+        if (f < f1)
+          __builtin_amdgcn_global_load_lds(src + size_t(f) * 1024 + lane * 16, dst + f * 1024,
+                                           16, 0, 0);
+      }
     }
   };
   auto fetch_slot = [&](int ci, char* dst) {
