@@ -295,16 +295,21 @@ __device__ __forceinline__ void stage_block_half(const float* src, float* dst, i
   }
 }
 
-// The backward's two walks add two waves to the four that compute: wave kLoader stages each
-// chunk's operand block and input tiles into LDS a chunk ahead, and wave kStorer writes the
-// results the computing waves leave in LDS (double-buffered, one buffer per chunk parity) to
-// global memory. A 16-byte store or a 1 KiB global-to-LDS load holds the compute unit's
-// vector-memory queue for tens of cycles and a wave stalls in order until the queue takes it;
-// in the computing waves these stalls took 35-45% of each chunk step. Each of the two waves
-// waits only for its own accesses (the loader for its loads before each barrier; the
-// storer's stores are never waited for), and all six pass the same barriers.
+// The backward's two walks add memory waves to the four that compute: wave kLoader stages
+// each chunk's operand block and input tiles into LDS a chunk ahead, and wave kStorer (in the
+// reverse walk kStorers waves from it) writes the results the computing waves leave in LDS
+// (double-buffered, one buffer per chunk parity) to global memory. A 16-byte store or a 1 KiB
+// global-to-LDS load holds the compute unit's vector-memory queue for tens of cycles and a
+// wave stalls in order until the queue takes it; in the computing waves these stalls took
+// 35-45% of each chunk step. Each memory wave waits only for its own accesses (the loader for
+// its loads before each barrier; the stores are never waited for), and all waves of the
+// workgroup pass the same barriers.
 constexpr int kLoader = kWalkWaves, kStorer = kWalkWaves + 1;
-constexpr int kWalkThreads = 64 * (kWalkWaves + 2);
+// the forward walk has one storer, the reverse walk (dS every chunk, transposed by its
+// storers, see copy_cols) two
+constexpr int kFwdThreads = 64 * (kWalkWaves + 2);
+constexpr int kStorers = 2;
+constexpr int kRevThreads = 64 * (kWalkWaves + 1 + kStorers);
 constexpr int kOutLd = 68;   // row stride (floats) of the LDS result tiles: 64 columns + 4
 
 // All N4 16-byte units of a block, issued by one wave.
@@ -346,9 +351,38 @@ __device__ __forceinline__ void copy_rows(const float* src, float* dst, size_t l
   }
 }
 
+// The storer's copy of a workgroup's DK x 64 state tile that the computing waves left in LDS
+// in their accumulator layout, column-major (column c of the tile at c * (DK + 4), rows
+// contiguous: each lane's 16-byte write is four rows of one column, no transpose on the
+// computing waves' chain). Quad (lane / 4) reads four rows of columns 4 quad .. + 3, one column
+// a lane, the quad transposes them, and lane j stores row 4 i + j, 16 bytes of four columns, to
+// row-major dst (rows ld floats apart): eight reads in flight ahead of their stores.
+template <int DK>
+__device__ __forceinline__ void copy_cols(const float* src, float* dst, size_t ld, int lane,
+                                          int part) {
+  constexpr int kLd = DK + 4;
+  constexpr int kPer = DK / 4 / kStorers;   // 4-row groups of one storer
+  static_assert(kPer % 8 == 0, "whole groups of eight");
+  const int qd = lane >> 2, j = lane & 3;
+#pragma unroll
+  for (int i0 = part * kPer; i0 < (part + 1) * kPer; i0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = *reinterpret_cast<const f32x4*>(src + (4 * qd + j) * kLd + 4 * (i0 + k));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float x[4] = {v[k][0], v[k][1], v[k][2], v[k][3]};
+      quad_transpose(x, lane);
+      *reinterpret_cast<f32x4*>(dst + size_t(4 * (i0 + k) + j) * ld + 4 * qd) =
+          f32x4{x[0], x[1], x[2], x[3]};
+    }
+  }
+}
+
 // ---- 1. forward walk: S0, X0 and U of every chunk
 template <typename Tio, int DK>
-__global__ __launch_bounds__(kWalkThreads) void cbwd_fwd_kernel(CBwdParams p) {
+__global__ __launch_bounds__(kFwdThreads) void cbwd_fwd_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
   using OB = OpBlock<DK>;
   // per buffer: the block's first kFwd floats, then the four 16 x 16 value tiles
@@ -483,13 +517,15 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_fwd_kernel(CBwdParams p) {
 
 // ---- 2. reverse walk: dS, dU, dY of every chunk, dv, and dh0
 template <typename Tio, int DK>
-__global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
+__global__ __launch_bounds__(kRevThreads) void cbwd_rev_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
   using OB = OpBlock<DK>;
   // per buffer: the operand block, then the four 16 x 16 tiles of output gradients
   constexpr int kTile = 64 * int(sizeof(Tio));
   constexpr int kBuf = OB::kFloats + kWalkWaves * kTile;
-  // results of a chunk: dS (the gradient of the state leaving it, DK rows), dU, dY, dv
+  // results of a chunk: dS (the gradient of the state leaving it; the 64 columns of DK + 4
+  // floats each, column-major, see copy_cols), dU, dY, dv (row-major)
+  static_assert(64 * (DK + 4) <= DK * kOutLd, "the column-major dS tile fits its region");
   constexpr int kOD = 0, kOdU = DK * kOutLd, kOdY = kOdU + 16 * kOutLd, kOdv = kOdY + 16 * kOutLd,
                 kOut = kOdv + 16 * kOutLd;
   __shared__ __attribute__((aligned(16))) float sb0[kBuf], sb1[kBuf];
@@ -531,8 +567,10 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
     }
     return;
   }
-  if (w == kStorer) {
-    // interval i (after barrier i - 1) writes what iteration i - 1 (chunk nch - i) left
+  if (w >= kStorer) {
+    // interval i (after barrier i - 1) writes what iteration i - 1 (chunk nch - i) left; the
+    // two storers take half of dS's rows each, dU and dY the first, dv the second
+    const int sp = w - kStorer;
     if (nch > 0) {
       lds_barrier();
       for (int i = 1; i <= nch; ++i) {
@@ -540,11 +578,14 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
         const float* src = so[(i - 1) & 1];
         const int c = nch - i, cs = bos + kC * c, L = min(kC, eos - cs);
         const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
-        copy_rows<DK>(src + kOD, p.dS + blk * DK * DV + col0, DV, DK, lane);
-        copy_rows<16>(src + kOdU, p.dU + blk * kC * DV + col0, DV, 16, lane);
-        copy_rows<16>(src + kOdY, p.dY + blk * kC * DV + col0, DV, 16, lane);
-        copy_rows<16>(src + kOdv, p.dv + (size_t(cs) * H + h) * DV + col0, size_t(H) * DV, L,
-                      lane);
+        copy_cols<DK>(src + kOD, p.dS + blk * DK * DV + col0, DV, lane, sp);
+        if (sp == 0) {
+          copy_rows<16>(src + kOdU, p.dU + blk * kC * DV + col0, DV, 16, lane);
+          copy_rows<16>(src + kOdY, p.dY + blk * kC * DV + col0, DV, 16, lane);
+        } else {
+          copy_rows<16>(src + kOdv, p.dv + (size_t(cs) * H + h) * DV + col0, size_t(H) * DV, L,
+                        lane);
+        }
       }
     }
     return;
@@ -568,9 +609,11 @@ __global__ __launch_bounds__(kWalkThreads) void cbwd_rev_kernel(CBwdParams p) {
       const int c = nch - 1 - i;
       const float* cur = (i & 1) ? sb1 : sb0;
       float* out = so[i & 1];
-      // the gradient of the state leaving the chunk
+      // the gradient of the state leaving the chunk, as the accumulators hold it (column
+      // 16 w + ln, rows 16 rb + 4 q4 .. + 3)
 #pragma unroll
-      for (int rb = 0; rb < NTD; ++rb) put_tile16(out + kOD + 16 * rb * kOutLd + 16 * w, D[rb], lane);
+      for (int rb = 0; rb < NTD; ++rb)
+        *reinterpret_cast<f32x4*>(out + kOD + (16 * w + ln) * (DK + 4) + 16 * rb + 4 * q4) = D[rb];
       const int cs = bos + kC * c, L = min(kC, eos - cs);
       const int sl = swz(ln);
       // s dO as the products' right operand: token 4 q4 + kk, this lane's column
@@ -1038,10 +1081,10 @@ static hipError_t launch_cbwd(const CBwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((cbwd_prep_kernel<Tio, DK>), chunks, dim3(DK), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(kWalkThreads), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_fwd_kernel<Tio, DK>), walk, dim3(kFwdThreads), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(kWalkThreads), 0, stream, p);
+  hipLaunchKernelGGL((cbwd_rev_kernel<Tio, DK>), walk, dim3(kRevThreads), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((cbwd_grad_kernel<Tio, DK>), chunks, dim3(4 * DK), 0, stream, p);
