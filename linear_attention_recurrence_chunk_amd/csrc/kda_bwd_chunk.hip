@@ -142,7 +142,8 @@ __device__ __forceinline__ void store_tile16(float* dst, size_t ld, f32x4 a, int
 // floor((bos_i - slot_tok0) / 16) + i is at most slot), the chunk's first token and length.
 // False for slots that no chunk uses. c_out (optional): the chunk's index in its sequence.
 __device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, int* cs_out,
-                                           int* L_out, int* c_out = nullptr) {
+                                           int* L_out, int* c_out = nullptr,
+                                           int* eos_out = nullptr) {
   auto first_tok = [&](int i) -> long long { return seq_first_token(p, i); };
   int lo = 0, hi = p.n_seqs - 1;
   while (lo < hi) {
@@ -156,8 +157,17 @@ __device__ __forceinline__ bool slot_chunk(const CBwdParams& p, long long slot, 
   *cs_out = int(bos + kC * c);
   *L_out = int(min((long long)kC, eos - *cs_out));
   if (c_out) *c_out = int(c);
+  if (eos_out) *eos_out = int(eos);
   return true;
 }
+
+// Which leaving-state gradients dS the reverse walk writes. With kAdvanceDS only those of odd
+// chunks and of each sequence's last chunk: the gradient pass advances an even chunk's from the
+// chunk after it, D = e^(G_C') D' + Q_G'^T (s dO') - K_G'^T diag(beta') dY' (the walk's own
+// update). It stages that chunk's dY and dO in LDS; for fp32 inputs at d_k = 128 the extra
+// tile would cost the gradient pass its second workgroup per CU, so there every dS is written.
+template <typename Tio, int DK>
+constexpr bool kAdvanceDS = sizeof(Tio) == 2 || DK == 64;
 
 // 16 x 16 product over the key channels: D[t][s] = sum_c X[t][c] Y[s][c] (token-major tiles)
 template <int DK>
@@ -515,7 +525,7 @@ __global__ __launch_bounds__(kFwdThreads) void cbwd_fwd_kernel(CBwdParams p) {
   }
 }
 
-// ---- 2. reverse walk: dS, dU, dY of every chunk, dv, and dh0
+// ---- 2. reverse walk: dS (see kAdvanceDS), dU, dY of every chunk, dv, and dh0
 template <typename Tio, int DK>
 __global__ __launch_bounds__(kRevThreads) void cbwd_rev_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
@@ -578,7 +588,8 @@ __global__ __launch_bounds__(kRevThreads) void cbwd_rev_kernel(CBwdParams p) {
         const float* src = so[(i - 1) & 1];
         const int c = nch - i, cs = bos + kC * c, L = min(kC, eos - cs);
         const size_t blk = size_t(cb_slot(sbos, n, c)) * H + h;
-        copy_cols<DK>(src + kOD, p.dS + blk * DK * DV + col0, DV, lane, sp);
+        if (!kAdvanceDS<Tio, DK> || (c & 1) || c == nch - 1)
+          copy_cols<DK>(src + kOD, p.dS + blk * DK * DV + col0, DV, lane, sp);
         if (sp == 0) {
           copy_rows<16>(src + kOdU, p.dU + blk * kC * DV + col0, DV, 16, lane);
           copy_rows<16>(src + kOdY, p.dY + blk * kC * DV + col0, DV, 16, lane);
@@ -610,10 +621,12 @@ __global__ __launch_bounds__(kRevThreads) void cbwd_rev_kernel(CBwdParams p) {
       const float* cur = (i & 1) ? sb1 : sb0;
       float* out = so[i & 1];
       // the gradient of the state leaving the chunk, as the accumulators hold it (column
-      // 16 w + ln, rows 16 rb + 4 q4 .. + 3)
+      // 16 w + ln, rows 16 rb + 4 q4 .. + 3), where it is kept
+      if (!kAdvanceDS<Tio, DK> || (c & 1) || c == nch - 1) {
 #pragma unroll
-      for (int rb = 0; rb < NTD; ++rb)
-        *reinterpret_cast<f32x4*>(out + kOD + (16 * w + ln) * (DK + 4) + 16 * rb + 4 * q4) = D[rb];
+        for (int rb = 0; rb < NTD; ++rb)
+          *reinterpret_cast<f32x4*>(out + kOD + (16 * w + ln) * (DK + 4) + 16 * rb + 4 * q4) = D[rb];
+      }
       const int cs = bos + kC * c, L = min(kC, eos - cs);
       const int sl = swz(ln);
       // s dO as the products' right operand: token 4 q4 + kk, this lane's column
@@ -807,22 +820,31 @@ template <typename Tio, int DK>
 __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
   constexpr int DV = DK;
   constexpr int LK = DK + 1, LV = DV + 4;
+  constexpr bool kAdv = kAdvanceDS<Tio, DK>;
+  constexpr int LVn = DV + 16 / int(sizeof(Tio));   // row stride of the chunk after's dO
   __shared__ float sKq[kC * LK], sKk[kC * LK], sQq[kC * LK];
   __shared__ float sG[kC * LK];   // G, then each token's log-decay gradient
   __shared__ __attribute__((aligned(16))) float sdO[kC * LV], sU[kC * LV], sdY[kC * LV];
-  __shared__ __attribute__((aligned(16))) float sUp[kC * LV];   // U of the chunk before (odd chunks)
+  // U of the chunk before (odd chunks), or dY of the chunk after (even chunks, kAdv)
+  __shared__ __attribute__((aligned(16))) float sUp[kC * LV];
+  // dO of the chunk after as loaded (even chunks, kAdv)
+  __shared__ __attribute__((aligned(16))) Tio sdOn[kAdv ? kC * LVn : 8];
   __shared__ float sB[kC * 17], sdT[kC * 17], sdM[kC * 17], sW[kC * 17], sT[kC * 20];
   __shared__ float sGm[DK], sGC[DK], sExtra[DK], sBeta[kC], sdb[kC];
 
   const int H = p.H;
   const int h = int(blockIdx.x % unsigned(H));
   const long long slot = blockIdx.x / unsigned(H);
-  int cs, L, ci;
-  if (!slot_chunk(p, slot, &cs, &L, &ci)) return;
+  int cs, L, ci, eos;
+  if (!slot_chunk(p, slot, &cs, &L, &ci, &eos)) return;
   const size_t blk = size_t(slot) * H + h;
   // the forward walk keeps the entering states of even chunks; an odd chunk's is advanced
-  // here from the one before it (the same sequence's previous slot)
+  // here from the one before it (the same sequence's previous slot). With kAdv the reverse walk
+  // keeps the leaving-state gradients of odd chunks and of the last; an even chunk's is
+  // advanced here from the one after it (the next slot, its first token csn, Ln tokens).
   const bool odd = (ci & 1) != 0;
+  const int csn = cs + kC, Ln = min(kC, eos - csn);
+  const bool ds_next = kAdv && !odd && Ln > 0;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q4 = lane >> 4, ln = lane & 15;
   const Tio* gq = reinterpret_cast<const Tio*>(p.q);
@@ -878,14 +900,31 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
       const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
       *reinterpret_cast<f32x4*>(dst + t * LV + j) = x[it];
     }
-    if (odd && tile == 1) {
-      const float* src = p.U + (blk - H) * kC * DV;
+    if ((odd && tile == 1) || (ds_next && tile == 2)) {
+      const float* src = odd ? p.U + (blk - H) * kC * DV : p.dY + (blk + H) * kC * DV;
 #pragma unroll
       for (int it = 0; it < 4; ++it) x[it] = ld4(src, 4 * size_t(v + DK * it));
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
         *reinterpret_cast<f32x4*>(sUp + t * LV + j) = x[it];
+      }
+    }
+    if constexpr (kAdv) {
+      if (ds_next && tile == 0) {
+        // rows past the chunk after's end read its first row (scaled by 0 where used)
+        using V4 = Tio __attribute__((ext_vector_type(4)));
+        V4 y[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
+          y[it] = *reinterpret_cast<const V4*>(gdo + (size_t(t < Ln ? csn + t : csn) * H + h) * DV + j);
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int e = v + DK * it, t = e / (DV / 4), j = 4 * (e % (DV / 4));
+          *reinterpret_cast<V4*>(sdOn + t * LVn + j) = y[it];
+        }
       }
     }
     if (tid - DK < kC) sBeta[tid - DK] = tid - DK < L ? p.beta[size_t(cs + tid - DK) * H + h] : 0.f;
@@ -986,9 +1025,10 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     // S0 of an odd chunk: e^(G_C) S0' + K^'^T U' from the chunk before (' marks its values),
     // the forward walk's update with the same products in the same order, here transposed:
     // lane (q4, ln) gets channel ch, value columns j .. j + 3 of column block i
+    // dS of an even chunk (kAdv): the reverse walk's update from the chunk after, likewise
     using OB = OpBlock<DK>;
     const float* s0 = p.S0 + (odd ? blk - H : blk) * DK * DV + size_t(ch) * DV;
-    const float* ds = p.dS + blk * DK * DV + size_t(ch) * DV;
+    const float* ds = p.dS + (ds_next ? blk + H : blk) * DK * DV + size_t(ch) * DV;
     float ech = 1.f, khp[4] = {0.f, 0.f, 0.f, 0.f};
     if (odd) {
       const float* ob = p.ops + (blk - H) * OB::kFloats;
@@ -999,16 +1039,42 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
         khp[kk] = ob[OB::kKH + t * DK + (ch ^ swz(t))];
       }
     }
+    float egn = 1.f, qgn[4] = {0.f, 0.f, 0.f, 0.f}, kgn[4] = {0.f, 0.f, 0.f, 0.f};
+    float nbt[4] = {0.f, 0.f, 0.f, 0.f};   // -beta of the chunk after's tokens
+    if (ds_next) {
+      const float* ob = p.ops + (blk + H) * OB::kFloats;
+      egn = ob[OB::kEGC + ch];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int t = 4 * q4 + kk;
+        const int a = t * DK + (ch ^ swz(t));
+        qgn[kk] = ob[OB::kQG + a];
+        kgn[kk] = ob[OB::kKG + a];
+        nbt[kk] = -ob[OB::kBeta + t];
+      }
+    }
 #pragma unroll 4
     for (int i = 0; i < DV / 16; ++i) {
       const int j = 16 * i + 4 * q4;
       f32x4 bs = ld4(s0, j);
-      const f32x4 bd = ld4(ds, j);
+      f32x4 bd = ld4(ds, j);
       if (odd) {
         bs *= ech;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           bs = mma_f32(sUp[(4 * q4 + kk) * LV + 16 * i + ln], khp[kk], bs);
+      }
+      if constexpr (kAdv) {
+        if (ds_next) {
+          bd *= egn;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int t = 4 * q4 + kk;
+            const float sdo = (p.scale * keep_f(t < Ln)) * to_f32(sdOn[t * LVn + 16 * i + ln]);
+            bd = mma_f32(sdo, qgn[kk], bd);
+            bd = mma_f32(nbt[kk] * sUp[t * LV + 16 * i + ln], kgn[kk], bd);
+          }
+        }
       }
       const f32x4 ao = *reinterpret_cast<const f32x4*>(sdO + ln * LV + j);
       const f32x4 ay = *reinterpret_cast<const f32x4*>(sdY + ln * LV + j);

@@ -65,6 +65,29 @@ def test_backward_bf16_varlen_with_h0(dk):
     assert torch.equal(got["dh0"][2].cpu(), dht[2])
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_backward_pairs_of_chunks(dtype, dk):
+    """Sequences whose last 16-token chunk is odd (full, or ragged down to one token) or even:
+    the gradient pass rebuilds the state of one chunk of each pair from its neighbour (an odd
+    chunk's entering state from the chunk before, an even chunk's leaving-state gradient from
+    the chunk after, also where that one is a ragged last chunk)."""
+    lengths = [20, 50, 32, 17, 16, 33, 111]
+    T = sum(lengths)
+    print(f"case backward pairs {dtype} dk={dk} lengths={lengths}", flush=True)
+    inp = wl.prefill_inputs(H=3, dk=dk, dv=dk, dtype=dtype, seed=60 + dk, h0_std=0.02,
+                            lengths=lengths)
+    gen = torch.Generator().manual_seed(14)
+    do = torch.randn(T, 3, dk, generator=gen)
+    if dtype == "bf16":
+        do = do.to(torch.bfloat16)
+    dht = torch.randn(len(lengths), 3, dk, dk, generator=gen)
+    errs, _ = _grads_vs_oracle(inp, do, dht, varlen=True, scale=0.9)
+    print(" ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for n, e in errs.items():
+        assert e <= tol, n
+
+
 def test_backward_floor_and_determinism():
     """Raw g x 10 (the floor at -5 bites on part of the channels, where dg must be exactly 0),
     no final-state gradient, fp32; two calls give the same bits."""
