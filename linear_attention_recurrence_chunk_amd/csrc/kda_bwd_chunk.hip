@@ -28,10 +28,13 @@
 //   0. cbwd_prep_kernel: one workgroup per (chunk, head) forms the chunk's operand block: the
 //      decayed tiles K_G, K^, Q_G, T, M, e^(G_C) and beta;
 //   1. cbwd_fwd_kernel: one wave per (sequence, head, 16-column tile) walks the chunks
-//      forward and stores each chunk's entering state S0, X0 and U;
+//      forward and stores the entering state S0 of even chunks, X0 and U of every chunk;
 //   2. cbwd_rev_kernel: the same waves walk back, storing dS (the gradient of the state
-//      leaving each chunk), dU and dY, writing dv, and dh0 at the sequence start;
-//   3. cbwd_grad_kernel: one workgroup per (chunk, head) forms dq, dk, dbeta and dg.
+//      leaving a chunk) of odd chunks and of the last (see kAdvanceDS), dU and dY of every
+//      chunk, writing dv, and dh0 at the sequence start;
+//   3. cbwd_grad_kernel: one workgroup per (chunk, head) rebuilds the state its walk did not
+//      keep from the neighbouring chunk's (the walk's own update), then forms dq, dk, dbeta
+//      and dg.
 // The fp32 prefill: the same operand pass, then c16_prefill_kernel, the forward walk producing
 // o = s (Q_G S0 + M U), the final state and checkpoints.
 // The walks stage each chunk's operand block into LDS (global-to-LDS loads) while the previous
@@ -315,8 +318,8 @@ __device__ __forceinline__ void stage_block_half(const float* src, float* dst, i
 // its loads before each barrier; the stores are never waited for), and all waves of the
 // workgroup pass the same barriers.
 constexpr int kLoader = kWalkWaves, kStorer = kWalkWaves + 1;
-// the forward walk has one storer, the reverse walk (dS every chunk, transposed by its
-// storers, see copy_cols) two
+// the forward walk has one storer, the reverse walk (whose dS tiles its storers transpose,
+// see copy_cols) two
 constexpr int kFwdThreads = 64 * (kWalkWaves + 2);
 constexpr int kStorers = 2;
 constexpr int kRevThreads = 64 * (kWalkWaves + 1 + kStorers);
@@ -390,7 +393,7 @@ __device__ __forceinline__ void copy_cols(const float* src, float* dst, size_t l
   }
 }
 
-// ---- 1. forward walk: S0, X0 and U of every chunk
+// ---- 1. forward walk: S0 of even chunks, X0 and U of every chunk
 template <typename Tio, int DK>
 __global__ __launch_bounds__(kFwdThreads) void cbwd_fwd_kernel(CBwdParams p) {
   constexpr int DV = DK, NTD = DK / 16;
