@@ -857,7 +857,9 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
   const float* wdU = p.dU + blk * kC * DV;
 
   // 1. the in-chunk decays and the key/query tiles (one thread per key channel), and s dO,
-  // U and dY (the other threads)
+  // U and dY (the other threads). The key-channel threads keep which of their tokens' g lie
+  // above the floor (bit t) for step 6, so that no load of g waits behind a store there.
+  unsigned live = 0;
   if (tid < DK) {
     float G[kC], kv[kC], qv[kC];
     float acc = 0.f;
@@ -865,7 +867,9 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     for (int t = 0; t < kC; ++t) {
       const bool valid = t < L;
       const size_t row = (size_t(valid ? cs + t : cs) * H + h) * DK + tid;
-      acc += fmaxf(p.g[row], p.g_min) * keep_f(valid);
+      const float gv = p.g[row];
+      live |= (gv > p.g_min ? 1u : 0u) << t;
+      acc += fmaxf(gv, p.g_min) * keep_f(valid);
       G[t] = acc;
       kv[t] = ld_keep(gk, row, valid);
       qv[t] = ld_keep(gq, row, valid);
@@ -1103,9 +1107,19 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     dkAk = mma_f32(sW[m * 17 + ln], kq_, dkAk);   // dB^T K_G
   }
 
-  // 5. dq, dk, and each token's log-decay gradient (query side + key side -)
+  // 5. dq, dk, and each token's log-decay gradient (query side + key side -); the four
+  // tokens' q and k are loaded before the first store (the stores could alias them)
   const float gm = sGm[ch], gc = sGC[ch];
   float khs = 0.f;
+  float qv4[4], kv4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * q4 + r;
+    const bool valid = t < L;
+    const size_t row = (size_t(valid ? cs + t : cs) * H + h) * DK + ch;
+    qv4[r] = ld_keep(gq, row, valid);
+    kv4[r] = ld_keep(gk, row, valid);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 4 * q4 + r;
@@ -1113,7 +1127,7 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     const float G = sG[t * LK + ch];
     const float eg = __expf(G), em = __expf(G - gm), emi = __expf(gm - G), eh = __expf(gc - G);
     const size_t row = (size_t(valid ? cs + t : cs) * H + h) * DK + ch;
-    const float qv = ld_keep(gq, row, valid), kv = ld_keep(gk, row, valid);
+    const float qv = qv4[r], kv = kv4[r];
     const float dq = aQ[r] * eg + dqM[r] * em;
     const float dkq = -sBeta[t] * aKg[r] * eg + dkAq[r] * em;
     const float dkk = (dkAk[r] + dkMk[r]) * emi;
@@ -1135,10 +1149,7 @@ __global__ __launch_bounds__(4 * DK) void cbwd_grad_kernel(CBwdParams p) {
     float run = sExtra[tid];
     for (int t = kC - 1; t >= 0; --t) {
       run += sG[t * LK + tid];
-      if (t < L) {
-        const size_t row = (size_t(cs + t) * H + h) * DK + tid;
-        p.dg[row] = p.g[row] > p.g_min ? run : 0.f;
-      }
+      if (t < L) p.dg[(size_t(cs + t) * H + h) * DK + tid] = (live >> t) & 1u ? run : 0.f;
     }
   }
 }
