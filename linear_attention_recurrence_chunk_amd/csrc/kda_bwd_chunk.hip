@@ -230,6 +230,9 @@ __global__ __launch_bounds__(DK) void cbwd_prep_kernel(CBwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q4 = lane >> 4, ln = lane & 15;
   const Tio* gq = reinterpret_cast<const Tio*>(p.q);
   const Tio* gk = reinterpret_cast<const Tio*>(p.k);
+  // beta of token tid (threads below kC), loaded before the block's stores: after them it
+  // would wait for its round trip alone, the stores possibly aliasing it
+  const float beta_raw = p.beta[size_t(tid < L ? cs + tid : cs) * H + h];
   {
     float G[kC], kv[kC], qv[kC];
     float acc = 0.f;
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(DK) void cbwd_prep_kernel(CBwdParams p) {
     ob[OB::kEGC + tid] = __expf(gc);
   }
   if (tid < kC) {
-    const float b = tid < L ? p.beta[size_t(cs + tid) * H + h] : 0.f;
+    const float b = tid < L ? beta_raw : 0.f;
     sBeta[tid] = b;
     ob[OB::kBeta + tid] = b;
   }
