@@ -49,6 +49,8 @@ SEGMENT_SRC = KERNEL_SRC + (os.path.join(CSRC, "kda_segment.hip"),)
 SEGMENT_COUNTERS = os.path.join(ROOT, "profiles", "segment_cp_ultralong_256k_counters.txt")
 VARLEN_SRC = KERNEL_SRC + (os.path.join(CSRC, "kda_api.hip"),)
 VARLEN_COUNTERS = os.path.join(ROOT, "profiles", "varlen_64_counters.txt")
+BACKWARD_SRC = (os.path.join(CSRC, "kda_bwd_chunk.hip"),)
+BACKWARD_COUNTERS = os.path.join(ROOT, "profiles", "chunk_bwd_8k_counters.txt")
 
 
 def algorithmic_bytes(T, H, dk, dv, io_bytes, out_bytes, n_seqs=1):
@@ -469,7 +471,8 @@ def bench_backward(kda, wl, torch, dev, stream, steps, warmup):
     return {"workload": f"backward of prefill_8k: T={T}, H={H}, d_k=d_v={dk}, bf16 q/k/v/do, "
                         "fp32 g/beta/h0/dht, fp32 gradients",
             "tokens_per_s": T / (avg * 1e-3), "ms_per_call": avg,
-            "roofline": hbm_roofline(nbytes, avg),
+            "roofline": hbm_roofline(nbytes, avg,
+                                     counter_traffic(BACKWARD_COUNTERS, BACKWARD_SRC)),
             "algorithmic_bytes_per_call": nbytes,
             "kernels": "cbwd_fwd_kernel (forward walk: chunk-entering states) + cbwd_rev_kernel "
                        "(reverse walk: leaving-state gradients, dv, dh0) + cbwd_grad_kernel "

@@ -65,6 +65,7 @@ def test_committed_counters_match_the_current_kernels():
     assert bench.counter_traffic(bench.RAW_COUNTERS) is not None
     assert bench.counter_traffic(bench.SEGMENT_COUNTERS, bench.SEGMENT_SRC) is not None
     assert bench.counter_traffic(bench.VARLEN_COUNTERS, bench.VARLEN_SRC) is not None
+    assert bench.counter_traffic(bench.BACKWARD_COUNTERS, bench.BACKWARD_SRC) is not None
 
 
 def test_hbm_roofline_object():
