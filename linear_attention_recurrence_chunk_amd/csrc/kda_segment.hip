@@ -66,10 +66,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
   }
   const long long nc = (eos - bos + 63) / 64;
 
-  // P_j is read one step ahead into registers (16-byte pieces of the thread's rows), so its
-  // HBM latency hides under the previous step.
+  // P_j and Q_j are read one step ahead into registers (16-byte pieces of the thread's rows of
+  // P; Q in the accumulator layout of S), so their HBM latency hides under the previous step
+  // (a load of Q_j in its own step would also be ordered after that step's S_in stores).
   constexpr int kPPT = DK * DK / (4 * 256);   // f32x4 pieces of P per thread
-  f32x4 pr[kPPT];
+  f32x4 pr[kPPT], qn[NTD];
   auto fetch = [&](int j) {
     const float* pq = p.pq + ((size_t(n) * p.n_seg + j) * p.H + h) * DK * ldpq;
 #pragma unroll
@@ -77,6 +78,10 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
       const int idx = (tid + 256 * i) * 4;
       pr[i] = *reinterpret_cast<const f32x4*>(pq + size_t(idx / DK) * ldpq + idx % DK);
     }
+#pragma unroll
+    for (int t = 0; t < NTD; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qn[t][e] = pq[size_t(16 * t + 4 * q4 + e) * ldpq + DK + col];
   };
   if (p.n_seg > 0) fetch(0);
 
@@ -120,11 +125,8 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
       f32x4 Sold[NTD];
 #pragma unroll
       for (int t = 0; t < NTD; ++t) Sold[t] = S[t];
-      const float* q = p.pq + seg * DK * ldpq + DK;
 #pragma unroll
-      for (int t = 0; t < NTD; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
+      for (int t = 0; t < NTD; ++t) S[t] = qn[t];
       if (j + 1 < p.n_seg) fetch(j + 1);
 #pragma unroll
       for (int t = 0; t < NTD; ++t) {
@@ -137,11 +139,8 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanParams p) {
       Frag Sh[NS], Sl[NS];
 #pragma unroll
       for (int pp = 0; pp < NS; ++pp) Pol::from_acc_split(S, pp, Sh[pp], Sl[pp]);
-      const float* q = p.pq + seg * DK * ldpq + DK;
 #pragma unroll
-      for (int t = 0; t < NTD; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[t][e] = q[size_t(16 * t + 4 * q4 + e) * ldpq + col];
+      for (int t = 0; t < NTD; ++t) S[t] = qn[t];
       if (j + 1 < p.n_seg) fetch(j + 1);
 #pragma unroll
       for (int pp = 0; pp < NS; ++pp) {
